@@ -1,0 +1,323 @@
+"""The latent KV cache in its packed byte form, written from the format spec.
+
+The pages fix what is stored -- per-head key latents and one joint value
+latent (technical review of arXiv 2606.08382, section 5.3, eq. 12; section
+2.2, eq. 2), rotated and mixed-precision quantized (section 6.1) -- but no
+byte layout.  This module implements format v1 (tiles of 64 tokens) on its
+own, from the specification below, so that the GPU packer can be checked
+against it to the bit.
+
+fp32 / bf16 caches (elements little-endian):
+  key   [B][Hkv][T_max][r_k]
+  value [B][T_max/64][R_v][64]            (channel-major inside a tile)
+
+q43 cache (r_k = 32: channels 0-7 at 4 bits, 8-31 at 3 bits; R_v a multiple
+of 128: channels [0, R_v/4) at 4 bits, the rest at 3 bits):
+  key codes  [B][Hkv][tile] blocks of 832 B, one 64-token tile each:
+      [0,256)   hi  u32[64]: key channel c (0..7) at bits 4c..4c+3
+      [256,512) lo0 u32[64]: lo channel i at bits 3i (i<5), 16+3(i-10) (10<=i<15)
+      [512,768) lo1 u32[64]: lo channel i at bits 3(i-5) (5<=i<10),
+                             16+3(i-15) (15<=i<20)
+      [768,832) lo2 u8[64]
+      lo channel 20+k (k<4) is bits 3k..3k+2 of a 12-bit remainder R whose
+      bits 0-7 are lo2, bit 8 = lo0 bit 15, bit 9 = lo0 bit 31,
+      bit 10 = lo1 bit 15, bit 11 = lo1 bit 31.  (lo channel i = key ch 8+i.)
+  key meta   [B][Hkv][tile][64][4] fp16: scale_hi, zero_hi, scale_lo, zero_lo
+  value codes [B][tile] blocks of 26*R_v B: the 4-bit groups (32 channels
+      each) first, then the 3-bit groups; a 4-bit group is
+      [half j<2][channel c<32][4 x u32], a 3-bit group [half j][c][3 x u32];
+      token 32j+u of the tile, u < 32:
+        4-bit: word u//8, bit 16*(v%2) + 4*(v//2) with v = u%8
+        3-bit, u < 30: word u//10, bit 16*(w%2) + 3*(w//2) with w = u%10
+        3-bit, u = 30: code bit k is bit 15 of word k; u = 31: bit 31 of word k
+  value meta [B][tile][2][R_v/32][64] fp16: plane 0 scales, plane 1 zeros.
+
+Appending tokens [pos, pos+n) changes only the bits and metadata of those
+tokens; every other bit of the buffers keeps its previous value.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import hadamard, quant
+
+TT = 64
+
+
+# ------------------------------------------------------------------ sizes --
+
+def layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache):
+    """Byte sizes of the four cache buffers."""
+    assert max_tokens % TT == 0
+    nt = max_tokens // TT
+    if cache in ("f32", "bf16"):
+        es = 4 if cache == "f32" else 2
+        return dict(key=batch * n_kv_heads * max_tokens * key_rank * es,
+                    key_meta=0,
+                    value=batch * nt * value_rank * TT * es,
+                    value_meta=0)
+    assert cache == "q43" and key_rank == 32 and value_rank % 128 == 0
+    return dict(key=batch * n_kv_heads * nt * 832,
+                key_meta=batch * n_kv_heads * nt * TT * 8,
+                value=batch * nt * value_rank * 26,
+                value_meta=batch * nt * 2 * (value_rank // 32) * TT * 2)
+
+
+# ------------------------------------------------------- bit-level tables --
+
+def _value_bit(u: int, bits: int, k: int):
+    """(word, bit) of code bit k of token u (< 32) in a channel's half-run."""
+    if bits == 4:
+        v = u % 8
+        return u // 8, 16 * (v % 2) + 4 * (v // 2) + k
+    if u < 30:
+        w = u % 10
+        return u // 10, 16 * (w % 2) + 3 * (w // 2) + k
+    return k, 15 if u == 30 else 31
+
+
+def _key_lo_bit(i: int, k: int):
+    """(plane, bit) of code bit k of lo channel i (< 24); plane 0=lo0, 1=lo1,
+    2=lo2 (byte)."""
+    if i < 5:
+        return 0, 3 * i + k
+    if i < 10:
+        return 1, 3 * (i - 5) + k
+    if i < 15:
+        return 0, 16 + 3 * (i - 10) + k
+    if i < 20:
+        return 1, 16 + 3 * (i - 15) + k
+    r = 3 * (i - 20) + k           # bit of the remainder R
+    if r < 8:
+        return 2, r
+    return {8: (0, 15), 9: (0, 31), 10: (1, 15), 11: (1, 31)}[r]
+
+
+# ------------------------------------------------------------ pack/unpack --
+
+def pack_key_tiles(codes: np.ndarray) -> np.ndarray:
+    """codes uint8 [N, 64, 32] -> bytes uint8 [N, 832]."""
+    n = codes.shape[0]
+    c = codes.astype(np.uint32)
+    hi = np.zeros((n, TT), np.uint32)
+    for ch in range(8):
+        hi |= (c[:, :, ch] & 15) << (4 * ch)
+    planes = [np.zeros((n, TT), np.uint32) for _ in range(3)]
+    for i in range(24):
+        for k in range(3):
+            p, b = _key_lo_bit(i, k)
+            planes[p] |= ((c[:, :, 8 + i] >> k) & 1) << b
+    out = np.empty((n, 832), np.uint8)
+    out[:, 0:256] = hi.astype("<u4").view(np.uint8).reshape(n, 256)
+    out[:, 256:512] = planes[0].astype("<u4").view(np.uint8).reshape(n, 256)
+    out[:, 512:768] = planes[1].astype("<u4").view(np.uint8).reshape(n, 256)
+    out[:, 768:832] = planes[2].astype(np.uint8)
+    return out
+
+
+def unpack_key_tiles(blob: np.ndarray) -> np.ndarray:
+    """bytes uint8 [N, 832] -> codes uint8 [N, 64, 32]."""
+    n = blob.shape[0]
+    blob = np.ascontiguousarray(blob)
+    hi = blob[:, 0:256].copy().view("<u4").astype(np.uint32)
+    lo0 = blob[:, 256:512].copy().view("<u4").astype(np.uint32)
+    lo1 = blob[:, 512:768].copy().view("<u4").astype(np.uint32)
+    lo2 = blob[:, 768:832].astype(np.uint32)
+    planes = [lo0, lo1, lo2]
+    codes = np.zeros((n, TT, 32), np.uint32)
+    for ch in range(8):
+        codes[:, :, ch] = (hi >> (4 * ch)) & 15
+    for i in range(24):
+        for k in range(3):
+            p, b = _key_lo_bit(i, k)
+            codes[:, :, 8 + i] |= ((planes[p] >> b) & 1) << k
+    return codes.astype(np.uint8)
+
+
+def _value_regions(value_rank: int):
+    """[(first channel, bits, byte offset, words per run)] per 32-ch group."""
+    n_hi = value_rank // 4
+    regs, off = [], 0
+    for g in range(value_rank // 32):
+        bits = 4 if 32 * g < n_hi else 3
+        regs.append((32 * g, bits, off, bits))
+        off += 2 * 32 * bits * 4
+    assert off == 26 * value_rank
+    return regs
+
+
+def pack_value_tiles(codes: np.ndarray) -> np.ndarray:
+    """codes uint8 [N, 64, R_v] -> bytes uint8 [N, 26*R_v]."""
+    n, _, rv = codes.shape
+    out = np.empty((n, 26 * rv), np.uint8)
+    c = codes.astype(np.uint32)
+    for c0, bits, off, nw in _value_regions(rv):
+        words = np.zeros((n, 2, 32, nw), np.uint32)   # [tile, half, ch, word]
+        grp = c[:, :, c0:c0 + 32]                      # [tile, token, ch]
+        for j in range(2):
+            for u in range(32):
+                col = grp[:, 32 * j + u, :]            # [tile, ch]
+                for k in range(bits):
+                    wd, b = _value_bit(u, bits, k)
+                    words[:, j, :, wd] |= ((col >> k) & 1) << b
+        size = 2 * 32 * nw * 4
+        out[:, off:off + size] = words.astype("<u4").view(np.uint8).reshape(n, size)
+    return out
+
+
+def unpack_value_tiles(blob: np.ndarray, value_rank: int) -> np.ndarray:
+    """bytes uint8 [N, 26*R_v] -> codes uint8 [N, 64, R_v]."""
+    n = blob.shape[0]
+    codes = np.zeros((n, TT, value_rank), np.uint32)
+    for c0, bits, off, nw in _value_regions(value_rank):
+        size = 2 * 32 * nw * 4
+        words = np.ascontiguousarray(blob[:, off:off + size]).view("<u4")
+        words = words.astype(np.uint32).reshape(n, 2, 32, nw)
+        for j in range(2):
+            for u in range(32):
+                for k in range(bits):
+                    wd, b = _value_bit(u, bits, k)
+                    codes[:, 32 * j + u, c0:c0 + 32] |= \
+                        ((words[:, j, :, wd] >> b) & 1) << k
+    return codes.astype(np.uint8)
+
+
+# ------------------------------------------------------------ bf16 helper --
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------ cache --
+
+class Cache:
+    """Byte-exact image of the four cache buffers, with append and read-out."""
+
+    def __init__(self, batch, n_kv_heads, key_rank, value_rank, max_tokens,
+                 cache, rotate=False, fill=0):
+        self.B, self.H, self.rk, self.rv = batch, n_kv_heads, key_rank, value_rank
+        self.T, self.kind, self.rotate = max_tokens, cache, rotate
+        self.nt = max_tokens // TT
+        sz = layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache)
+        self.buf = {k: np.full(v, fill, np.uint8) for k, v in sz.items()}
+
+    @classmethod
+    def for_workload(cls, w, fill=0, batch=None, max_tokens=None):
+        return cls(w.batch if batch is None else batch, w.n_kv_heads,
+                   w.key_rank, w.value_rank,
+                   w.max_tokens if max_tokens is None else max_tokens,
+                   w.cache, w.rotate, fill)
+
+    # -- views -------------------------------------------------------------
+    def _elem_views(self):
+        dt = np.float32 if self.kind == "f32" else np.uint16
+        k = self.buf["key"].view(dt).reshape(self.B, self.H, self.T, self.rk)
+        v = self.buf["value"].view(dt).reshape(self.B, self.nt, self.rv, TT)
+        return k, v
+
+    def _q_views(self):
+        k = self.buf["key"].reshape(self.B, self.H, self.nt, 832)
+        km = self.buf["key_meta"].view(np.uint16).reshape(self.B, self.H, self.nt, TT, 4)
+        v = self.buf["value"].reshape(self.B, self.nt, 26 * self.rv)
+        vm = self.buf["value_meta"].view(np.uint16).reshape(
+            self.B, self.nt, 2, self.rv // 32, TT)
+        return k, km, v, vm
+
+    # -- append ------------------------------------------------------------
+    def append(self, z_key, z_value, pos, n):
+        """Store tokens [pos, pos+n) of every batch element.
+
+        z_key float32 [B, n, Hkv, r_k], z_value float32 [B, n, R_v]
+        (technical review, Algorithm 2 step 3: quantize and append)."""
+        assert 0 <= pos and pos + n <= self.T
+        zk = np.asarray(z_key, np.float32)
+        zv = np.asarray(z_value, np.float32)
+        if n == 0:
+            return
+        if self.kind in ("f32", "bf16"):
+            k, v = self._elem_views()
+            if self.kind == "f32":
+                kk, vv = zk, zv
+            else:
+                kk, vv = to_bf16_bits(zk), to_bf16_bits(zv)
+            k[:, :, pos:pos + n, :] = np.transpose(kk, (0, 2, 1, 3))
+            for i in range(n):
+                t = pos + i
+                v[:, t // TT, :, t % TT] = vv[:, i, :]
+            return
+        if self.rotate:
+            zk = hadamard.rotate_latent_f32(zk, self.rk // 4)
+            zv = hadamard.rotate_latent_f32(zv, self.rv // 4)
+        kq_hi = quant.quantize(zk[..., :8], 4)
+        kq_lo = quant.quantize(zk[..., 8:], 3)
+        nhi = self.rv // 4
+        vgr = zv.reshape(self.B, n, self.rv // 32, 32)
+        vq4 = quant.quantize(vgr[:, :, :nhi // 32], 4)
+        vq3 = quant.quantize(vgr[:, :, nhi // 32:], 3)
+        kcodes = np.concatenate([kq_hi[0], kq_lo[0]], axis=-1)     # [B,n,H,32]
+        vcodes = np.concatenate([vq4[0], vq3[0]], axis=2).reshape(self.B, n, self.rv)
+        vscale = np.concatenate([vq4[1], vq3[1]], axis=2)          # [B,n,G]
+        vzero = np.concatenate([vq4[2], vq3[2]], axis=2)
+        kb, km, vb, vm = self._q_views()
+        for tile in range(pos // TT, (pos + n - 1) // TT + 1):
+            t0 = tile * TT
+            lo, hi = max(pos, t0), min(pos + n, t0 + TT)
+            sl_in = slice(lo - pos, hi - pos)
+            sl_t = slice(lo - t0, hi - t0)
+            # keys
+            cur = unpack_key_tiles(kb[:, :, tile].reshape(-1, 832)).reshape(
+                self.B, self.H, TT, 32)
+            cur[:, :, sl_t, :] = np.transpose(kcodes[:, sl_in], (0, 2, 1, 3))
+            kb[:, :, tile] = pack_key_tiles(cur.reshape(-1, TT, 32)).reshape(
+                self.B, self.H, 832)
+            meta = np.stack([kq_hi[1], kq_hi[2], kq_lo[1], kq_lo[2]], axis=-1)
+            km[:, :, tile, sl_t, :] = np.transpose(meta[:, sl_in], (0, 2, 1, 3))
+            # values
+            curv = unpack_value_tiles(vb[:, tile], self.rv)
+            curv[:, sl_t, :] = vcodes[:, sl_in]
+            vb[:, tile] = pack_value_tiles(curv)
+            vm[:, tile, 0, :, sl_t] = np.transpose(vscale[:, sl_in], (0, 2, 1))
+            vm[:, tile, 1, :, sl_t] = np.transpose(vzero[:, sl_in], (0, 2, 1))
+
+    # -- read-out ----------------------------------------------------------
+    def key_latents(self, b, seq_len):
+        """Dequantized (stored, i.e. rotated if enabled) key latents
+        float64 [seq_len, Hkv, r_k] of batch element b."""
+        if self.kind in ("f32", "bf16"):
+            k, _ = self._elem_views()
+            x = k[b, :, :seq_len, :]
+            x = x if self.kind == "f32" else from_bf16_bits(x)
+            return np.transpose(x, (1, 0, 2)).astype(np.float64)
+        kb, km, _, _ = self._q_views()
+        nt = (seq_len + TT - 1) // TT
+        codes = unpack_key_tiles(kb[b, :, :nt].reshape(-1, 832)).reshape(
+            self.H, nt * TT, 32)
+        meta = km[b, :, :nt].reshape(self.H, nt * TT, 4)
+        hi = quant.dequantize(codes[..., :8], meta[..., 0], meta[..., 1])
+        lo = quant.dequantize(codes[..., 8:], meta[..., 2], meta[..., 3])
+        x = np.concatenate([hi, lo], axis=-1)[:, :seq_len]
+        return np.transpose(x, (1, 0, 2))
+
+    def value_latents(self, b, seq_len):
+        """Dequantized joint value latents float64 [seq_len, R_v]."""
+        nt = (seq_len + TT - 1) // TT
+        if self.kind in ("f32", "bf16"):
+            _, v = self._elem_views()
+            x = v[b, :nt]
+            x = x if self.kind == "f32" else from_bf16_bits(x)
+            x = np.transpose(x, (0, 2, 1)).reshape(nt * TT, self.rv)
+            return x[:seq_len].astype(np.float64)
+        _, _, vb, vm = self._q_views()
+        codes = unpack_value_tiles(vb[b, :nt], self.rv)            # [nt,64,R]
+        g = self.rv // 32
+        s = np.transpose(vm[b, :nt, 0], (0, 2, 1))                  # [nt,64,G]
+        z = np.transpose(vm[b, :nt, 1], (0, 2, 1))
+        x = quant.dequantize(codes.reshape(nt, TT, g, 32), s, z)
+        return x.reshape(nt * TT, self.rv)[:seq_len]
