@@ -1,0 +1,193 @@
+"""Python binding of libstarkv.so (argument marshalling only).
+
+Every function mirrors an entry point of include/starkv.h and passes device
+pointers (torch.Tensor.data_ptr()) and the current HIP stream through ctypes;
+all computation happens in the library's HIP kernels.  Importing this module
+does not load the library; the first call does, and raises if it is missing
+(build it with `python -m decode_attention_starkv_amd.build`).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libstarkv.so")
+
+STARKV_OK = 0
+STARKV_EINVAL = -1
+STARKV_EUNSUPPORTED = -2
+STARKV_ECAPACITY = -3
+STARKV_EWORKSPACE = -4
+STARKV_ELAUNCH = -5
+
+CACHE_F32, CACHE_BF16, CACHE_Q43 = 0, 1, 2
+DTYPES = {"f32": CACHE_F32, "bf16": CACHE_BF16, "q43": CACHE_Q43}
+BUF_KEY, BUF_KEY_META, BUF_VALUE, BUF_VALUE_META = 0, 1, 2, 3
+OP_DECODE, OP_PREFILL = 0, 1
+
+ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
+                "starkv_decode_splits", "starkv_append", "starkv_decode",
+                "starkv_prefill", "starkv_strerror")
+
+
+class StarkvConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "key_rank",
+        "value_rank", "max_tokens", "cache_dtype", "rotate", "num_splits")]
+
+
+class StarkvCache(ctypes.Structure):
+    _fields_ = [("key", ctypes.c_void_p), ("key_meta", ctypes.c_void_p),
+                ("value", ctypes.c_void_p), ("value_meta", ctypes.c_void_p)]
+
+
+class StarkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {starkv_strerror(status)} ({status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libstarkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m decode_attention_starkv_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.starkv_cache_bytes.argtypes = [P(StarkvConfig), i32]
+    lib.starkv_cache_bytes.restype = sz
+    lib.starkv_workspace_bytes.argtypes = [P(StarkvConfig), i32, i32]
+    lib.starkv_workspace_bytes.restype = sz
+    lib.starkv_decode_splits.argtypes = [P(StarkvConfig), i32]
+    lib.starkv_decode_splits.restype = i32
+    lib.starkv_append.argtypes = [P(StarkvConfig), P(StarkvCache), vp, vp, i32, i32, vp]
+    lib.starkv_append.restype = ctypes.c_int
+    lib.starkv_decode.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp, vp,
+                                  f32, vp, vp, sz, vp]
+    lib.starkv_decode.restype = ctypes.c_int
+    lib.starkv_prefill.argtypes = [P(StarkvConfig), P(StarkvCache), i32, i32, vp, i32,
+                                   vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.starkv_prefill.restype = ctypes.c_int
+    lib.starkv_strerror.argtypes = [ctypes.c_int]
+    lib.starkv_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def make_config(batch, n_q_heads, n_kv_heads, head_dim, key_rank, value_rank,
+                max_tokens, cache_dtype, rotate=False, num_splits=0) -> StarkvConfig:
+    dt = DTYPES[cache_dtype] if isinstance(cache_dtype, str) else int(cache_dtype)
+    return StarkvConfig(batch, n_q_heads, n_kv_heads, head_dim, key_rank,
+                        value_rank, max_tokens, dt, int(bool(rotate)),
+                        num_splits)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libstarkv must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def starkv_strerror(status: int) -> str:
+    return load_library().starkv_strerror(status).decode()
+
+
+def starkv_cache_bytes(cfg: StarkvConfig, buffer: int) -> int:
+    return load_library().starkv_cache_bytes(ctypes.byref(cfg), buffer)
+
+
+def starkv_workspace_bytes(cfg: StarkvConfig, op: int, n_tokens: int) -> int:
+    return load_library().starkv_workspace_bytes(ctypes.byref(cfg), op, n_tokens)
+
+
+def starkv_decode_splits(cfg: StarkvConfig, seq_len: int) -> int:
+    return load_library().starkv_decode_splits(ctypes.byref(cfg), seq_len)
+
+
+class LatentCache:
+    """The four device buffers of one layer's cache (torch uint8 tensors)."""
+
+    def __init__(self, cfg: StarkvConfig, device="cuda", fill: int | None = 0):
+        import torch
+        self.cfg = cfg
+        self.buffers = []
+        for which in range(4):
+            n = starkv_cache_bytes(cfg, which)
+            if n == 0 and which in (BUF_KEY, BUF_VALUE):
+                raise StarkvError(STARKV_EINVAL, "LatentCache")
+            t = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+            if fill is not None:
+                t.fill_(fill)
+            self.buffers.append(t)
+
+    @property
+    def struct(self) -> StarkvCache:
+        return StarkvCache(*(b.data_ptr() for b in self.buffers))
+
+    def nbytes(self) -> int:
+        return sum(starkv_cache_bytes(self.cfg, w) for w in range(4))
+
+
+def starkv_append(cfg, cache: LatentCache, z_key, z_value, pos: int,
+                  n: int | None = None, stream=None) -> None:
+    """z_key fp32 [B, n, Hkv, r_k], z_value fp32 [B, n, R_v] (device)."""
+    n = z_key.shape[1] if n is None else n
+    cs = cache.struct
+    st = load_library().starkv_append(ctypes.byref(cfg), ctypes.byref(cs),
+                                      _ptr(z_key), _ptr(z_value), pos, n,
+                                      _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_append")
+
+
+def starkv_decode(cfg, cache: LatentCache, seq_len: int, q, B_key, B_value,
+                  sm_scale: float, out, workspace, stream=None) -> None:
+    cs = cache.struct
+    st = load_library().starkv_decode(
+        ctypes.byref(cfg), ctypes.byref(cs), seq_len, _ptr(q), _ptr(B_key),
+        _ptr(B_value), sm_scale, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_decode")
+
+
+def starkv_prefill(cfg, cache: LatentCache, ctx_len: int, chunk: int, x,
+                   hidden: int, A_key, A_value, q, B_key, B_value,
+                   sm_scale: float, out, workspace, z_debug=None,
+                   stream=None) -> None:
+    cs = cache.struct
+    st = load_library().starkv_prefill(
+        ctypes.byref(cfg), ctypes.byref(cs), ctx_len, chunk, _ptr(x), hidden,
+        _ptr(A_key), _ptr(A_value), _ptr(q), _ptr(B_key), _ptr(B_value),
+        sm_scale, _ptr(out), _ptr(z_debug), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_prefill")
+
+
+def workspace(cfg, op: int, n_tokens: int, device="cuda"):
+    """Allocate a workspace tensor of the size the library asks for."""
+    import torch
+    n = starkv_workspace_bytes(cfg, op, n_tokens)
+    if n == 0:
+        raise StarkvError(STARKV_EINVAL, "starkv_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)

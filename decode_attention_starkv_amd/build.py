@@ -1,0 +1,57 @@
+"""Build libstarkv.so in-tree with hipcc for gfx950.
+
+Usage: python -m decode_attention_starkv_amd.build  (or call build()).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libstarkv.so")
+SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wno-unused-result",
+    # packed fp32 instructions are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fvisibility=hidden",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; ROCm is required to build libstarkv")
+    return path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libstarkv.so next to this file."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    fd, tmp = tempfile.mkstemp(suffix=".so", dir=HERE)
+    os.close(fd)
+    cmd = [hipcc(), *HIPCC_FLAGS, "-x", "hip", *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        os.unlink(tmp)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

@@ -1,0 +1,344 @@
+// Latent append: rotate (optional), quantize and pack new tokens into the
+// cache -- step 3 of Algorithm 2 in the technical review of arXiv 2606.08382
+// (section 6.2), with the block-wise Hadamard rotation and 4/3-bit mixed
+// precision of section 6.1 (eq. 13, eq. 14).
+//
+// Every floating-point step here is a single IEEE fp32 operation (no FMA
+// contraction) so the packed bytes are reproducible bit for bit:
+//   rotation: butterflies (a, b) -> (a + b, a - b) at strides 1, 2, 4, ...,
+//             then one multiply by the fp32 value nearest 1/sqrt(m);
+//   zero  = fp16(min) rounded toward -inf, scale = fp16((max - zero) / L)
+//           rounded toward +inf, code = clamp(rint((x - zero) / scale), 0, L).
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace starkv {
+namespace {
+
+__device__ inline uint16_t f16_bits_rn(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ inline float f16_value(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// One representable fp16 value toward -inf.
+__device__ inline uint16_t f16_step_down(uint16_t b) {
+  if ((b & 0x7FFF) == 0) return 0x8001;
+  return (b & 0x8000) ? (uint16_t)(b + 1) : (uint16_t)(b - 1);
+}
+// One representable fp16 value toward +inf.
+__device__ inline uint16_t f16_step_up(uint16_t b) {
+  if ((b & 0x7FFF) == 0) return 0x0001;
+  return (b & 0x8000) ? (uint16_t)(b - 1) : (uint16_t)(b + 1);
+}
+
+struct QParams {
+  float zf, sf;
+  uint16_t zb, sb;
+};
+
+// Zero and scale of a group from its min and max (L = 2^bits - 1).
+__device__ inline QParams group_params(float lo, float hi, float levels) {
+  QParams p;
+  p.zb = f16_bits_rn(lo);
+  if (f16_value(p.zb) > lo) p.zb = f16_step_down(p.zb);
+  p.zf = f16_value(p.zb);
+  float s32 = __fdiv_rn(__fsub_rn(hi, p.zf), levels);
+  p.sb = f16_bits_rn(s32);
+  if (f16_value(p.sb) < s32) p.sb = f16_step_up(p.sb);
+  p.sf = f16_value(p.sb);
+  return p;
+}
+
+__device__ inline uint32_t code_of(float x, const QParams& p, float levels) {
+  if (p.sf == 0.0f) return 0u;
+  float q = rintf(__fdiv_rn(__fsub_rn(x, p.zf), p.sf));
+  q = fminf(fmaxf(q, 0.0f), levels);
+  return (uint32_t)q;
+}
+
+// In-register fp32 Walsh-Hadamard transform of 8 consecutive values.
+__device__ inline void fwht8(float* x) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i & h) == 0) {
+        float a = x[i], b = x[i + h];
+        x[i] = __fadd_rn(a, b);
+        x[i + h] = __fsub_rn(a, b);
+      }
+    }
+  }
+  const float c = inv_sqrt_pow2(8);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __fmul_rn(x[i], c);
+}
+
+// ------------------------------------------------------------ F32 / BF16 --
+
+__device__ inline uint16_t bf16_bits_rn(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <bool kBf16>
+__global__ void append_plain_keys(const float* __restrict__ zk, void* key,
+                                  Dims d, int pos, int n) {
+  size_t total = (size_t)d.B * n * d.Hkv * d.rk;
+  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  int c = idx % d.rk;
+  size_t r = idx / d.rk;
+  int h = r % d.Hkv;
+  r /= d.Hkv;
+  int i = r % n;
+  int b = r / n;
+  size_t dst = (((size_t)b * d.Hkv + h) * d.Tmax + pos + i) * d.rk + c;
+  if (kBf16)
+    static_cast<uint16_t*>(key)[dst] = bf16_bits_rn(zk[idx]);
+  else
+    static_cast<float*>(key)[dst] = zk[idx];
+}
+
+template <bool kBf16>
+__global__ void append_plain_values(const float* __restrict__ zv, void* value,
+                                    Dims d, int pos, int n) {
+  size_t total = (size_t)d.B * n * d.rv;
+  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  int c = idx % d.rv;
+  size_t r = idx / d.rv;
+  int i = r % n;
+  int b = r / n;
+  int t = pos + i;
+  size_t dst = (((size_t)b * d.NT + t / kTile) * d.rv + c) * kTile + t % kTile;
+  if (kBf16)
+    static_cast<uint16_t*>(value)[dst] = bf16_bits_rn(zv[idx]);
+  else
+    static_cast<float*>(value)[dst] = zv[idx];
+}
+
+// ------------------------------------------------------------------- Q43 --
+
+// One thread per (batch, token, KV head): 32 key channels, channels 0-7 at
+// 4 bits and 8-31 at 3 bits.  The key tile format is token-major, so every
+// word written here belongs to this token alone.
+__global__ void append_q43_keys(const float* __restrict__ zk,
+                                uint8_t* __restrict__ key,
+                                uint16_t* __restrict__ kmeta, Dims d, int pos,
+                                int n) {
+  size_t total = (size_t)d.B * n * d.Hkv;
+  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  int h = idx % d.Hkv;
+  int i = (idx / d.Hkv) % n;
+  int b = idx / ((size_t)d.Hkv * n);
+  int t = pos + i;
+  int tile = t / kTile, u = t % kTile;
+
+  float x[32];
+  const float4* src = reinterpret_cast<const float4*>(zk + idx * 32);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float4 v = src[k];
+    x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+  }
+  if (d.rotate) {
+    fwht8(x); fwht8(x + 8); fwht8(x + 16); fwht8(x + 24);
+  }
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int c = 1; c < 8; ++c) { lo = fminf(lo, x[c]); hi = fmaxf(hi, x[c]); }
+  QParams ph = group_params(lo, hi, 15.0f);
+  lo = x[8]; hi = x[8];
+#pragma unroll
+  for (int c = 9; c < 32; ++c) { lo = fminf(lo, x[c]); hi = fmaxf(hi, x[c]); }
+  QParams pl = group_params(lo, hi, 7.0f);
+
+  uint32_t whi = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) whi |= code_of(x[c], ph, 15.0f) << (4 * c);
+  uint32_t q[24];
+#pragma unroll
+  for (int c = 0; c < 24; ++c) q[c] = code_of(x[8 + c], pl, 7.0f);
+  // lo channel i: i<5 -> lo0 bit 3i; 5<=i<10 -> lo1 bit 3(i-5);
+  // 10<=i<15 -> lo0 bit 16+3(i-10); 15<=i<20 -> lo1 bit 16+3(i-15);
+  // 20<=i<24 -> remainder R bit 3(i-20): R[0:8] = lo2,
+  // R8 = lo0 b15, R9 = lo0 b31, R10 = lo1 b15, R11 = lo1 b31.
+  uint32_t lo0 = 0, lo1 = 0;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    lo0 |= q[k] << (3 * k);
+    lo1 |= q[5 + k] << (3 * k);
+    lo0 |= q[10 + k] << (16 + 3 * k);
+    lo1 |= q[15 + k] << (16 + 3 * k);
+  }
+  uint32_t R = q[20] | (q[21] << 3) | (q[22] << 6) | (q[23] << 9);
+  lo0 |= ((R >> 8) & 1u) << 15;
+  lo0 |= ((R >> 9) & 1u) << 31;
+  lo1 |= ((R >> 10) & 1u) << 15;
+  lo1 |= ((R >> 11) & 1u) << 31;
+
+  size_t blk = ((size_t)b * d.Hkv + h) * d.NT + tile;
+  uint8_t* kb = key + blk * kKeyBlock;
+  reinterpret_cast<uint32_t*>(kb)[u] = whi;
+  reinterpret_cast<uint32_t*>(kb + 256)[u] = lo0;
+  reinterpret_cast<uint32_t*>(kb + 512)[u] = lo1;
+  kb[768 + u] = (uint8_t)(R & 0xFFu);
+  uint16_t* km = kmeta + (blk * kTile + u) * 4;
+  km[0] = ph.sb; km[1] = ph.zb; km[2] = pl.sb; km[3] = pl.zb;
+}
+
+// One workgroup (4 waves) per (batch, touched tile, block of 256 value
+// channels).  Phase 1: each wave takes tokens u = wave, wave+4, ...: lane l
+// holds channels l + 64r (r < 4), rotates them (butterflies by lane shuffles
+// for strides < 64 and in-register for 64 and 128), quantizes per 32-channel
+// group (reduction over half-waves) and writes codes to LDS.  Phase 2: thread
+// t packs channel t's runs of 32 tokens, merging with the previous words
+// where the token range covers a run only partly.
+__global__ __launch_bounds__(256) void append_q43_values(
+    const float* __restrict__ zv, uint8_t* __restrict__ value,
+    uint16_t* __restrict__ vmeta, Dims d, int pos, int n) {
+  __shared__ uint8_t codes[kTile][256];
+  const int cb = blockIdx.x;
+  const int tile = pos / kTile + blockIdx.y;
+  const int b = blockIdx.z;
+  const int t0 = tile * kTile;
+  const int ulo = max(pos, t0) - t0;
+  const int uhi = min(pos + n, t0 + kTile) - t0;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int n_hi = d.rv / 4;
+  const int G = d.rv / 32;
+  const int m = pow2_divisor(n_hi);  // rotation block size
+  const float rc = inv_sqrt_pow2(m);
+  uint16_t* vm = vmeta + ((size_t)b * d.NT + tile) * 2 * G * kTile;
+
+  for (int u = ulo + wave; u < uhi; u += 4) {
+    const float* src = zv + ((size_t)b * n + (t0 + u - pos)) * d.rv + cb * 256;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = src[lane + 64 * r];
+    if (d.rotate) {
+      for (int h = 1; h < m && h < 64; h <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = __shfl_xor(x[r], h);
+          x[r] = (lane & h) ? __fsub_rn(p, x[r]) : __fadd_rn(x[r], p);
+        }
+      }
+      if (m > 64) {  // stride 64: registers (0,1), (2,3)
+        float a0 = x[0], b0 = x[1], a1 = x[2], b1 = x[3];
+        x[0] = __fadd_rn(a0, b0); x[1] = __fsub_rn(a0, b0);
+        x[2] = __fadd_rn(a1, b1); x[3] = __fsub_rn(a1, b1);
+      }
+      if (m > 128) {  // stride 128: registers (0,2), (1,3)
+        float a0 = x[0], b0 = x[2], a1 = x[1], b1 = x[3];
+        x[0] = __fadd_rn(a0, b0); x[2] = __fsub_rn(a0, b0);
+        x[1] = __fadd_rn(a1, b1); x[3] = __fsub_rn(a1, b1);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = __fmul_rn(x[r], rc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float lo = x[r], hi = x[r];
+#pragma unroll
+      for (int s = 1; s < 32; s <<= 1) {
+        lo = fminf(lo, __shfl_xor(lo, s));
+        hi = fmaxf(hi, __shfl_xor(hi, s));
+      }
+      int ch = cb * 256 + lane + 64 * r;
+      float levels = ch < n_hi ? 15.0f : 7.0f;
+      QParams p = group_params(lo, hi, levels);
+      codes[u][lane + 64 * r] = (uint8_t)code_of(x[r], p, levels);
+      if ((lane & 31) == 0) {
+        int g = ch / 32;
+        vm[(size_t)g * kTile + u] = p.sb;
+        vm[(size_t)(G + g) * kTile + u] = p.zb;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int ch = cb * 256 + threadIdx.x;
+  const int g = ch / 32, c = ch % 32;
+  const int NH = n_hi / 32;
+  const bool four = g < NH;
+  uint8_t* vt = value + ((size_t)b * d.NT + tile) * 26 * d.rv;
+  uint8_t* grp = four ? vt + (size_t)g * 1024 : vt + (size_t)NH * 1024 + (size_t)(g - NH) * 768;
+  for (int j = 0; j < 2; ++j) {
+    int a = max(ulo - 32 * j, 0), e = min(uhi - 32 * j, 32);
+    if (a >= e) continue;
+    uint32_t w[4] = {0, 0, 0, 0}, mask[4] = {0, 0, 0, 0};
+    if (four) {
+      for (int uu = a; uu < e; ++uu) {
+        uint32_t k = codes[32 * j + uu][threadIdx.x];
+        int v = uu % 8;
+        int bit = 16 * (v % 2) + 4 * (v / 2);
+        w[uu / 8] |= k << bit;
+        mask[uu / 8] |= 0xFu << bit;
+      }
+    } else {
+      for (int uu = a; uu < e; ++uu) {
+        uint32_t k = codes[32 * j + uu][threadIdx.x];
+        if (uu < 30) {
+          int ww = uu % 10;
+          int bit = 16 * (ww % 2) + 3 * (ww / 2);
+          w[uu / 10] |= k << bit;
+          mask[uu / 10] |= 0x7u << bit;
+        } else {
+          int bit = uu == 30 ? 15 : 31;
+#pragma unroll
+          for (int kk = 0; kk < 3; ++kk) {
+            w[kk] |= ((k >> kk) & 1u) << bit;
+            mask[kk] |= 1u << bit;
+          }
+        }
+      }
+    }
+    const int nw = four ? 4 : 3;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(grp + (size_t)(32 * j + c) * nw * 4);
+    bool whole = (a == 0 && e == 32);
+    for (int k = 0; k < nw; ++k) {
+      uint32_t val = whole ? w[k] : ((dst[k] & ~mask[k]) | w[k]);
+      dst[k] = val;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const Dims& d, const starkv_cache& cache,
+                         const float* zk, const float* zv, int pos, int n,
+                         hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int T = 256;
+  if (d.dtype == STARKV_CACHE_Q43) {
+    size_t nk = (size_t)d.B * n * d.Hkv;
+    append_q43_keys<<<(unsigned)((nk + T - 1) / T), T, 0, s>>>(
+        zk, static_cast<uint8_t*>(cache.key),
+        static_cast<uint16_t*>(cache.key_meta), d, pos, n);
+    int tiles = (pos + n - 1) / kTile - pos / kTile + 1;
+    dim3 grid(d.rv / 256, tiles, d.B);
+    append_q43_values<<<grid, 256, 0, s>>>(
+        zv, static_cast<uint8_t*>(cache.value),
+        static_cast<uint16_t*>(cache.value_meta), d, pos, n);
+  } else {
+    bool bf = d.dtype == STARKV_CACHE_BF16;
+    size_t nk = (size_t)d.B * n * d.Hkv * d.rk;
+    size_t nv = (size_t)d.B * n * d.rv;
+    if (bf) {
+      append_plain_keys<true><<<(unsigned)((nk + T - 1) / T), T, 0, s>>>(zk, cache.key, d, pos, n);
+      append_plain_values<true><<<(unsigned)((nv + T - 1) / T), T, 0, s>>>(zv, cache.value, d, pos, n);
+    } else {
+      append_plain_keys<false><<<(unsigned)((nk + T - 1) / T), T, 0, s>>>(zk, cache.key, d, pos, n);
+      append_plain_values<false><<<(unsigned)((nv + T - 1) / T), T, 0, s>>>(zv, cache.value, d, pos, n);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace starkv

@@ -266,25 +266,37 @@ class Cache:
         vscale = np.concatenate([vq4[1], vq3[1]], axis=2)          # [B,n,G]
         vzero = np.concatenate([vq4[2], vq3[2]], axis=2)
         kb, km, vb, vm = self._q_views()
-        for tile in range(pos // TT, (pos + n - 1) // TT + 1):
-            t0 = tile * TT
-            lo, hi = max(pos, t0), min(pos + n, t0 + TT)
-            sl_in = slice(lo - pos, hi - pos)
-            sl_t = slice(lo - t0, hi - t0)
-            # keys
-            cur = unpack_key_tiles(kb[:, :, tile].reshape(-1, 832)).reshape(
-                self.B, self.H, TT, 32)
-            cur[:, :, sl_t, :] = np.transpose(kcodes[:, sl_in], (0, 2, 1, 3))
-            kb[:, :, tile] = pack_key_tiles(cur.reshape(-1, TT, 32)).reshape(
-                self.B, self.H, 832)
-            meta = np.stack([kq_hi[1], kq_hi[2], kq_lo[1], kq_lo[2]], axis=-1)
-            km[:, :, tile, sl_t, :] = np.transpose(meta[:, sl_in], (0, 2, 1, 3))
-            # values
-            curv = unpack_value_tiles(vb[:, tile], self.rv)
-            curv[:, sl_t, :] = vcodes[:, sl_in]
-            vb[:, tile] = pack_value_tiles(curv)
-            vm[:, tile, 0, :, sl_t] = np.transpose(vscale[:, sl_in], (0, 2, 1))
-            vm[:, tile, 1, :, sl_t] = np.transpose(vzero[:, sl_in], (0, 2, 1))
+        ta, tb = pos // TT, (pos + n - 1) // TT + 1     # touched tiles
+        nt = tb - ta
+        # token-in-window index of every stored token of the touched tiles
+        win = np.arange(ta * TT, tb * TT) - pos          # [nt*64]
+        sel = (win >= 0) & (win < n)
+        src = np.clip(win, 0, max(n - 1, 0))
+        # keys: unpack the touched tiles, overwrite the appended tokens, repack
+        cur = unpack_key_tiles(kb[:, :, ta:tb].reshape(-1, 832)).reshape(
+            self.B, self.H, nt * TT, 32)
+        newk = np.transpose(kcodes, (0, 2, 1, 3))[:, :, src]
+        cur = np.where(sel[None, None, :, None], newk, cur)
+        kb[:, :, ta:tb] = pack_key_tiles(cur.reshape(-1, TT, 32)).reshape(
+            self.B, self.H, nt, 832)
+        meta = np.stack([kq_hi[1], kq_hi[2], kq_lo[1], kq_lo[2]], axis=-1)
+        oldm = km[:, :, ta:tb].reshape(self.B, self.H, nt * TT, 4)
+        newm = np.transpose(meta, (0, 2, 1, 3))[:, :, src]
+        km[:, :, ta:tb] = np.where(sel[None, None, :, None], newm, oldm).reshape(
+            self.B, self.H, nt, TT, 4)
+        # values
+        curv = unpack_value_tiles(vb[:, ta:tb].reshape(-1, 26 * self.rv),
+                                  self.rv).reshape(self.B, nt * TT, self.rv)
+        curv = np.where(sel[None, :, None], vcodes[:, src], curv)
+        vb[:, ta:tb] = pack_value_tiles(curv.reshape(-1, TT, self.rv)).reshape(
+            self.B, nt, 26 * self.rv)
+        for plane, arr in ((0, vscale), (1, vzero)):
+            old_ = np.transpose(vm[:, ta:tb, plane], (0, 2, 1, 3)).reshape(
+                self.B, -1, nt * TT)                       # [B, G, nt*64]
+            new_ = np.transpose(arr, (0, 2, 1))[:, :, src]
+            upd = np.where(sel[None, None, :], new_, old_)
+            vm[:, ta:tb, plane] = np.transpose(
+                upd.reshape(self.B, -1, nt, TT), (0, 2, 1, 3))
 
     # -- read-out ----------------------------------------------------------
     def key_latents(self, b, seq_len):
