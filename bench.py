@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of latent-KV decode attention on one MI355X.
+
+One step = one decode step of the whole hot path for a batch of sequences:
+starkv_append of the step's new token (quantize + pack, n = 1 per sequence)
+followed by starkv_decode over seq_len cached tokens (query projection, split
+scores + online softmax + MFMA P.Z_v, split merge, value up-projection).
+
+Default workload: B = 16 sequences, T = 32768 cached tokens, LLaMA-2-7B-shaped
+(32 heads, d_h 128, key rank 32 per head, joint value rank 1024), 4/3-bit
+Hadamard-rotated latent cache -- 1216 bytes per token, 637.5 MB per step.
+Inputs are seeded synthetic tensors already resident in HBM; before each
+timed step a 1 GiB buffer is written so the 256 MB Infinity Cache and the L2s
+hold none of the cache (as when the other layers of a model run in between).
+
+Prints one JSON line (metric, value = tokens attended per second = B*T / step
+time, roofline of the split kernel measured with HIP events on its launch
+stream, CPU oracle baseline on a bounded sample).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("latent-KV decode attention: tokens attended/s and % HBM roofline "
+          "at B=16, T=32K")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+COUNTERS = os.path.join(ROOT, "profiles", "split_kernel_l2_q43_counters.json")
+DECODE_SRC = os.path.join(ROOT, "decode_attention_starkv_amd", "csrc", "decode.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="l2_q43")
+    p.add_argument("--batch", type=int, default=0)
+    p.add_argument("--seq-len", type=int, default=0)
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    return p.parse_args()
+
+
+def algorithmic_bytes(w, cfg, seq_len, sk):
+    """Cache bytes one decode call must read (codes + fp16 scale/zero) for
+    seq_len tokens of every sequence, and the factor bytes."""
+    per_token = sum(sk.starkv_cache_bytes(cfg, i) for i in range(4)) / (
+        cfg.batch * cfg.max_tokens)
+    cache = per_token * cfg.batch * seq_len
+    es = 4 if w.cache == "f32" else 2
+    factors = (w.n_kv_heads * w.head_dim * w.key_rank
+               + w.n_kv_heads * w.head_dim * w.value_rank) * es
+    return cache, factors
+
+
+def fill_cache(w, cfg, cache, seq_len, sk, torch):
+    """Append seq_len synthetic tokens to every sequence, on the GPU."""
+    import synth
+    kstd = torch.tensor(synth.key_channel_std(w), dtype=torch.float32, device="cuda")
+    vstd = torch.tensor(synth.value_channel_std(w), dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    chunk = 4096
+    for p0 in range(0, seq_len, chunk):
+        n = min(chunk, seq_len - p0)
+        zk = torch.randn((cfg.batch, n, w.n_kv_heads, w.key_rank), device="cuda",
+                         generator=gen) * kstd
+        zv = torch.randn((cfg.batch, n, w.value_rank), device="cuda",
+                         generator=gen) * vstd
+        sk.starkv_append(cfg, cache, zk.contiguous(), zv.contiguous(), p0, n)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(w, seq_len):
+    """The oracle, as it stands, on one sequence of the workload: decode of
+    all heads over seq_len tokens (its cache build is setup, not timed)."""
+    import numpy as np
+    import synth
+    from oracle import attention as oa
+    from oracle import cache as oc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    w1 = w.replace(batch=1)
+    c = oc.Cache.for_workload(w1, max_tokens=((seq_len + 63) // 64) * 64)
+    for p0 in range(0, seq_len, 8192):
+        n = min(8192, seq_len - p0)
+        zk, zv = synth.batch_latents(w1, p0, n)
+        c.append(zk, zv, p0, n)
+    bk, bv = synth.factors(w1)
+    q = synth.queries(w1)
+    t0 = time.perf_counter()
+    out = oa.decode(c, seq_len, q, bk, bv, 1 / math.sqrt(w.head_dim),
+                    w.n_q_heads, w.rotate)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    return {"value": seq_len / dt, "unit": "tokens attended/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"1 sequence x {seq_len} tokens x {w.n_q_heads} heads "
+                      f"(fp64 numpy, {dt:.1f} s)"}
+
+
+def traffic_from_counters():
+    """HBM bytes per split-kernel launch from committed rocprofv3 counters,
+    or None if the kernel source changed since they were taken."""
+    if not os.path.exists(COUNTERS):
+        return None
+    rec = json.load(open(COUNTERS))
+    src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("decode_hip_sha256") != src:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                          "--gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import decode_attention_starkv_amd as sk
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.batch:
+        w = w.replace(batch=args.batch)
+    seq_len = args.seq_len or w.seq_len
+    cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                         w.key_rank, w.value_rank, ((seq_len + 63) // 64) * 64,
+                         w.cache, w.rotate, args.splits)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# workload {w.name} B={w.batch} T={seq_len} splits="
+          f"{sk.starkv_decode_splits(cfg, seq_len)}", file=sys.stderr, flush=True)
+
+    cache = sk.LatentCache(cfg)
+    fill_cache(w, cfg, cache, seq_len, sk, torch)
+    bk, bv = synth.factors(w)
+    dt = torch.float32 if w.cache == "f32" else torch.bfloat16
+    bk_t = torch.from_numpy(bk).to(dev, dt)
+    bv_t = torch.from_numpy(bv).to(dev, dt)
+    q_t = torch.from_numpy(synth.queries(w)).to(dev, dt)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev)
+    ws = sk.workspace(cfg, sk.OP_DECODE, seq_len)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 1)
+    new_k = (torch.randn((w.batch, 1, w.n_kv_heads, w.key_rank), device=dev,
+                         generator=gen)
+             * torch.tensor(synth.key_channel_std(w), dtype=torch.float32, device=dev))
+    new_v = (torch.randn((w.batch, 1, w.value_rank), device=dev, generator=gen)
+             * torch.tensor(synth.value_channel_std(w), dtype=torch.float32, device=dev))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(w.head_dim)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    for e in ev:
+        e.record()          # create the events before handing them out
+    torch.cuda.synchronize()
+
+    def step(timed):
+        if not args.no_flush:
+            flush.fill_(step.i & 0xFF)
+        step.i += 1
+        ev[5].record()
+        sk.starkv_append(cfg, cache, new_k, new_v, seq_len - 1, 1)
+        sk.starkv_decode_profiled(cfg, cache, seq_len, q_t, bk_t, bv_t, scale,
+                                  out, ws, ev[:5])
+        ev[6].record()
+        if timed:
+            torch.cuda.synchronize()
+            return (ev[5].elapsed_time(ev[6]),
+                    [ev[i].elapsed_time(ev[i + 1]) for i in range(4)],
+                    ev[5].elapsed_time(ev[0]))
+        return None
+    step.i = 0
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    step_ms, kern_ms, app_ms = [], [[], [], [], []], []
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        t, k, a = step(True)
+        step_ms.append(t)
+        app_ms.append(a)
+        for j in range(4):
+            kern_ms[j].append(k[j])
+        print(f"# step {i} {t:.4f} ms (split {k[1]:.4f} ms)", file=sys.stderr,
+              flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    assert torch.isfinite(out).all()
+
+    mean = lambda v: sum(v) / len(v)
+    ms = mean(step_ms)
+    split_ms = mean(kern_ms[1])
+    cache_bytes, factor_bytes = algorithmic_bytes(w, cfg, seq_len, sk)
+    achieved = cache_bytes / (split_ms * 1e-3) / 1e9
+    tokens = w.batch * seq_len
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens attended/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} decode", "batch": w.batch,
+                   "seq_len": seq_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "key_rank": w.key_rank, "value_rank": w.value_rank,
+                   "cache": w.cache + (" rotated" if w.rotate else ""),
+                   "splits": sk.starkv_decode_splits(cfg, seq_len),
+                   "cache_flushed_before_step": not args.no_flush},
+        "roofline": {"bound": "hbm", "kernel": "split_kernel",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_counters()},
+        "step_hbm_frac": (cache_bytes + factor_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms": {"append": mean(app_ms), "qproj": mean(kern_ms[0]),
+                       "split": split_ms, "merge": mean(kern_ms[2]),
+                       "vproj": mean(kern_ms[3])},
+        "algorithmic_bytes": {"cache": cache_bytes, "factors": factor_bytes},
+        "wall_s_timed_loop": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, min(seq_len, args.cpu_sample_tokens))
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -29,7 +29,7 @@ OP_DECODE, OP_PREFILL = 0, 1
 
 ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_decode_splits", "starkv_append", "starkv_decode",
-                "starkv_prefill", "starkv_strerror")
+                "starkv_decode_profiled", "starkv_prefill", "starkv_strerror")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -75,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.starkv_decode.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp, vp,
                                   f32, vp, vp, sz, vp]
     lib.starkv_decode.restype = ctypes.c_int
+    lib.starkv_decode_profiled.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp,
+                                           vp, f32, vp, vp, sz, vp, P(vp)]
+    lib.starkv_decode_profiled.restype = ctypes.c_int
     lib.starkv_prefill.argtypes = [P(StarkvConfig), P(StarkvCache), i32, i32, vp, i32,
                                    vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     lib.starkv_prefill.restype = ctypes.c_int
@@ -168,6 +171,21 @@ def starkv_decode(cfg, cache: LatentCache, seq_len: int, q, B_key, B_value,
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != STARKV_OK:
         raise StarkvError(st, "starkv_decode")
+
+
+def starkv_decode_profiled(cfg, cache: LatentCache, seq_len: int, q, B_key,
+                           B_value, sm_scale: float, out, workspace, events,
+                           stream=None) -> None:
+    """events: five torch.cuda.Event(enable_timing=True) recorded by the
+    library before/after its four kernels on the launch stream."""
+    handles = (ctypes.c_void_p * 5)(*(e.cuda_event for e in events))
+    cs = cache.struct
+    st = load_library().starkv_decode_profiled(
+        ctypes.byref(cfg), ctypes.byref(cs), seq_len, _ptr(q), _ptr(B_key),
+        _ptr(B_value), sm_scale, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), handles)
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_decode_profiled")
 
 
 def starkv_prefill(cfg, cache: LatentCache, ctx_len: int, chunk: int, x,

@@ -75,7 +75,7 @@ int choose_splits(const starkv_config& c, int seq_len) {
   const int n_tiles = (seq_len + kTile - 1) / kTile;
   int s = c.num_splits > 0 ? c.num_splits
                            : (kTargetGroups + c.batch - 1) / c.batch;
-  s = std::max(1, std::min(s, n_tiles));
+  s = std::max(1, std::min(std::min(s, n_tiles), kMaxSplits));
   const int tps = (n_tiles + s - 1) / s;
   return (n_tiles + tps - 1) / tps;  // no empty splits
 }
@@ -123,10 +123,11 @@ int starkv_append(const starkv_config* cfg, const starkv_cache* cache,
   return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
 }
 
-int starkv_decode(const starkv_config* cfg, const starkv_cache* cache,
-                  int32_t seq_len, const void* q, const void* B_key,
-                  const void* B_value, float sm_scale, float* out,
-                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+static int decode_impl(const starkv_config* cfg, const starkv_cache* cache,
+                       int32_t seq_len, const void* q, const void* B_key,
+                       const void* B_value, float sm_scale, float* out,
+                       void* workspace, size_t ws_bytes, hipStream_t stream,
+                       hipEvent_t* events) {
   int st = check_config(cfg);
   if (st != STARKV_OK) return st;
   if ((st = check_cache(cfg, cache)) != STARKV_OK) return st;
@@ -140,8 +141,27 @@ int starkv_decode(const starkv_config* cfg, const starkv_cache* cache,
   if (!workspace || !aligned16(workspace) || ws_bytes < lay.total)
     return STARKV_EWORKSPACE;
   hipError_t e = launch_decode(d, *cache, seq_len, q, B_key, B_value, sm_scale,
-                               out, static_cast<char*>(workspace), lay, stream);
+                               out, static_cast<char*>(workspace), lay, stream,
+                               events);
   return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
+}
+
+int starkv_decode(const starkv_config* cfg, const starkv_cache* cache,
+                  int32_t seq_len, const void* q, const void* B_key,
+                  const void* B_value, float sm_scale, float* out,
+                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(cfg, cache, seq_len, q, B_key, B_value, sm_scale, out,
+                     workspace, ws_bytes, stream, nullptr);
+}
+
+int starkv_decode_profiled(const starkv_config* cfg, const starkv_cache* cache,
+                           int32_t seq_len, const void* q, const void* B_key,
+                           const void* B_value, float sm_scale, float* out,
+                           void* workspace, size_t ws_bytes,
+                           hipStream_t stream, hipEvent_t* events) {
+  if (!events) return STARKV_EINVAL;
+  return decode_impl(cfg, cache, seq_len, q, B_key, B_value, sm_scale, out,
+                     workspace, ws_bytes, stream, events);
 }
 
 int starkv_prefill(const starkv_config* cfg, const starkv_cache* cache,

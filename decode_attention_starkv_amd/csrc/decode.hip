@@ -75,171 +75,161 @@ __device__ inline void lds_barrier() {
 
 // ------------------------------------------------------------------ qproj --
 
+// One workgroup per (b, h): q is staged in LDS, 256 threads split the d_h
+// contraction into chunks, the chunks are summed, then wave 0 rotates,
+// scales and packs the record.
 template <int FMT>
-__global__ __launch_bounds__(64) void qproj_kernel(const void* __restrict__ q,
-                                                   const void* __restrict__ bk,
-                                                   Dims d, float qscale,
-                                                   void* __restrict__ qt) {
+__global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
+                                                    const void* __restrict__ bk,
+                                                    Dims d, float qscale,
+                                                    void* __restrict__ qt) {
+  __shared__ float qs[256];
+  __shared__ float part[256];
+  __shared__ _Float16 sq[32];
   const int bh = blockIdx.x;
   const int b = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
+  if (t < d.dh) {
+    const size_t qi = ((size_t)b * d.Hq + h) * d.dh + t;
+    qs[t] = FMT == STARKV_CACHE_F32 ? static_cast<const float*>(q)[qi]
+                                    : bf16v(static_cast<const uint16_t*>(q)[qi]);
+  }
+  __syncthreads();
+  const int rkp = d.rk <= 32 ? 32 : 64;
+  const int c = t % rkp, chunk = t / rkp, nch = 256 / rkp;
+  const int klen = (d.dh + nch - 1) / nch;
   float acc = 0.0f;
-  if (lane < d.rk) {
-    for (int k = 0; k < d.dh; ++k) {
-      float qv, bv;
-      size_t qi = ((size_t)b * d.Hq + h) * d.dh + k;
-      size_t bi = ((size_t)g * d.dh + k) * d.rk + lane;
-      if (FMT == STARKV_CACHE_F32) {
-        qv = static_cast<const float*>(q)[qi];
-        bv = static_cast<const float*>(bk)[bi];
-      } else {
-        qv = bf16v(static_cast<const uint16_t*>(q)[qi]);
-        bv = bf16v(static_cast<const uint16_t*>(bk)[bi]);
-      }
-      acc = fmaf(qv, bv, acc);
+  if (c < d.rk) {
+    const int k0 = chunk * klen, k1 = min(d.dh, k0 + klen);
+    for (int k = k0; k < k1; ++k) {
+      const size_t bi = ((size_t)g * d.dh + k) * d.rk + c;
+      const float bv = FMT == STARKV_CACHE_F32 ? static_cast<const float*>(bk)[bi]
+                                               : bf16v(static_cast<const uint16_t*>(bk)[bi]);
+      acc = fmaf(qs[k], bv, acc);
     }
   }
+  part[t] = acc;
+  __syncthreads();
+  if (t >= 64) return;
+  float v = 0.0f;
+  if (t < rkp)
+    for (int ch = 0; ch < nch; ++ch) v += part[ch * rkp + t];
   if (FMT == STARKV_CACHE_Q43 && d.rotate) {
     // stored key latents are rotated by blocks of 8 (hi block 0-7, lo
     // blocks 8-15, 16-23, 24-31): rotate q~ the same way (eq. 13).
 #pragma unroll
     for (int s = 1; s < 8; s <<= 1) {
-      float p = __shfl_xor(acc, s);
-      acc = (lane & s) ? p - acc : acc + p;
+      float p = __shfl_xor(v, s);
+      v = (t & s) ? p - v : v + p;
     }
-    acc *= inv_sqrt_pow2(8);
+    v *= inv_sqrt_pow2(8);
   }
-  acc *= qscale;
+  v *= qscale;
   if (FMT != STARKV_CACHE_Q43) {
-    if (lane < d.rk) static_cast<float*>(qt)[(size_t)bh * kPlainRec + lane] = acc;
+    if (t < d.rk) static_cast<float*>(qt)[(size_t)bh * kPlainRec + t] = v;
     return;
   }
-  __shared__ _Float16 sq[32];
-  if (lane < 32) sq[lane] = (_Float16)acc;
-  __syncthreads();
+  if (t < 32) sq[t] = (_Float16)v;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
   uint32_t* rec = static_cast<uint32_t*>(qt) + (size_t)bh * kQ43Rec;
-  if (lane < 16) {
-    int a, c;  // channel pair (a -> low half, c -> high half)
-    if (lane < 4) { a = lane; c = lane + 4; }
-    else if (lane < 9) { a = 8 + (lane - 4); c = 8 + 10 + (lane - 4); }
-    else if (lane < 14) { a = 8 + 5 + (lane - 9); c = 8 + 15 + (lane - 9); }
-    else if (lane == 14) { a = 8 + 20; c = 8 + 22; }
-    else { a = 8 + 21; c = 8 + 23; }
-    uint32_t lo = __builtin_bit_cast(uint16_t, sq[a]);
-    uint32_t hi = __builtin_bit_cast(uint16_t, sq[c]);
-    rec[lane] = lo | (hi << 16);
-  } else if (lane == 16) {
+  if (t < 16) {
+    int a, cc;  // channel pair (a -> low half, cc -> high half)
+    if (t < 4) { a = t; cc = t + 4; }
+    else if (t < 9) { a = 8 + (t - 4); cc = 8 + 10 + (t - 4); }
+    else if (t < 14) { a = 8 + 5 + (t - 9); cc = 8 + 15 + (t - 9); }
+    else if (t == 14) { a = 8 + 20; cc = 8 + 22; }
+    else { a = 8 + 21; cc = 8 + 23; }
+    const uint32_t lo = __builtin_bit_cast(uint16_t, sq[a]);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, sq[cc]);
+    rec[t] = lo | (hi << 16);
+  } else if (t == 16) {
     float s = 0.0f;
-    for (int c = 0; c < 8; ++c) s += (float)sq[c];
+    for (int k = 0; k < 8; ++k) s += (float)sq[k];
     rec[16] = __builtin_bit_cast(uint32_t, s);
-  } else if (lane == 17) {
+  } else if (t == 17) {
     float s = 0.0f;
-    for (int c = 8; c < 32; ++c) s += (float)sq[c];
+    for (int k = 8; k < 32; ++k) s += (float)sq[k];
     rec[17] = __builtin_bit_cast(uint32_t, s);
   }
 }
 
-// ------------------------------------------------------------ key scores --
+// ---------------------------------------------------- fp32 / bf16 split --
 
-// Scores of one 64-token tile for the G query heads of KV head kh; lane = token.
+// Scores of one 64-token tile for the G query heads of KV head kh from an
+// unquantized cache; lane = token, query records read from LDS.
 template <int FMT, int G>
-__device__ inline void score_tile(const SplitArgs& a, int b, int kh, int tile,
-                                  int lane, float* sc) {
+__device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
+                                        int b, int kh, int tile, int lane,
+                                        float* sc) {
   const Dims& d = a.d;
-  if constexpr (FMT == STARKV_CACHE_Q43) {
-    const size_t blk = ((size_t)b * d.Hkv + kh) * d.NT + tile;
-    const uint8_t* kb = static_cast<const uint8_t*>(a.key) + blk * kKeyBlock;
-    const uint32_t whi = reinterpret_cast<const uint32_t*>(kb)[lane];
-    const uint32_t w0 = reinterpret_cast<const uint32_t*>(kb + 256)[lane];
-    const uint32_t w1 = reinterpret_cast<const uint32_t*>(kb + 512)[lane];
-    const uint32_t r8 = kb[768 + lane];
-    const uint2 mt = reinterpret_cast<const uint2*>(a.kmeta)[blk * kTile + lane];
-    const float s_hi = f16v(mt.x & 0xFFFFu) * kTwo24, z_hi = f16v(mt.x >> 16);
-    const float s_lo = f16v(mt.y & 0xFFFFu) * kTwo24, z_lo = f16v(mt.y >> 16);
-    uint32_t ph[4], pl[12];
+  const size_t row = (((size_t)b * d.Hkv + kh) * d.Tmax + (size_t)tile * kTile + lane) * d.rk;
+  const float* recs = qrec + (size_t)kh * G * kPlainRec;
+  float acc[G];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ph[i] = (whi >> (4 * i)) & 0x000F000Fu;
+  for (int j = 0; j < G; ++j) acc[j] = 0.0f;
+  for (int c0 = 0; c0 < d.rk; c0 += 8) {
+    float z[8];
+    if constexpr (FMT == STARKV_CACHE_F32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.key) + row + c0);
+      const float4 u = p[0], v = p[1];
+      z[0] = u.x; z[1] = u.y; z[2] = u.z; z[3] = u.w;
+      z[4] = v.x; z[5] = v.y; z[6] = v.z; z[7] = v.w;
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.key) + row + c0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      pl[i] = (w0 >> (3 * i)) & 0x00070007u;
-      pl[5 + i] = (w1 >> (3 * i)) & 0x00070007u;
+      for (int e = 0; e < 4; ++e) {
+        z[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+        z[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+      }
     }
-    const uint32_t R = r8 | (((w0 >> 15) & 1u) << 8) | ((w0 >> 31) << 9) |
-                       (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
-    pl[10] = (R & 7u) | (((R >> 6) & 7u) << 16);
-    pl[11] = ((R >> 3) & 7u) | (((R >> 9) & 7u) << 16);
-    const uint32_t* recs = static_cast<const uint32_t*>(a.qt) +
-                           ((size_t)b * d.Hq + (size_t)kh * G) * kQ43Rec;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const uint32_t* rec = recs + j * kQ43Rec;
-      float ah = 0.0f, al = 0.0f;
+      const float* qr = recs + j * kPlainRec + c0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ah = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, ph[i]),
-                                    __builtin_bit_cast(h2, rec[i]), ah, false);
-#pragma unroll
-      for (int i = 0; i < 12; ++i)
-        al = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pl[i]),
-                                    __builtin_bit_cast(h2, rec[4 + i]), al, false);
-      const float qs_hi = __builtin_bit_cast(float, rec[16]);
-      const float qs_lo = __builtin_bit_cast(float, rec[17]);
-      sc[j] = fmaf(s_hi, ah, fmaf(z_hi, qs_hi, fmaf(s_lo, al, z_lo * qs_lo)));
+      for (int e = 0; e < 8; ++e) acc[j] = fmaf(qr[e], z[e], acc[j]);
     }
-  } else {
-    const size_t row = (((size_t)b * d.Hkv + kh) * d.Tmax + (size_t)tile * kTile + lane) * d.rk;
-    const float* recs = static_cast<const float*>(a.qt) +
-                        ((size_t)b * d.Hq + (size_t)kh * G) * kPlainRec;
-    float acc[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) acc[j] = 0.0f;
-    for (int c0 = 0; c0 < d.rk; c0 += 8) {
-      float z[8];
-      if constexpr (FMT == STARKV_CACHE_F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.key) + row + c0);
-        float4 u = p[0], v = p[1];
-        z[0] = u.x; z[1] = u.y; z[2] = u.z; z[3] = u.w;
-        z[4] = v.x; z[5] = v.y; z[6] = v.z; z[7] = v.w;
-      } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.key) + row + c0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          z[2 * e] = __builtin_bit_cast(float, w[e] << 16);
-          z[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float* qr = recs + j * kPlainRec + c0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j] = fmaf(qr[e], z[e], acc[j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) sc[j] = acc[j];
   }
+#pragma unroll
+  for (int j = 0; j < G; ++j) sc[j] = acc[j];
 }
-
-// ------------------------------------------------------------ split kernel --
 
 // Row of the 32x32 MFMA accumulator held in register v of a lane.
 __device__ inline int acc_row(int v, int lane) {
   return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
 }
 
+// Online-softmax update of one query head over one tile (lane = token):
+// the reference max moves only when a score exceeds it by more than 2^kLazy,
+// decided by a wave vote, so the common tile needs no reduction.
+__device__ inline float softmax_step(float x, float& mr, float& l, float& alpha,
+                                     bool& moved) {
+  alpha = 1.0f;
+  moved = false;
+  if (__builtin_amdgcn_ballot_w64(x > mr + kLazy) != 0) {
+    const float mt = wave_max(x);
+    alpha = exp2f(mr - mt);
+    mr = mt;
+    l *= alpha;
+    moved = true;
+  }
+  const float p = exp2f(x - mr);
+  l += p;
+  return p;
+}
+
 template <int FMT, int G>
 __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   constexpr int NW = kDecodeWaves;
   constexpr int KVI = G >= 4 ? 1 : 4 / G;  // KV heads per wave (Hq <= 32)
-  constexpr bool kQ = FMT == STARKV_CACHE_Q43;
-  constexpr int PS = kQ ? 72 : 68;          // P row stride (elements)
+  constexpr int PS = 68;                    // P row stride (floats)
   const Dims& d = a.d;
 
-  __shared__ __attribute__((aligned(16))) float p_raw[2 * 32 * 68];
+  __shared__ __attribute__((aligned(16))) float p_raw[2 * 32 * PS];
+  __shared__ __attribute__((aligned(16))) float qrec[32 * kPlainRec];
   __shared__ float alpha_l[2][32];
   __shared__ int flag_l[2];
-  __shared__ float bias_l[32][33];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -248,13 +238,13 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   const int n_tiles = (a.seq_len + kTile - 1) / kTile;
   const int tile0 = sp * a.tiles_per_split;
   const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
-  const int GV = d.rv / 32;                 // value column tiles / groups
-  const int NH = kQ ? d.rv / 128 : 0;       // 4-bit value groups
+  const int GV = d.rv / 32;
 
-  for (int i = tid; i < 2 * 32 * 68; i += 512) p_raw[i] = 0.0f;
+  for (int i = tid; i < 2 * 32 * PS; i += 512) p_raw[i] = 0.0f;
+  for (int i = tid; i < d.Hq * kPlainRec; i += 512)
+    qrec[i] = static_cast<const float*>(a.qt)[(size_t)b * d.Hq * kPlainRec + i];
   if (tid < 64) alpha_l[tid >> 5][tid & 31] = 1.0f;
   if (tid < 2) flag_l[tid] = -1;
-  for (int i = tid; i < 32 * 33; i += 512) (&bias_l[0][0])[i] = 0.0f;
   __syncthreads();
 
   float m_ref[KVI * G], l_lane[KVI * G];
@@ -263,119 +253,45 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  f32x16 bacc = f32x16{};
-
   const int j = lane >> 5, m = lane & 31;
 
   for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
     const int buf = it & 1;
-    const int rem = a.seq_len - tile * kTile;     // valid tokens in this tile
+    const int rem = a.seq_len - tile * kTile;
     const bool valid = lane < rem;
-    // ------------------------------------------------------------ scores
 #pragma unroll
     for (int ki = 0; ki < KVI; ++ki) {
       const int kh = wave + ki * NW;
       if (kh < d.Hkv) {
         float sc[G];
-        score_tile<FMT, G>(a, b, kh, tile, lane, sc);
+        score_tile_plain<FMT, G>(a, qrec, b, kh, tile, lane, sc);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
           const int h = kh * G + jj;
-          const float x = valid ? sc[jj] : -INFINITY;
-          const float mt = wave_max(x);
-          float mr = m_ref[ki * G + jj];
-          float alpha = 1.0f;
-          if (mt > mr + kLazy) {
-            alpha = exp2f(mr - mt);
-            mr = mt;
-            m_ref[ki * G + jj] = mt;
-          }
-          const float p = exp2f(x - mr);
-          l_lane[ki * G + jj] = fmaf(l_lane[ki * G + jj], alpha, p);
-          if constexpr (kQ)
-            reinterpret_cast<_Float16*>(p_raw)[(buf * 32 + h) * PS + lane] = (_Float16)p;
-          else
-            p_raw[(buf * 32 + h) * PS + lane] = p;
+          float alpha;
+          bool moved;
+          const float p = softmax_step(valid ? sc[jj] : -INFINITY, m_ref[ki * G + jj],
+                                       l_lane[ki * G + jj], alpha, moved);
+          p_raw[(buf * 32 + h) * PS + lane] = p;
           if (lane == 0) {
             alpha_l[buf][h] = alpha;
-            if (alpha != 1.0f) flag_l[buf] = it;
+            if (moved) flag_l[buf] = it;
           }
         }
       }
     }
     lds_barrier();
-    // ------------------------------------------------------------ values
     if (flag_l[buf] == it) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float al = alpha_l[buf][acc_row(v, lane)];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[ni][v] *= al;
-        bacc[v] *= al;
       }
     }
     const bool partial = rem < kTile;
-    if constexpr (kQ) {
-      const _Float16* prow = reinterpret_cast<const _Float16*>(p_raw) + (buf * 32 + m) * PS + 32 * j;
-      h8 A[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
-      const uint8_t* vt = static_cast<const uint8_t*>(a.value) + ((size_t)b * d.NT + tile) * 26 * d.rv;
-      const _Float16* vm = reinterpret_cast<const _Float16*>(a.vmeta) + ((size_t)b * d.NT + tile) * 2 * GV * kTile;
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int n = wave + ni * NW;
-        if (n < GV) {
-          uint32_t pr[16];
-          if (n < NH) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(vt + (size_t)n * 1024 + (32 * j + m) * 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) pr[4 * r + i] = (w[r] >> (4 * i)) & 0x000F000Fu;
-          } else {
-            const uint32_t* wp = reinterpret_cast<const uint32_t*>(
-                vt + (size_t)NH * 1024 + (size_t)(n - NH) * 768 + (32 * j + m) * 12);
-            const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2];
-#pragma unroll
-            for (int i = 0; i < 5; ++i) {
-              pr[i] = (w0 >> (3 * i)) & 0x00070007u;
-              pr[5 + i] = (w1 >> (3 * i)) & 0x00070007u;
-              pr[10 + i] = (w2 >> (3 * i)) & 0x00070007u;
-            }
-            pr[15] = ((w0 >> 15) & 0x00010001u) | ((w1 >> 14) & 0x00020002u) |
-                     ((w2 >> 13) & 0x00040004u);
-          }
-          const _Float16* sp_ = vm + (size_t)n * kTile + 32 * j;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            h8 S = *reinterpret_cast<const h8*>(sp_ + 8 * r);
-            if (partial) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (32 * j + 8 * r + e >= rem) S[e] = (_Float16)0.0f;
-            }
-            const h8 Ap = A[r] * S;
-            const u32x4 bw = {pr[4 * r], pr[4 * r + 1], pr[4 * r + 2], pr[4 * r + 3]};
-            acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ap, __builtin_bit_cast(h8, bw), acc[ni], 0, 0, 0);
-          }
-        }
-      }
-      if (wave == it % NW) {  // zero-point term P z, one wave per tile
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          h8 Z = h8{};
-          if (m < GV) Z = *reinterpret_cast<const h8*>(vm + (size_t)(GV + m) * kTile + 32 * j + 8 * r);
-          if (partial) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (32 * j + 8 * r + e >= rem) Z[e] = (_Float16)0.0f;
-          }
-          bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z, bacc, 0, 0, 0);
-        }
-      }
-    } else if constexpr (FMT == STARKV_CACHE_BF16) {
-      const float* prow = p_raw + (buf * 32 + m) * PS + 32 * j;
+    const float* prow = p_raw + (buf * 32 + m) * PS + 32 * j;
+    if constexpr (FMT == STARKV_CACHE_BF16) {
       bf8 Ah[4], Al[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -406,7 +322,6 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
         }
       }
     } else {
-      const float* prow = p_raw + (buf * 32 + m) * PS + 32 * j;
       const float* vbase = static_cast<const float*>(a.value);
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
@@ -422,11 +337,283 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
     }
   }
 
-  // ---------------------------------------------------------------- finish
-  if constexpr (kQ) {
+  const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
+  for (int ni = 0; ni < 4; ++ni) {
+    const int n = wave + ni * NW;
+    if (n < GV) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = acc_row(v, lane);
+        if (row < d.Hq) a.part_o[(obase + row) * d.rv + n * 32 + m] = acc[ni][v];
+      }
+    }
   }
+#pragma unroll
+  for (int ki = 0; ki < KVI; ++ki) {
+    const int kh = wave + ki * NW;
+    if (kh < d.Hkv) {
+#pragma unroll
+      for (int jj = 0; jj < G; ++jj) {
+        const float l = wave_sum(l_lane[ki * G + jj]);
+        if (lane == 0) {
+          const int h = kh * G + jj;
+          a.part_ml[(obase + h) * 2] = m_ref[ki * G + jj];
+          a.part_ml[(obase + h) * 2 + 1] = l;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- Q43 split --
+
+// Bytes of one tile's value codes + value scales/zeros staged in LDS.
+__host__ __device__ constexpr int q43_value_stage_bytes(int rv) {
+  return 26 * rv + 2 * (rv / 32) * kTile * 2;
+}
+constexpr int kMaxValueStage = q43_value_stage_bytes(1024);   // 34816
+
+// Copy `bytes` (a multiple of 16) from global to LDS with direct-to-LDS
+// loads: each lane moves 16 bytes; the wave's 64 lanes fill 1 KB.
+__device__ inline void dma_to_lds(const uint8_t* src, uint8_t* lds_dst, int bytes,
+                                  int tid) {
+  const int chunks = bytes >> 4;
+  for (int c0 = (tid & ~63); c0 < chunks; c0 += 512) {
+    const int c = c0 + (tid & 63);
+    if (c < chunks)
+      __builtin_amdgcn_global_load_lds(
+          src + (size_t)c * 16,
+          (__attribute__((address_space(3))) void*)(lds_dst + (size_t)c0 * 16), 16, 0, 0);
+  }
+}
+
+// Q43 split kernel.  Workgroup = (sequence b, token split), 8 waves.  Per
+// 64-token tile:
+//   scores  wave w takes KV heads w, w+8, ...; lane = token; the 4-bit and
+//           3-bit key codes become fp16 pairs by shift+mask and meet the
+//           query pairs in v_dot2_f32_f16; p = exp2(score - m_ref) goes to
+//           LDS as fp16 (the stacked-head P tile, 32 rows).
+//   values  wave w takes value groups w, w+8, ... (32 channels each, one
+//           MFMA column tile); A = P * scale (per token, per group) in
+//           fp16, B = codes as fp16 subnormals, 4 x mfma 32x32x16 per tile;
+//           one wave per tile adds P x zero (one MFMA column per group).
+// Prefetch: right after a tile's barrier the next tile's value codes and
+// scales/zeros are loaded straight into the other LDS stage and its key codes
+// into registers, so the value phase of this tile hides their latency.
+template <int G>
+__global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int KVI = G >= 4 ? 1 : 4 / G;
+  constexpr int PS = 72;                     // P row stride (halves)
+  const Dims& d = a.d;
+
+  __shared__ __attribute__((aligned(16))) uint8_t vstage[2][kMaxValueStage];
+  __shared__ __attribute__((aligned(16))) _Float16 p_l[2][32 * PS];
+  __shared__ __attribute__((aligned(16))) uint32_t qrec[32 * kQ43Rec];
+  __shared__ float alpha_l[2][32];
+  __shared__ int flag_l[2];
+  __shared__ float bias_l[32][33];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int b = blockIdx.y, sp = blockIdx.x;
+  const int n_tiles = (a.seq_len + kTile - 1) / kTile;
+  const int tile0 = sp * a.tiles_per_split;
+  const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
+  const int GV = d.rv / 32;         // value groups (MFMA column tiles)
+  const int NH = d.rv / 128;        // 4-bit value groups
+  const int code_bytes = 26 * d.rv;
+  const int meta_bytes = 2 * GV * kTile * 2;
+  const int j = lane >> 5, m = lane & 31;
+
+  for (int i = tid; i < 2 * 32 * PS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
+  for (int i = tid; i < d.Hq * kQ43Rec; i += 512)
+    qrec[i] = static_cast<const uint32_t*>(a.qt)[(size_t)b * d.Hq * kQ43Rec + i];
+  if (tid < 64) alpha_l[tid >> 5][tid & 31] = 1.0f;
+  if (tid < 2) flag_l[tid] = -1;
+  for (int i = tid; i < 32 * 33; i += 512) (&bias_l[0][0])[i] = 0.0f;
+
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.key);
+  const uint2* kmeta = reinterpret_cast<const uint2*>(a.kmeta);
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.value);
+  const uint8_t* vmbase = reinterpret_cast<const uint8_t*>(a.vmeta);
+
+  uint32_t kc[KVI][6];
+  auto load_keys = [&](int tile) {
+#pragma unroll
+    for (int ki = 0; ki < KVI; ++ki) {
+      const int kh = wave + ki * NW;
+      if (kh < d.Hkv) {
+        const size_t blk = ((size_t)b * d.Hkv + kh) * d.NT + tile;
+        const uint8_t* kb = kbase + blk * kKeyBlock;
+        kc[ki][0] = reinterpret_cast<const uint32_t*>(kb)[lane];
+        kc[ki][1] = reinterpret_cast<const uint32_t*>(kb + 256)[lane];
+        kc[ki][2] = reinterpret_cast<const uint32_t*>(kb + 512)[lane];
+        kc[ki][3] = kb[768 + lane];
+        const uint2 mt = kmeta[blk * kTile + lane];
+        kc[ki][4] = mt.x;
+        kc[ki][5] = mt.y;
+      }
+    }
+  };
+  auto stage_values = [&](int tile, int buf) {
+    const size_t t = (size_t)b * d.NT + tile;
+    dma_to_lds(vbase + t * code_bytes, &vstage[buf][0], code_bytes, tid);
+    dma_to_lds(vmbase + t * meta_bytes, &vstage[buf][code_bytes], meta_bytes, tid);
+  };
+
+  if (tile0 < tile1) {
+    stage_values(tile0, 0);
+    load_keys(tile0);
+  }
+  __syncthreads();
+
+  float m_ref[KVI * G], l_lane[KVI * G];
+#pragma unroll
+  for (int i = 0; i < KVI * G; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  f32x16 bacc = f32x16{};
+
+  for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
+    const int buf = it & 1;
+    const int rem = a.seq_len - tile * kTile;   // valid tokens in this tile
+    const bool valid = lane < rem;
+
+    // ------------------------------------------------------------ scores
+#pragma unroll
+    for (int ki = 0; ki < KVI; ++ki) {
+      const int kh = wave + ki * NW;
+      if (kh < d.Hkv) {
+        const uint32_t whi = kc[ki][0], w0 = kc[ki][1], w1 = kc[ki][2], r8 = kc[ki][3];
+        const float s_hi = f16v(kc[ki][4] & 0xFFFFu) * kTwo24, z_hi = f16v(kc[ki][4] >> 16);
+        const float s_lo = f16v(kc[ki][5] & 0xFFFFu) * kTwo24, z_lo = f16v(kc[ki][5] >> 16);
+        uint32_t ph[4], pl[12];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ph[i] = (whi >> (4 * i)) & 0x000F000Fu;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          pl[i] = (w0 >> (3 * i)) & 0x00070007u;
+          pl[5 + i] = (w1 >> (3 * i)) & 0x00070007u;
+        }
+        const uint32_t R = r8 | (((w0 >> 15) & 1u) << 8) | ((w0 >> 31) << 9) |
+                           (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
+        pl[10] = (R & 7u) | (((R >> 6) & 7u) << 16);
+        pl[11] = ((R >> 3) & 7u) | (((R >> 9) & 7u) << 16);
+#pragma unroll
+        for (int jj = 0; jj < G; ++jj) {
+          const int h = kh * G + jj;
+          const uint32_t* rec = qrec + h * kQ43Rec;
+          float ah = 0.0f, al = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ah = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, ph[i]),
+                                        __builtin_bit_cast(h2, rec[i]), ah, false);
+#pragma unroll
+          for (int i = 0; i < 12; ++i)
+            al = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pl[i]),
+                                        __builtin_bit_cast(h2, rec[4 + i]), al, false);
+          const float qs_hi = __builtin_bit_cast(float, rec[16]);
+          const float qs_lo = __builtin_bit_cast(float, rec[17]);
+          const float sc = fmaf(s_hi, ah, fmaf(z_hi, qs_hi, fmaf(s_lo, al, z_lo * qs_lo)));
+          float alpha;
+          bool moved;
+          const float p = softmax_step(valid ? sc : -INFINITY, m_ref[ki * G + jj],
+                                       l_lane[ki * G + jj], alpha, moved);
+          p_l[buf][h * PS + lane] = (_Float16)p;
+          if (lane == 0) {
+            alpha_l[buf][h] = alpha;
+            if (moved) flag_l[buf] = it;
+          }
+        }
+      }
+    }
+    // this tile's staged values (and everything older) have landed in LDS
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (tile + 1 < tile1) {
+      stage_values(tile + 1, buf ^ 1);
+      load_keys(tile + 1);
+    }
+
+    // ------------------------------------------------------------ values
+    if (flag_l[buf] == it) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float al = alpha_l[buf][acc_row(v, lane)];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[ni][v] *= al;
+        bacc[v] *= al;
+      }
+    }
+    const bool partial = rem < kTile;
+    const _Float16* prow = &p_l[buf][m * PS + 32 * j];
+    const uint8_t* vt = &vstage[buf][0];
+    const _Float16* vm = reinterpret_cast<const _Float16*>(vt + code_bytes);
+    h8 A[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = wave + ni * NW;
+      if (n < GV) {
+        uint32_t pr[16];
+        if (n < NH) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(vt + n * 1024 + (32 * j + m) * 16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[4 * r + i] = (w[r] >> (4 * i)) & 0x000F000Fu;
+        } else {
+          const uint32_t* wp = reinterpret_cast<const uint32_t*>(
+              vt + NH * 1024 + (n - NH) * 768 + (32 * j + m) * 12);
+          const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2];
+#pragma unroll
+          for (int i = 0; i < 5; ++i) {
+            pr[i] = (w0 >> (3 * i)) & 0x00070007u;
+            pr[5 + i] = (w1 >> (3 * i)) & 0x00070007u;
+            pr[10 + i] = (w2 >> (3 * i)) & 0x00070007u;
+          }
+          pr[15] = ((w0 >> 15) & 0x00010001u) | ((w1 >> 14) & 0x00020002u) |
+                   ((w2 >> 13) & 0x00040004u);
+        }
+        const _Float16* srow = vm + n * kTile + 32 * j;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          h8 S = *reinterpret_cast<const h8*>(srow + 8 * r);
+          if (partial) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (32 * j + 8 * r + e >= rem) S[e] = (_Float16)0.0f;
+          }
+          const u32x4 bw = {pr[4 * r], pr[4 * r + 1], pr[4 * r + 2], pr[4 * r + 3]};
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r] * S, __builtin_bit_cast(h8, bw),
+                                                          acc[ni], 0, 0, 0);
+        }
+      }
+    }
+    if (wave == it % NW) {  // zero-point term P z for every group of this tile
+      const _Float16* zrow = vm + (GV + m) * kTile + 32 * j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        h8 Z = h8{};
+        if (m < GV) Z = *reinterpret_cast<const h8*>(zrow + 8 * r);
+        if (partial) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (32 * j + 8 * r + e >= rem) Z[e] = (_Float16)0.0f;
+        }
+        bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z, bacc, 0, 0, 0);
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- finish
+#pragma unroll
+  for (int v = 0; v < 16; ++v) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
   __syncthreads();
   const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
 #pragma unroll
@@ -436,11 +623,8 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = acc_row(v, lane);
-        if (row < d.Hq) {
-          float val = acc[ni][v];
-          if constexpr (kQ) val = fmaf(val, kTwo24, bias_l[row][n]);
-          a.part_o[(obase + row) * d.rv + n * 32 + m] = val;
-        }
+        if (row < d.Hq)
+          a.part_o[(obase + row) * d.rv + n * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
       }
     }
   }
@@ -463,30 +647,44 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 
 // ------------------------------------------------------------------ merge --
 
+// One workgroup per (b, h): weights of the splits from their (m, l), the
+// weighted sum of their partial outputs, then the inverse rotation.
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     Dims d, int splits,
                                                     float* __restrict__ obar) {
+  __shared__ float ms[kMaxSplits], ws[kMaxSplits];
   __shared__ float buf[1024];
+  __shared__ float inv_l;
   const int bh = blockIdx.x;
   const int b = bh / d.Hq, h = bh % d.Hq;
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s)
-    mx = fmaxf(mx, part_ml[(((size_t)b * splits + s) * d.Hq + h) * 2]);
-  float L = 0.0f;
-  for (int s = 0; s < splits; ++s) {
+  const int t = threadIdx.x;
+  for (int s = t; s < splits; s += 256) {
     const size_t k = (((size_t)b * splits + s) * d.Hq + h) * 2;
-    const float l = part_ml[k + 1];
-    if (l > 0.0f) L += exp2f(part_ml[k] - mx) * l;
+    ms[s] = part_ml[k];
+    ws[s] = part_ml[k + 1];
   }
-  const float inv = 1.0f / L;
-  for (int c = threadIdx.x; c < d.rv; c += 256) {
-    float o = 0.0f;
+  __syncthreads();
+  if (t == 0) {
+    float mx = -INFINITY;
+    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, ms[s]);
+    float L = 0.0f;
     for (int s = 0; s < splits; ++s) {
-      const size_t k = (((size_t)b * splits + s) * d.Hq + h);
-      const float l = part_ml[k * 2 + 1];
-      if (l > 0.0f) o = fmaf(exp2f(part_ml[k * 2] - mx), part_o[k * d.rv + c], o);
+      const float l = ws[s];
+      const float wgt = l > 0.0f ? exp2f(ms[s] - mx) : 0.0f;
+      ms[s] = wgt;
+      L = fmaf(wgt, l, L);
     }
+    inv_l = 1.0f / L;
+  }
+  __syncthreads();
+  const float inv = inv_l;
+  for (int c = t; c < d.rv; c += 256) {
+    float o = 0.0f;
+    const float* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + c;
+    const size_t stride = (size_t)d.Hq * d.rv;
+#pragma unroll 4
+    for (int s = 0; s < splits; ++s) o = fmaf(ms[s], src[s * stride], o);
     buf[c] = o * inv;
   }
   if (d.dtype == STARKV_CACHE_Q43 && d.rotate) {
@@ -494,7 +692,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const int mb = pow2_divisor(d.rv / 4);
     for (int hs = 1; hs < mb; hs <<= 1) {
       __syncthreads();
-      for (int idx = threadIdx.x; idx < d.rv / 2; idx += 256) {
+      for (int idx = t; idx < d.rv / 2; idx += 256) {
         const int i = (idx / hs) * 2 * hs + (idx % hs);
         const float x = buf[i], y = buf[i + hs];
         buf[i] = x + y;
@@ -502,65 +700,82 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
       }
     }
     __syncthreads();
-    const float c = inv_sqrt_pow2(mb);
-    for (int i = threadIdx.x; i < d.rv; i += 256) buf[i] *= c;
+    const float cst = inv_sqrt_pow2(mb);
+    for (int i = t; i < d.rv; i += 256) buf[i] *= cst;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < d.rv; c += 256) obar[(size_t)bh * d.rv + c] = buf[c];
+  for (int c = t; c < d.rv; c += 256) obar[(size_t)bh * d.rv + c] = buf[c];
 }
 
 // ------------------------------------------------------------------ vproj --
 
-// out[b, h, dd] = sum_c obar[b, h, c] * B_value[g*d_h + dd, c]; one workgroup
-// per (head, 16 output rows) reads those B_value rows once for every b.
+// out[b, h, r] = sum_c obar[b, h, c] * B_value[g*d_h + r, c] on MFMA 16x16x32
+// bf16: one wave per (head, 16 rows, 16 sequences).  obar (fp32) is split
+// into bf16 high and low parts; fp32 factors are split the same way.
 template <int FMT>
-__global__ __launch_bounds__(256) void vproj_kernel(const float* __restrict__ obar,
-                                                    const void* __restrict__ bv,
-                                                    Dims d, float* __restrict__ out) {
+__global__ __launch_bounds__(64) void vproj_kernel(const float* __restrict__ obar,
+                                                   const void* __restrict__ bv,
+                                                   Dims d, float* __restrict__ out) {
+  typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int h = blockIdx.x, g = h / d.G;
-  const int r0 = blockIdx.y * 16 + (threadIdx.x & 7) * 2;
-  for (int b = threadIdx.x >> 3; b < d.B; b += 32) {
-    const float* ob = obar + ((size_t)b * d.Hq + h) * d.rv;
-    float o0 = 0.0f, o1 = 0.0f;
-    const size_t row0 = ((size_t)g * d.dh + r0) * d.rv;
-    for (int c = 0; c < d.rv; c += 8) {
-      const float4 x0 = *reinterpret_cast<const float4*>(ob + c);
-      const float4 x1 = *reinterpret_cast<const float4*>(ob + c + 4);
-      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      float w0[8], w1[8];
-      if (FMT == STARKV_CACHE_F32) {
-        const float* p0 = static_cast<const float*>(bv) + row0 + c;
-        const float* p1 = p0 + d.rv;
+  const int r0 = blockIdx.y * 16, b0 = blockIdx.z * 16;
+  const int l = threadIdx.x, i16 = l & 15, ks = l >> 4;
+  const int bb = b0 + i16;
+  const float* arow = obar + ((size_t)min(bb, d.B - 1) * d.Hq + h) * d.rv + ks * 8;
+  const size_t brow = ((size_t)g * d.dh + r0 + i16) * d.rv + ks * 8;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < d.rv; k0 += 32) {
+    const float4 x0 = *reinterpret_cast<const float4*>(arow + k0);
+    const float4 x1 = *reinterpret_cast<const float4*>(arow + k0 + 4);
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    bf8v ah, al;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { w0[e] = p0[e]; w1[e] = p1[e]; }
-      } else {
-        const uint4 u0 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(bv) + row0 + c);
-        const uint4 u1 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(bv) + row0 + d.rv + c);
-        const uint32_t a0[4] = {u0.x, u0.y, u0.z, u0.w}, a1[4] = {u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w0[2 * e] = __builtin_bit_cast(float, a0[e] << 16);
-          w0[2 * e + 1] = __builtin_bit_cast(float, a0[e] & 0xFFFF0000u);
-          w1[2 * e] = __builtin_bit_cast(float, a1[e] << 16);
-          w1[2 * e + 1] = __builtin_bit_cast(float, a1[e] & 0xFFFF0000u);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { o0 = fmaf(xs[e], w0[e], o0); o1 = fmaf(xs[e], w1[e], o1); }
+    for (int e = 0; e < 8; ++e) {
+      const float x = bb < d.B ? xs[e] : 0.0f;
+      ah[e] = (__bf16)x;
+      al[e] = (__bf16)(x - (float)ah[e]);
     }
-    float* dst = out + ((size_t)b * d.Hq + h) * d.dh + r0;
-    dst[0] = o0;
-    dst[1] = o1;
+    if constexpr (FMT == STARKV_CACHE_F32) {
+      const float* p = static_cast<const float*>(bv) + brow + k0;
+      bf8v bh, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bh[e] = (__bf16)p[e];
+        bl[e] = (__bf16)(p[e] - (float)bh[e]);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    } else {
+      const bf8v bw = *reinterpret_cast<const bf8v*>(static_cast<const uint16_t*>(bv) + brow + k0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int ob = b0 + ks * 4 + v;   // row of C = sequence, column = output row
+    if (ob < d.B) out[((size_t)ob * d.Hq + h) * d.dh + r0 + i16] = acc[v];
   }
 }
 
 template <int FMT>
 hipError_t launch_split(int G, dim3 grid, const SplitArgs& sa, hipStream_t s) {
-  switch (G) {
-    case 1: split_kernel<FMT, 1><<<grid, 512, 0, s>>>(sa); break;
-    case 2: split_kernel<FMT, 2><<<grid, 512, 0, s>>>(sa); break;
-    case 4: split_kernel<FMT, 4><<<grid, 512, 0, s>>>(sa); break;
-    default: split_kernel<FMT, 8><<<grid, 512, 0, s>>>(sa); break;
+  if constexpr (FMT == STARKV_CACHE_Q43) {
+    switch (G) {
+      case 1: split_q43_kernel<1><<<grid, 512, 0, s>>>(sa); break;
+      case 2: split_q43_kernel<2><<<grid, 512, 0, s>>>(sa); break;
+      case 4: split_q43_kernel<4><<<grid, 512, 0, s>>>(sa); break;
+      default: split_q43_kernel<8><<<grid, 512, 0, s>>>(sa); break;
+    }
+  } else {
+    switch (G) {
+      case 1: split_kernel<FMT, 1><<<grid, 512, 0, s>>>(sa); break;
+      case 2: split_kernel<FMT, 2><<<grid, 512, 0, s>>>(sa); break;
+      case 4: split_kernel<FMT, 4><<<grid, 512, 0, s>>>(sa); break;
+      default: split_kernel<FMT, 8><<<grid, 512, 0, s>>>(sa); break;
+    }
   }
   return hipGetLastError();
 }
@@ -569,14 +784,17 @@ template <int FMT>
 hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
                       const void* q, const void* bk, const void* bv,
                       float sm_scale, float* out, char* ws, const DecodeWs& lay,
-                      hipStream_t s) {
+                      hipStream_t s, hipEvent_t* ev) {
   void* qt = ws + lay.qt;
   float* part_o = reinterpret_cast<float*>(ws + lay.part_o);
   float* part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
   float* obar = reinterpret_cast<float*>(ws + lay.obar);
-  qproj_kernel<FMT><<<d.B * d.Hq, 64, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
+  auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], s); };
+  mark(0);
+  qproj_kernel<FMT><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  mark(1);
   SplitArgs sa;
   sa.d = d;
   sa.seq_len = seq_len;
@@ -592,11 +810,15 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   sa.part_ml = part_ml;
   e = launch_split<FMT>(d.G, dim3(lay.splits, d.B), sa, s);
   if (e != hipSuccess) return e;
+  mark(2);
   merge_kernel<<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  vproj_kernel<FMT><<<dim3(d.Hq, d.dh / 16), 256, 0, s>>>(obar, bv, d, out);
-  return hipGetLastError();
+  mark(3);
+  vproj_kernel<FMT><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64, 0, s>>>(obar, bv, d, out);
+  e = hipGetLastError();
+  mark(4);
+  return e;
 }
 
 }  // namespace
@@ -622,14 +844,14 @@ DecodeWs decode_ws_layout(const Dims& d, int splits) {
 hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,
                          const void* q, const void* bk, const void* bv,
                          float sm_scale, float* out, char* ws,
-                         const DecodeWs& lay, hipStream_t s) {
+                         const DecodeWs& lay, hipStream_t s, hipEvent_t* ev) {
   switch (d.dtype) {
     case STARKV_CACHE_F32:
-      return decode_fmt<STARKV_CACHE_F32>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s);
+      return decode_fmt<STARKV_CACHE_F32>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev);
     case STARKV_CACHE_BF16:
-      return decode_fmt<STARKV_CACHE_BF16>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s);
+      return decode_fmt<STARKV_CACHE_BF16>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev);
     default:
-      return decode_fmt<STARKV_CACHE_Q43>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s);
+      return decode_fmt<STARKV_CACHE_Q43>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev);
   }
 }
 

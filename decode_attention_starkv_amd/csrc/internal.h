@@ -13,6 +13,7 @@ constexpr int kTile = 64;          // tokens per cache tile (format v1)
 constexpr int kKeyBlock = 832;     // bytes of one Q43 key tile of one KV head
 constexpr int kMaxQHeads = 32;     // rows of the stacked-head P operand
 constexpr int kDecodeWaves = 8;    // waves per decode workgroup
+constexpr int kMaxSplits = 1024;   // decode token splits per sequence
 
 // Shape of one call, copied by value into every kernel.
 struct Dims {
@@ -50,7 +51,8 @@ hipError_t launch_append(const Dims& d, const starkv_cache& cache,
 hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,
                          const void* q, const void* bk, const void* bv,
                          float sm_scale, float* out, char* ws,
-                         const DecodeWs& lay, hipStream_t s);
+                         const DecodeWs& lay, hipStream_t s,
+                         hipEvent_t* events = nullptr);
 
 struct PrefillWs {
   size_t z, qt, part, total;

@@ -163,6 +163,19 @@ STARKV_API int starkv_decode(const starkv_config* cfg, const starkv_cache* cache
                   const void* B_value, float sm_scale, float* out,
                   void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* starkv_decode that also records events[0..4] (host array of created
+ * hipEvent_t) on `stream`: before the query projection, before the split
+ * kernel, before the merge, before the value up-projection and after it, so
+ * a caller can time each kernel on the stream it runs on.  Same arguments,
+ * results and errors as starkv_decode; EINVAL if events is NULL. */
+STARKV_API int starkv_decode_profiled(const starkv_config* cfg,
+                                      const starkv_cache* cache,
+                                      int32_t seq_len, const void* q,
+                                      const void* B_key, const void* B_value,
+                                      float sm_scale, float* out,
+                                      void* workspace, size_t ws_bytes,
+                                      hipStream_t stream, hipEvent_t* events);
+
 /* Chunked causal prefill of one chunk (review Algorithm 2, steps 1-3, then
  * causal attention over the stored cache):
  *   x       bf16 [B][C][D]          hidden states of the chunk
