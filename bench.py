@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run one plain 1 GiB device-to-device copy, the "
+                        "reference for scaling HBM byte counters")
     return p.parse_args()
 
 
@@ -133,6 +136,16 @@ def main():
                           "--gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "read_bytes": 1 << 30,
+                          "write_bytes": 1 << 30}))
+        return
 
     import decode_attention_starkv_amd as sk
     import synth

@@ -182,7 +182,7 @@ __global__ void append_q43_keys(const float* __restrict__ zk,
   lo1 |= ((R >> 10) & 1u) << 15;
   lo1 |= ((R >> 11) & 1u) << 31;
 
-  size_t blk = ((size_t)b * d.Hkv + h) * d.NT + tile;
+  size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + h;
   uint8_t* kb = key + blk * kKeyBlock;
   reinterpret_cast<uint32_t*>(kb)[u] = whi;
   reinterpret_cast<uint32_t*>(kb + 256)[u] = lo0;

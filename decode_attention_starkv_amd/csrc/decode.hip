@@ -21,6 +21,8 @@
 // zero are folded outside the inner products:
 //   keys:   q~ . z_hat = s * 2^24 * (q~ . k 2^-24) + z * sum(q~)
 //   values: P Z_hat    = 2^24 * ((P * s) k 2^-24) + P z      (per 32-ch group)
+#include <type_traits>
+
 #include "internal.h"
 
 namespace starkv {
@@ -31,6 +33,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTwo24 = 16777216.0f;
@@ -368,6 +371,9 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 
 // ------------------------------------------------------------- Q43 split --
 
+// Cache-policy bits of a non-temporal load.
+constexpr int kNonTemporal = 2;
+
 // Bytes of one tile's value codes + value scales/zeros staged in LDS.
 __host__ __device__ constexpr int q43_value_stage_bytes(int rv) {
   return 26 * rv + 2 * (rv / 32) * kTile * 2;
@@ -375,7 +381,10 @@ __host__ __device__ constexpr int q43_value_stage_bytes(int rv) {
 constexpr int kMaxValueStage = q43_value_stage_bytes(1024);   // 34816
 
 // Copy `bytes` (a multiple of 16) from global to LDS with direct-to-LDS
-// loads: each lane moves 16 bytes; the wave's 64 lanes fill 1 KB.
+// loads: each lane moves 16 bytes; the wave's 64 lanes fill 1 KB.  The cache
+// is read exactly once per call, so the loads are non-temporal: streaming
+// past L2 and the Infinity Cache measures ~1.5x the bandwidth of
+// cache-allocating loads on MI355X.
 __device__ inline void dma_to_lds(const uint8_t* src, uint8_t* lds_dst, int bytes,
                                   int tid) {
   const int chunks = bytes >> 4;
@@ -384,27 +393,44 @@ __device__ inline void dma_to_lds(const uint8_t* src, uint8_t* lds_dst, int byte
     if (c < chunks)
       __builtin_amdgcn_global_load_lds(
           src + (size_t)c * 16,
-          (__attribute__((address_space(3))) void*)(lds_dst + (size_t)c0 * 16), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(lds_dst + (size_t)c0 * 16), 16, 0,
+          kNonTemporal);
+  }
+}
+
+// 16 fp16 pairs (tokens 2p, 2p+1) of one channel's 32-token run: 4-bit run
+// in 4 words, 3-bit run in 3 words (see the format description).
+template <bool kFour>
+__device__ inline uint32_t run_pair(const u32x4& w, int p) {
+  if constexpr (kFour) {
+    return (w[p >> 2] >> (4 * (p & 3))) & 0x000F000Fu;
+  } else {
+    if (p < 15) return (w[p / 5] >> (3 * (p % 5))) & 0x00070007u;
+    return ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
+           ((w[2] >> 13) & 0x00040004u);
   }
 }
 
 // Q43 split kernel.  Workgroup = (sequence b, token split), 8 waves.  Per
 // 64-token tile:
-//   scores  wave w takes KV heads w, w+8, ...; lane = token; the 4-bit and
-//           3-bit key codes become fp16 pairs by shift+mask and meet the
-//           query pairs in v_dot2_f32_f16; p = exp2(score - m_ref) goes to
-//           LDS as fp16 (the stacked-head P tile, 32 rows).
-//   values  wave w takes value groups w, w+8, ... (32 channels each, one
-//           MFMA column tile); A = P * scale (per token, per group) in
-//           fp16, B = codes as fp16 subnormals, 4 x mfma 32x32x16 per tile;
-//           one wave per tile adds P x zero (one MFMA column per group).
+//   scores  wave w takes KV heads w, w+8, ... (KVI of them); lane = token;
+//           the 4-bit and 3-bit key codes become fp16 pairs by shift+mask
+//           and meet the query pairs in v_dot2_f32_f16; p = exp2(score -
+//           m_ref) goes to LDS as fp16 (the stacked-head P tile, 32 rows).
+//   values  wave w takes the NI value groups w*NI .. w*NI+NI-1 (32 channels
+//           each, one MFMA column tile).  The 4-bit groups are the first
+//           R_v/128 = 2*NI, so waves 0-1 run the 4-bit path and waves 2-7
+//           the 3-bit path, each without per-group branches.  A = P * scale
+//           (per token, per group) in fp16, B = codes as fp16 subnormals,
+//           mfma 32x32x16 ordered so consecutive MFMAs are independent; one
+//           wave per tile adds P x zero (one MFMA column per group).
 // Prefetch: right after a tile's barrier the next tile's value codes and
-// scales/zeros are loaded straight into the other LDS stage and its key codes
-// into registers, so the value phase of this tile hides their latency.
-template <int G>
+// scales/zeros are loaded straight into the other LDS stage, and the key
+// codes of the tile after next into a second register set, so every load has
+// a full tile of compute to arrive before the barrier that waits for it.
+template <int G, int KVI, int NI>
 __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   constexpr int NW = kDecodeWaves;
-  constexpr int KVI = G >= 4 ? 1 : 4 / G;
   constexpr int PS = 72;                     // P row stride (halves)
   const Dims& d = a.d;
 
@@ -422,11 +448,12 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   const int n_tiles = (a.seq_len + kTile - 1) / kTile;
   const int tile0 = sp * a.tiles_per_split;
   const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
-  const int GV = d.rv / 32;         // value groups (MFMA column tiles)
-  const int NH = d.rv / 128;        // 4-bit value groups
-  const int code_bytes = 26 * d.rv;
+  const int GV = NI * NW;            // value groups (MFMA column tiles)
+  const int NH = 2 * NI;             // 4-bit value groups
+  const int code_bytes = 26 * 32 * GV;
   const int meta_bytes = 2 * GV * kTile * 2;
   const int j = lane >> 5, m = lane & 31;
+  const bool has_keys = wave < d.Hkv;  // false only when Hkv < 8
 
   for (int i = tid; i < 2 * 32 * PS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
   for (int i = tid; i < d.Hq * kQ43Rec; i += 512)
@@ -436,26 +463,25 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   for (int i = tid; i < 32 * 33; i += 512) (&bias_l[0][0])[i] = 0.0f;
 
   const uint8_t* kbase = static_cast<const uint8_t*>(a.key);
-  const uint2* kmeta = reinterpret_cast<const uint2*>(a.kmeta);
+  const u32x2* kmeta = reinterpret_cast<const u32x2*>(a.kmeta);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.value);
   const uint8_t* vmbase = reinterpret_cast<const uint8_t*>(a.vmeta);
 
-  uint32_t kc[KVI][6];
-  auto load_keys = [&](int tile) {
+  uint32_t kc[KVI][6], kn[KVI][6];
+  auto load_keys = [&](int tile, uint32_t (&dst)[KVI][6]) {
+    if (!has_keys) return;
 #pragma unroll
     for (int ki = 0; ki < KVI; ++ki) {
       const int kh = wave + ki * NW;
-      if (kh < d.Hkv) {
-        const size_t blk = ((size_t)b * d.Hkv + kh) * d.NT + tile;
-        const uint8_t* kb = kbase + blk * kKeyBlock;
-        kc[ki][0] = reinterpret_cast<const uint32_t*>(kb)[lane];
-        kc[ki][1] = reinterpret_cast<const uint32_t*>(kb + 256)[lane];
-        kc[ki][2] = reinterpret_cast<const uint32_t*>(kb + 512)[lane];
-        kc[ki][3] = kb[768 + lane];
-        const uint2 mt = kmeta[blk * kTile + lane];
-        kc[ki][4] = mt.x;
-        kc[ki][5] = mt.y;
-      }
+      const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + kh;
+      const uint8_t* kb = kbase + blk * kKeyBlock;
+      dst[ki][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + lane);
+      dst[ki][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + lane);
+      dst[ki][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + lane);
+      dst[ki][3] = __builtin_nontemporal_load(kb + 768 + lane);
+      const u32x2 mt = __builtin_nontemporal_load(kmeta + blk * kTile + lane);
+      dst[ki][4] = mt[0];
+      dst[ki][5] = mt[1];
     }
   };
   auto stage_values = [&](int tile, int buf) {
@@ -466,16 +492,17 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 
   if (tile0 < tile1) {
     stage_values(tile0, 0);
-    load_keys(tile0);
+    load_keys(tile0, kc);
+    if (tile0 + 1 < tile1) load_keys(tile0 + 1, kn);
   }
   __syncthreads();
 
   float m_ref[KVI * G], l_lane[KVI * G];
 #pragma unroll
   for (int i = 0; i < KVI * G; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
-  f32x16 acc[4];
+  f32x16 acc[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NI; ++i) acc[i] = f32x16{};
   f32x16 bacc = f32x16{};
 
   for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
@@ -484,10 +511,11 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     const bool valid = lane < rem;
 
     // ------------------------------------------------------------ scores
+    if (has_keys) {
+      float x[KVI * G];
 #pragma unroll
-    for (int ki = 0; ki < KVI; ++ki) {
-      const int kh = wave + ki * NW;
-      if (kh < d.Hkv) {
+      for (int ki = 0; ki < KVI; ++ki) {
+        const int kh = wave + ki * NW;
         const uint32_t whi = kc[ki][0], w0 = kc[ki][1], w1 = kc[ki][2], r8 = kc[ki][3];
         const float s_hi = f16v(kc[ki][4] & 0xFFFFu) * kTwo24, z_hi = f16v(kc[ki][4] >> 16);
         const float s_lo = f16v(kc[ki][5] & 0xFFFFu) * kTwo24, z_lo = f16v(kc[ki][5] >> 16);
@@ -505,8 +533,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         pl[11] = ((R >> 3) & 7u) | (((R >> 9) & 7u) << 16);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
-          const int h = kh * G + jj;
-          const uint32_t* rec = qrec + h * kQ43Rec;
+          const uint32_t* rec = qrec + (kh * G + jj) * kQ43Rec;
           float ah = 0.0f, al = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -519,25 +546,59 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
           const float qs_hi = __builtin_bit_cast(float, rec[16]);
           const float qs_lo = __builtin_bit_cast(float, rec[17]);
           const float sc = fmaf(s_hi, ah, fmaf(z_hi, qs_hi, fmaf(s_lo, al, z_lo * qs_lo)));
-          float alpha;
-          bool moved;
-          const float p = softmax_step(valid ? sc : -INFINITY, m_ref[ki * G + jj],
-                                       l_lane[ki * G + jj], alpha, moved);
-          p_l[buf][h * PS + lane] = (_Float16)p;
-          if (lane == 0) {
-            alpha_l[buf][h] = alpha;
-            if (moved) flag_l[buf] = it;
-          }
+          x[ki * G + jj] = valid ? sc : -INFINITY;
         }
       }
+      bool big = false;
+#pragma unroll
+      for (int i = 0; i < KVI * G; ++i) big |= x[i] > m_ref[i] + kLazy;
+      if (__builtin_amdgcn_ballot_w64(big) != 0) {
+        // rare: some head's reference max must move up
+#pragma unroll
+        for (int i = 0; i < KVI * G; ++i) {
+          const int h = (wave + (i / G) * NW) * G + (i % G);
+          float alpha = 1.0f;
+          if (__builtin_amdgcn_ballot_w64(x[i] > m_ref[i] + kLazy) != 0) {
+            const float mt = wave_max(x[i]);
+            alpha = exp2f(m_ref[i] - mt);
+            m_ref[i] = mt;
+            l_lane[i] *= alpha;
+            if (lane == 0) flag_l[buf] = it;
+          }
+          if (lane == 0) alpha_l[buf][h] = alpha;
+        }
+      } else if (lane < KVI * G) {
+        // keep every alpha of this wave's heads at 1 for this buffer
+        const int i = lane;
+        alpha_l[buf][(wave + (i / G) * NW) * G + (i % G)] = 1.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < KVI * G; ++i) {
+        const int h = (wave + (i / G) * NW) * G + (i % G);
+        const float p = __builtin_amdgcn_exp2f(x[i] - m_ref[i]);
+        l_lane[i] += p;
+        p_l[buf][h * PS + lane] = (_Float16)p;
+      }
     }
-    // this tile's staged values (and everything older) have landed in LDS
+    // Everything in flight was issued after the previous barrier: this
+    // tile's staged values and the next tile's keys.
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (tile + 1 < tile1) {
-      stage_values(tile + 1, buf ^ 1);
-      load_keys(tile + 1);
+    const int rem_v = rem;
+    if (rem_v < kTile) {
+      // last, partial tile: zero the scales and zeros of the missing tokens
+      // so that unused cache bytes never reach the MFMA operands
+      _Float16* vmz = reinterpret_cast<_Float16*>(&vstage[buf][code_bytes]);
+      for (int i = tid; i < 2 * GV * kTile; i += 512)
+        if ((i & (kTile - 1)) >= rem_v) vmz[i] = (_Float16)0.0f;
+      lds_barrier();
     }
+    if (tile + 1 < tile1) stage_values(tile + 1, buf ^ 1);
+#pragma unroll
+    for (int ki = 0; ki < KVI; ++ki)
+#pragma unroll
+      for (int e = 0; e < 6; ++e) kc[ki][e] = kn[ki][e];
+    if (tile + 2 < tile1) load_keys(tile + 2, kn);
 
     // ------------------------------------------------------------ values
     if (flag_l[buf] == it) {
@@ -545,67 +606,51 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       for (int v = 0; v < 16; ++v) {
         const float al = alpha_l[buf][acc_row(v, lane)];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[ni][v] *= al;
+        for (int ni = 0; ni < NI; ++ni) acc[ni][v] *= al;
         bacc[v] *= al;
       }
     }
-    const bool partial = rem < kTile;
     const _Float16* prow = &p_l[buf][m * PS + 32 * j];
     const uint8_t* vt = &vstage[buf][0];
     const _Float16* vm = reinterpret_cast<const _Float16*>(vt + code_bytes);
     h8 A[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
+    const int n0 = wave * NI;          // first value group of this wave
+    auto value_tiles = [&](auto four) {
+      constexpr bool kFour = decltype(four)::value;
+      u32x4 W[NI];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int n = wave + ni * NW;
-      if (n < GV) {
-        uint32_t pr[16];
-        if (n < NH) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(vt + n * 1024 + (32 * j + m) * 16);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pr[4 * r + i] = (w[r] >> (4 * i)) & 0x000F000Fu;
+      for (int ni = 0; ni < NI; ++ni) {
+        const int n = n0 + ni;
+        if constexpr (kFour) {
+          W[ni] = *reinterpret_cast<const u32x4*>(vt + n * 1024 + (32 * j + m) * 16);
         } else {
           const uint32_t* wp = reinterpret_cast<const uint32_t*>(
               vt + NH * 1024 + (n - NH) * 768 + (32 * j + m) * 12);
-          const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2];
-#pragma unroll
-          for (int i = 0; i < 5; ++i) {
-            pr[i] = (w0 >> (3 * i)) & 0x00070007u;
-            pr[5 + i] = (w1 >> (3 * i)) & 0x00070007u;
-            pr[10 + i] = (w2 >> (3 * i)) & 0x00070007u;
-          }
-          pr[15] = ((w0 >> 15) & 0x00010001u) | ((w1 >> 14) & 0x00020002u) |
-                   ((w2 >> 13) & 0x00040004u);
+          W[ni] = u32x4{wp[0], wp[1], wp[2], 0u};
         }
-        const _Float16* srow = vm + n * kTile + 32 * j;
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          h8 S = *reinterpret_cast<const h8*>(srow + 8 * r);
-          if (partial) {
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (32 * j + 8 * r + e >= rem) S[e] = (_Float16)0.0f;
-          }
-          const u32x4 bw = {pr[4 * r], pr[4 * r + 1], pr[4 * r + 2], pr[4 * r + 3]};
+        for (int ni = 0; ni < NI; ++ni) {
+          const h8 S = *reinterpret_cast<const h8*>(vm + (n0 + ni) * kTile + 32 * j + 8 * r);
+          const u32x4 bw = {run_pair<kFour>(W[ni], 4 * r), run_pair<kFour>(W[ni], 4 * r + 1),
+                            run_pair<kFour>(W[ni], 4 * r + 2), run_pair<kFour>(W[ni], 4 * r + 3)};
           acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r] * S, __builtin_bit_cast(h8, bw),
                                                           acc[ni], 0, 0, 0);
         }
       }
-    }
+    };
+    if (wave < 2) value_tiles(std::true_type{});
+    else value_tiles(std::false_type{});
     if (wave == it % NW) {  // zero-point term P z for every group of this tile
       const _Float16* zrow = vm + (GV + m) * kTile + 32 * j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         h8 Z = h8{};
         if (m < GV) Z = *reinterpret_cast<const h8*>(zrow + 8 * r);
-        if (partial) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (32 * j + 8 * r + e >= rem) Z[e] = (_Float16)0.0f;
-        }
         bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z, bacc, 0, 0, 0);
       }
     }
@@ -617,31 +662,51 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   __syncthreads();
   const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int n = wave + ni * NW;
-    if (n < GV) {
+  for (int ni = 0; ni < NI; ++ni) {
+    const int n = wave * NI + ni;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = acc_row(v, lane);
-        if (row < d.Hq)
-          a.part_o[(obase + row) * d.rv + n * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
+    for (int v = 0; v < 16; ++v) {
+      const int row = acc_row(v, lane);
+      if (row < d.Hq)
+        a.part_o[(obase + row) * d.rv + n * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
+    }
+  }
+  if (has_keys) {
+#pragma unroll
+    for (int i = 0; i < KVI * G; ++i) {
+      const float l = wave_sum(l_lane[i]);
+      if (lane == 0) {
+        const int h = (wave + (i / G) * NW) * G + (i % G);
+        a.part_ml[(obase + h) * 2] = m_ref[i];
+        a.part_ml[(obase + h) * 2 + 1] = l;
       }
     }
   }
-#pragma unroll
-  for (int ki = 0; ki < KVI; ++ki) {
-    const int kh = wave + ki * NW;
-    if (kh < d.Hkv) {
-#pragma unroll
-      for (int jj = 0; jj < G; ++jj) {
-        const float l = wave_sum(l_lane[ki * G + jj]);
-        if (lane == 0) {
-          const int h = kh * G + jj;
-          a.part_ml[(obase + h) * 2] = m_ref[ki * G + jj];
-          a.part_ml[(obase + h) * 2 + 1] = l;
-        }
-      }
-    }
+}
+
+template <int G, int KVI>
+hipError_t launch_q43_ni(int NI, dim3 grid, const SplitArgs& sa, hipStream_t s) {
+  switch (NI) {
+    case 1: split_q43_kernel<G, KVI, 1><<<grid, 512, 0, s>>>(sa); break;
+    case 2: split_q43_kernel<G, KVI, 2><<<grid, 512, 0, s>>>(sa); break;
+    case 4: split_q43_kernel<G, KVI, 4><<<grid, 512, 0, s>>>(sa); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_q43(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t s) {
+  const int NI = d.rv / 256;
+  const int KVI = d.Hkv >= 8 ? d.Hkv / 8 : 1;
+  switch (d.G * 8 + KVI) {
+    case 1 * 8 + 1: return launch_q43_ni<1, 1>(NI, grid, sa, s);
+    case 1 * 8 + 2: return launch_q43_ni<1, 2>(NI, grid, sa, s);
+    case 1 * 8 + 4: return launch_q43_ni<1, 4>(NI, grid, sa, s);
+    case 2 * 8 + 1: return launch_q43_ni<2, 1>(NI, grid, sa, s);
+    case 2 * 8 + 2: return launch_q43_ni<2, 2>(NI, grid, sa, s);
+    case 4 * 8 + 1: return launch_q43_ni<4, 1>(NI, grid, sa, s);
+    case 8 * 8 + 1: return launch_q43_ni<8, 1>(NI, grid, sa, s);
+    default: return hipErrorNotSupported;
   }
 }
 
@@ -761,23 +826,18 @@ __global__ __launch_bounds__(64) void vproj_kernel(const float* __restrict__ oba
 }
 
 template <int FMT>
-hipError_t launch_split(int G, dim3 grid, const SplitArgs& sa, hipStream_t s) {
+hipError_t launch_split(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t s) {
   if constexpr (FMT == STARKV_CACHE_Q43) {
-    switch (G) {
-      case 1: split_q43_kernel<1><<<grid, 512, 0, s>>>(sa); break;
-      case 2: split_q43_kernel<2><<<grid, 512, 0, s>>>(sa); break;
-      case 4: split_q43_kernel<4><<<grid, 512, 0, s>>>(sa); break;
-      default: split_q43_kernel<8><<<grid, 512, 0, s>>>(sa); break;
-    }
+    return launch_q43(d, grid, sa, s);
   } else {
-    switch (G) {
+    switch (d.G) {
       case 1: split_kernel<FMT, 1><<<grid, 512, 0, s>>>(sa); break;
       case 2: split_kernel<FMT, 2><<<grid, 512, 0, s>>>(sa); break;
       case 4: split_kernel<FMT, 4><<<grid, 512, 0, s>>>(sa); break;
       default: split_kernel<FMT, 8><<<grid, 512, 0, s>>>(sa); break;
     }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <int FMT>
@@ -808,7 +868,7 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   sa.qt = qt;
   sa.part_o = part_o;
   sa.part_ml = part_ml;
-  e = launch_split<FMT>(d.G, dim3(lay.splits, d.B), sa, s);
+  e = launch_split<FMT>(d, dim3(lay.splits, d.B), sa, s);
   if (e != hipSuccess) return e;
   mark(2);
   merge_kernel<<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);

@@ -91,9 +91,9 @@ typedef struct starkv_config {
  * 64 tokens):
  *   F32/BF16: key [B][Hkv][T_max][r_k], value [B][T_max/64][R_v][64];
  *             key_meta and value_meta are unused (may be NULL).
- *   Q43:      key  [B][Hkv][T_max/64] blocks of 832 B (4-bit plane u32[64],
+ *   Q43:      key  [B][T_max/64][Hkv] blocks of 832 B (4-bit plane u32[64],
  *             3-bit planes u32[64], u32[64], u8[64], token-major);
- *             key_meta [B][Hkv][T_max/64][64][4] fp16 (scale_hi, zero_hi,
+ *             key_meta [B][T_max/64][Hkv][64][4] fp16 (scale_hi, zero_hi,
  *             scale_lo, zero_lo);
  *             value [B][T_max/64] blocks of 26*R_v B (per 32-channel group,
  *             channel-major runs of 32 tokens, 4-bit groups first);

@@ -13,7 +13,8 @@ fp32 / bf16 caches (elements little-endian):
 
 q43 cache (r_k = 32: channels 0-7 at 4 bits, 8-31 at 3 bits; R_v a multiple
 of 128: channels [0, R_v/4) at 4 bits, the rest at 3 bits):
-  key codes  [B][Hkv][tile] blocks of 832 B, one 64-token tile each:
+  key codes  [B][tile][Hkv] blocks of 832 B, one 64-token tile each (the
+      blocks of all KV heads of a tile are contiguous):
       [0,256)   hi  u32[64]: key channel c (0..7) at bits 4c..4c+3
       [256,512) lo0 u32[64]: lo channel i at bits 3i (i<5), 16+3(i-10) (10<=i<15)
       [512,768) lo1 u32[64]: lo channel i at bits 3(i-5) (5<=i<10),
@@ -22,7 +23,7 @@ of 128: channels [0, R_v/4) at 4 bits, the rest at 3 bits):
       lo channel 20+k (k<4) is bits 3k..3k+2 of a 12-bit remainder R whose
       bits 0-7 are lo2, bit 8 = lo0 bit 15, bit 9 = lo0 bit 31,
       bit 10 = lo1 bit 15, bit 11 = lo1 bit 31.  (lo channel i = key ch 8+i.)
-  key meta   [B][Hkv][tile][64][4] fp16: scale_hi, zero_hi, scale_lo, zero_lo
+  key meta   [B][tile][Hkv][64][4] fp16: scale_hi, zero_hi, scale_lo, zero_lo
   value codes [B][tile] blocks of 26*R_v B: the 4-bit groups (32 channels
       each) first, then the 3-bit groups; a 4-bit group is
       [half j<2][channel c<32][4 x u32], a 3-bit group [half j][c][3 x u32];
@@ -223,8 +224,11 @@ class Cache:
         return k, v
 
     def _q_views(self):
-        k = self.buf["key"].reshape(self.B, self.H, self.nt, 832)
-        km = self.buf["key_meta"].view(np.uint16).reshape(self.B, self.H, self.nt, TT, 4)
+        """Key views with axes (batch, head, tile, ...) over the tile-major
+        buffers (writes through the views land in the buffers)."""
+        k = self.buf["key"].reshape(self.B, self.nt, self.H, 832).transpose(0, 2, 1, 3)
+        km = self.buf["key_meta"].view(np.uint16).reshape(
+            self.B, self.nt, self.H, TT, 4).transpose(0, 2, 1, 3, 4)
         v = self.buf["value"].reshape(self.B, self.nt, 26 * self.rv)
         vm = self.buf["value_meta"].view(np.uint16).reshape(
             self.B, self.nt, 2, self.rv // 32, TT)
