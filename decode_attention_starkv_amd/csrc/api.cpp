@@ -26,8 +26,8 @@ int check_config(const starkv_config* c) {
   if (c->head_dim % 16 != 0 || c->head_dim > 256) return STARKV_EUNSUPPORTED;
   if (c->value_rank % 32 != 0 || c->value_rank > 1024) return STARKV_EUNSUPPORTED;
   if (c->cache_dtype == STARKV_CACHE_Q43) {
-    if (c->key_rank != 32 || c->value_rank % 256 != 0 || c->value_rank == 768 ||
-        (c->n_kv_heads > 8 && c->n_kv_heads % 8 != 0))
+    if (c->key_rank != 32 || c->value_rank % 256 != 0 ||
+        (c->n_kv_heads > 4 && c->n_kv_heads % 4 != 0))
       return STARKV_EUNSUPPORTED;
   } else {
     if (c->rotate) return STARKV_EUNSUPPORTED;

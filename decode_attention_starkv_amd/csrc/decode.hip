@@ -374,30 +374,6 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 // Cache-policy bits of a non-temporal load.
 constexpr int kNonTemporal = 2;
 
-// Bytes of one tile's value codes + value scales/zeros staged in LDS.
-__host__ __device__ constexpr int q43_value_stage_bytes(int rv) {
-  return 26 * rv + 2 * (rv / 32) * kTile * 2;
-}
-constexpr int kMaxValueStage = q43_value_stage_bytes(1024);   // 34816
-
-// Copy `bytes` (a multiple of 16) from global to LDS with direct-to-LDS
-// loads: each lane moves 16 bytes; the wave's 64 lanes fill 1 KB.  The cache
-// is read exactly once per call, so the loads are non-temporal: streaming
-// past L2 and the Infinity Cache measures ~1.5x the bandwidth of
-// cache-allocating loads on MI355X.
-__device__ inline void dma_to_lds(const uint8_t* src, uint8_t* lds_dst, int bytes,
-                                  int tid) {
-  const int chunks = bytes >> 4;
-  for (int c0 = (tid & ~63); c0 < chunks; c0 += 512) {
-    const int c = c0 + (tid & 63);
-    if (c < chunks)
-      __builtin_amdgcn_global_load_lds(
-          src + (size_t)c * 16,
-          (__attribute__((address_space(3))) void*)(lds_dst + (size_t)c0 * 16), 16, 0,
-          kNonTemporal);
-  }
-}
-
 // 16 fp16 pairs (tokens 2p, 2p+1) of one channel's 32-token run: 4-bit run
 // in 4 words, 3-bit run in 3 words (see the format description).
 template <bool kFour>
@@ -411,30 +387,57 @@ __device__ inline uint32_t run_pair(const u32x4& w, int p) {
   }
 }
 
-// Q43 split kernel.  Workgroup = (sequence b, token split), 8 waves.  Per
-// 64-token tile:
-//   scores  wave w takes KV heads w, w+8, ... (KVI of them); lane = token;
-//           the 4-bit and 3-bit key codes become fp16 pairs by shift+mask
-//           and meet the query pairs in v_dot2_f32_f16; p = exp2(score -
-//           m_ref) goes to LDS as fp16 (the stacked-head P tile, 32 rows).
-//   values  wave w takes the NI value groups w*NI .. w*NI+NI-1 (32 channels
-//           each, one MFMA column tile).  The 4-bit groups are the first
-//           R_v/128 = 2*NI, so waves 0-1 run the 4-bit path and waves 2-7
-//           the 3-bit path, each without per-group branches.  A = P * scale
-//           (per token, per group) in fp16, B = codes as fp16 subnormals,
-//           mfma 32x32x16 ordered so consecutive MFMAs are independent; one
-//           wave per tile adds P x zero (one MFMA column per group).
-// Prefetch: right after a tile's barrier the next tile's value codes and
-// scales/zeros are loaded straight into the other LDS stage, and the key
-// codes of the tile after next into a second register set, so every load has
-// a full tile of compute to arrive before the barrier that waits for it.
-template <int G, int KVI, int NI>
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Copy `bytes` from global to LDS with one wave: direct-to-LDS loads, 1 KB
+// per instruction, always ceil(bytes / 1024) instructions.  The cache is read
+// exactly once per call, so the loads are non-temporal: streaming past L2 and
+// the Infinity Cache measures ~1.5x the bandwidth of cache-allocating loads.
+__device__ inline void wave_dma(const uint8_t* src, uint8_t* lds_dst, int bytes, int lane) {
+  for (int k = 0; k * 1024 < bytes; ++k) {
+    const int off = k * 1024 + lane * 16;
+    if (off < bytes)
+      __builtin_amdgcn_global_load_lds(
+          src + off, (__attribute__((address_space(3))) void*)(lds_dst + k * 1024), 16, 0,
+          kNonTemporal);
+  }
+}
+
+constexpr int kValueSlots = 3;     // tiles of value data in flight per value wave
+constexpr int kMaxNIV = 8;         // value groups per value wave (R_v <= 1024)
+constexpr int kValueSlotBytes = kMaxNIV * 1280;   // codes + scales + zeros
+
+// Q43 split kernel, warp-specialized.  Workgroup = (sequence b, token split),
+// 8 waves; waves w and w+4 share a SIMD.
+//   score waves 0-3: wave s owns KV heads s, s+4, ... (KVS of them); lane =
+//     token; key codes (loaded one barrier period ahead into registers) become
+//     fp16 pairs by shift+mask and meet the query pairs in v_dot2_f32_f16;
+//     p = exp2(score - m_ref) goes to a 2-slot LDS ring as the stacked-head
+//     P tile (32 rows, fp16).
+//   value waves 4-7: wave v owns the NIV value groups v*NIV .. v*NIV+NIV-1
+//     (32 channels each, one MFMA column tile); since R_v/4 channels are
+//     4-bit, value wave 0 holds exactly the 4-bit groups.  Each value wave
+//     streams its own groups' codes, scales and zeros into a private 3-slot
+//     LDS ring (direct-to-LDS, non-temporal), so it waits on its own loads
+//     only.  A = P * scale in fp16, B = codes as fp16 subnormals,
+//     mfma 32x32x16; P x zero adds the zero points.
+// One barrier per tile hands P over: while the value waves contract tile t,
+// the score waves already score tile t+1.
+template <int G, int KVS, int NIV>
 __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
-  constexpr int NW = kDecodeWaves;
-  constexpr int PS = 72;                     // P row stride (halves)
+  constexpr int PS = 72;                        // P row stride (halves)
+  constexpr bool kFourW0 = true;                // value wave 0: 4-bit groups
+  constexpr int kDmaHi = NIV + 2 * ((NIV * 128 + 1023) / 1024);
+  constexpr int kDmaLo = (NIV * 768 + 1023) / 1024 + 2 * ((NIV * 128 + 1023) / 1024);
+  (void)kFourW0;
   const Dims& d = a.d;
 
-  __shared__ __attribute__((aligned(16))) uint8_t vstage[2][kMaxValueStage];
+  __shared__ __attribute__((aligned(16))) uint8_t vring[kValueSlots][4][kValueSlotBytes];
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][32 * PS];
   __shared__ __attribute__((aligned(16))) uint32_t qrec[32 * kQ43Rec];
   __shared__ float alpha_l[2][32];
@@ -448,12 +451,9 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   const int n_tiles = (a.seq_len + kTile - 1) / kTile;
   const int tile0 = sp * a.tiles_per_split;
   const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
-  const int GV = NI * NW;            // value groups (MFMA column tiles)
-  const int NH = 2 * NI;             // 4-bit value groups
-  const int code_bytes = 26 * 32 * GV;
-  const int meta_bytes = 2 * GV * kTile * 2;
+  const int GV = 4 * NIV;            // value groups
+  const int NH = NIV;                // 4-bit value groups
   const int j = lane >> 5, m = lane & 31;
-  const bool has_keys = wave < d.Hkv;  // false only when Hkv < 8
 
   for (int i = tid; i < 2 * 32 * PS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
   for (int i = tid; i < d.Hq * kQ43Rec; i += 512)
@@ -461,61 +461,44 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   if (tid < 64) alpha_l[tid >> 5][tid & 31] = 1.0f;
   if (tid < 2) flag_l[tid] = -1;
   for (int i = tid; i < 32 * 33; i += 512) (&bias_l[0][0])[i] = 0.0f;
-
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.key);
-  const u32x2* kmeta = reinterpret_cast<const u32x2*>(a.kmeta);
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.value);
-  const uint8_t* vmbase = reinterpret_cast<const uint8_t*>(a.vmeta);
-
-  uint32_t kc[KVI][6], kn[KVI][6];
-  auto load_keys = [&](int tile, uint32_t (&dst)[KVI][6]) {
-    if (!has_keys) return;
-#pragma unroll
-    for (int ki = 0; ki < KVI; ++ki) {
-      const int kh = wave + ki * NW;
-      const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + kh;
-      const uint8_t* kb = kbase + blk * kKeyBlock;
-      dst[ki][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + lane);
-      dst[ki][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + lane);
-      dst[ki][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + lane);
-      dst[ki][3] = __builtin_nontemporal_load(kb + 768 + lane);
-      const u32x2 mt = __builtin_nontemporal_load(kmeta + blk * kTile + lane);
-      dst[ki][4] = mt[0];
-      dst[ki][5] = mt[1];
-    }
-  };
-  auto stage_values = [&](int tile, int buf) {
-    const size_t t = (size_t)b * d.NT + tile;
-    dma_to_lds(vbase + t * code_bytes, &vstage[buf][0], code_bytes, tid);
-    dma_to_lds(vmbase + t * meta_bytes, &vstage[buf][code_bytes], meta_bytes, tid);
-  };
-
-  if (tile0 < tile1) {
-    stage_values(tile0, 0);
-    load_keys(tile0, kc);
-    if (tile0 + 1 < tile1) load_keys(tile0 + 1, kn);
-  }
   __syncthreads();
 
-  float m_ref[KVI * G], l_lane[KVI * G];
-#pragma unroll
-  for (int i = 0; i < KVI * G; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
-  f32x16 acc[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) acc[i] = f32x16{};
-  f32x16 bacc = f32x16{};
+  const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
 
-  for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
-    const int buf = it & 1;
-    const int rem = a.seq_len - tile * kTile;   // valid tokens in this tile
-    const bool valid = lane < rem;
-
-    // ------------------------------------------------------------ scores
-    if (has_keys) {
-      float x[KVI * G];
+  if (wave < 4) {
+    // ================================================================ scores
+    const int sw = wave;
+    const bool has_keys = sw < d.Hkv;
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.key);
+    const u32x2* kmeta = reinterpret_cast<const u32x2*>(a.kmeta);
+    uint32_t kc[KVS][6];
+    auto load_keys = [&](int tile, uint32_t (&dst)[KVS][6]) {
 #pragma unroll
-      for (int ki = 0; ki < KVI; ++ki) {
-        const int kh = wave + ki * NW;
+      for (int ki = 0; ki < KVS; ++ki) {
+        const int kh = sw + ki * 4;
+        const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + kh;
+        const uint8_t* kb = kbase + blk * kKeyBlock;
+        dst[ki][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + lane);
+        dst[ki][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + lane);
+        dst[ki][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + lane);
+        dst[ki][3] = __builtin_nontemporal_load(kb + 768 + lane);
+        const u32x2 mt = __builtin_nontemporal_load(kmeta + blk * kTile + lane);
+        dst[ki][4] = mt[0];
+        dst[ki][5] = mt[1];
+      }
+    };
+    float m_ref[KVS * G], l_lane[KVS * G];
+#pragma unroll
+    for (int i = 0; i < KVS * G; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
+
+    // scores of tile `tile` into P slot `slot`; `it` = its index in the split
+    auto score = [&](int tile, int it, int slot) {
+      const int rem = a.seq_len - tile * kTile;
+      const bool valid = lane < rem;
+      float x[KVS * G];
+#pragma unroll
+      for (int ki = 0; ki < KVS; ++ki) {
+        const int kh = sw + ki * 4;
         const uint32_t whi = kc[ki][0], w0 = kc[ki][1], w1 = kc[ki][2], r8 = kc[ki][3];
         const float s_hi = f16v(kc[ki][4] & 0xFFFFu) * kTwo24, z_hi = f16v(kc[ki][4] >> 16);
         const float s_lo = f16v(kc[ki][5] & 0xFFFFu) * kTwo24, z_lo = f16v(kc[ki][5] >> 16);
@@ -551,161 +534,229 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       }
       bool big = false;
 #pragma unroll
-      for (int i = 0; i < KVI * G; ++i) big |= x[i] > m_ref[i] + kLazy;
+      for (int i = 0; i < KVS * G; ++i) big |= x[i] > m_ref[i] + kLazy;
       if (__builtin_amdgcn_ballot_w64(big) != 0) {
         // rare: some head's reference max must move up
 #pragma unroll
-        for (int i = 0; i < KVI * G; ++i) {
-          const int h = (wave + (i / G) * NW) * G + (i % G);
+        for (int i = 0; i < KVS * G; ++i) {
+          const int h = (sw + (i / G) * 4) * G + (i % G);
           float alpha = 1.0f;
           if (__builtin_amdgcn_ballot_w64(x[i] > m_ref[i] + kLazy) != 0) {
             const float mt = wave_max(x[i]);
             alpha = exp2f(m_ref[i] - mt);
             m_ref[i] = mt;
             l_lane[i] *= alpha;
-            if (lane == 0) flag_l[buf] = it;
+            if (lane == 0) flag_l[slot] = it;
           }
-          if (lane == 0) alpha_l[buf][h] = alpha;
+          if (lane == 0) alpha_l[slot][h] = alpha;
         }
-      } else if (lane < KVI * G) {
-        // keep every alpha of this wave's heads at 1 for this buffer
+      } else if (lane < KVS * G) {
         const int i = lane;
-        alpha_l[buf][(wave + (i / G) * NW) * G + (i % G)] = 1.0f;
+        alpha_l[slot][(sw + (i / G) * 4) * G + (i % G)] = 1.0f;
       }
 #pragma unroll
-      for (int i = 0; i < KVI * G; ++i) {
-        const int h = (wave + (i / G) * NW) * G + (i % G);
+      for (int i = 0; i < KVS * G; ++i) {
+        const int h = (sw + (i / G) * 4) * G + (i % G);
         const float p = __builtin_amdgcn_exp2f(x[i] - m_ref[i]);
         l_lane[i] += p;
-        p_l[buf][h * PS + lane] = (_Float16)p;
-      }
-    }
-    // Everything in flight was issued after the previous barrier: this
-    // tile's staged values and the next tile's keys.
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    const int rem_v = rem;
-    if (rem_v < kTile) {
-      // last, partial tile: zero the scales and zeros of the missing tokens
-      // so that unused cache bytes never reach the MFMA operands
-      _Float16* vmz = reinterpret_cast<_Float16*>(&vstage[buf][code_bytes]);
-      for (int i = tid; i < 2 * GV * kTile; i += 512)
-        if ((i & (kTile - 1)) >= rem_v) vmz[i] = (_Float16)0.0f;
-      lds_barrier();
-    }
-    if (tile + 1 < tile1) stage_values(tile + 1, buf ^ 1);
-#pragma unroll
-    for (int ki = 0; ki < KVI; ++ki)
-#pragma unroll
-      for (int e = 0; e < 6; ++e) kc[ki][e] = kn[ki][e];
-    if (tile + 2 < tile1) load_keys(tile + 2, kn);
-
-    // ------------------------------------------------------------ values
-    if (flag_l[buf] == it) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float al = alpha_l[buf][acc_row(v, lane)];
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[ni][v] *= al;
-        bacc[v] *= al;
-      }
-    }
-    const _Float16* prow = &p_l[buf][m * PS + 32 * j];
-    const uint8_t* vt = &vstage[buf][0];
-    const _Float16* vm = reinterpret_cast<const _Float16*>(vt + code_bytes);
-    h8 A[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
-    const int n0 = wave * NI;          // first value group of this wave
-    auto value_tiles = [&](auto four) {
-      constexpr bool kFour = decltype(four)::value;
-      u32x4 W[NI];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int n = n0 + ni;
-        if constexpr (kFour) {
-          W[ni] = *reinterpret_cast<const u32x4*>(vt + n * 1024 + (32 * j + m) * 16);
-        } else {
-          const uint32_t* wp = reinterpret_cast<const uint32_t*>(
-              vt + NH * 1024 + (n - NH) * 768 + (32 * j + m) * 12);
-          W[ni] = u32x4{wp[0], wp[1], wp[2], 0u};
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const h8 S = *reinterpret_cast<const h8*>(vm + (n0 + ni) * kTile + 32 * j + 8 * r);
-          const u32x4 bw = {run_pair<kFour>(W[ni], 4 * r), run_pair<kFour>(W[ni], 4 * r + 1),
-                            run_pair<kFour>(W[ni], 4 * r + 2), run_pair<kFour>(W[ni], 4 * r + 3)};
-          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r] * S, __builtin_bit_cast(h8, bw),
-                                                          acc[ni], 0, 0, 0);
-        }
+        p_l[slot][h * PS + lane] = (_Float16)p;
       }
     };
-    if (wave < 2) value_tiles(std::true_type{});
-    else value_tiles(std::false_type{});
-    if (wave == it % NW) {  // zero-point term P z for every group of this tile
-      const _Float16* zrow = vm + (GV + m) * kTile + 32 * j;
+
+    // Keys live in one register set: a tile's codes are loaded as soon as the
+    // previous tile's scores are done, a full barrier period before use.
+    if (tile0 < tile1 && has_keys) {
+      load_keys(tile0, kc);
+      score(tile0, 0, 0);
+      if (tile0 + 1 < tile1) load_keys(tile0 + 1, kc);
+    }
+    lds_barrier();
+    for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
+      if (tile + 1 < tile1 && has_keys) {
+        score(tile + 1, it + 1, (it + 1) & 1);
+        if (tile + 2 < tile1) load_keys(tile + 2, kc);
+      }
+      lds_barrier();
+    }
+    __syncthreads();   // value waves add their zero-point terms to bias_l
+    __syncthreads();   // value waves write their partial outputs
+    if (has_keys) {
+#pragma unroll
+      for (int i = 0; i < KVS * G; ++i) {
+        const float l = wave_sum(l_lane[i]);
+        if (lane == 0) {
+          const int h = (sw + (i / G) * 4) * G + (i % G);
+          a.part_ml[(obase + h) * 2] = m_ref[i];
+          a.part_ml[(obase + h) * 2 + 1] = l;
+        }
+      }
+    }
+  } else {
+    // ================================================================ values
+    const int vw = wave - 4;
+    const int n0 = vw * NIV;                 // first value group of this wave
+    const bool four = vw == 0;
+    const int code_bytes = NIV * (four ? 1024 : 768);
+    const int code_off = four ? 0 : NH * 1024 + (n0 - NH) * 768;
+    const int meta_bytes = NIV * kTile * 2;   // one plane of this wave's groups
+    const uint8_t* vbase = static_cast<const uint8_t*>(a.value);
+    const uint8_t* vmbase = reinterpret_cast<const uint8_t*>(a.vmeta);
+    const size_t tile_bytes = (size_t)26 * 32 * GV;
+    const size_t meta_tile = (size_t)2 * GV * kTile * 2;
+    uint8_t* ring = &vring[0][vw][0];
+    constexpr size_t kSlotStride = (size_t)4 * kValueSlotBytes;
+
+    auto stage = [&](int tile, int slot) {
+      const size_t t = (size_t)b * d.NT + tile;
+      uint8_t* dst = ring + slot * kSlotStride;
+      wave_dma(vbase + t * tile_bytes + code_off, dst, code_bytes, lane);
+      wave_dma(vmbase + t * meta_tile + (size_t)n0 * kTile * 2, dst + NIV * 1024, meta_bytes, lane);
+      wave_dma(vmbase + t * meta_tile + (size_t)(GV + n0) * kTile * 2,
+               dst + NIV * 1024 + meta_bytes, meta_bytes, lane);
+    };
+    // The whole tile loop is instantiated once per code width so that the
+    // accumulators of the two variants never meet in one live range.
+    auto run_values = [&](auto fourc) {
+    constexpr bool kFour = decltype(fourc)::value;
+    f32x16 acc[NIV];
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) acc[i] = f32x16{};
+    f32x16 bacc = f32x16{};
+
+    if (tile0 < tile1) {
+      stage(tile0, 0);
+      if (tile0 + 1 < tile1) stage(tile0 + 1, 1);
+    }
+    lds_barrier();      // P of the first tile is ready
+    for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
+      const int pslot = it & 1;
+      const int vslot = it % kValueSlots;
+      if (tile + 2 < tile1) stage(tile + 2, (it + 2) % kValueSlots);
+      // wait for this tile's stage: later stages may stay in flight
+      const int ahead = min(2, tile1 - 1 - tile);
+      if constexpr (kFour) {
+        if (ahead == 2) wait_vmcnt<2 * kDmaHi>();
+        else if (ahead == 1) wait_vmcnt<kDmaHi>();
+        else wait_vmcnt<0>();
+      } else {
+        if (ahead == 2) wait_vmcnt<2 * kDmaLo>();
+        else if (ahead == 1) wait_vmcnt<kDmaLo>();
+        else wait_vmcnt<0>();
+      }
+      uint8_t* vt = ring + vslot * kSlotStride;
+      _Float16* sc_l = reinterpret_cast<_Float16*>(vt + NIV * 1024);
+      _Float16* zr_l = sc_l + NIV * kTile;
+      const int rem = a.seq_len - tile * kTile;
+      if (rem < kTile) {
+        // last, partial tile: zero the missing tokens' scales and zeros so
+        // unused cache bytes never reach the MFMA operands
+        for (int i = lane; i < 2 * NIV * kTile; i += 64)
+          if ((i & (kTile - 1)) >= rem) sc_l[i] = (_Float16)0.0f;
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+      }
+      if (flag_l[pslot] == it) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float al = alpha_l[pslot][acc_row(v, lane)];
+#pragma unroll
+          for (int ni = 0; ni < NIV; ++ni) acc[ni][v] *= al;
+          bacc[v] *= al;
+        }
+      }
+      const _Float16* prow = &p_l[pslot][m * PS + 32 * j];
+      h8 A[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
+      {
+        // two column tiles at a time: their MFMAs are independent
+#pragma unroll
+        for (int n2 = 0; n2 < NIV; n2 += 2) {
+          u32x4 W[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int ni = n2 + q;
+            if constexpr (kFour) {
+              W[q] = *reinterpret_cast<const u32x4*>(vt + ni * 1024 + (32 * j + m) * 16);
+            } else {
+              const uint32_t* wp = reinterpret_cast<const uint32_t*>(vt + ni * 768 + (32 * j + m) * 12);
+              W[q] = u32x4{wp[0], wp[1], wp[2], 0u};
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int ni = n2 + q;
+              const h8 S = *reinterpret_cast<const h8*>(sc_l + ni * kTile + 32 * j + 8 * r);
+              const u32x4 bw = {run_pair<kFour>(W[q], 4 * r), run_pair<kFour>(W[q], 4 * r + 1),
+                                run_pair<kFour>(W[q], 4 * r + 2), run_pair<kFour>(W[q], 4 * r + 3)};
+              acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r] * S, __builtin_bit_cast(h8, bw),
+                                                              acc[ni], 0, 0, 0);
+            }
+            // keep the scheduler from hoisting every later tile's operand
+            // loads above these MFMAs (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      // zero points of this wave's groups: columns n0 .. n0+NIV-1
+      const bool zcol = m >= n0 && m < n0 + NIV;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         h8 Z = h8{};
-        if (m < GV) Z = *reinterpret_cast<const h8*>(zrow + 8 * r);
+        if (zcol) Z = *reinterpret_cast<const h8*>(zr_l + (m - n0) * kTile + 32 * j + 8 * r);
         bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z, bacc, 0, 0, 0);
       }
+      lds_barrier();
     }
-  }
-
-  // ---------------------------------------------------------------- finish
 #pragma unroll
-  for (int v = 0; v < 16; ++v) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
-  __syncthreads();
-  const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
+    for (int v = 0; v < 16; ++v)
+      if (m >= n0 && m < n0 + NIV) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
+    __syncthreads();
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    const int n = wave * NI + ni;
+    for (int ni = 0; ni < NIV; ++ni) {
+      const int n = n0 + ni;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = acc_row(v, lane);
-      if (row < d.Hq)
-        a.part_o[(obase + row) * d.rv + n * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
-    }
-  }
-  if (has_keys) {
-#pragma unroll
-    for (int i = 0; i < KVI * G; ++i) {
-      const float l = wave_sum(l_lane[i]);
-      if (lane == 0) {
-        const int h = (wave + (i / G) * NW) * G + (i % G);
-        a.part_ml[(obase + h) * 2] = m_ref[i];
-        a.part_ml[(obase + h) * 2 + 1] = l;
+      for (int v = 0; v < 16; ++v) {
+        const int row = acc_row(v, lane);
+        if (row < d.Hq)
+          a.part_o[(obase + row) * d.rv + n * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
       }
     }
+    __syncthreads();
+    };
+    if (four) run_values(std::true_type{});
+    else run_values(std::false_type{});
   }
 }
 
-template <int G, int KVI>
-hipError_t launch_q43_ni(int NI, dim3 grid, const SplitArgs& sa, hipStream_t s) {
-  switch (NI) {
-    case 1: split_q43_kernel<G, KVI, 1><<<grid, 512, 0, s>>>(sa); break;
-    case 2: split_q43_kernel<G, KVI, 2><<<grid, 512, 0, s>>>(sa); break;
-    case 4: split_q43_kernel<G, KVI, 4><<<grid, 512, 0, s>>>(sa); break;
+template <int G, int KVS>
+hipError_t launch_q43_niv(int NIV, dim3 grid, const SplitArgs& sa, hipStream_t s) {
+  switch (NIV) {
+    case 2: split_q43_kernel<G, KVS, 2><<<grid, 512, 0, s>>>(sa); break;
+    case 4: split_q43_kernel<G, KVS, 4><<<grid, 512, 0, s>>>(sa); break;
+    case 6: split_q43_kernel<G, KVS, 6><<<grid, 512, 0, s>>>(sa); break;
+    case 8: split_q43_kernel<G, KVS, 8><<<grid, 512, 0, s>>>(sa); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_q43(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t s) {
-  const int NI = d.rv / 256;
-  const int KVI = d.Hkv >= 8 ? d.Hkv / 8 : 1;
-  switch (d.G * 8 + KVI) {
-    case 1 * 8 + 1: return launch_q43_ni<1, 1>(NI, grid, sa, s);
-    case 1 * 8 + 2: return launch_q43_ni<1, 2>(NI, grid, sa, s);
-    case 1 * 8 + 4: return launch_q43_ni<1, 4>(NI, grid, sa, s);
-    case 2 * 8 + 1: return launch_q43_ni<2, 1>(NI, grid, sa, s);
-    case 2 * 8 + 2: return launch_q43_ni<2, 2>(NI, grid, sa, s);
-    case 4 * 8 + 1: return launch_q43_ni<4, 1>(NI, grid, sa, s);
-    case 8 * 8 + 1: return launch_q43_ni<8, 1>(NI, grid, sa, s);
+  const int NIV = d.rv / 128;
+  const int KVS = d.Hkv >= 4 ? d.Hkv / 4 : 1;
+  switch (d.G * 16 + KVS) {
+    case 1 * 16 + 1: return launch_q43_niv<1, 1>(NIV, grid, sa, s);
+    case 1 * 16 + 2: return launch_q43_niv<1, 2>(NIV, grid, sa, s);
+    case 1 * 16 + 4: return launch_q43_niv<1, 4>(NIV, grid, sa, s);
+    case 1 * 16 + 8: return launch_q43_niv<1, 8>(NIV, grid, sa, s);
+    case 2 * 16 + 1: return launch_q43_niv<2, 1>(NIV, grid, sa, s);
+    case 2 * 16 + 2: return launch_q43_niv<2, 2>(NIV, grid, sa, s);
+    case 2 * 16 + 4: return launch_q43_niv<2, 4>(NIV, grid, sa, s);
+    case 4 * 16 + 1: return launch_q43_niv<4, 1>(NIV, grid, sa, s);
+    case 4 * 16 + 2: return launch_q43_niv<4, 2>(NIV, grid, sa, s);
+    case 8 * 16 + 1: return launch_q43_niv<8, 1>(NIV, grid, sa, s);
     default: return hipErrorNotSupported;
   }
 }

@@ -73,7 +73,8 @@ typedef enum {
 typedef struct starkv_config {
   int32_t batch;       /* B */
   int32_t n_q_heads;   /* Hq <= 32, a multiple of n_kv_heads */
-  int32_t n_kv_heads;  /* Hkv; Hq / Hkv in {1, 2, 4, 8} */
+  int32_t n_kv_heads;  /* Hkv; Hq / Hkv in {1, 2, 4, 8}; Q43 with Hkv > 4
+                          needs Hkv a multiple of 4 */
   int32_t head_dim;    /* d_h, a multiple of 16, <= 256 */
   int32_t key_rank;    /* r_k per KV head: <= 64 and a multiple of 8 for
                           F32/BF16; exactly 32 for Q43 */
