@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("latent-KV decode attention: tokens attended/s and % HBM roofline "
           "at B=16, T=32K")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published peak
 COUNTERS = os.path.join(ROOT, "profiles", "split_kernel_l2_q43_counters.json")
 DECODE_SRC = os.path.join(ROOT, "decode_attention_starkv_amd", "csrc", "decode.hip")
 
@@ -122,6 +123,131 @@ def cpu_baseline(w, seq_len, min_s=10.0, max_reps=30):
                       f"{dt:.1f} s total)"}
 
 
+def prefill_pairs(ctx, chunk, n_q_heads):
+    """(query, head, key) pairs of a causal chunk: query i sees ctx + i + 1."""
+    return n_q_heads * (chunk * ctx + chunk * (chunk + 1) // 2)
+
+
+def cpu_baseline_prefill(w, n_rows=64):
+    """The oracle, as it stands, on a bounded sample of the prefill workload:
+    causal attention of n_rows evenly spaced queries of the chunk (all heads)
+    over the cache; building the cache is setup, not timed."""
+    import numpy as np
+    import synth
+    from oracle import attention as oa
+    from oracle import cache as oc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    ctx, chunk = w.seq_len, w.chunk
+    total = ctx + chunk
+    c = oc.Cache.for_workload(w, max_tokens=((total + 63) // 64) * 64)
+    for p0 in range(0, total, 8192):
+        n = min(8192, total - p0)
+        zk, zv = synth.batch_latents(w, p0, n)
+        c.append(zk, zv, p0, n)
+    bk, bv = synth.factors(w)
+    _, _, _, q = synth.prefill_inputs(w)
+    rows = np.linspace(0, chunk - 1, n_rows).astype(np.int64)
+    t0 = time.perf_counter()
+    out = oa.causal_attention(c, ctx, q, bk, bv, 1 / math.sqrt(w.head_dim),
+                              w.n_q_heads, w.rotate, rows=rows)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    return {"value": n_rows / dt, "unit": "chunk tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"causal attention of {n_rows} evenly spaced queries x "
+                      f"{w.n_q_heads} heads of the {chunk}-token chunk over "
+                      f"{ctx}+ cached tokens (fp64 numpy, {dt:.1f} s)"}
+
+
+def run_prefill(args, w, torch, sk, synth):
+    ctx, chunk = (args.seq_len or w.seq_len), w.chunk
+    T = ((ctx + chunk + 63) // 64) * 64
+    cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                         w.key_rank, w.value_rank, T, w.cache, w.rotate)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# workload {w.name} B={w.batch} ctx={ctx} chunk={chunk}", file=sys.stderr,
+          flush=True)
+    cache = sk.LatentCache(cfg)
+    if ctx:
+        fill_cache(w, cfg, cache, ctx, sk, torch)
+    x, ak, av, q = synth.prefill_inputs(w, chunk)
+    bk, bv = synth.factors(w)
+    bf = torch.bfloat16
+    x_t = torch.from_numpy(x).to(dev, bf).reshape(w.batch, chunk, w.hidden).contiguous()
+    ak_t = torch.from_numpy(ak).to(dev, bf)
+    av_t = torch.from_numpy(av).to(dev, bf)
+    q_t = torch.from_numpy(q).to(dev, bf).reshape(w.batch, chunk, w.n_q_heads,
+                                                   w.head_dim).contiguous()
+    bk_t = torch.from_numpy(bk).to(dev, bf)
+    bv_t = torch.from_numpy(bv).to(dev, bf)
+    out = torch.empty((w.batch, chunk, w.n_q_heads, w.head_dim), device=dev)
+    ws = sk.workspace(cfg, sk.OP_PREFILL, chunk)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+
+    def step(i):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        sk.starkv_prefill_profiled(cfg, cache, ctx, chunk, x_t, w.hidden, ak_t, av_t,
+                                   q_t, bk_t, bv_t, scale, out, ws, ev)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    step_ms, kern = [], [[] for _ in range(5)]
+    for i in range(args.steps):
+        step(i)
+        torch.cuda.synchronize()
+        step_ms.append(ev[0].elapsed_time(ev[5]))
+        for k in range(5):
+            kern[k].append(ev[k].elapsed_time(ev[k + 1]))
+        print(f"# step {i} {step_ms[-1]:.3f} ms (attention {kern[3][-1]:.3f} ms)",
+              file=sys.stderr, flush=True)
+    assert torch.isfinite(out).all()
+    mean = lambda v: sum(v) / len(v)
+    ms = mean(step_ms)
+    attn_ms = mean(kern[3])
+    pairs = prefill_pairs(ctx, chunk, w.n_q_heads) * w.batch
+    attn_flops = pairs * 2 * (w.key_rank + w.value_rank)
+    gemm_flops = 2 * w.batch * chunk * w.hidden * (w.n_kv_heads * w.key_rank + w.value_rank)
+    achieved = attn_flops / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": "chunked causal prefill over the latent cache: chunk tokens/s",
+        "value": w.batch * chunk / (ms * 1e-3),
+        "unit": "chunk tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{w.name} prefill", "batch": w.batch,
+                   "ctx_len": ctx, "chunk": chunk, "hidden": w.hidden,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "key_rank": w.key_rank,
+                   "value_rank": w.value_rank,
+                   "cache": w.cache + (" rotated" if w.rotate else "")},
+        "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel",
+                     "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS,
+                     "traffic": None},
+        "kernels_ms": {"gemm": mean(kern[0]), "append": mean(kern[1]),
+                       "qproj": mean(kern[2]), "attention": attn_ms,
+                       "merge_vproj": mean(kern[4])},
+        "algorithmic_flops": {"attention": attn_flops, "projection": gemm_flops},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_prefill(w)
+    print(json.dumps(res))
+
+
 def traffic_from_counters():
     """HBM bytes per split-kernel launch from committed rocprofv3 counters,
     or None if the kernel source changed since they were taken."""
@@ -158,6 +284,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.batch:
         w = w.replace(batch=args.batch)
+    if w.chunk:
+        return run_prefill(args, w, torch, sk, synth)
     seq_len = args.seq_len or w.seq_len
     cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
                          w.key_rank, w.value_rank, ((seq_len + 63) // 64) * 64,

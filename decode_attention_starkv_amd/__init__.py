@@ -29,7 +29,8 @@ OP_DECODE, OP_PREFILL = 0, 1
 
 ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_decode_splits", "starkv_append", "starkv_decode",
-                "starkv_decode_profiled", "starkv_prefill", "starkv_strerror")
+                "starkv_decode_profiled", "starkv_prefill",
+                "starkv_prefill_profiled", "starkv_strerror")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -81,6 +82,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.starkv_prefill.argtypes = [P(StarkvConfig), P(StarkvCache), i32, i32, vp, i32,
                                    vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     lib.starkv_prefill.restype = ctypes.c_int
+    lib.starkv_prefill_profiled.argtypes = [P(StarkvConfig), P(StarkvCache), i32, i32, vp,
+                                            i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz,
+                                            vp, P(vp)]
+    lib.starkv_prefill_profiled.restype = ctypes.c_int
     lib.starkv_strerror.argtypes = [ctypes.c_int]
     lib.starkv_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -200,6 +205,23 @@ def starkv_prefill(cfg, cache: LatentCache, ctx_len: int, chunk: int, x,
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != STARKV_OK:
         raise StarkvError(st, "starkv_prefill")
+
+
+def starkv_prefill_profiled(cfg, cache: LatentCache, ctx_len: int, chunk: int,
+                            x, hidden: int, A_key, A_value, q, B_key, B_value,
+                            sm_scale: float, out, workspace, events,
+                            z_debug=None, stream=None) -> None:
+    """events: six torch.cuda.Event(enable_timing=True) recorded by the
+    library around its launches on the launch stream."""
+    handles = (ctypes.c_void_p * 6)(*(e.cuda_event for e in events))
+    cs = cache.struct
+    st = load_library().starkv_prefill_profiled(
+        ctypes.byref(cfg), ctypes.byref(cs), ctx_len, chunk, _ptr(x), hidden,
+        _ptr(A_key), _ptr(A_value), _ptr(q), _ptr(B_key), _ptr(B_value),
+        sm_scale, _ptr(out), _ptr(z_debug), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), handles)
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_prefill_profiled")
 
 
 def workspace(cfg, op: int, n_tokens: int, device="cuda"):

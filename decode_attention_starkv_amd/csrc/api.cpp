@@ -166,12 +166,12 @@ int starkv_decode_profiled(const starkv_config* cfg, const starkv_cache* cache,
                      workspace, ws_bytes, stream, events);
 }
 
-int starkv_prefill(const starkv_config* cfg, const starkv_cache* cache,
-                   int32_t ctx_len, int32_t chunk, const void* x,
-                   int32_t hidden, const void* A_key, const void* A_value,
-                   const void* q, const void* B_key, const void* B_value,
-                   float sm_scale, float* out, float* z_debug, void* workspace,
-                   size_t ws_bytes, hipStream_t stream) {
+static int prefill_impl(const starkv_config* cfg, const starkv_cache* cache,
+                        int32_t ctx_len, int32_t chunk, const void* x,
+                        int32_t hidden, const void* A_key, const void* A_value,
+                        const void* q, const void* B_key, const void* B_value,
+                        float sm_scale, float* out, float* z_debug, void* workspace,
+                        size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
   int st = check_config(cfg);
   if (st != STARKV_OK) return st;
   if ((st = check_cache(cfg, cache)) != STARKV_OK) return st;
@@ -182,18 +182,42 @@ int starkv_prefill(const starkv_config* cfg, const starkv_cache* cache,
       !aligned16(q) || !aligned16(B_key) || !aligned16(B_value) ||
       !aligned16(out) || (z_debug && !aligned16(z_debug)))
     return STARKV_EINVAL;
-  if (cfg->cache_dtype != STARKV_CACHE_Q43 || hidden % 64 != 0)
-    return STARKV_EUNSUPPORTED;
   const Dims d = make_dims(*cfg);
+  if (hidden % 64 != 0 || !prefill_supported(d)) return STARKV_EUNSUPPORTED;
   const PrefillWs lay = prefill_ws_layout(d, chunk);
   if (!workspace || !aligned16(workspace) || ws_bytes < lay.total)
     return STARKV_EWORKSPACE;
   hipError_t e = launch_prefill(d, *cache, ctx_len, chunk, x, hidden, A_key,
                                 A_value, q, B_key, B_value, sm_scale, out,
                                 z_debug, static_cast<char*>(workspace), lay,
-                                stream);
+                                stream, events);
   if (e == hipErrorNotSupported) return STARKV_EUNSUPPORTED;
   return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
+}
+
+int starkv_prefill(const starkv_config* cfg, const starkv_cache* cache,
+                   int32_t ctx_len, int32_t chunk, const void* x,
+                   int32_t hidden, const void* A_key, const void* A_value,
+                   const void* q, const void* B_key, const void* B_value,
+                   float sm_scale, float* out, float* z_debug, void* workspace,
+                   size_t ws_bytes, hipStream_t stream) {
+  return prefill_impl(cfg, cache, ctx_len, chunk, x, hidden, A_key, A_value, q,
+                      B_key, B_value, sm_scale, out, z_debug, workspace,
+                      ws_bytes, stream, nullptr);
+}
+
+int starkv_prefill_profiled(const starkv_config* cfg, const starkv_cache* cache,
+                            int32_t ctx_len, int32_t chunk, const void* x,
+                            int32_t hidden, const void* A_key,
+                            const void* A_value, const void* q,
+                            const void* B_key, const void* B_value,
+                            float sm_scale, float* out, float* z_debug,
+                            void* workspace, size_t ws_bytes,
+                            hipStream_t stream, hipEvent_t* events) {
+  if (!events) return STARKV_EINVAL;
+  return prefill_impl(cfg, cache, ctx_len, chunk, x, hidden, A_key, A_value, q,
+                      B_key, B_value, sm_scale, out, z_debug, workspace,
+                      ws_bytes, stream, events);
 }
 
 const char* starkv_strerror(int status) {

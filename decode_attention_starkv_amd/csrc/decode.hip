@@ -23,26 +23,11 @@
 //   values: P Z_hat    = 2^24 * ((P * s) k 2^-24) + P z      (per 32-ch group)
 #include <type_traits>
 
-#include "internal.h"
+#include "device.h"
 
 namespace starkv {
 namespace {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTwo24 = 16777216.0f;
-// The running max used for the probabilities is only moved when a tile's max
-// exceeds it by more than this (log2 units), so probabilities stay <= 2^8 and
-// the accumulators are rescaled rarely.
-constexpr float kLazy = 8.0f;
-constexpr int kQ43Rec = 20;   // dwords per (b, h) query record, Q43
-constexpr int kPlainRec = 64; // floats per (b, h) query record, F32/BF16
 
 struct SplitArgs {
   Dims d;
@@ -55,26 +40,6 @@ struct SplitArgs {
   float* part_o;
   float* part_ml;
 };
-
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
-  return x;
-}
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s);
-  return x;
-}
-__device__ inline float f16v(uint32_t bits16) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-__device__ inline float bf16v(uint32_t bits16) {
-  return __builtin_bit_cast(float, bits16 << 16);
-}
-__device__ inline void lds_barrier() {
-  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // ------------------------------------------------------------------ qproj --
 
@@ -196,11 +161,6 @@ __device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
   }
 #pragma unroll
   for (int j = 0; j < G; ++j) sc[j] = acc[j];
-}
-
-// Row of the 32x32 MFMA accumulator held in register v of a lane.
-__device__ inline int acc_row(int v, int lane) {
-  return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
 }
 
 // Online-softmax update of one query head over one tile (lane = token):
@@ -371,22 +331,6 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 
 // ------------------------------------------------------------- Q43 split --
 
-// Cache-policy bits of a non-temporal load.
-constexpr int kNonTemporal = 2;
-
-// 16 fp16 pairs (tokens 2p, 2p+1) of one channel's 32-token run: 4-bit run
-// in 4 words, 3-bit run in 3 words (see the format description).
-template <bool kFour>
-__device__ inline uint32_t run_pair(const u32x4& w, int p) {
-  if constexpr (kFour) {
-    return (w[p >> 2] >> (4 * (p & 3))) & 0x000F000Fu;
-  } else {
-    if (p < 15) return (w[p / 5] >> (3 * (p % 5))) & 0x00070007u;
-    return ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
-           ((w[2] >> 13) & 0x00040004u);
-  }
-}
-
 // s_waitcnt vmcnt(N) for a compile-time N.
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -499,36 +443,10 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
         const int kh = sw + ki * 4;
-        const uint32_t whi = kc[ki][0], w0 = kc[ki][1], w1 = kc[ki][2], r8 = kc[ki][3];
-        const float s_hi = f16v(kc[ki][4] & 0xFFFFu) * kTwo24, z_hi = f16v(kc[ki][4] >> 16);
-        const float s_lo = f16v(kc[ki][5] & 0xFFFFu) * kTwo24, z_lo = f16v(kc[ki][5] >> 16);
-        uint32_t ph[4], pl[12];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ph[i] = (whi >> (4 * i)) & 0x000F000Fu;
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          pl[i] = (w0 >> (3 * i)) & 0x00070007u;
-          pl[5 + i] = (w1 >> (3 * i)) & 0x00070007u;
-        }
-        const uint32_t R = r8 | (((w0 >> 15) & 1u) << 8) | ((w0 >> 31) << 9) |
-                           (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
-        pl[10] = (R & 7u) | (((R >> 6) & 7u) << 16);
-        pl[11] = ((R >> 3) & 7u) | (((R >> 9) & 7u) << 16);
+        const KeyLane kl = unpack_key_lane(kc[ki]);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
-          const uint32_t* rec = qrec + (kh * G + jj) * kQ43Rec;
-          float ah = 0.0f, al = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ah = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, ph[i]),
-                                        __builtin_bit_cast(h2, rec[i]), ah, false);
-#pragma unroll
-          for (int i = 0; i < 12; ++i)
-            al = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pl[i]),
-                                        __builtin_bit_cast(h2, rec[4 + i]), al, false);
-          const float qs_hi = __builtin_bit_cast(float, rec[16]);
-          const float qs_lo = __builtin_bit_cast(float, rec[17]);
-          const float sc = fmaf(s_hi, ah, fmaf(z_hi, qs_hi, fmaf(s_lo, al, z_lo * qs_lo)));
+          const float sc = key_score(kl, qrec + (kh * G + jj) * kQ43Rec);
           x[ki * G + jj] = valid ? sc : -INFINITY;
         }
       }
@@ -950,6 +868,23 @@ DecodeWs decode_ws_layout(const Dims& d, int splits) {
   off += align256((size_t)d.B * d.Hq * d.rv * 4);
   w.total = off;
   return w;
+}
+
+hipError_t launch_qproj_q43(const Dims& d, const void* q, const void* bk,
+                           float sm_scale, void* qt, hipStream_t s) {
+  qproj_kernel<STARKV_CACHE_Q43><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_vproj_q43(const Dims& d, const float* part_o,
+                                  const float* part_ml, int splits, const void* bv,
+                                  float* obar, float* out, hipStream_t s) {
+  merge_kernel<<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, splits, obar);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  vproj_kernel<STARKV_CACHE_Q43><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64, 0, s>>>(
+      obar, bv, d, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,

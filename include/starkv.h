@@ -199,6 +199,22 @@ STARKV_API int starkv_prefill(const starkv_config* cfg, const starkv_cache* cach
                    float sm_scale, float* out, float* z_debug,
                    void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* starkv_prefill that also records events[0..5] (host array of created
+ * hipEvent_t) on `stream`: before the latent projection, before the append,
+ * before the query projection, before the causal attention kernel, before
+ * the normalisation + value up-projection and after it.  Same arguments,
+ * results and errors as starkv_prefill; EINVAL if events is NULL. */
+STARKV_API int starkv_prefill_profiled(const starkv_config* cfg,
+                                       const starkv_cache* cache,
+                                       int32_t ctx_len, int32_t chunk,
+                                       const void* x, int32_t hidden,
+                                       const void* A_key, const void* A_value,
+                                       const void* q, const void* B_key,
+                                       const void* B_value, float sm_scale,
+                                       float* out, float* z_debug,
+                                       void* workspace, size_t ws_bytes,
+                                       hipStream_t stream, hipEvent_t* events);
+
 /* (host) Static description of a status code. */
 STARKV_API const char* starkv_strerror(int status);
 

@@ -112,16 +112,27 @@ def project_latents(x, a_key, a_value, n_kv_heads, key_rank):
 
 def prefill(cache, ctx_len, x, a_key, a_value, q, bk, bv, sm_scale,
             n_q_heads, rotate, rows=None, heads=None):
-    """Chunked causal prefill for batch element 0.
+    """Chunked causal prefill of a one-sequence cache.
 
     Projects the chunk X [C, D] into latents, appends them at [ctx_len,
     ctx_len + C) (rotation + quantization as in Cache.append), then query i
     (absolute position ctx_len + i) attends to positions 0 .. ctx_len + i of
     the stored cache.  Returns out [len(rows), len(heads), d_h] float64.
     """
+    assert cache.B == 1
     c = x.shape[0]
     zk, zv = project_latents(x, a_key, a_value, cache.H, cache.rk)
     cache.append(zk[None], zv[None], ctx_len, c)
+    return causal_attention(cache, ctx_len, q, bk, bv, sm_scale, n_q_heads,
+                            rotate, rows, heads)
+
+
+def causal_attention(cache, ctx_len, q, bk, bv, sm_scale, n_q_heads, rotate,
+                     rows=None, heads=None, batch=0):
+    """Causal attention of a chunk's queries q [C, Hq, d_h] (query i at
+    absolute position ctx_len + i) over positions 0 .. ctx_len + i of the
+    stored cache of one batch element.  out [len(rows), len(heads), d_h]."""
+    c = q.shape[0]
     total = ctx_len + c
     q = np.asarray(q, np.float64)
     d_h = q.shape[-1]
@@ -129,8 +140,8 @@ def prefill(cache, ctx_len, x, a_key, a_value, q, bk, bv, sm_scale,
     bk_e, bv_e = effective_factors(bk, bv, rotate, cache.rk, cache.rv)
     rows = np.arange(c) if rows is None else np.asarray(rows)
     heads = range(n_q_heads) if heads is None else heads
-    zkl = cache.key_latents(0, total)
-    zvl = cache.value_latents(0, total)
+    zkl = cache.key_latents(batch, total)
+    zvl = cache.value_latents(batch, total)
     out = np.zeros((len(rows), len(heads), d_h))
     pos = np.arange(total)
     for hi, h in enumerate(heads):
