@@ -126,12 +126,11 @@ __global__ void append_plain_values(const float* __restrict__ zv, void* value,
 // One thread per (batch, token, KV head): 32 key channels, channels 0-7 at
 // 4 bits and 8-31 at 3 bits.  The key tile format is token-major, so every
 // word written here belongs to this token alone.
-__global__ void append_q43_keys(const float* __restrict__ zk,
-                                uint8_t* __restrict__ key,
-                                uint16_t* __restrict__ kmeta, Dims d, int pos,
-                                int n) {
+__device__ inline void append_q43_keys(const float* __restrict__ zk,
+                                       uint8_t* __restrict__ key,
+                                       uint16_t* __restrict__ kmeta, const Dims& d,
+                                       int pos, int n, size_t idx) {
   size_t total = (size_t)d.B * n * d.Hkv;
-  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   int h = idx % d.Hkv;
   int i = (idx / d.Hkv) % n;
@@ -199,13 +198,11 @@ __global__ void append_q43_keys(const float* __restrict__ zk,
 // group (reduction over half-waves) and writes codes to LDS.  Phase 2: thread
 // t packs channel t's runs of 32 tokens, merging with the previous words
 // where the token range covers a run only partly.
-__global__ __launch_bounds__(256) void append_q43_values(
+__device__ inline void append_q43_values(
     const float* __restrict__ zv, uint8_t* __restrict__ value,
-    uint16_t* __restrict__ vmeta, Dims d, int pos, int n) {
-  __shared__ uint8_t codes[kTile][256];
-  const int cb = blockIdx.x;
-  const int tile = pos / kTile + blockIdx.y;
-  const int b = blockIdx.z;
+    uint16_t* __restrict__ vmeta, const Dims& d, int pos, int n, int cb,
+    int tile_off, int b, uint8_t (*codes)[256]) {
+  const int tile = pos / kTile + tile_off;
   const int t0 = tile * kTile;
   const int ulo = max(pos, t0) - t0;
   const int uhi = min(pos + n, t0 + kTile) - t0;
@@ -309,6 +306,26 @@ __global__ __launch_bounds__(256) void append_q43_values(
   }
 }
 
+// Keys and values of one append in a single launch: blocks [0, key_blocks)
+// take 256 (batch, token, KV head) key items each, the rest one (block of
+// 256 value channels, touched tile, batch) value item each.
+__global__ __launch_bounds__(256) void append_q43_kernel(
+    const float* __restrict__ zk, const float* __restrict__ zv,
+    uint8_t* __restrict__ key, uint16_t* __restrict__ kmeta,
+    uint8_t* __restrict__ value, uint16_t* __restrict__ vmeta, Dims d, int pos,
+    int n, int key_blocks, int tiles) {
+  __shared__ uint8_t codes[kTile][256];
+  const int blk = blockIdx.x;
+  if (blk < key_blocks) {
+    append_q43_keys(zk, key, kmeta, d, pos, n, (size_t)blk * 256 + threadIdx.x);
+    return;
+  }
+  const int vb = blk - key_blocks;
+  const int ncb = d.rv / 256;
+  const int cb = vb % ncb, rest = vb / ncb;
+  append_q43_values(zv, value, vmeta, d, pos, n, cb, rest % tiles, rest / tiles, codes);
+}
+
 }  // namespace
 
 hipError_t launch_append(const Dims& d, const starkv_cache& cache,
@@ -317,15 +334,14 @@ hipError_t launch_append(const Dims& d, const starkv_cache& cache,
   if (n == 0) return hipSuccess;
   const int T = 256;
   if (d.dtype == STARKV_CACHE_Q43) {
-    size_t nk = (size_t)d.B * n * d.Hkv;
-    append_q43_keys<<<(unsigned)((nk + T - 1) / T), T, 0, s>>>(
-        zk, static_cast<uint8_t*>(cache.key),
-        static_cast<uint16_t*>(cache.key_meta), d, pos, n);
-    int tiles = (pos + n - 1) / kTile - pos / kTile + 1;
-    dim3 grid(d.rv / 256, tiles, d.B);
-    append_q43_values<<<grid, 256, 0, s>>>(
-        zv, static_cast<uint8_t*>(cache.value),
-        static_cast<uint16_t*>(cache.value_meta), d, pos, n);
+    const size_t nk = (size_t)d.B * n * d.Hkv;
+    const size_t key_blocks = (nk + T - 1) / T;
+    const int tiles = (pos + n - 1) / kTile - pos / kTile + 1;
+    const size_t blocks = key_blocks + (size_t)(d.rv / 256) * tiles * d.B;
+    append_q43_kernel<<<(unsigned)blocks, T, 0, s>>>(
+        zk, zv, static_cast<uint8_t*>(cache.key),
+        static_cast<uint16_t*>(cache.key_meta), static_cast<uint8_t*>(cache.value),
+        static_cast<uint16_t*>(cache.value_meta), d, pos, n, (int)key_blocks, tiles);
   } else {
     bool bf = d.dtype == STARKV_CACHE_BF16;
     size_t nk = (size_t)d.B * n * d.Hkv * d.rk;

@@ -69,6 +69,7 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
   float acc = 0.0f;
   if (c < d.rk) {
     const int k0 = chunk * klen, k1 = min(d.dh, k0 + klen);
+#pragma unroll 16
     for (int k = k0; k < k1; ++k) {
       const size_t bi = ((size_t)g * d.dh + k) * d.rk + c;
       const float bv = FMT == STARKV_CACHE_F32 ? static_cast<const float*>(bk)[bi]
@@ -352,23 +353,34 @@ __device__ inline void wave_dma(const uint8_t* src, uint8_t* lds_dst, int bytes,
   }
 }
 
-constexpr int kValueSlots = 3;     // tiles of value data in flight per value wave
+constexpr int kValueSlots = 4;     // LDS ring slots per value wave
+constexpr int kValueAhead = kValueSlots - 1;   // tiles staged ahead of use
 constexpr int kMaxNIV = 8;         // value groups per value wave (R_v <= 1024)
-constexpr int kValueSlotBytes = kMaxNIV * 1280;   // codes + scales + zeros
+// one slot: the 4-bit wave's codes + scales + zeros, then the three 3-bit
+// waves' (1024 + 128 + 128 and 768 + 128 + 128 bytes per group)
+constexpr int kHiRegion = kMaxNIV * 1280;
+constexpr int kLoRegion = kMaxNIV * 1024;
+constexpr int kSlotBytes = kHiRegion + 3 * kLoRegion;
+// fp32 row stride of the epilogue's per-wave staging of partial rows (kept
+// in the value ring): 32 rows of up to 256 columns, padded so the two row
+// halves a store instruction writes fall in different LDS banks
+constexpr int kStageRow = kMaxNIV * 32 + 8;
+static_assert(4 * 32 * kStageRow * 4 <= kValueSlots * kSlotBytes, "staging fits the ring");
 
 // Q43 split kernel, warp-specialized.  Workgroup = (sequence b, token split),
 // 8 waves; waves w and w+4 share a SIMD.
 //   score waves 0-3: wave s owns KV heads s, s+4, ... (KVS of them); lane =
-//     token; key codes (loaded one barrier period ahead into registers) become
+//     token; key codes (loaded two barrier periods ahead into alternating
+//     register sets) become
 //     fp16 pairs by shift+mask and meet the query pairs in v_dot2_f32_f16;
 //     p = exp2(score - m_ref) goes to a 2-slot LDS ring as the stacked-head
 //     P tile (32 rows, fp16).
 //   value waves 4-7: wave v owns the NIV value groups v*NIV .. v*NIV+NIV-1
 //     (32 channels each, one MFMA column tile); since R_v/4 channels are
 //     4-bit, value wave 0 holds exactly the 4-bit groups.  Each value wave
-//     streams its own groups' codes, scales and zeros into a private 3-slot
-//     LDS ring (direct-to-LDS, non-temporal), so it waits on its own loads
-//     only.  A = P * scale in fp16, B = codes as fp16 subnormals,
+//     streams its own groups' codes, scales and zeros into a private 4-slot
+//     LDS ring (direct-to-LDS, non-temporal) three tiles ahead, so it waits
+//     on its own loads only.  A = P * scale in fp16, B = codes as fp16 subnormals,
 //     mfma 32x32x16; P x zero adds the zero points.
 // One barrier per tile hands P over: while the value waves contract tile t,
 // the score waves already score tile t+1.
@@ -381,7 +393,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   (void)kFourW0;
   const Dims& d = a.d;
 
-  __shared__ __attribute__((aligned(16))) uint8_t vring[kValueSlots][4][kValueSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vring[kValueSlots * kSlotBytes];
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][32 * PS];
   __shared__ __attribute__((aligned(16))) uint32_t qrec[32 * kQ43Rec];
   __shared__ float alpha_l[2][32];
@@ -415,7 +427,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     const bool has_keys = sw < d.Hkv;
     const uint8_t* kbase = static_cast<const uint8_t*>(a.key);
     const u32x2* kmeta = reinterpret_cast<const u32x2*>(a.kmeta);
-    uint32_t kc[KVS][6];
+    uint32_t kA[KVS][6], kB[KVS][6];
     auto load_keys = [&](int tile, uint32_t (&dst)[KVS][6]) {
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
@@ -436,7 +448,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     for (int i = 0; i < KVS * G; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
 
     // scores of tile `tile` into P slot `slot`; `it` = its index in the split
-    auto score = [&](int tile, int it, int slot) {
+    auto score = [&](int tile, int it, int slot, const uint32_t (&kc)[KVS][6]) {
       const int rem = a.seq_len - tile * kTile;
       const bool valid = lane < rem;
       float x[KVS * G];
@@ -481,18 +493,28 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       }
     };
 
-    // Keys live in one register set: a tile's codes are loaded as soon as the
-    // previous tile's scores are done, a full barrier period before use.
-    if (tile0 < tile1 && has_keys) {
-      load_keys(tile0, kc);
-      score(tile0, 0, 0);
-      if (tile0 + 1 < tile1) load_keys(tile0 + 1, kc);
+    // Keys alternate between two register sets (tile tile0 + k in set k & 1):
+    // iteration it scores tile tile0 + it + 1 and refills its set with tile
+    // tile0 + it + 3, so codes arrive two barrier periods before use.  One
+    // barrier per iteration, as in the value waves.
+    const int n_it = tile1 - tile0;
+    if (n_it > 0 && has_keys) {
+      load_keys(tile0, kA);
+      if (n_it > 1) load_keys(tile0 + 1, kB);
+      score(tile0, 0, 0, kA);
+      if (n_it > 2) load_keys(tile0 + 2, kA);
     }
     lds_barrier();
-    for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
-      if (tile + 1 < tile1 && has_keys) {
-        score(tile + 1, it + 1, (it + 1) & 1);
-        if (tile + 2 < tile1) load_keys(tile + 2, kc);
+    for (int it = 0; it < n_it; it += 2) {
+      if (it + 1 < n_it && has_keys) {
+        score(tile0 + it + 1, it + 1, (it + 1) & 1, kB);
+        if (it + 3 < n_it) load_keys(tile0 + it + 3, kB);
+      }
+      lds_barrier();
+      if (it + 1 >= n_it) break;
+      if (it + 2 < n_it && has_keys) {
+        score(tile0 + it + 2, it + 2, (it + 2) & 1, kA);
+        if (it + 4 < n_it) load_keys(tile0 + it + 4, kA);
       }
       lds_barrier();
     }
@@ -521,16 +543,15 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     const uint8_t* vmbase = reinterpret_cast<const uint8_t*>(a.vmeta);
     const size_t tile_bytes = (size_t)26 * 32 * GV;
     const size_t meta_tile = (size_t)2 * GV * kTile * 2;
-    uint8_t* ring = &vring[0][vw][0];
-    constexpr size_t kSlotStride = (size_t)4 * kValueSlotBytes;
+    uint8_t* ring = vring + (four ? 0 : kHiRegion + (vw - 1) * kLoRegion);
 
     auto stage = [&](int tile, int slot) {
       const size_t t = (size_t)b * d.NT + tile;
-      uint8_t* dst = ring + slot * kSlotStride;
+      uint8_t* dst = ring + slot * kSlotBytes;
       wave_dma(vbase + t * tile_bytes + code_off, dst, code_bytes, lane);
-      wave_dma(vmbase + t * meta_tile + (size_t)n0 * kTile * 2, dst + NIV * 1024, meta_bytes, lane);
+      wave_dma(vmbase + t * meta_tile + (size_t)n0 * kTile * 2, dst + code_bytes, meta_bytes, lane);
       wave_dma(vmbase + t * meta_tile + (size_t)(GV + n0) * kTile * 2,
-               dst + NIV * 1024 + meta_bytes, meta_bytes, lane);
+               dst + code_bytes + meta_bytes, meta_bytes, lane);
     };
     // The whole tile loop is instantiated once per code width so that the
     // accumulators of the two variants never meet in one live range.
@@ -541,28 +562,22 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     for (int i = 0; i < NIV; ++i) acc[i] = f32x16{};
     f32x16 bacc = f32x16{};
 
-    if (tile0 < tile1) {
-      stage(tile0, 0);
-      if (tile0 + 1 < tile1) stage(tile0 + 1, 1);
-    }
+    for (int k = 0; k < kValueAhead && tile0 + k < tile1; ++k) stage(tile0 + k, k);
     lds_barrier();      // P of the first tile is ready
     for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
       const int pslot = it & 1;
       const int vslot = it % kValueSlots;
-      if (tile + 2 < tile1) stage(tile + 2, (it + 2) % kValueSlots);
-      // wait for this tile's stage: later stages may stay in flight
-      const int ahead = min(2, tile1 - 1 - tile);
-      if constexpr (kFour) {
-        if (ahead == 2) wait_vmcnt<2 * kDmaHi>();
-        else if (ahead == 1) wait_vmcnt<kDmaHi>();
-        else wait_vmcnt<0>();
-      } else {
-        if (ahead == 2) wait_vmcnt<2 * kDmaLo>();
-        else if (ahead == 1) wait_vmcnt<kDmaLo>();
-        else wait_vmcnt<0>();
+      if (tile + kValueAhead < tile1) stage(tile + kValueAhead, (it + kValueAhead) % kValueSlots);
+      // wait for this tile's stage: the later stages may stay in flight
+      constexpr int kDma = kFour ? kDmaHi : kDmaLo;
+      switch (min(kValueAhead, tile1 - 1 - tile)) {
+        case 3: wait_vmcnt<3 * kDma>(); break;
+        case 2: wait_vmcnt<2 * kDma>(); break;
+        case 1: wait_vmcnt<kDma>(); break;
+        default: wait_vmcnt<0>(); break;
       }
-      uint8_t* vt = ring + vslot * kSlotStride;
-      _Float16* sc_l = reinterpret_cast<_Float16*>(vt + NIV * 1024);
+      uint8_t* vt = ring + vslot * kSlotBytes;
+      _Float16* sc_l = reinterpret_cast<_Float16*>(vt + code_bytes);
       _Float16* zr_l = sc_l + NIV * kTile;
       const int rem = a.seq_len - tile * kTile;
       if (rem < kTile) {
@@ -612,9 +627,6 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
               acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r] * S, __builtin_bit_cast(h8, bw),
                                                               acc[ni], 0, 0, 0);
             }
-            // keep the scheduler from hoisting every later tile's operand
-            // loads above these MFMAs (register pressure)
-            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
@@ -631,16 +643,27 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (m >= n0 && m < n0 + NIV) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
-    __syncthreads();
+    __syncthreads();   // bias complete; no wave uses the value ring any more
+    // The partial rows go out through LDS (this wave's region of the ring)
+    // as 16-byte stores of whole row segments instead of 4-byte scatters.
+    float* st = reinterpret_cast<float*>(vring) + vw * 32 * kStageRow;
 #pragma unroll
     for (int ni = 0; ni < NIV; ++ni) {
       const int n = n0 + ni;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = acc_row(v, lane);
-        if (row < d.Hq)
-          a.part_o[(obase + row) * d.rv + n * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
+        st[row * kStageRow + ni * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
       }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own staging writes done
+    __builtin_amdgcn_wave_barrier();
+    constexpr int kChunks = NIV * 8;       // 16-byte chunks per row segment
+    for (int c = lane; c < 32 * kChunks; c += 64) {
+      const int row = c / kChunks, k = c % kChunks;
+      if (row < d.Hq)
+        *reinterpret_cast<float4*>(a.part_o + (obase + row) * d.rv + n0 * 32 + 4 * k) =
+            *reinterpret_cast<const float4*>(st + row * kStageRow + 4 * k);
     }
     __syncthreads();
     };
@@ -713,13 +736,38 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   }
   __syncthreads();
   const float inv = inv_l;
-  for (int c = t; c < d.rv; c += 256) {
-    float o = 0.0f;
+  // 4 consecutive channels per thread, 8 splits' loads in flight at once
+  const size_t stride = (size_t)d.Hq * d.rv;
+  for (int c = 4 * t; c < d.rv; c += 1024) {
     const float* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + c;
-    const size_t stride = (size_t)d.Hq * d.rv;
-#pragma unroll 4
-    for (int s = 0; s < splits; ++s) o = fmaf(ms[s], src[s * stride], o);
-    buf[c] = o * inv;
+    float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+      float4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        x[u] = *reinterpret_cast<const float4*>(src + (size_t)(s + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = ms[s + u];
+        o.x = fmaf(wgt, x[u].x, o.x);
+        o.y = fmaf(wgt, x[u].y, o.y);
+        o.z = fmaf(wgt, x[u].z, o.z);
+        o.w = fmaf(wgt, x[u].w, o.w);
+      }
+    }
+    for (; s < splits; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
+      const float wgt = ms[s];
+      o.x = fmaf(wgt, x.x, o.x);
+      o.y = fmaf(wgt, x.y, o.y);
+      o.z = fmaf(wgt, x.z, o.z);
+      o.w = fmaf(wgt, x.w, o.w);
+    }
+    buf[c] = o.x * inv;
+    buf[c + 1] = o.y * inv;
+    buf[c + 2] = o.z * inv;
+    buf[c + 3] = o.w * inv;
   }
   if (d.dtype == STARKV_CACHE_Q43 && d.rotate) {
     // undo the block rotation of the stored value latents: (Z H) H = Z (eq. 13)
@@ -744,26 +792,31 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 // ------------------------------------------------------------------ vproj --
 
 // out[b, h, r] = sum_c obar[b, h, c] * B_value[g*d_h + r, c] on MFMA 16x16x32
-// bf16: one wave per (head, 16 rows, 16 sequences).  obar (fp32) is split
-// into bf16 high and low parts; fp32 factors are split the same way.
+// bf16: one workgroup per (head, 16 rows, 16 sequences); its 4 waves take
+// interleaved 32-wide K steps (several loads in flight each) and their
+// partial tiles are summed through LDS.  obar (fp32) is split into bf16 high
+// and low parts; fp32 factors are split the same way.
+constexpr int kVprojWaves = 4;
+
 template <int FMT>
-__global__ __launch_bounds__(64) void vproj_kernel(const float* __restrict__ obar,
-                                                   const void* __restrict__ bv,
-                                                   Dims d, float* __restrict__ out) {
-  typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(64 * kVprojWaves) void vproj_kernel(
+    const float* __restrict__ obar, const void* __restrict__ bv, Dims d,
+    float* __restrict__ out) {
+  __shared__ f32x4 red[kVprojWaves - 1][64];
   const int h = blockIdx.x, g = h / d.G;
   const int r0 = blockIdx.y * 16, b0 = blockIdx.z * 16;
-  const int l = threadIdx.x, i16 = l & 15, ks = l >> 4;
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i16 = l & 15, ks = l >> 4;
   const int bb = b0 + i16;
   const float* arow = obar + ((size_t)min(bb, d.B - 1) * d.Hq + h) * d.rv + ks * 8;
   const size_t brow = ((size_t)g * d.dh + r0 + i16) * d.rv + ks * 8;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < d.rv; k0 += 32) {
+#pragma unroll 8
+  for (int k0 = w * 32; k0 < d.rv; k0 += 32 * kVprojWaves) {
     const float4 x0 = *reinterpret_cast<const float4*>(arow + k0);
     const float4 x1 = *reinterpret_cast<const float4*>(arow + k0 + 4);
     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    bf8v ah, al;
+    bf8 ah, al;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = bb < d.B ? xs[e] : 0.0f;
@@ -772,7 +825,7 @@ __global__ __launch_bounds__(64) void vproj_kernel(const float* __restrict__ oba
     }
     if constexpr (FMT == STARKV_CACHE_F32) {
       const float* p = static_cast<const float*>(bv) + brow + k0;
-      bf8v bh, bl;
+      bf8 bh, bl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         bh[e] = (__bf16)p[e];
@@ -782,11 +835,16 @@ __global__ __launch_bounds__(64) void vproj_kernel(const float* __restrict__ oba
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
     } else {
-      const bf8v bw = *reinterpret_cast<const bf8v*>(static_cast<const uint16_t*>(bv) + brow + k0);
+      const bf8 bw = *reinterpret_cast<const bf8*>(static_cast<const uint16_t*>(bv) + brow + k0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
     }
   }
+  if (w > 0) red[w - 1][l] = acc;
+  __syncthreads();
+  if (w > 0) return;
+#pragma unroll
+  for (int i = 0; i < kVprojWaves - 1; ++i) acc += red[i][l];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int ob = b0 + ks * 4 + v;   // row of C = sequence, column = output row
@@ -844,7 +902,7 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(3);
-  vproj_kernel<FMT><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64, 0, s>>>(obar, bv, d, out);
+  vproj_kernel<FMT><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64 * kVprojWaves, 0, s>>>(obar, bv, d, out);
   e = hipGetLastError();
   mark(4);
   return e;
@@ -882,7 +940,7 @@ hipError_t launch_merge_vproj_q43(const Dims& d, const float* part_o,
   merge_kernel<<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, splits, obar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  vproj_kernel<STARKV_CACHE_Q43><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64, 0, s>>>(
+  vproj_kernel<STARKV_CACHE_Q43><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64 * kVprojWaves, 0, s>>>(
       obar, bv, d, out);
   return hipGetLastError();
 }

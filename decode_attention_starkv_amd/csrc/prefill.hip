@@ -10,6 +10,8 @@
 //             softmax, then P Z_v on MFMA against an fp16 value tile
 //             dequantized once per workgroup into LDS (section 5.3, eq. 12)
 //   merge, vproj   the decode kernels with one split per query row
+#include <type_traits>
+
 #include "device.h"
 
 namespace starkv {
@@ -154,8 +156,8 @@ struct AttnArgs {
 //   phase B  wave w scores tile t+1 for query head w of the group and all 8
 //            queries (lane = token, codes as fp16 pairs in v_dot2, lazy
 //            online softmax) into the other P slot, and contracts tile t:
-//            rows (w & 1) * 32 .. +31 against its R_v / 128 column tiles
-//            on mfma 32x32x16 f16;
+//            both row tiles against its R_v / 256 column tiles on mfma
+//            32x32x16 f16;
 //   barrier
 // Causal mask: query i (absolute position ctx + i) sees cached positions
 // 0 .. ctx + i.  Value tokens past the workgroup's last position are zeroed
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int NH = d.rv / 128;          // 4-bit value groups
   const size_t vtile_bytes = (size_t)26 * d.rv;
   const size_t mtile = (size_t)2 * NG * kTile;     // fp16 elements
-  auto dequant = [&](int tile) {
+  auto dequant = [&](int tile, auto maskc) {
+    constexpr bool kMask = decltype(maskc)::value;
     const size_t t = (size_t)b * d.NT + tile;
     const uint8_t* vb = a.value + t * vtile_bytes;
     const uint16_t* vm = a.vmeta + t * mtile;
@@ -294,9 +297,11 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
           const uint32_t sbits = S[q], zbits = Z[q];
           h2 v = __builtin_elementwise_fma(kv, __builtin_bit_cast(h2, sbits),
                                            __builtin_bit_cast(h2, zbits));
-          const int tk = t0 + 2 * p;
-          if (tk > pmax) v[0] = (_Float16)0.0f;
-          if (tk + 1 > pmax) v[1] = (_Float16)0.0f;
+          if constexpr (kMask) {
+            const int tk = t0 + 2 * p;
+            if (tk > pmax) v[0] = (_Float16)0.0f;
+            if (tk + 1 > pmax) v[1] = (_Float16)0.0f;
+          }
           o[q] = __builtin_bit_cast(uint32_t, v);
         }
         const int chunk = (4 * jj + r4) ^ (ch & 7);
@@ -306,39 +311,45 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   };
 
   // -------------------------------------------------------------- contract
-  const int rt = wave & 1;                     // MFMA row tile: queries rt*4 .. rt*4+3
-  const int ct0 = (wave >> 1) * NCT;           // first value column tile
-  f32x16 acc[NCT];
+  // Wave w owns value column tiles w*NCT .. w*NCT+NCT-1 for both row tiles,
+  // so each value fragment read from LDS feeds two MFMAs.
+  const int ct0 = wave * NCT;
+  f32x16 acc[2][NCT];
 #pragma unroll
-  for (int i = 0; i < NCT; ++i) acc[i] = f32x16{};
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < NCT; ++i) acc[rt][i] = f32x16{};
 
   auto contract = [&](int slot, int it) {
     if (flag_l[slot] == it) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float al = alpha_l[slot][rt * 32 + acc_row(v, lane)];
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[ct][v] *= al;
-      }
+        for (int v = 0; v < 16; ++v) {
+          const float al = alpha_l[slot][rt * 32 + acc_row(v, lane)];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) acc[rt][ct][v] *= al;
+        }
     }
-    const _Float16* prow = &p_l[slot][(rt * 32 + m) * kPS + 32 * j];
-    h8 A[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
+    for (int r = 0; r < 4; ++r) {
+      const h8 A0 = *reinterpret_cast<const h8*>(&p_l[slot][m * kPS + 32 * j + 8 * r]);
+      const h8 A1 = *reinterpret_cast<const h8*>(&p_l[slot][(32 + m) * kPS + 32 * j + 8 * r]);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const uint8_t* row = zt + (size_t)((ct0 + ct) * 32 + m) * kZRow;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int ct = 0; ct < NCT; ++ct) {
+        const uint8_t* row = zt + (size_t)((ct0 + ct) * 32 + m) * kZRow;
         const h8 Bv = *reinterpret_cast<const h8*>(row + (((4 * j + r) ^ (m & 7)) * 16));
-        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Bv, acc[ct], 0, 0, 0);
+        acc[0][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, Bv, acc[0][ct], 0, 0, 0);
+        acc[1][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1, Bv, acc[1][ct], 0, 0, 0);
       }
     }
   };
 
   score(0, 0, 0);
   for (int tile = 0, it = 0; tile <= tile_last; ++tile, ++it) {
-    dequant(tile);
+    // only the workgroup's last tile can hold tokens past its last position
+    if (tile * kTile + kTile - 1 > pmax) dequant(tile, std::true_type{});
+    else dequant(tile, std::false_type{});
     lds_barrier();          // Z tile and P of this tile visible
     if (tile < tile_last) score(tile + 1, it + 1, (it + 1) & 1);
     contract(it & 1, it);
@@ -347,16 +358,18 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
 
   // ---------------------------------------------------------------- output
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = rt * 32 + acc_row(v, lane);
-      const int qi = rr >> 3, hh = rr & 7;
-      if (qi < nq)
-        a.part_o[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + hh) * d.rv +
-                 (ct0 + ct) * 32 + m] = acc[ct][v];
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = rt * 32 + acc_row(v, lane);
+        const int qi = rr >> 3, hh = rr & 7;
+        if (qi < nq)
+          a.part_o[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + hh) * d.rv +
+                   (ct0 + ct) * 32 + m] = acc[rt][ct][v];
+      }
     }
-  }
 #pragma unroll
   for (int qi = 0; qi < kPQ; ++qi) {
     const float l = wave_sum(l_lane[qi]);
@@ -371,17 +384,17 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
 template <int G>
 hipError_t launch_attn_g(int nct, dim3 grid, const AttnArgs& aa, hipStream_t s) {
   switch (nct) {
+    case 1: prefill_attn_kernel<G, 1><<<grid, 512, 0, s>>>(aa); break;
     case 2: prefill_attn_kernel<G, 2><<<grid, 512, 0, s>>>(aa); break;
+    case 3: prefill_attn_kernel<G, 3><<<grid, 512, 0, s>>>(aa); break;
     case 4: prefill_attn_kernel<G, 4><<<grid, 512, 0, s>>>(aa); break;
-    case 6: prefill_attn_kernel<G, 6><<<grid, 512, 0, s>>>(aa); break;
-    case 8: prefill_attn_kernel<G, 8><<<grid, 512, 0, s>>>(aa); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t s) {
-  const int nct = d.rv / 128;
+  const int nct = d.rv / 256;
   switch (d.G) {
     case 1: return launch_attn_g<1>(nct, grid, aa, s);
     case 2: return launch_attn_g<2>(nct, grid, aa, s);
