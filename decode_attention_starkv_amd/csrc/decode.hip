@@ -399,6 +399,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   __shared__ float alpha_l[2][32];
   __shared__ int flag_l[2];
   __shared__ float bias_l[32][33];
+  __shared__ float l_row[32];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -417,6 +418,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   if (tid < 64) alpha_l[tid >> 5][tid & 31] = 1.0f;
   if (tid < 2) flag_l[tid] = -1;
   for (int i = tid; i < 32 * 33; i += 512) (&bias_l[0][0])[i] = 0.0f;
+  if (tid < 32) l_row[tid] = 1.0f;
   __syncthreads();
 
   const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
@@ -518,19 +520,20 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       }
       lds_barrier();
     }
-    __syncthreads();   // value waves add their zero-point terms to bias_l
-    __syncthreads();   // value waves write their partial outputs
     if (has_keys) {
 #pragma unroll
       for (int i = 0; i < KVS * G; ++i) {
         const float l = wave_sum(l_lane[i]);
         if (lane == 0) {
           const int h = (sw + (i / G) * 4) * G + (i % G);
+          l_row[h] = l;
           a.part_ml[(obase + h) * 2] = m_ref[i];
           a.part_ml[(obase + h) * 2 + 1] = l;
         }
       }
     }
+    __syncthreads();   // value waves add their zero-point terms to bias_l
+    __syncthreads();   // value waves write their partial outputs
   } else {
     // ================================================================ values
     const int vw = wave - 4;
@@ -643,27 +646,37 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (m >= n0 && m < n0 + NIV) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
-    __syncthreads();   // bias complete; no wave uses the value ring any more
-    // The partial rows go out through LDS (this wave's region of the ring)
-    // as 16-byte stores of whole row segments instead of 4-byte scatters.
+    __syncthreads();   // bias and l complete; no wave uses the value ring any more
+    // The partial rows, divided by their l (so that fp16 holds them), go
+    // out through LDS (this wave's region of the ring) as 16-byte stores of
+    // whole row segments instead of 2-byte scatters.
     float* st = reinterpret_cast<float*>(vring) + vw * 32 * kStageRow;
+    float inv_l[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) inv_l[v] = 1.0f / l_row[acc_row(v, lane)];
 #pragma unroll
     for (int ni = 0; ni < NIV; ++ni) {
       const int n = n0 + ni;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = acc_row(v, lane);
-        st[row * kStageRow + ni * 32 + m] = fmaf(acc[ni][v], kTwo24, bias_l[row][n]);
+        st[row * kStageRow + ni * 32 + m] =
+            fmaf(acc[ni][v], kTwo24, bias_l[row][n]) * inv_l[v];
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own staging writes done
     __builtin_amdgcn_wave_barrier();
-    constexpr int kChunks = NIV * 8;       // 16-byte chunks per row segment
+    constexpr int kChunks = NIV * 4;       // 16-byte (8 x fp16) chunks per row segment
+    _Float16* po = reinterpret_cast<_Float16*>(a.part_o);
     for (int c = lane; c < 32 * kChunks; c += 64) {
       const int row = c / kChunks, k = c % kChunks;
-      if (row < d.Hq)
-        *reinterpret_cast<float4*>(a.part_o + (obase + row) * d.rv + n0 * 32 + 4 * k) =
-            *reinterpret_cast<const float4*>(st + row * kStageRow + 4 * k);
+      if (row < d.Hq) {
+        const float4 x0 = *reinterpret_cast<const float4*>(st + row * kStageRow + 8 * k);
+        const float4 x1 = *reinterpret_cast<const float4*>(st + row * kStageRow + 8 * k + 4);
+        const h8 o = {(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                      (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+        *reinterpret_cast<h8*>(po + (obase + row) * d.rv + n0 * 32 + 8 * k) = o;
+      }
     }
     __syncthreads();
     };
@@ -704,12 +717,28 @@ hipError_t launch_q43(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t
 
 // ------------------------------------------------------------------ merge --
 
+// 4 consecutive partial values as fp32 (fp32 partials: one 16-byte load;
+// fp16 partials: one 8-byte load).
+__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ inline float4 load4(const _Float16* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  // element picks go through scalars: a bit-cast applied directly to an
+  // ext_vector element is lowered as a cast of element 0
+  const uint32_t w0 = w[0], w1 = w[1];
+  const h2 a = __builtin_bit_cast(h2, w0), b = __builtin_bit_cast(h2, w1);
+  return float4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+}
+
 // One workgroup per (b, h): weights of the splits from their (m, l), the
-// weighted sum of their partial outputs, then the inverse rotation.
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
+// weighted sum of their partial outputs, then the inverse rotation.  fp32
+// partials are unnormalised sums (weight 2^(m_s - m)); fp16 partials are
+// already divided by their own l_s (weight 2^(m_s - m) * l_s).
+template <typename PT>
+__global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     Dims d, int splits,
                                                     float* __restrict__ obar) {
+  constexpr bool kNormalised = std::is_same<PT, _Float16>::value;
   __shared__ float ms[kMaxSplits], ws[kMaxSplits];
   __shared__ float buf[1024];
   __shared__ float inv_l;
@@ -729,7 +758,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     for (int s = 0; s < splits; ++s) {
       const float l = ws[s];
       const float wgt = l > 0.0f ? exp2f(ms[s] - mx) : 0.0f;
-      ms[s] = wgt;
+      ms[s] = kNormalised ? wgt * l : wgt;
       L = fmaf(wgt, l, L);
     }
     inv_l = 1.0f / L;
@@ -739,14 +768,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   // 4 consecutive channels per thread, 8 splits' loads in flight at once
   const size_t stride = (size_t)d.Hq * d.rv;
   for (int c = 4 * t; c < d.rv; c += 1024) {
-    const float* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + c;
+    const PT* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + c;
     float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
     int s = 0;
     for (; s + 8 <= splits; s += 8) {
       float4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        x[u] = *reinterpret_cast<const float4*>(src + (size_t)(s + u) * stride);
+      for (int u = 0; u < 8; ++u) x[u] = load4(src + (size_t)(s + u) * stride);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float wgt = ms[s + u];
@@ -757,7 +785,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
       }
     }
     for (; s < splits; ++s) {
-      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
+      const float4 x = load4(src + (size_t)s * stride);
       const float wgt = ms[s];
       o.x = fmaf(wgt, x.x, o.x);
       o.y = fmaf(wgt, x.y, o.y);
@@ -898,7 +926,11 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   e = launch_split<FMT>(d, dim3(lay.splits, d.B), sa, s);
   if (e != hipSuccess) return e;
   mark(2);
-  merge_kernel<<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
+  if constexpr (FMT == STARKV_CACHE_Q43)
+    merge_kernel<_Float16><<<d.B * d.Hq, 256, 0, s>>>(
+        reinterpret_cast<const _Float16*>(part_o), part_ml, d, lay.splits, obar);
+  else
+    merge_kernel<float><<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(3);
@@ -937,7 +969,7 @@ hipError_t launch_qproj_q43(const Dims& d, const void* q, const void* bk,
 hipError_t launch_merge_vproj_q43(const Dims& d, const float* part_o,
                                   const float* part_ml, int splits, const void* bv,
                                   float* obar, float* out, hipStream_t s) {
-  merge_kernel<<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, splits, obar);
+  merge_kernel<float><<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, splits, obar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   vproj_kernel<STARKV_CACHE_Q43><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64 * kVprojWaves, 0, s>>>(
