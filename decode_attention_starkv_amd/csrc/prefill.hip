@@ -6,9 +6,10 @@
 //   gemm      Z = X [A_key | A_value] (bf16 in, fp32 out) on MFMA 32x32x16
 //   append    the decode-path append kernels (rotation + 4/3-bit packing)
 //   qproj     q~ for every query of the chunk (the decode kernel, rows = B*C)
-//   attn      per (8 queries, 8 query heads): latent scores with an online
-//             softmax, then P Z_v on MFMA against an fp16 value tile
-//             dequantized once per workgroup into LDS (section 5.3, eq. 12)
+//   attn      per (16 queries, 8 query heads, half of R_v): latent scores on
+//             MFMA with an online softmax, then P Z_v on MFMA against an
+//             fp16 value tile dequantized once per workgroup into LDS
+//             (section 5.3, eq. 12)
 //   merge, vproj   the decode kernels with one split per query row
 #include <type_traits>
 
@@ -127,11 +128,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------------- attn --
 
-constexpr int kPQ = 8;        // queries per workgroup
+constexpr int kPQ = 16;       // queries per workgroup
 constexpr int kPH = 8;        // query heads per workgroup
+constexpr int kRows = kPQ * kPH;   // rows of the stacked P tile
 constexpr int kPS = 72;       // P row stride (halves)
 constexpr int kZRow = 128;    // bytes of one dequantized value channel (64 tokens)
 constexpr int kMaxRv = 1024;
+constexpr int kHalfRv = kMaxRv / 2;   // value columns per workgroup (at most)
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   Dims d;
@@ -145,113 +150,183 @@ struct AttnArgs {
   float* part_ml;         // [B*C][Hq][2]
 };
 
-// Workgroup = (8 consecutive queries, 8 query heads, sequence b), 8 waves.
-// Rows of the stacked P tile: row = query * 8 + head (64 rows, two MFMA row
-// tiles).  Per 64-token tile:
-//   phase A  all threads dequantize the tile's value latents (all R_v
-//            channels) into LDS as fp16: z + s * code, one packed fp16 FMA
-//            per token pair, rows of 64 tokens with 16-byte chunks swizzled
-//            by channel so that MFMA operand reads spread over the banks;
+// Workgroup = (16 consecutive queries, 8 query heads, half of the value
+// columns, sequence b), 8 waves.  Rows of the stacked P tile: row = query * 8
+// + head (128 rows = four MFMA row tiles).  Per 64-token tile:
+//   phase A  all threads dequantize the tile's value latents of this
+//            column half into LDS as fp16 (z + s * code: one packed fp16
+//            FMA per token pair; rows of 64 tokens, 16-byte chunks swizzled
+//            by channel so that MFMA operand reads spread over the banks);
 //   barrier
-//   phase B  wave w scores tile t+1 for query head w of the group and all 8
-//            queries (lane = token, codes as fp16 pairs in v_dot2, lazy
-//            online softmax) into the other P slot, and contracts tile t:
-//            both row tiles against its R_v / 256 column tiles on mfma
+//   phase B  wave w scores tile t+1 for query head w and all 16 queries on
+//            MFMA 16x16x32: A = the queries' latent pairs (once with only
+//            the 4-bit part, once with only the 3-bit part), B = the raw
+//            codes as fp16 subnormals, K slots in the order the packed key
+//            words give them; scales and zero points are applied to the
+//            two partial dots afterwards; a lazy online softmax writes P to
+//            the other P slot.  It also contracts tile t: row tiles 2(w&1),
+//            2(w&1)+1 against its R_v/256 value column tiles on MFMA
 //            32x32x16 f16;
 //   barrier
+// The two column halves compute the same scores; the first writes (m, l).
 // Causal mask: query i (absolute position ctx + i) sees cached positions
 // 0 .. ctx + i.  Value tokens past the workgroup's last position are zeroed
 // so that unwritten cache bytes never reach the MFMA operands.
 template <int G, int NCT>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const Dims& d = a.d;
-  __shared__ __attribute__((aligned(16))) uint8_t zt[kMaxRv * kZRow];
-  __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kPQ * kPH * kPS];
+  __shared__ __attribute__((aligned(16))) uint8_t zt[kHalfRv * kZRow];
+  __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kRows * kPS];
   __shared__ __attribute__((aligned(16))) uint32_t qrec[kPQ * kPH * kQ43Rec];
-  __shared__ float alpha_l[2][kPQ * kPH];
+  __shared__ float alpha_l[2][kRows];
   __shared__ int flag_l[2];
 
-  // XCD-aware order: consecutive workgroups of one XCD (blockIdx % 8) are
-  // the head groups of one query block, so they share value tiles in that
-  // XCD's L2; the query blocks with the longest causal span start first.
+  // XCD-aware order: the 8 workgroups of one query block (4 head groups x
+  // 2 column halves for 32 heads) run on one XCD (blockIdx % 8) and share
+  // its L2; the query blocks with the longest causal span start first.
   const int L = blockIdx.x;
   const int xcd = L & 7, k = L >> 3;
-  const int hg = k % a.n_hg;
-  const int qb = a.n_qb_pad - 1 - ((k / a.n_hg) * 8 + xcd);
+  const int per_qb = 2 * a.n_hg;
+  const int sub = k % per_qb;
+  const int hg = sub % a.n_hg, cs = sub / a.n_hg;
+  const int qb = a.n_qb_pad - 1 - ((k / per_qb) * 8 + xcd);
   if (qb >= a.n_qb) return;   // padding workgroup; uniform, before any barrier
   const int b = blockIdx.y;
   const int q0 = qb * kPQ;
   const int nq = min(kPQ, a.chunk - q0);
-  const int pmax = a.ctx + q0 + nq - 1;     // last position any row may see
+  const int pfirst = a.ctx + q0;            // first query's position
+  const int pmax = pfirst + nq - 1;         // last position any row may see
   const int tile_last = pmax / kTile;
+  const int cols = d.rv / 2, col0 = cs * cols;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m = lane & 31, j = lane >> 5;
+  const int m = lane & 31, j = lane >> 5;   // 32x32 operand coordinates
+  const int c16 = lane & 15, g16 = lane >> 4;  // 16x16 operand coordinates
 
-  for (int i = tid; i < 2 * kPQ * kPH * kPS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
+  for (int i = tid; i < 2 * kRows * kPS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
   for (int i = tid; i < kPQ * kPH * kQ43Rec; i += 512) {
     const int qi = i / (kPH * kQ43Rec), r = i % (kPH * kQ43Rec);
     qrec[i] = qi < nq ? a.qt[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH) * kQ43Rec + r]
                       : 0u;
   }
-  if (tid < 2 * kPQ * kPH) (&alpha_l[0][0])[tid] = 1.0f;
+  if (tid < 2 * kRows) (&alpha_l[0][0])[tid] = 1.0f;
   if (tid < 2) flag_l[tid] = -1;
   __syncthreads();
 
-  // ---------------------------------------------------------------- scores
+  // ------------------------------------------------------------ score setup
   const int hl = wave;                          // query head within the group
   const int h = hg * kPH + hl;
   const int g = h / G;
-  float m_ref[kPQ], l_lane[kPQ];
+  // K group of this lane's 16x16x32 operands: the record holds the 4 hi
+  // pairs then the 12 lo pairs (channel order of the key words); K group 0
+  // = hi pairs, 1 = lo pairs 0-3, 2 = lo pairs 5-8, 3 = lo pairs 4, 9-11.
+  int qidx[4];
+  if (g16 == 0) { qidx[0] = 0; qidx[1] = 1; qidx[2] = 2; qidx[3] = 3; }
+  else if (g16 == 1) { qidx[0] = 4; qidx[1] = 5; qidx[2] = 6; qidx[3] = 7; }
+  else if (g16 == 2) { qidx[0] = 9; qidx[1] = 10; qidx[2] = 11; qidx[3] = 12; }
+  else { qidx[0] = 8; qidx[1] = 13; qidx[2] = 14; qidx[3] = 15; }
+  // per lane: queries g16*4 + v (v < 4) of the 16x16 result
+  float m_ref[4], l_lane[4];
 #pragma unroll
-  for (int i = 0; i < kPQ; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
+  for (int v = 0; v < 4; ++v) { m_ref[v] = -INFINITY; l_lane[v] = 0.0f; }
 
+  // scores of tile `tile` (pair index it) into P slot `slot`
   auto score = [&](int tile, int it, int slot) {
+    // A operands (rows = queries c16): once with only the 4-bit part of the
+    // query pairs, once with only the 3-bit part; and the queries' sums
+    h8 a_hi, a_lo;
+    {
+      const uint32_t* rec = qrec + (c16 * kPH + hl) * kQ43Rec;
+      const h8 v = __builtin_bit_cast(h8, u32x4{rec[qidx[0]], rec[qidx[1]], rec[qidx[2]], rec[qidx[3]]});
+      a_hi = g16 == 0 ? v : h8{};
+      a_lo = g16 == 0 ? h8{} : v;
+    }
+    float qs_hi[4], qs_lo[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t* rec = qrec + ((g16 * 4 + v) * kPH + hl) * kQ43Rec;
+      qs_hi[v] = __builtin_bit_cast(float, rec[16]);
+      qs_lo[v] = __builtin_bit_cast(float, rec[17]);
+    }
     const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + g;
     const uint8_t* kb = a.key + blk * kKeyBlock;
-    uint32_t kc[6];
-    kc[0] = reinterpret_cast<const uint32_t*>(kb)[lane];
-    kc[1] = reinterpret_cast<const uint32_t*>(kb + 256)[lane];
-    kc[2] = reinterpret_cast<const uint32_t*>(kb + 512)[lane];
-    kc[3] = kb[768 + lane];
-    const u32x2 mt = a.kmeta[blk * kTile + lane];
-    kc[4] = mt[0];
-    kc[5] = mt[1];
-    const KeyLane kl = unpack_key_lane(kc);
-    const int tok = tile * kTile + lane;
-    float x[kPQ];
+    const bool masked = tile * kTile + kTile - 1 > pfirst;   // uniform
+    float x[4][4];   // [16-token block][query v]
 #pragma unroll
-    for (int qi = 0; qi < kPQ; ++qi) {
-      const bool valid = qi < nq && tok <= a.ctx + q0 + qi;
-      const float sc = key_score(kl, qrec + (qi * kPH + hl) * kQ43Rec);
-      x[qi] = valid ? sc : -INFINITY;
+    for (int bl = 0; bl < 4; ++bl) {
+      const int u = bl * 16 + c16;            // token within the tile
+      // this lane's 4 code pairs for K group g16
+      const uint32_t wa = reinterpret_cast<const uint32_t*>(kb + (g16 == 0 ? 0 : g16 == 2 ? 512 : 256))[u];
+      uint32_t bw[4];
+      if (g16 < 3) {
+        const int sh = g16 == 0 ? 4 : 3;
+        const uint32_t mk = g16 == 0 ? 0x000F000Fu : 0x00070007u;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) bw[kk] = (wa >> (sh * kk)) & mk;
+      } else {
+        const uint32_t w1 = reinterpret_cast<const uint32_t*>(kb + 512)[u];
+        const uint32_t r8 = kb[768 + u];
+        const uint32_t R = r8 | (((wa >> 15) & 1u) << 8) | ((wa >> 31) << 9) |
+                           (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
+        bw[0] = (wa >> 12) & 0x00070007u;
+        bw[1] = (w1 >> 12) & 0x00070007u;
+        bw[2] = (R & 7u) | (((R >> 6) & 7u) << 16);
+        bw[3] = ((R >> 3) & 7u) | (((R >> 9) & 7u) << 16);
+      }
+      const h8 bv = __builtin_bit_cast(h8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+      const f32x4v dh = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bv, f32x4v{}, 0, 0, 0);
+      const f32x4v dl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bv, f32x4v{}, 0, 0, 0);
+      const u32x2 mt = a.kmeta[blk * kTile + u];
+      const uint32_t m0 = mt[0], m1 = mt[1];
+      const float s_hi = f16v(m0 & 0xFFFFu) * kTwo24, z_hi = f16v(m0 >> 16);
+      const float s_lo = f16v(m1 & 0xFFFFu) * kTwo24, z_lo = f16v(m1 >> 16);
+      const int tok = tile * kTile + u;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int q = g16 * 4 + v;
+        const float sc = fmaf(s_hi, dh[v], fmaf(z_hi, qs_hi[v], fmaf(s_lo, dl[v], z_lo * qs_lo[v])));
+        x[bl][v] = (!masked || (q < nq && tok <= pfirst + q)) ? sc : -INFINITY;
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (g16 * 4 + v >= nq) x[bl][v] = -INFINITY;
     }
     bool big = false;
 #pragma unroll
-    for (int qi = 0; qi < kPQ; ++qi) big |= x[qi] > m_ref[qi] + kLazy;
+    for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) big |= x[bl][v] > m_ref[v] + kLazy;
     if (__builtin_amdgcn_ballot_w64(big) != 0) {
 #pragma unroll
-      for (int qi = 0; qi < kPQ; ++qi) {
+      for (int v = 0; v < 4; ++v) {
+        float gm = fmaxf(fmaxf(x[0][v], x[1][v]), fmaxf(x[2][v], x[3][v]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
         float alpha = 1.0f;
-        if (__builtin_amdgcn_ballot_w64(x[qi] > m_ref[qi] + kLazy) != 0) {
-          const float mx = wave_max(x[qi]);
-          alpha = m_ref[qi] == -INFINITY ? 0.0f : exp2f(m_ref[qi] - mx);
-          m_ref[qi] = mx;
-          l_lane[qi] *= alpha;
-          if (lane == 0) flag_l[slot] = it;
+        if (gm > m_ref[v] + kLazy) {          // uniform in the 16-lane group
+          alpha = m_ref[v] == -INFINITY ? 0.0f : exp2f(m_ref[v] - gm);
+          m_ref[v] = gm;
+          l_lane[v] *= alpha;
+          if (c16 == 0) flag_l[slot] = it;
         }
-        if (lane == 0) alpha_l[slot][qi * kPH + hl] = alpha;
+        if (c16 == 0) alpha_l[slot][(g16 * 4 + v) * kPH + hl] = alpha;
       }
     } else if (lane < kPQ) {
       alpha_l[slot][lane * kPH + hl] = 1.0f;
     }
 #pragma unroll
-    for (int qi = 0; qi < kPQ; ++qi) {
-      const float p = x[qi] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[qi] - m_ref[qi]);
-      l_lane[qi] += p;
-      p_l[slot][(qi * kPH + hl) * kPS + lane] = (_Float16)p;
-    }
+    for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = x[bl][v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[bl][v] - m_ref[v]);
+        l_lane[v] += p;
+        p_l[slot][((g16 * 4 + v) * kPH + hl) * kPS + bl * 16 + c16] = (_Float16)p;
+      }
   };
 
   // ----------------------------------------------------- value dequantize
@@ -259,27 +334,29 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int NH = d.rv / 128;          // 4-bit value groups
   const size_t vtile_bytes = (size_t)26 * d.rv;
   const size_t mtile = (size_t)2 * NG * kTile;     // fp16 elements
+  const int g_first = col0 / 32;      // first value group of this half
   auto dequant = [&](int tile, auto maskc) {
     constexpr bool kMask = decltype(maskc)::value;
     const size_t t = (size_t)b * d.NT + tile;
     const uint8_t* vb = a.value + t * vtile_bytes;
     const uint16_t* vm = a.vmeta + t * mtile;
     const int tok_base = tile * kTile;
-    for (int r = tid; r < 2 * d.rv; r += 512) {
-      const int gi = r >> 6, e = r & 63;          // group; (half, channel) in it
+    for (int r = tid; r < 2 * cols; r += 512) {
+      const int gl = r >> 6, e = r & 63;          // group in the half; (half, channel)
+      const int gi = g_first + gl;
       const int jj = e >> 5, c = e & 31;
       const bool four = gi < NH;                  // uniform per wave
       u32x4 w;
       if (four) {
         w = *reinterpret_cast<const u32x4*>(vb + (size_t)gi * 1024 + e * 16);
       } else {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(vb + (size_t)NH * 1024 +
-                                                              (size_t)(gi - NH) * 768 + e * 12);
-        w = u32x4{p[0], p[1], p[2], 0u};
+        const uint32_t* pw = reinterpret_cast<const uint32_t*>(vb + (size_t)NH * 1024 +
+                                                               (size_t)(gi - NH) * 768 + e * 12);
+        w = u32x4{pw[0], pw[1], pw[2], 0u};
       }
       const u32x4* sp = reinterpret_cast<const u32x4*>(vm + (size_t)gi * kTile + 32 * jj);
       const u32x4* zp = reinterpret_cast<const u32x4*>(vm + (size_t)(NG + gi) * kTile + 32 * jj);
-      const int ch = gi * 32 + c;
+      const int ch = gl * 32 + c;                 // column within the half
       uint8_t* row = zt + (size_t)ch * kZRow;
       const int t0 = tok_base + 32 * jj;
 #pragma unroll
@@ -311,9 +388,11 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   };
 
   // -------------------------------------------------------------- contract
-  // Wave w owns value column tiles w*NCT .. w*NCT+NCT-1 for both row tiles,
-  // so each value fragment read from LDS feeds two MFMAs.
-  const int ct0 = wave * NCT;
+  // Wave w: row tiles rt0 = 2 (w & 1) and rt0 + 1, value column tiles
+  // (w >> 1) * NCT .. + NCT - 1 of this half; each value fragment read from
+  // LDS feeds two MFMAs and each P fragment NCT.
+  const int rt0 = 2 * (wave & 1);
+  const int ct0 = (wave >> 1) * NCT;
   f32x16 acc[2][NCT];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
@@ -326,15 +405,15 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float al = alpha_l[slot][rt * 32 + acc_row(v, lane)];
+          const float al = alpha_l[slot][(rt0 + rt) * 32 + acc_row(v, lane)];
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) acc[rt][ct][v] *= al;
         }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const h8 A0 = *reinterpret_cast<const h8*>(&p_l[slot][m * kPS + 32 * j + 8 * r]);
-      const h8 A1 = *reinterpret_cast<const h8*>(&p_l[slot][(32 + m) * kPS + 32 * j + 8 * r]);
+      const h8 A0 = *reinterpret_cast<const h8*>(&p_l[slot][(rt0 * 32 + m) * kPS + 32 * j + 8 * r]);
+      const h8 A1 = *reinterpret_cast<const h8*>(&p_l[slot][((rt0 + 1) * 32 + m) * kPS + 32 * j + 8 * r]);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const uint8_t* row = zt + (size_t)((ct0 + ct) * 32 + m) * kZRow;
@@ -350,10 +429,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
     // only the workgroup's last tile can hold tokens past its last position
     if (tile * kTile + kTile - 1 > pmax) dequant(tile, std::true_type{});
     else dequant(tile, std::false_type{});
-    lds_barrier();          // Z tile and P of this tile visible
+    lds_barrier();          // value tile and P of this tile visible
     if (tile < tile_last) score(tile + 1, it + 1, (it + 1) & 1);
+    // keep the scoring and the contraction apart (register pressure); the
+    // other wave of the SIMD overlaps them
+    __builtin_amdgcn_sched_barrier(0);
     contract(it & 1, it);
-    lds_barrier();          // Z tile and this P slot free
+    lds_barrier();          // value tile and this P slot free
   }
 
   // ---------------------------------------------------------------- output
@@ -363,20 +445,25 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int rr = rt * 32 + acc_row(v, lane);
+        const int rr = (rt0 + rt) * 32 + acc_row(v, lane);
         const int qi = rr >> 3, hh = rr & 7;
         if (qi < nq)
           a.part_o[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + hh) * d.rv +
-                   (ct0 + ct) * 32 + m] = acc[rt][ct][v];
+                   col0 + (ct0 + ct) * 32 + m] = acc[rt][ct][v];
       }
     }
+  if (cs == 0) {
 #pragma unroll
-  for (int qi = 0; qi < kPQ; ++qi) {
-    const float l = wave_sum(l_lane[qi]);
-    if (lane == 0 && qi < nq) {
-      const size_t o = (((size_t)b * a.chunk + q0 + qi) * d.Hq + h) * 2;
-      a.part_ml[o] = m_ref[qi];
-      a.part_ml[o + 1] = l;
+    for (int v = 0; v < 4; ++v) {
+      float l = l_lane[v];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o);
+      const int q = g16 * 4 + v;
+      if (c16 == 0 && q < nq) {
+        const size_t o = (((size_t)b * a.chunk + q0 + q) * d.Hq + h) * 2;
+        a.part_ml[o] = m_ref[v];
+        a.part_ml[o + 1] = l;
+      }
     }
   }
 }
@@ -496,7 +583,7 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   aa.qt = static_cast<const uint32_t*>(qt);
   aa.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   aa.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
-  e = launch_attn(d, dim3(aa.n_qb_pad * aa.n_hg, d.B), aa, s);
+  e = launch_attn(d, dim3(aa.n_qb_pad * aa.n_hg * 2, d.B), aa, s);
   if (e != hipSuccess) return e;
   mark(4);
 
