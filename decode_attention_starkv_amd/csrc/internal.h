@@ -64,7 +64,7 @@ hipError_t launch_merge_vproj_q43(const Dims& d, const float* part_o,
 
 // Workspace carve-up of one prefill call (byte offsets, 256-aligned).
 struct PrefillWs {
-  size_t zk, zv, qt, part_o, part_ml, obar, total;
+  size_t zk, zv, qt, kd, part_o, part_ml, obar, total;
 };
 PrefillWs prefill_ws_layout(const Dims& d, int chunk);
 hipError_t launch_prefill(const Dims& d, const starkv_cache& cache,

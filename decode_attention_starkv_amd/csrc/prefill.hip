@@ -126,6 +126,61 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     }
 }
 
+__device__ inline void wait_vmcnt0() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ------------------------------------------------------------- key dequant --
+
+// fp16 key latents z + s * code of positions [0, n) of every sequence and KV
+// head, channels in their natural order: [B][T_max][Hkv][32] (64 bytes per
+// token and head).  One thread per (sequence, position, KV head).  The
+// attention kernel reads them as MFMA operands.
+__global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restrict__ key,
+                                                          const u32x2* __restrict__ kmeta,
+                                                          Dims d, int n,
+                                                          _Float16* __restrict__ kd) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)d.B * n * d.Hkv) return;
+  const int h = idx % d.Hkv;
+  const int t = (idx / d.Hkv) % n;
+  const int b = idx / ((size_t)d.Hkv * n);
+  const int tile = t / kTile, u = t % kTile;
+  const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + h;
+  const uint8_t* kb = key + blk * kKeyBlock;
+  const uint32_t whi = reinterpret_cast<const uint32_t*>(kb)[u];
+  const uint32_t w0 = reinterpret_cast<const uint32_t*>(kb + 256)[u];
+  const uint32_t w1 = reinterpret_cast<const uint32_t*>(kb + 512)[u];
+  const uint32_t R = kb[768 + u] | (((w0 >> 15) & 1u) << 8) | ((w0 >> 31) << 9) |
+                     (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
+  const u32x2 mt = kmeta[blk * kTile + u];
+  const uint32_t m0 = mt[0], m1 = mt[1];
+  const _Float16 s_hi = __builtin_bit_cast(_Float16, (uint16_t)(m0 & 0xFFFFu));
+  const _Float16 z_hi = __builtin_bit_cast(_Float16, (uint16_t)(m0 >> 16));
+  const _Float16 s_lo = __builtin_bit_cast(_Float16, (uint16_t)(m1 & 0xFFFFu));
+  const _Float16 z_lo = __builtin_bit_cast(_Float16, (uint16_t)(m1 >> 16));
+  _Float16 v[32];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    v[c] = (_Float16)fmaf((float)s_hi, (float)((whi >> (4 * c)) & 15u), (float)z_hi);
+  // 3-bit channel i (= key channel 8 + i): i < 5 lo0 bits 3i, i < 10 lo1
+  // bits 3(i-5), i < 15 lo0 bits 16+3(i-10), i < 20 lo1 bits 16+3(i-15),
+  // else bits 3(i-20) of the 12-bit remainder
+#pragma unroll
+  for (int i = 0; i < 24; ++i) {
+    uint32_t code;
+    if (i < 5) code = (w0 >> (3 * i)) & 7u;
+    else if (i < 10) code = (w1 >> (3 * (i - 5))) & 7u;
+    else if (i < 15) code = (w0 >> (16 + 3 * (i - 10))) & 7u;
+    else if (i < 20) code = (w1 >> (16 + 3 * (i - 15))) & 7u;
+    else code = (R >> (3 * (i - 20))) & 7u;
+    v[8 + i] = (_Float16)fmaf((float)s_lo, (float)code, (float)z_lo);
+  }
+  h8* dst = reinterpret_cast<h8*>(kd + (((size_t)b * d.Tmax + t) * d.Hkv + h) * 32);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    dst[k] = h8{v[8 * k], v[8 * k + 1], v[8 * k + 2], v[8 * k + 3],
+                v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]};
+}
+
 // ------------------------------------------------------------------- attn --
 
 constexpr int kPQ = 16;       // queries per workgroup
@@ -135,6 +190,11 @@ constexpr int kPS = 72;       // P row stride (halves)
 constexpr int kZRow = 128;    // bytes of one dequantized value channel (64 tokens)
 constexpr int kMaxRv = 1024;
 constexpr int kHalfRv = kMaxRv / 2;   // value columns per workgroup (at most)
+// packed value data of one tile and one column half, staged in LDS: codes
+// (at most 8 four-bit + 8 three-bit groups), then scales, then zeros
+constexpr int kVCodeMax = 8 * 1024 + 8 * 768;
+constexpr int kVMetaMax = (kHalfRv / 32) * kTile * 2;
+constexpr int kVSlot = kVCodeMax + 2 * kVMetaMax;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -146,6 +206,7 @@ struct AttnArgs {
   const uint8_t* value;
   const uint16_t* vmeta;
   const uint32_t* qt;     // [B*C][Hq][kQ43Rec]
+  const _Float16* kd;     // [B][T_max][Hkv][32] fp16 key latents
   float* part_o;          // [B*C][Hq][R_v]
   float* part_ml;         // [B*C][Hq][2]
 };
@@ -159,12 +220,10 @@ struct AttnArgs {
 //            by channel so that MFMA operand reads spread over the banks);
 //   barrier
 //   phase B  wave w scores tile t+1 for query head w and all 16 queries on
-//            MFMA 16x16x32: A = the queries' latent pairs (once with only
-//            the 4-bit part, once with only the 3-bit part), B = the raw
-//            codes as fp16 subnormals, K slots in the order the packed key
-//            words give them; scales and zero points are applied to the
-//            two partial dots afterwards; a lazy online softmax writes P to
-//            the other P slot.  It also contracts tile t: row tiles 2(w&1),
+//            MFMA 16x16x32 (A = the queries' latent vectors, B = the fp16
+//            key latents a pre-pass dequantized from the packed cache); a
+//            lazy online softmax writes P to the other P slot.  It also
+//            contracts tile t: row tiles 2(w&1),
 //            2(w&1)+1 against its R_v/256 value column tiles on MFMA
 //            32x32x16 f16;
 //   barrier
@@ -177,7 +236,9 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const Dims& d = a.d;
   __shared__ __attribute__((aligned(16))) uint8_t zt[kHalfRv * kZRow];
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kRows * kPS];
-  __shared__ __attribute__((aligned(16))) uint32_t qrec[kPQ * kPH * kQ43Rec];
+  // the queries' latent vectors in natural channel order (fp16)
+  __shared__ __attribute__((aligned(16))) _Float16 qnat[kPQ * kPH * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t vst[2][kVSlot];
   __shared__ float alpha_l[2][kRows];
   __shared__ int flag_l[2];
 
@@ -205,10 +266,23 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int c16 = lane & 15, g16 = lane >> 4;  // 16x16 operand coordinates
 
   for (int i = tid; i < 2 * kRows * kPS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
-  for (int i = tid; i < kPQ * kPH * kQ43Rec; i += 512) {
-    const int qi = i / (kPH * kQ43Rec), r = i % (kPH * kQ43Rec);
-    qrec[i] = qi < nq ? a.qt[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH) * kQ43Rec + r]
-                      : 0u;
+  // the query records hold 16 channel pairs (lo half, hi half) in the order
+  // of the packed key words; put every channel back in its place
+  for (int i = tid; i < kPQ * kPH * 16; i += 512) {
+    const int qh = i >> 4, t = i & 15;       // (query, head) and pair
+    const int qi = qh / kPH;
+    int ca, cb;
+    if (t < 4) { ca = t; cb = t + 4; }
+    else if (t < 9) { ca = 8 + (t - 4); cb = 18 + (t - 4); }
+    else if (t < 14) { ca = 13 + (t - 9); cb = 23 + (t - 9); }
+    else if (t == 14) { ca = 28; cb = 30; }
+    else { ca = 29; cb = 31; }
+    const uint32_t pr = qi < nq
+        ? a.qt[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH) * kQ43Rec +
+               (qh % kPH) * kQ43Rec + t]
+        : 0u;
+    qnat[qh * 32 + ca] = __builtin_bit_cast(_Float16, (uint16_t)(pr & 0xFFFFu));
+    qnat[qh * 32 + cb] = __builtin_bit_cast(_Float16, (uint16_t)(pr >> 16));
   }
   if (tid < 2 * kRows) (&alpha_l[0][0])[tid] = 1.0f;
   if (tid < 2) flag_l[tid] = -1;
@@ -218,83 +292,37 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int hl = wave;                          // query head within the group
   const int h = hg * kPH + hl;
   const int g = h / G;
-  // K group of this lane's 16x16x32 operands: the record holds the 4 hi
-  // pairs then the 12 lo pairs (channel order of the key words); K group 0
-  // = hi pairs, 1 = lo pairs 0-3, 2 = lo pairs 5-8, 3 = lo pairs 4, 9-11.
-  int qidx[4];
-  if (g16 == 0) { qidx[0] = 0; qidx[1] = 1; qidx[2] = 2; qidx[3] = 3; }
-  else if (g16 == 1) { qidx[0] = 4; qidx[1] = 5; qidx[2] = 6; qidx[3] = 7; }
-  else if (g16 == 2) { qidx[0] = 9; qidx[1] = 10; qidx[2] = 11; qidx[3] = 12; }
-  else { qidx[0] = 8; qidx[1] = 13; qidx[2] = 14; qidx[3] = 15; }
   // per lane: queries g16*4 + v (v < 4) of the 16x16 result
   float m_ref[4], l_lane[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) { m_ref[v] = -INFINITY; l_lane[v] = 0.0f; }
+  // P tile: row R, token u stored at chunk (u / 8) ^ (R / 32) of the row, so
+  // that the four row tiles' writes fall in different LDS banks
+  auto p_at = [&](int slot, int R, int u) -> _Float16* {
+    return &p_l[slot][R * kPS + (((u >> 3) ^ (R >> 5)) << 3) + (u & 7)];
+  };
 
-  // scores of tile `tile` (pair index it) into P slot `slot`
+  // scores of tile `tile` (index it in the loop) into P slot `slot`: MFMA
+  // 16x16x32 with A = the 16 queries' latent vectors, B = 16 tokens' fp16
+  // key latents, both in natural channel order
   auto score = [&](int tile, int it, int slot) {
-    // A operands (rows = queries c16): once with only the 4-bit part of the
-    // query pairs, once with only the 3-bit part; and the queries' sums
-    h8 a_hi, a_lo;
-    {
-      const uint32_t* rec = qrec + (c16 * kPH + hl) * kQ43Rec;
-      const h8 v = __builtin_bit_cast(h8, u32x4{rec[qidx[0]], rec[qidx[1]], rec[qidx[2]], rec[qidx[3]]});
-      a_hi = g16 == 0 ? v : h8{};
-      a_lo = g16 == 0 ? h8{} : v;
-    }
-    float qs_hi[4], qs_lo[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint32_t* rec = qrec + ((g16 * 4 + v) * kPH + hl) * kQ43Rec;
-      qs_hi[v] = __builtin_bit_cast(float, rec[16]);
-      qs_lo[v] = __builtin_bit_cast(float, rec[17]);
-    }
-    const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + g;
-    const uint8_t* kb = a.key + blk * kKeyBlock;
+    const h8 aq = *reinterpret_cast<const h8*>(&qnat[(c16 * kPH + hl) * 32 + g16 * 8]);
     const bool masked = tile * kTile + kTile - 1 > pfirst;   // uniform
+    const _Float16* kdt = a.kd + (((size_t)b * d.Tmax + tile * kTile) * d.Hkv + g) * 32 + g16 * 8;
+    h8 bk[4];
+#pragma unroll
+    for (int bl = 0; bl < 4; ++bl)
+      bk[bl] = *reinterpret_cast<const h8*>(kdt + (size_t)(bl * 16 + c16) * d.Hkv * 32);
     float x[4][4];   // [16-token block][query v]
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl) {
-      const int u = bl * 16 + c16;            // token within the tile
-      // this lane's 4 code pairs for K group g16
-      const uint32_t wa = reinterpret_cast<const uint32_t*>(kb + (g16 == 0 ? 0 : g16 == 2 ? 512 : 256))[u];
-      uint32_t bw[4];
-      if (g16 < 3) {
-        const int sh = g16 == 0 ? 4 : 3;
-        const uint32_t mk = g16 == 0 ? 0x000F000Fu : 0x00070007u;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) bw[kk] = (wa >> (sh * kk)) & mk;
-      } else {
-        const uint32_t w1 = reinterpret_cast<const uint32_t*>(kb + 512)[u];
-        const uint32_t r8 = kb[768 + u];
-        const uint32_t R = r8 | (((wa >> 15) & 1u) << 8) | ((wa >> 31) << 9) |
-                           (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
-        bw[0] = (wa >> 12) & 0x00070007u;
-        bw[1] = (w1 >> 12) & 0x00070007u;
-        bw[2] = (R & 7u) | (((R >> 6) & 7u) << 16);
-        bw[3] = ((R >> 3) & 7u) | (((R >> 9) & 7u) << 16);
-      }
-      const h8 bv = __builtin_bit_cast(h8, u32x4{bw[0], bw[1], bw[2], bw[3]});
-      const f32x4v dh = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bv, f32x4v{}, 0, 0, 0);
-      const f32x4v dl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bv, f32x4v{}, 0, 0, 0);
-      const u32x2 mt = a.kmeta[blk * kTile + u];
-      const uint32_t m0 = mt[0], m1 = mt[1];
-      const float s_hi = f16v(m0 & 0xFFFFu) * kTwo24, z_hi = f16v(m0 >> 16);
-      const float s_lo = f16v(m1 & 0xFFFFu) * kTwo24, z_lo = f16v(m1 >> 16);
-      const int tok = tile * kTile + u;
+      const f32x4v dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bk[bl], f32x4v{}, 0, 0, 0);
+      const int tok = tile * kTile + bl * 16 + c16;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int q = g16 * 4 + v;
-        const float sc = fmaf(s_hi, dh[v], fmaf(z_hi, qs_hi[v], fmaf(s_lo, dl[v], z_lo * qs_lo[v])));
-        x[bl][v] = (!masked || (q < nq && tok <= pfirst + q)) ? sc : -INFINITY;
+        x[bl][v] = (!masked || (q < nq && tok <= pfirst + q)) ? dq[v] : -INFINITY;
       }
-    }
-    if (masked) {
-#pragma unroll
-      for (int bl = 0; bl < 4; ++bl)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (g16 * 4 + v >= nq) x[bl][v] = -INFINITY;
     }
     bool big = false;
 #pragma unroll
@@ -325,7 +353,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
       for (int v = 0; v < 4; ++v) {
         const float p = x[bl][v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[bl][v] - m_ref[v]);
         l_lane[v] += p;
-        p_l[slot][((g16 * 4 + v) * kPH + hl) * kPS + bl * 16 + c16] = (_Float16)p;
+        *p_at(slot, (g16 * 4 + v) * kPH + hl, bl * 16 + c16) = (_Float16)p;
       }
   };
 
@@ -335,27 +363,50 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const size_t vtile_bytes = (size_t)26 * d.rv;
   const size_t mtile = (size_t)2 * NG * kTile;     // fp16 elements
   const int g_first = col0 / 32;      // first value group of this half
-  auto dequant = [&](int tile, auto maskc) {
-    constexpr bool kMask = decltype(maskc)::value;
+  const int ngh = cols / 32;          // value groups of this half
+  auto goff = [&](int gi) { return gi < NH ? gi * 1024 : NH * 1024 + (gi - NH) * 768; };
+  const int code_lo = goff(g_first), code_bytes = goff(g_first + ngh) - code_lo;
+  const int meta_bytes = ngh * kTile * 2;
+  // direct-to-LDS copy of one tile's codes, scales and zeros of this half
+  // into ring slot `slot`; wave w moves the 1 KB pieces w, w + 8, ...
+  auto stage = [&](int tile, int slot) {
     const size_t t = (size_t)b * d.NT + tile;
-    const uint8_t* vb = a.value + t * vtile_bytes;
-    const uint16_t* vm = a.vmeta + t * mtile;
+    const uint8_t* src[3] = {a.value + t * vtile_bytes + code_lo,
+                             reinterpret_cast<const uint8_t*>(a.vmeta + t * mtile + (size_t)g_first * kTile),
+                             reinterpret_cast<const uint8_t*>(a.vmeta + t * mtile + (size_t)(NG + g_first) * kTile)};
+    const int len[3] = {code_bytes, meta_bytes, meta_bytes};
+    const int dst[3] = {0, kVCodeMax, kVCodeMax + kVMetaMax};
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      for (int piece = wave; piece * 1024 < len[k]; piece += 8) {
+        const int off = piece * 1024 + lane * 16;
+        if (off < len[k])
+          __builtin_amdgcn_global_load_lds(
+              src[k] + off,
+              (__attribute__((address_space(3))) void*)(&vst[slot][dst[k] + piece * 1024]), 16, 0, 0);
+      }
+  };
+  auto dequant = [&](int tile, int slot, auto maskc) {
+    constexpr bool kMask = decltype(maskc)::value;
+    const uint8_t* vb = vst[slot];
+    const uint16_t* vm_s = reinterpret_cast<const uint16_t*>(vb + kVCodeMax);
+    const uint16_t* vm_z = reinterpret_cast<const uint16_t*>(vb + kVCodeMax + kVMetaMax);
     const int tok_base = tile * kTile;
     for (int r = tid; r < 2 * cols; r += 512) {
       const int gl = r >> 6, e = r & 63;          // group in the half; (half, channel)
       const int gi = g_first + gl;
       const int jj = e >> 5, c = e & 31;
       const bool four = gi < NH;                  // uniform per wave
+      const uint8_t* gp = vb + goff(gi) - code_lo;
       u32x4 w;
       if (four) {
-        w = *reinterpret_cast<const u32x4*>(vb + (size_t)gi * 1024 + e * 16);
+        w = *reinterpret_cast<const u32x4*>(gp + e * 16);
       } else {
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>(vb + (size_t)NH * 1024 +
-                                                               (size_t)(gi - NH) * 768 + e * 12);
+        const uint32_t* pw = reinterpret_cast<const uint32_t*>(gp + e * 12);
         w = u32x4{pw[0], pw[1], pw[2], 0u};
       }
-      const u32x4* sp = reinterpret_cast<const u32x4*>(vm + (size_t)gi * kTile + 32 * jj);
-      const u32x4* zp = reinterpret_cast<const u32x4*>(vm + (size_t)(NG + gi) * kTile + 32 * jj);
+      const u32x4* sp = reinterpret_cast<const u32x4*>(vm_s + gl * kTile + 32 * jj);
+      const u32x4* zp = reinterpret_cast<const u32x4*>(vm_z + gl * kTile + 32 * jj);
       const int ch = gl * 32 + c;                 // column within the half
       uint8_t* row = zt + (size_t)ch * kZRow;
       const int t0 = tok_base + 32 * jj;
@@ -412,8 +463,8 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const h8 A0 = *reinterpret_cast<const h8*>(&p_l[slot][(rt0 * 32 + m) * kPS + 32 * j + 8 * r]);
-      const h8 A1 = *reinterpret_cast<const h8*>(&p_l[slot][((rt0 + 1) * 32 + m) * kPS + 32 * j + 8 * r]);
+      const h8 A0 = *reinterpret_cast<const h8*>(p_at(slot, rt0 * 32 + m, 32 * j + 8 * r));
+      const h8 A1 = *reinterpret_cast<const h8*>(p_at(slot, (rt0 + 1) * 32 + m, 32 * j + 8 * r));
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const uint8_t* row = zt + (size_t)((ct0 + ct) * 32 + m) * kZRow;
@@ -424,18 +475,24 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
     }
   };
 
+  stage(0, 0);
   score(0, 0, 0);
+  wait_vmcnt0();
+  __syncthreads();          // packed values of tile 0 in LDS
   for (int tile = 0, it = 0; tile <= tile_last; ++tile, ++it) {
+    // packed values of the next tile stream in while this one is processed
+    if (tile < tile_last) stage(tile + 1, (it + 1) & 1);
     // only the workgroup's last tile can hold tokens past its last position
-    if (tile * kTile + kTile - 1 > pmax) dequant(tile, std::true_type{});
-    else dequant(tile, std::false_type{});
+    if (tile * kTile + kTile - 1 > pmax) dequant(tile, it & 1, std::true_type{});
+    else dequant(tile, it & 1, std::false_type{});
     lds_barrier();          // value tile and P of this tile visible
     if (tile < tile_last) score(tile + 1, it + 1, (it + 1) & 1);
     // keep the scoring and the contraction apart (register pressure); the
     // other wave of the SIMD overlaps them
     __builtin_amdgcn_sched_barrier(0);
     contract(it & 1, it);
-    lds_barrier();          // value tile and this P slot free
+    wait_vmcnt0();          // this wave's pieces of the next tile have landed
+    lds_barrier();          // value tile and this P slot free; next tile staged
   }
 
   // ---------------------------------------------------------------- output
@@ -505,6 +562,8 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
   off += align256p(M * d.rv * 4);
   w.qt = off;
   off += align256p(M * d.Hq * kQ43Rec * 4);
+  w.kd = off;   // fp16 key latents of every cached position, [B][T_max][Hkv][32]
+  off += align256p((size_t)d.B * d.Tmax * d.Hkv * 32 * 2);
   w.part_o = off;
   off += align256p(M * d.Hq * d.rv * 4);
   w.part_ml = off;
@@ -560,6 +619,17 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   if (e != hipSuccess) return e;
   mark(2);
 
+  // fp16 key latents of every position the chunk's queries can see
+  _Float16* kd = reinterpret_cast<_Float16*>(ws + lay.kd);
+  {
+    const int n = ctx_len + chunk;
+    const size_t items = (size_t)d.B * n * d.Hkv;
+    key_dequant_kernel<<<(unsigned)((items + 255) / 256), 256, 0, s>>>(
+        static_cast<const uint8_t*>(cache.key), static_cast<const u32x2*>(cache.key_meta), d, n, kd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
   // query records for every (query, head) of the chunk
   Dims dq = d;
   dq.B = M;
@@ -581,6 +651,7 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   aa.value = static_cast<const uint8_t*>(cache.value);
   aa.vmeta = static_cast<const uint16_t*>(cache.value_meta);
   aa.qt = static_cast<const uint32_t*>(qt);
+  aa.kd = kd;
   aa.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   aa.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
   e = launch_attn(d, dim3(aa.n_qb_pad * aa.n_hg * 2, d.B), aa, s);
