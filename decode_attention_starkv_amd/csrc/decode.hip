@@ -729,8 +729,11 @@ __device__ inline float4 load4(const _Float16* p) {
   return float4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
 }
 
-// One workgroup per (b, h): weights of the splits from their (m, l), the
-// weighted sum of their partial outputs, then the inverse rotation.  fp32
+// One workgroup per (b, h): weights of the splits from their (m, l) (wave
+// reductions), the weighted sum of their partial outputs (4 consecutive
+// channels per thread), then the inverse rotation in registers: a rotation
+// block has at most 256 channels = one wave's 64 lanes, so its butterflies
+// are in-register (strides 1, 2) or lane shuffles (strides 4 .. 128).  fp32
 // partials are unnormalised sums (weight 2^(m_s - m)); fp16 partials are
 // already divided by their own l_s (weight 2^(m_s - m) * l_s).
 template <typename PT>
@@ -739,37 +742,30 @@ __global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_
                                                     Dims d, int splits,
                                                     float* __restrict__ obar) {
   constexpr bool kNormalised = std::is_same<PT, _Float16>::value;
-  __shared__ float ms[kMaxSplits], ws[kMaxSplits];
-  __shared__ float buf[1024];
-  __shared__ float inv_l;
+  __shared__ float ms[kMaxSplits];
   const int bh = blockIdx.x;
   const int b = bh / d.Hq, h = bh % d.Hq;
-  const int t = threadIdx.x;
-  for (int s = t; s < splits; s += 256) {
+  const int t = threadIdx.x, lane = t & 63;
+  // every wave reduces the same (m, l) values; wave 0 publishes the weights
+  float mx = -INFINITY;
+  for (int s = lane; s < splits; s += 64)
+    mx = fmaxf(mx, part_ml[(((size_t)b * splits + s) * d.Hq + h) * 2]);
+  mx = wave_max(mx);
+  float L = 0.0f;
+  for (int s = lane; s < splits; s += 64) {
     const size_t k = (((size_t)b * splits + s) * d.Hq + h) * 2;
-    ms[s] = part_ml[k];
-    ws[s] = part_ml[k + 1];
+    const float l = part_ml[k + 1];
+    const float wgt = l > 0.0f ? exp2f(part_ml[k] - mx) : 0.0f;
+    if (t < 64) ms[s] = kNormalised ? wgt * l : wgt;
+    L = fmaf(wgt, l, L);
   }
+  const float inv = 1.0f / wave_sum(L);
   __syncthreads();
-  if (t == 0) {
-    float mx = -INFINITY;
-    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, ms[s]);
-    float L = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const float l = ws[s];
-      const float wgt = l > 0.0f ? exp2f(ms[s] - mx) : 0.0f;
-      ms[s] = kNormalised ? wgt * l : wgt;
-      L = fmaf(wgt, l, L);
-    }
-    inv_l = 1.0f / L;
-  }
-  __syncthreads();
-  const float inv = inv_l;
-  // 4 consecutive channels per thread, 8 splits' loads in flight at once
-  const size_t stride = (size_t)d.Hq * d.rv;
-  for (int c = 4 * t; c < d.rv; c += 1024) {
+  const int c = 4 * t;
+  float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (c < d.rv) {
+    const size_t stride = (size_t)d.Hq * d.rv;
     const PT* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + c;
-    float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
     int s = 0;
     for (; s + 8 <= splits; s += 8) {
       float4 x[8];
@@ -792,29 +788,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_
       o.z = fmaf(wgt, x.z, o.z);
       o.w = fmaf(wgt, x.w, o.w);
     }
-    buf[c] = o.x * inv;
-    buf[c + 1] = o.y * inv;
-    buf[c + 2] = o.z * inv;
-    buf[c + 3] = o.w * inv;
+    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
   }
   if (d.dtype == STARKV_CACHE_Q43 && d.rotate) {
     // undo the block rotation of the stored value latents: (Z H) H = Z (eq. 13)
     const int mb = pow2_divisor(d.rv / 4);
-    for (int hs = 1; hs < mb; hs <<= 1) {
-      __syncthreads();
-      for (int idx = t; idx < d.rv / 2; idx += 256) {
-        const int i = (idx / hs) * 2 * hs + (idx % hs);
-        const float x = buf[i], y = buf[i + hs];
-        buf[i] = x + y;
-        buf[i + hs] = x - y;
-      }
+    // strides 1 and 2: inside the thread's 4 channels
+    float a0 = o.x + o.y, a1 = o.x - o.y, a2 = o.z + o.w, a3 = o.z - o.w;
+    o = float4{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+    // strides 4 .. mb/2: partner channels sit 1 .. mb/8 lanes away
+    for (int hs = 4; hs < mb; hs <<= 1) {
+      const int dl = hs >> 2;
+      const float4 p = {__shfl_xor(o.x, dl), __shfl_xor(o.y, dl), __shfl_xor(o.z, dl),
+                        __shfl_xor(o.w, dl)};
+      if (c & hs) o = float4{p.x - o.x, p.y - o.y, p.z - o.z, p.w - o.w};
+      else o = float4{o.x + p.x, o.y + p.y, o.z + p.z, o.w + p.w};
     }
-    __syncthreads();
     const float cst = inv_sqrt_pow2(mb);
-    for (int i = t; i < d.rv; i += 256) buf[i] *= cst;
+    o.x *= cst; o.y *= cst; o.z *= cst; o.w *= cst;
   }
-  __syncthreads();
-  for (int c = t; c < d.rv; c += 256) obar[(size_t)bh * d.rv + c] = buf[c];
+  if (c < d.rv) *reinterpret_cast<float4*>(obar + (size_t)bh * d.rv + c) = o;
 }
 
 // ------------------------------------------------------------------ vproj --
