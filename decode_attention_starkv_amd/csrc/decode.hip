@@ -46,7 +46,14 @@ struct SplitArgs {
 // One workgroup per (b, h): q is staged in LDS, 256 threads split the d_h
 // contraction into chunks, the chunks are summed, then wave 0 rotates,
 // scales and packs the record.
-template <int FMT>
+// Q43 records come in two layouts:
+//   kFieldRec (decode scores): the 17 fp16 pairs that meet the in-place code
+//     fields of the key words (each entry times 2^-p for a field at bit p;
+//     channel 31 split over three one-bit fields), then sum(q_hi) 2^-24 and
+//     sum(q_lo) 2^-24 as fp32;
+//   otherwise: 16 channel pairs in the order of the key words (prefill puts
+//     them back in channel order), then sum(q_hi), sum(q_lo).
+template <int FMT, bool kFieldRec>
 __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
                                                     const void* __restrict__ bk,
                                                     Dims d, float qscale,
@@ -102,7 +109,35 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   uint32_t* rec = static_cast<uint32_t*>(qt) + (size_t)bh * kQ43Rec;
-  if (t < 16) {
+  float qsum_scale = 1.0f;
+  if constexpr (kFieldRec) {
+    qsum_scale = 1.0f / kTwo24;
+    if (t < 17) {
+      int a, cc;        // channels of the low and the high half
+      float sa, sc;     // their field weights (2^-bit position, or the bit's weight)
+      if (t < 4) {
+        // channels 0-3 / 4-7; odd pairs sit at bit 4 of their byte
+        a = t;
+        cc = t + 4;
+        sa = sc = (t & 1) ? 1.0f / 16.0f : 1.0f;
+      } else if (t < 14) {
+        const int i = (t - 4) / 5, f = (t - 4) % 5;
+        a = 8 + 5 * i + f;
+        cc = 18 + 5 * i + f;
+        sa = sc = f == 1 || f == 4 ? 1.0f / 8.0f : f == 2 ? 1.0f / 64.0f : 1.0f;
+      } else if (t == 14) {
+        a = 28; cc = 29; sa = 1.0f; sc = 1.0f / 8.0f;
+      } else if (t == 15) {
+        a = 30; cc = 31; sa = 1.0f / 64.0f; sc = 1.0f / 256.0f;
+      } else {
+        a = 31; cc = 31; sa = 2.0f; sc = 4.0f;
+      }
+      const _Float16 lo = (_Float16)((float)sq[a] * sa);
+      const _Float16 hi = (_Float16)((float)sq[cc] * sc);
+      rec[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+  } else if (t < 16) {
     int a, cc;  // channel pair (a -> low half, cc -> high half)
     if (t < 4) { a = t; cc = t + 4; }
     else if (t < 9) { a = 8 + (t - 4); cc = 8 + 10 + (t - 4); }
@@ -112,14 +147,16 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
     const uint32_t lo = __builtin_bit_cast(uint16_t, sq[a]);
     const uint32_t hi = __builtin_bit_cast(uint16_t, sq[cc]);
     rec[t] = lo | (hi << 16);
-  } else if (t == 16) {
+  }
+  const int qs_at = kFieldRec ? 17 : 16;
+  if (t == 32) {
     float s = 0.0f;
     for (int k = 0; k < 8; ++k) s += (float)sq[k];
-    rec[16] = __builtin_bit_cast(uint32_t, s);
-  } else if (t == 17) {
+    rec[qs_at] = __builtin_bit_cast(uint32_t, s * qsum_scale);
+  } else if (t == 33) {
     float s = 0.0f;
     for (int k = 8; k < 32; ++k) s += (float)sq[k];
-    rec[17] = __builtin_bit_cast(uint32_t, s);
+    rec[qs_at + 1] = __builtin_bit_cast(uint32_t, s * qsum_scale);
   }
 }
 
@@ -445,15 +482,21 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         dst[ki][5] = mt[1];
       }
     };
-    float m_ref[KVS * G], l_lane[KVS * G];
+    // m_ref: reference max (log2 units); thr = (m_ref + kLazy) 2^-24, the
+    // move threshold in the 2^-24 units the scores come in
+    float m_ref[KVS * G], l_lane[KVS * G], thr[KVS * G];
 #pragma unroll
-    for (int i = 0; i < KVS * G; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
+    for (int i = 0; i < KVS * G; ++i) {
+      m_ref[i] = -INFINITY;
+      l_lane[i] = 0.0f;
+      thr[i] = -INFINITY;
+    }
 
     // scores of tile `tile` into P slot `slot`; `it` = its index in the split
     auto score = [&](int tile, int it, int slot, const uint32_t (&kc)[KVS][6]) {
       const int rem = a.seq_len - tile * kTile;
       const bool valid = lane < rem;
-      float x[KVS * G];
+      float x[KVS * G];   // scores times 2^-24
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
         const int kh = sw + ki * 4;
@@ -466,17 +509,18 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       }
       bool big = false;
 #pragma unroll
-      for (int i = 0; i < KVS * G; ++i) big |= x[i] > m_ref[i] + kLazy;
+      for (int i = 0; i < KVS * G; ++i) big |= x[i] > thr[i];
       if (__builtin_amdgcn_ballot_w64(big) != 0) {
         // rare: some head's reference max must move up
 #pragma unroll
         for (int i = 0; i < KVS * G; ++i) {
           const int h = (sw + (i / G) * 4) * G + (i % G);
           float alpha = 1.0f;
-          if (__builtin_amdgcn_ballot_w64(x[i] > m_ref[i] + kLazy) != 0) {
-            const float mt = wave_max(x[i]);
+          if (__builtin_amdgcn_ballot_w64(x[i] > thr[i]) != 0) {
+            const float mt = wave_max(x[i]) * kTwo24;
             alpha = exp2f(m_ref[i] - mt);
             m_ref[i] = mt;
+            thr[i] = (mt + kLazy) * (1.0f / kTwo24);
             l_lane[i] *= alpha;
             if (lane == 0) flag_l[slot] = it;
           }
@@ -489,7 +533,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
       for (int i = 0; i < KVS * G; ++i) {
         const int h = (sw + (i / G) * 4) * G + (i % G);
-        const float p = __builtin_amdgcn_exp2f(x[i] - m_ref[i]);
+        const float p = __builtin_amdgcn_exp2f(fmaf(x[i], kTwo24, -m_ref[i]));
         l_lane[i] += p;
         p_l[slot][h * PS + lane] = (_Float16)p;
       }
@@ -899,7 +943,7 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   float* obar = reinterpret_cast<float*>(ws + lay.obar);
   auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], s); };
   mark(0);
-  qproj_kernel<FMT><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
+  qproj_kernel<FMT, true><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(1);
@@ -955,7 +999,7 @@ DecodeWs decode_ws_layout(const Dims& d, int splits) {
 
 hipError_t launch_qproj_q43(const Dims& d, const void* q, const void* bk,
                            float sm_scale, void* qt, hipStream_t s) {
-  qproj_kernel<STARKV_CACHE_Q43><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
+  qproj_kernel<STARKV_CACHE_Q43, false><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
   return hipGetLastError();
 }
 

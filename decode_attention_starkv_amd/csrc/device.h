@@ -62,52 +62,71 @@ __device__ inline uint32_t run_pair(const u32x4& w, int p) {
   }
 }
 
-// One Q43 key tile of one KV head as seen by one lane (= token): the 4-bit
-// and 3-bit codes as fp16 pairs (raw bits, i.e. k * 2^-24) in the order of
-// the query record, and the group scales (times 2^24) and zeros.
+// One Q43 key tile of one KV head as seen by one lane (= token), as 17 fp16
+// pairs whose halves hold codes (or parts of codes) in place: a field with
+// value c at bit p <= 7 of a half reads as the subnormal c * 2^(p-24), so
+// the query record carries the matching 2^-p and no field is shifted down.
+// mhi / mlo: the meta words (s | z << 16, fp16) of the 4-bit and the 3-bit
+// group.
 struct KeyLane {
-  uint32_t ph[4], pl[12];
-  float s_hi, z_hi, s_lo, z_lo;
+  uint32_t pr[17];
+  uint32_t mhi, mlo;
 };
 
 // kc: the lane's hi word, lo0 word, lo1 word, lo2 byte and its two meta
-// words (s_hi | z_hi << 16, s_lo | z_lo << 16).
+// words.  Word layout: hi = channels 0-3 (low half) and 4-7 (high half) as
+// nibbles; lo0 / lo1 = channels 8-12 / 13-17 (low) and 18-22 / 23-27 (high)
+// as 3-bit fields at bits 0, 3, .., 12 of each half; the byte holds channels
+// 28, 29 and the two low bits of 30; bit 15 of lo0 is the top bit of 30 and
+// bit 31 of lo0, bits 15 and 31 of lo1 are the three bits of 31.
 __device__ inline KeyLane unpack_key_lane(const uint32_t (&kc)[6]) {
   KeyLane k;
-  const uint32_t whi = kc[0], w0 = kc[1], w1 = kc[2], r8 = kc[3];
-  k.s_hi = f16v(kc[4] & 0xFFFFu) * kTwo24;
-  k.z_hi = f16v(kc[4] >> 16);
-  k.s_lo = f16v(kc[5] & 0xFFFFu) * kTwo24;
-  k.z_lo = f16v(kc[5] >> 16);
+  const uint32_t whi = kc[0], r8 = kc[3];
+  k.pr[0] = whi & 0x000F000Fu;              // ch 0, 4 at bit 0
+  k.pr[1] = whi & 0x00F000F0u;              // ch 1, 5 at bit 4
+  const uint32_t wh8 = whi >> 8;
+  k.pr[2] = wh8 & 0x000F000Fu;              // ch 2, 6 at bit 0
+  k.pr[3] = wh8 & 0x00F000F0u;              // ch 3, 7 at bit 4
 #pragma unroll
-  for (int i = 0; i < 4; ++i) k.ph[i] = (whi >> (4 * i)) & 0x000F000Fu;
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    k.pl[i] = (w0 >> (3 * i)) & 0x00070007u;
-    k.pl[5 + i] = (w1 >> (3 * i)) & 0x00070007u;
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t w = kc[1 + i];
+    k.pr[4 + 5 * i] = w & 0x00070007u;      // fields 0 at bit 0
+    k.pr[5 + 5 * i] = w & 0x00380038u;      // fields 1 at bit 3
+    k.pr[6 + 5 * i] = w & 0x01C001C0u;      // fields 2 at bit 6
+    const uint32_t t = w >> 9;
+    k.pr[7 + 5 * i] = t & 0x00070007u;      // fields 3 at bit 0
+    k.pr[8 + 5 * i] = t & 0x00380038u;      // fields 4 at bit 3
   }
-  const uint32_t R = r8 | (((w0 >> 15) & 1u) << 8) | ((w0 >> 31) << 9) |
-                     (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
-  k.pl[10] = (R & 7u) | (((R >> 6) & 7u) << 16);
-  k.pl[11] = ((R >> 3) & 7u) | (((R >> 9) & 7u) << 16);
+  const uint32_t x = r8 | (r8 << 16);
+  k.pr[14] = x & 0x00380007u;               // ch 28 at bit 0, ch 29 at bit 3
+  // ch 30 at bit 6 (two byte bits + bit 15 of lo0 moved to bit 8), bit 0
+  // of ch 31 (bit 31 of lo0) at bit 8 of the high half
+  k.pr[15] = ((kc[1] >> 7) & 0x01000100u) | (r8 & 0xC0u);
+  k.pr[16] = (kc[2] >> 15) & 0x00010001u;   // bits 1 and 2 of ch 31
+  k.mhi = kc[4];
+  k.mlo = kc[5];
   return k;
 }
 
-// Latent score (log2 units, pre-scaled) of one key lane against one Q43
-// query record (16 fp16 pairs, then the sums of the hi and lo query parts).
+// Latent score of one key lane against one Q43 query record (17 fp16
+// pairs, then the sums of the hi and lo query parts times 2^-24), in units
+// of 2^-24 (log2 domain, pre-scaled):
+//   s_hi (q_hi . k_hi 2^-24) + s_lo (q_lo . k_lo 2^-24) + (z_hi sum q_hi + z_lo sum q_lo) 2^-24
 __device__ inline float key_score(const KeyLane& k, const uint32_t* rec) {
   float ah = 0.0f, al = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    ah = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, k.ph[i]),
+    ah = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, k.pr[i]),
                                 __builtin_bit_cast(h2, rec[i]), ah, false);
 #pragma unroll
-  for (int i = 0; i < 12; ++i)
-    al = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, k.pl[i]),
-                                __builtin_bit_cast(h2, rec[4 + i]), al, false);
-  const float qs_hi = __builtin_bit_cast(float, rec[16]);
-  const float qs_lo = __builtin_bit_cast(float, rec[17]);
-  return fmaf(k.s_hi, ah, fmaf(k.z_hi, qs_hi, fmaf(k.s_lo, al, k.z_lo * qs_lo)));
+  for (int i = 4; i < 17; ++i)
+    al = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, k.pr[i]),
+                                __builtin_bit_cast(h2, rec[i]), al, false);
+  const h2 mh = __builtin_bit_cast(h2, k.mhi), ml = __builtin_bit_cast(h2, k.mlo);
+  const float qs_hi = __builtin_bit_cast(float, rec[17]);
+  const float qs_lo = __builtin_bit_cast(float, rec[18]);
+  return fmaf((float)mh[0], ah,
+              fmaf((float)ml[0], al, fmaf((float)mh[1], qs_hi, (float)ml[1] * qs_lo)));
 }
 
 }  // namespace starkv
