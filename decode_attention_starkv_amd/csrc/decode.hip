@@ -432,11 +432,12 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint8_t vring[kValueSlots * kSlotBytes];
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][32 * PS];
-  __shared__ __attribute__((aligned(16))) uint32_t qrec[32 * kQ43Rec];
+  __shared__ __attribute__((aligned(16))) uint32_t qrec[kMaxQHeads * kQ43Rec];
   __shared__ float alpha_l[2][32];
   __shared__ int flag_l[2];
   __shared__ float bias_l[32][33];
   __shared__ float l_row[32];
+  __shared__ __attribute__((aligned(16))) _Float16 zo_l[2 * kTile];   // zeros, then ones
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -449,13 +450,14 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   const int NH = NIV;                // 4-bit value groups
   const int j = lane >> 5, m = lane & 31;
 
-  for (int i = tid; i < 2 * 32 * PS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
+  for (int i = tid; i < 2 * 32 * PS / 8; i += 512) reinterpret_cast<h8*>(&p_l[0][0])[i] = h8{};
   for (int i = tid; i < d.Hq * kQ43Rec; i += 512)
     qrec[i] = static_cast<const uint32_t*>(a.qt)[(size_t)b * d.Hq * kQ43Rec + i];
   if (tid < 64) alpha_l[tid >> 5][tid & 31] = 1.0f;
   if (tid < 2) flag_l[tid] = -1;
   for (int i = tid; i < 32 * 33; i += 512) (&bias_l[0][0])[i] = 0.0f;
   if (tid < 32) l_row[tid] = 1.0f;
+  if (tid < 2 * kTile) zo_l[tid] = tid < kTile ? (_Float16)0.0f : (_Float16)1.0f;
   __syncthreads();
 
   const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
@@ -484,11 +486,10 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     };
     // m_ref: reference max (log2 units); thr = (m_ref + kLazy) 2^-24, the
     // move threshold in the 2^-24 units the scores come in
-    float m_ref[KVS * G], l_lane[KVS * G], thr[KVS * G];
+    float m_ref[KVS * G], thr[KVS * G];
 #pragma unroll
     for (int i = 0; i < KVS * G; ++i) {
       m_ref[i] = -INFINITY;
-      l_lane[i] = 0.0f;
       thr[i] = -INFINITY;
     }
 
@@ -499,11 +500,10 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       float x[KVS * G];   // scores times 2^-24
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
-        const int kh = sw + ki * 4;
         const KeyLane kl = unpack_key_lane(kc[ki]);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
-          const float sc = key_score(kl, qrec + (kh * G + jj) * kQ43Rec);
+          const float sc = key_score(kl, qrec + ((sw + ki * 4) * G + jj) * kQ43Rec);
           x[ki * G + jj] = valid ? sc : -INFINITY;
         }
       }
@@ -521,7 +521,6 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
             alpha = exp2f(m_ref[i] - mt);
             m_ref[i] = mt;
             thr[i] = (mt + kLazy) * (1.0f / kTwo24);
-            l_lane[i] *= alpha;
             if (lane == 0) flag_l[slot] = it;
           }
           if (lane == 0) alpha_l[slot][h] = alpha;
@@ -534,7 +533,6 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       for (int i = 0; i < KVS * G; ++i) {
         const int h = (sw + (i / G) * 4) * G + (i % G);
         const float p = __builtin_amdgcn_exp2f(fmaf(x[i], kTwo24, -m_ref[i]));
-        l_lane[i] += p;
         p_l[slot][h * PS + lane] = (_Float16)p;
       }
     };
@@ -564,16 +562,13 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       }
       lds_barrier();
     }
-    if (has_keys) {
+    // the running max of each head; its exp-sum l comes out of the value
+    // waves' zero-point product (a column of ones)
+    if (has_keys && lane == 0) {
 #pragma unroll
       for (int i = 0; i < KVS * G; ++i) {
-        const float l = wave_sum(l_lane[i]);
-        if (lane == 0) {
-          const int h = (sw + (i / G) * 4) * G + (i % G);
-          l_row[h] = l;
-          a.part_ml[(obase + h) * 2] = m_ref[i];
-          a.part_ml[(obase + h) * 2 + 1] = l;
-        }
+        const int h = (sw + (i / G) * 4) * G + (i % G);
+        a.part_ml[(obase + h) * 2] = m_ref[i];
       }
     }
     __syncthreads();   // value waves add their zero-point terms to bias_l
@@ -677,19 +672,32 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
           }
         }
       }
-      // zero points of this wave's groups: columns n0 .. n0+NIV-1
+      // zero points of this wave's groups: columns n0 .. n0+NIV-1; the
+      // 4-bit wave (n0 = 0) also sums P into column NIV: l of every head,
+      // rescaled with the accumulators and made of the same fp16 P
+      // (other columns read a row of zeros: no masked loads)
       const bool zcol = m >= n0 && m < n0 + NIV;
+      const _Float16* zsrc = zcol ? zr_l + (m - n0) * kTile
+                                  : (kFour && m == NIV) ? zo_l + kTile : zo_l;
+      h8 Z[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        h8 Z = h8{};
-        if (zcol) Z = *reinterpret_cast<const h8*>(zr_l + (m - n0) * kTile + 32 * j + 8 * r);
-        bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z, bacc, 0, 0, 0);
-      }
+      for (int r = 0; r < 4; ++r) Z[r] = *reinterpret_cast<const h8*>(zsrc + 32 * j + 8 * r);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z[r], bacc, 0, 0, 0);
       lds_barrier();
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (m >= n0 && m < n0 + NIV) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
+    if (kFour && m == NIV) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = acc_row(v, lane);
+        l_row[row] = bacc[v];
+        if (row < d.Hq) a.part_ml[(obase + row) * 2 + 1] = bacc[v];
+      }
+    }
     __syncthreads();   // bias and l complete; no wave uses the value ring any more
     // The partial rows, divided by their l (so that fp16 holds them), go
     // out through LDS (this wave's region of the ring) as 16-byte stores of
@@ -697,7 +705,10 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     float* st = reinterpret_cast<float*>(vring) + vw * 32 * kStageRow;
     float inv_l[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) inv_l[v] = 1.0f / l_row[acc_row(v, lane)];
+    for (int v = 0; v < 16; ++v) {
+      const float l = l_row[acc_row(v, lane)];
+      inv_l[v] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
 #pragma unroll
     for (int ni = 0; ni < NIV; ++ni) {
       const int n = n0 + ni;
