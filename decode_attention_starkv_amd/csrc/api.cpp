@@ -68,15 +68,16 @@ size_t cache_bytes(const starkv_config& c, int which) {
   }
 }
 
-// MI355X has 256 compute units; one decode workgroup per unit fills it.
-constexpr int kTargetGroups = 256;
+// MI355X has 256 compute units; the split count fills every unit with as
+// many decode workgroups as stay resident on it.
+constexpr int kComputeUnits = 256;
 
 }  // namespace
 
 int choose_splits(const starkv_config& c, int seq_len) {
   const int n_tiles = (seq_len + kTile - 1) / kTile;
-  int s = c.num_splits > 0 ? c.num_splits
-                           : (kTargetGroups + c.batch - 1) / c.batch;
+  const int groups = kComputeUnits * decode_groups_per_cu(make_dims(c));
+  int s = c.num_splits > 0 ? c.num_splits : (groups + c.batch - 1) / c.batch;
   s = std::max(1, std::min(std::min(s, n_tiles), kMaxSplits));
   const int tps = (n_tiles + s - 1) / s;
   return (n_tiles + tps - 1) / tps;  // no empty splits

@@ -392,17 +392,23 @@ __device__ inline void wave_dma(const uint8_t* src, uint8_t* lds_dst, int bytes,
 
 constexpr int kValueSlots = 4;     // LDS ring slots per value wave
 constexpr int kValueAhead = kValueSlots - 1;   // tiles staged ahead of use
-constexpr int kMaxNIV = 8;         // value groups per value wave (R_v <= 1024)
+// Value ring of a kernel whose value waves own NIV groups each (R_v = 128 NIV,
+// NIV <= 8); sized per NIV so that small value ranks leave room for a second
+// workgroup on the compute unit.
 // one slot: the 4-bit wave's codes + scales + zeros, then the three 3-bit
 // waves' (1024 + 128 + 128 and 768 + 128 + 128 bytes per group)
-constexpr int kHiRegion = kMaxNIV * 1280;
-constexpr int kLoRegion = kMaxNIV * 1024;
-constexpr int kSlotBytes = kHiRegion + 3 * kLoRegion;
+constexpr int hi_region(int niv) { return niv * 1280; }
+constexpr int lo_region(int niv) { return niv * 1024; }
+constexpr int slot_bytes(int niv) { return hi_region(niv) + 3 * lo_region(niv); }
 // fp32 row stride of the epilogue's per-wave staging of partial rows (kept
-// in the value ring): 32 rows of up to 256 columns, padded so the two row
-// halves a store instruction writes fall in different LDS banks
-constexpr int kStageRow = kMaxNIV * 32 + 8;
-static_assert(4 * 32 * kStageRow * 4 <= kValueSlots * kSlotBytes, "staging fits the ring");
+// in the value ring): 32 rows of 32 NIV columns, padded so the two row halves
+// a store instruction writes fall in different LDS banks
+constexpr int stage_row(int niv) { return niv * 32 + 8; }
+constexpr int ring_bytes(int niv) {
+  return kValueSlots * slot_bytes(niv) > 4 * 32 * stage_row(niv) * 4
+             ? kValueSlots * slot_bytes(niv)
+             : 4 * 32 * stage_row(niv) * 4;
+}
 
 // Q43 split kernel, warp-specialized.  Workgroup = (sequence b, token split),
 // 8 waves; waves w and w+4 share a SIMD.
@@ -430,7 +436,9 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   (void)kFourW0;
   const Dims& d = a.d;
 
-  __shared__ __attribute__((aligned(16))) uint8_t vring[kValueSlots * kSlotBytes];
+  constexpr int kHiRegion = hi_region(NIV), kLoRegion = lo_region(NIV);
+  constexpr int kSlotBytes = slot_bytes(NIV), kStageRow = stage_row(NIV);
+  __shared__ __attribute__((aligned(16))) uint8_t vring[ring_bytes(NIV)];
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][32 * PS];
   __shared__ __attribute__((aligned(16))) uint32_t qrec[kMaxQHeads * kQ43Rec];
   __shared__ float alpha_l[2][32];
@@ -571,8 +579,9 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         a.part_ml[(obase + h) * 2] = m_ref[i];
       }
     }
-    __syncthreads();   // value waves add their zero-point terms to bias_l
-    __syncthreads();   // value waves write their partial outputs
+    // the value waves add their zero-point terms and l; the (m, l) stores
+    // need not complete before the barrier, so it waits on LDS only
+    lds_barrier();
   } else {
     // ================================================================ values
     const int vw = wave - 4;
@@ -698,7 +707,9 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         if (row < d.Hq) a.part_ml[(obase + row) * 2 + 1] = bacc[v];
       }
     }
-    __syncthreads();   // bias and l complete; no wave uses the value ring any more
+    // bias and l complete; no wave uses the value ring any more (every stage
+    // was waited for in the last iteration)
+    lds_barrier();
     // The partial rows, divided by their l (so that fp16 holds them), go
     // out through LDS (this wave's region of the ring) as 16-byte stores of
     // whole row segments instead of 2-byte scatters.
@@ -733,41 +744,50 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         *reinterpret_cast<h8*>(po + (obase + row) * d.rv + n0 * 32 + 8 * k) = o;
       }
     }
-    __syncthreads();
     };
     if (four) run_values(std::true_type{});
     else run_values(std::false_type{});
   }
 }
 
+// The Q43 split kernel for a shape: G query heads per KV head, KVS KV heads
+// per score wave, NIV value groups per value wave.
+using SplitFn = void (*)(SplitArgs);
+
 template <int G, int KVS>
-hipError_t launch_q43_niv(int NIV, dim3 grid, const SplitArgs& sa, hipStream_t s) {
+SplitFn q43_kernel_niv(int NIV) {
   switch (NIV) {
-    case 2: split_q43_kernel<G, KVS, 2><<<grid, 512, 0, s>>>(sa); break;
-    case 4: split_q43_kernel<G, KVS, 4><<<grid, 512, 0, s>>>(sa); break;
-    case 6: split_q43_kernel<G, KVS, 6><<<grid, 512, 0, s>>>(sa); break;
-    case 8: split_q43_kernel<G, KVS, 8><<<grid, 512, 0, s>>>(sa); break;
-    default: return hipErrorNotSupported;
+    case 2: return split_q43_kernel<G, KVS, 2>;
+    case 4: return split_q43_kernel<G, KVS, 4>;
+    case 6: return split_q43_kernel<G, KVS, 6>;
+    case 8: return split_q43_kernel<G, KVS, 8>;
+    default: return nullptr;
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_q43(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t s) {
+SplitFn q43_kernel(const Dims& d) {
   const int NIV = d.rv / 128;
   const int KVS = d.Hkv >= 4 ? d.Hkv / 4 : 1;
   switch (d.G * 16 + KVS) {
-    case 1 * 16 + 1: return launch_q43_niv<1, 1>(NIV, grid, sa, s);
-    case 1 * 16 + 2: return launch_q43_niv<1, 2>(NIV, grid, sa, s);
-    case 1 * 16 + 4: return launch_q43_niv<1, 4>(NIV, grid, sa, s);
-    case 1 * 16 + 8: return launch_q43_niv<1, 8>(NIV, grid, sa, s);
-    case 2 * 16 + 1: return launch_q43_niv<2, 1>(NIV, grid, sa, s);
-    case 2 * 16 + 2: return launch_q43_niv<2, 2>(NIV, grid, sa, s);
-    case 2 * 16 + 4: return launch_q43_niv<2, 4>(NIV, grid, sa, s);
-    case 4 * 16 + 1: return launch_q43_niv<4, 1>(NIV, grid, sa, s);
-    case 4 * 16 + 2: return launch_q43_niv<4, 2>(NIV, grid, sa, s);
-    case 8 * 16 + 1: return launch_q43_niv<8, 1>(NIV, grid, sa, s);
-    default: return hipErrorNotSupported;
+    case 1 * 16 + 1: return q43_kernel_niv<1, 1>(NIV);
+    case 1 * 16 + 2: return q43_kernel_niv<1, 2>(NIV);
+    case 1 * 16 + 4: return q43_kernel_niv<1, 4>(NIV);
+    case 1 * 16 + 8: return q43_kernel_niv<1, 8>(NIV);
+    case 2 * 16 + 1: return q43_kernel_niv<2, 1>(NIV);
+    case 2 * 16 + 2: return q43_kernel_niv<2, 2>(NIV);
+    case 2 * 16 + 4: return q43_kernel_niv<2, 4>(NIV);
+    case 4 * 16 + 1: return q43_kernel_niv<4, 1>(NIV);
+    case 4 * 16 + 2: return q43_kernel_niv<4, 2>(NIV);
+    case 8 * 16 + 1: return q43_kernel_niv<8, 1>(NIV);
+    default: return nullptr;
   }
+}
+
+hipError_t launch_q43(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t s) {
+  const SplitFn k = q43_kernel(d);
+  if (!k) return hipErrorNotSupported;
+  hipLaunchKernelGGL(k, grid, dim3(512), 0, s, sa);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ merge --
@@ -991,6 +1011,18 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
 }  // namespace
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int decode_groups_per_cu(const Dims& d) {
+  if (d.dtype != STARKV_CACHE_Q43) return 1;
+  const SplitFn k = q43_kernel(d);
+  int n = 0;
+  if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void*>(k), 512, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();   // no device to ask: one group per unit
+    return 1;
+  }
+  return n;
+}
 
 DecodeWs decode_ws_layout(const Dims& d, int splits) {
   DecodeWs w;

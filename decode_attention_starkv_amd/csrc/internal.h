@@ -42,6 +42,9 @@ struct DecodeWs {
   int splits;
 };
 DecodeWs decode_ws_layout(const Dims& d, int splits);
+// Decode split workgroups that stay resident on one compute unit together
+// (1 when it cannot be asked, e.g. without a device).
+int decode_groups_per_cu(const Dims& d);
 int choose_splits(const starkv_config& c, int seq_len);
 
 // Launchers; each returns hipSuccess or the launch error.
