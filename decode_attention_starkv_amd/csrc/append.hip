@@ -96,7 +96,10 @@ __global__ void append_plain_keys(const float* __restrict__ zk, void* key,
   r /= d.Hkv;
   int i = r % n;
   int b = r / n;
-  size_t dst = (((size_t)b * d.Hkv + h) * d.Tmax + pos + i) * d.rk + c;
+  // [B][Hkv][tile][r_k/8][64 tokens][8 channels]
+  const int t = pos + i;
+  size_t dst = (((((size_t)b * d.Hkv + h) * d.NT + t / kTile) * (d.rk / 8) + c / 8) * kTile +
+                t % kTile) * 8 + c % 8;
   if (kBf16)
     static_cast<uint16_t*>(key)[dst] = bf16_bits_rn(zk[idx]);
   else
@@ -114,7 +117,10 @@ __global__ void append_plain_values(const float* __restrict__ zv, void* value,
   int i = r % n;
   int b = r / n;
   int t = pos + i;
-  size_t dst = (((size_t)b * d.NT + t / kTile) * d.rv + c) * kTile + t % kTile;
+  // [B][tile][R_v/32][8 token blocks][32 channels][8 tokens]
+  const int u = t % kTile;
+  size_t dst = (((((size_t)b * d.NT + t / kTile) * (d.rv / 32) + c / 32) * 8 + u / 8) * 32 +
+                c % 32) * 8 + u % 8;
   if (kBf16)
     static_cast<uint16_t*>(value)[dst] = bf16_bits_rn(zv[idx]);
   else

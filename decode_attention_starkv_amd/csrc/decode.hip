@@ -163,42 +163,98 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
 // ---------------------------------------------------- fp32 / bf16 split --
 
 // Scores of one 64-token tile for the G query heads of KV head kh from an
-// unquantized cache; lane = token, query records read from LDS.
-template <int FMT, int G>
+// unquantized cache; lane = token, the key row (RK channels, of which the
+// first d.rk are real) loaded whole, query records read from LDS.
+template <int FMT, int G, int RK>
 __device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
                                         int b, int kh, int tile, int lane,
                                         float* sc) {
   const Dims& d = a.d;
-  const size_t row = (((size_t)b * d.Hkv + kh) * d.Tmax + (size_t)tile * kTile + lane) * d.rk;
-  const float* recs = qrec + (size_t)kh * G * kPlainRec;
-  float acc[G];
+  // chunk c of this token's key row: [b][kh][tile][c][lane][8 channels]
+  const size_t row0 = (((size_t)b * d.Hkv + kh) * d.NT + tile) * (d.rk / 8) * (kTile * 8) + lane * 8;
+  // the record offset is made opaque per call so the records are read from
+  // LDS where they are used instead of being held in registers across tiles
+  int rec_off = kh * G * kPlainRec;
+  __asm__ volatile("" : "+s"(rec_off));
+  const float* recs = qrec + rec_off;
+  constexpr int NC = RK / 8;              // 8-channel chunks
+  constexpr int CW = FMT == STARKV_CACHE_F32 ? 8 : 4;   // dwords per chunk
+  if constexpr (G * RK > 64) {
+    // many heads per key row: one chunk at a time, all G products per chunk
+    float acc[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) acc[j] = 0.0f;
-  for (int c0 = 0; c0 < d.rk; c0 += 8) {
-    float z[8];
-    if constexpr (FMT == STARKV_CACHE_F32) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.key) + row + c0);
-      const float4 u = p[0], v = p[1];
-      z[0] = u.x; z[1] = u.y; z[2] = u.z; z[3] = u.w;
-      z[4] = v.x; z[5] = v.y; z[6] = v.z; z[7] = v.w;
-    } else {
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.key) + row + c0);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int j = 0; j < G; ++j) acc[j] = 0.0f;
+#pragma unroll 1
+    for (int c = 0; c < NC && 8 * c < d.rk; ++c) {
+      float z[8];
+      const size_t row = row0 + (size_t)c * (kTile * 8);
+      if constexpr (FMT == STARKV_CACHE_F32) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.key) + row);
+        const u32x4 u = __builtin_nontemporal_load(p), v = __builtin_nontemporal_load(p + 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z[2 * e] = __builtin_bit_cast(float, w[e] << 16);
-        z[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+        for (int e = 0; e < 4; ++e) {
+          z[e] = __builtin_bit_cast(float, u[e]);
+          z[4 + e] = __builtin_bit_cast(float, v[e]);
+        }
+      } else {
+        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            static_cast<const uint16_t*>(a.key) + row));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = u[e];
+          z[2 * e] = __builtin_bit_cast(float, w << 16);
+          z[2 * e + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j] = fmaf(recs[j * kPlainRec + 8 * c + e], z[e], acc[j]);
     }
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float* qr = recs + j * kPlainRec + c0;
+    for (int j = 0; j < G; ++j) sc[j] = acc[j];
+    return;
+  }
+  uint32_t kw[NC][CW];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j] = fmaf(qr[e], z[e], acc[j]);
+  for (int c = 0; c < NC; ++c) {
+    const bool live = RK == 64 || RK == 32 || 8 * c < d.rk;
+    const size_t row = row0 + (size_t)(live ? c : 0) * (kTile * 8);
+    if constexpr (FMT == STARKV_CACHE_F32) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.key) + row);
+      const u32x4 u = live ? __builtin_nontemporal_load(p) : u32x4{};
+      const u32x4 v = live ? __builtin_nontemporal_load(p + 1) : u32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kw[c][e] = u[e];
+        kw[c][4 + e] = v[e];
+      }
+    } else {
+      const u32x4 u = live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                 static_cast<const uint16_t*>(a.key) + row))
+                           : u32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kw[c][e] = u[e];
     }
   }
 #pragma unroll
-  for (int j = 0; j < G; ++j) sc[j] = acc[j];
+  for (int j = 0; j < G; ++j) {
+    // one head at a time: its record is read right before its products
+    __builtin_amdgcn_sched_barrier(0);
+    const float* qr = recs + j * kPlainRec;
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float z;
+        if constexpr (FMT == STARKV_CACHE_F32) z = __builtin_bit_cast(float, kw[c][e]);
+        else z = __builtin_bit_cast(float, (e & 1) ? kw[c][e >> 1] & 0xFFFF0000u
+                                                   : kw[c][e >> 1] << 16);
+        acc = fmaf(qr[8 * c + e], z, acc);
+      }
+    sc[j] = acc;
+  }
 }
 
 // Online-softmax update of one query head over one tile (lane = token):
@@ -220,17 +276,29 @@ __device__ inline float softmax_step(float x, float& mr, float& l, float& alpha,
   return p;
 }
 
-template <int FMT, int G>
+// Split kernel for unquantized caches: 8 waves, each scores KVI KV heads
+// (lane = token) and then contracts NI value groups (32 channels each) with
+// the stacked-head P tile on MFMA.  A tile's value operands are requested
+// before its scores are computed, so both streams are in flight together.
+// bf16 caches write fp16 partial rows divided by their own l; fp32 caches
+// write unnormalised fp32 rows.
+template <int FMT, int G, int RK>
 __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   constexpr int NW = kDecodeWaves;
   constexpr int KVI = G >= 4 ? 1 : 4 / G;  // KV heads per wave (Hq <= 32)
+  constexpr int NI = kMaxQHeads * 32 / 32 / NW;   // value groups per wave (R_v <= 1024)
   constexpr int PS = 68;                    // P row stride (floats)
+  constexpr bool kBF = FMT == STARKV_CACHE_BF16;
+  // bf16 value operands requested before the scores where registers allow
+  // (one query head per KV head, key rows of <= 32 channels); else at use
+  constexpr bool kPreV = kBF && G == 1 && RK <= 32;
   const Dims& d = a.d;
 
   __shared__ __attribute__((aligned(16))) float p_raw[2 * 32 * PS];
   __shared__ __attribute__((aligned(16))) float qrec[32 * kPlainRec];
   __shared__ float alpha_l[2][32];
   __shared__ int flag_l[2];
+  __shared__ float l_row[32];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -251,21 +319,39 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   float m_ref[KVI * G], l_lane[KVI * G];
 #pragma unroll
   for (int i = 0; i < KVI * G; ++i) { m_ref[i] = -INFINITY; l_lane[i] = 0.0f; }
-  f32x16 acc[4];
+  f32x16 acc[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NI; ++i) acc[i] = f32x16{};
   const int j = lane >> 5, m = lane & 31;
 
   for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
     const int buf = it & 1;
     const int rem = a.seq_len - tile * kTile;
     const bool valid = lane < rem;
+    const bool partial = rem < kTile;
+    // value operands of this tile (bf16): 4 K-steps of 8 tokens per group
+    bf8 Zv[NI][4];
+    auto load_values = [&]() {
+      const uint16_t* vbase = static_cast<const uint16_t*>(a.value);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int n = wave + ni * NW;
+        // K-step r, lane half j: tokens 16r + 8j .. +7 = token block 2r + j
+        const uint16_t* zp =
+            vbase + (((size_t)b * d.NT + tile) * GV + min(n, GV - 1)) * (8 * 256) + (j * 32 + m) * 8;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Zv[ni][r] = n < GV ? __builtin_nontemporal_load(reinterpret_cast<const bf8*>(zp + r * 512))
+                             : bf8{};
+      }
+    };
+    if constexpr (kPreV) load_values();
 #pragma unroll
     for (int ki = 0; ki < KVI; ++ki) {
       const int kh = wave + ki * NW;
       if (kh < d.Hkv) {
         float sc[G];
-        score_tile_plain<FMT, G>(a, qrec, b, kh, tile, lane, sc);
+        score_tile_plain<FMT, G, RK>(a, qrec, b, kh, tile, lane, sc);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
           const int h = kh * G + jj;
@@ -287,50 +373,52 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
       for (int v = 0; v < 16; ++v) {
         const float al = alpha_l[buf][acc_row(v, lane)];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[ni][v] *= al;
+        for (int ni = 0; ni < NI; ++ni) acc[ni][v] *= al;
       }
     }
-    const bool partial = rem < kTile;
-    const float* prow = p_raw + (buf * 32 + m) * PS + 32 * j;
-    if constexpr (FMT == STARKV_CACHE_BF16) {
-      bf8 Ah[4], Al[4];
+    if constexpr (kBF) {
+      if constexpr (!kPreV) load_values();
+      const float* prow = p_raw + (buf * 32 + m) * PS + 8 * j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        // P as bf16 high and low parts (two products per K-step); K-step r,
+        // lane half j covers tokens 16r + 8j .. +7
+        bf8 Ah, Al;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = prow[8 * r + e];
+          const float p = prow[16 * r + e];
           const __bf16 hi = (__bf16)p;
-          Ah[r][e] = hi;
-          Al[r][e] = (__bf16)(p - (float)hi);
+          Ah[e] = hi;
+          Al[e] = (__bf16)(p - (float)hi);
         }
-      const uint16_t* vbase = static_cast<const uint16_t*>(a.value);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int n = wave + ni * NW;
-        if (n < GV) {
-          const uint16_t* zp = vbase + (((size_t)b * d.NT + tile) * d.rv + n * 32 + m) * kTile + 32 * j;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            bf8 Z = *reinterpret_cast<const bf8*>(zp + 8 * r);
+        for (int ni = 0; ni < NI; ++ni) {
+          const int n = wave + ni * NW;
+          if (n < GV) {
+            bf8 Z = Zv[ni][r];
             if (partial) {
+              // unused cache slots never reach the operands
 #pragma unroll
               for (int e = 0; e < 8; ++e)
-                if (32 * j + 8 * r + e >= rem) Z[e] = (__bf16)0.0f;
+                if (16 * r + 8 * j + e >= rem) Z[e] = (__bf16)0.0f;
             }
-            acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah[r], Z, acc[ni], 0, 0, 0);
-            acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al[r], Z, acc[ni], 0, 0, 0);
+            acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, Z, acc[ni], 0, 0, 0);
+            acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al, Z, acc[ni], 0, 0, 0);
           }
         }
       }
     } else {
+      // fp32 products, K = 2: step r, lane half j is token 32j + r
+      const float* prow = p_raw + (buf * 32 + m) * PS + 32 * j;
       const float* vbase = static_cast<const float*>(a.value);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
         const int n = wave + ni * NW;
         if (n < GV) {
-          const float* zp = vbase + (((size_t)b * d.NT + tile) * d.rv + n * 32 + m) * kTile + 32 * j;
+          const float* zp = vbase + (((size_t)b * d.NT + tile) * GV + n) * (8 * 256) + m * 8;
           for (int r = 0; r < 32; ++r) {
-            const float z = (partial && 32 * j + r >= rem) ? 0.0f : zp[r];
+            const int u = 32 * j + r;
+            const float z = (partial && u >= rem) ? 0.0f : zp[(u >> 3) * 256 + (u & 7)];
             acc[ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(prow[r], z, acc[ni], 0, 0, 0);
           }
         }
@@ -340,17 +428,6 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 
   const size_t obase = ((size_t)b * a.splits + sp) * d.Hq;
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int n = wave + ni * NW;
-    if (n < GV) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = acc_row(v, lane);
-        if (row < d.Hq) a.part_o[(obase + row) * d.rv + n * 32 + m] = acc[ni][v];
-      }
-    }
-  }
-#pragma unroll
   for (int ki = 0; ki < KVI; ++ki) {
     const int kh = wave + ki * NW;
     if (kh < d.Hkv) {
@@ -359,8 +436,29 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
         const float l = wave_sum(l_lane[ki * G + jj]);
         if (lane == 0) {
           const int h = kh * G + jj;
+          l_row[h] = l;
           a.part_ml[(obase + h) * 2] = m_ref[ki * G + jj];
           a.part_ml[(obase + h) * 2 + 1] = l;
+        }
+      }
+    }
+  }
+  lds_barrier();   // l of every head
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const int n = wave + ni * NW;
+    if (n < GV) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = acc_row(v, lane);
+        if (row < d.Hq) {
+          const size_t o = (obase + row) * d.rv + n * 32 + m;
+          if constexpr (kBF) {
+            const float l = l_row[row];
+            reinterpret_cast<_Float16*>(a.part_o)[o] = (_Float16)(l > 0.0f ? acc[ni][v] / l : 0.0f);
+          } else {
+            a.part_o[o] = acc[ni][v];
+          }
         }
       }
     }
@@ -953,11 +1051,21 @@ hipError_t launch_split(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream
   if constexpr (FMT == STARKV_CACHE_Q43) {
     return launch_q43(d, grid, sa, s);
   } else {
-    switch (d.G) {
-      case 1: split_kernel<FMT, 1><<<grid, 512, 0, s>>>(sa); break;
-      case 2: split_kernel<FMT, 2><<<grid, 512, 0, s>>>(sa); break;
-      case 4: split_kernel<FMT, 4><<<grid, 512, 0, s>>>(sa); break;
-      default: split_kernel<FMT, 8><<<grid, 512, 0, s>>>(sa); break;
+    // key rows of up to 16 / 32 / 64 channels (d.rk is a multiple of 8)
+    const int rkc = d.rk <= 16 ? 16 : d.rk <= 32 ? 32 : 64;
+    switch (d.G * 128 + rkc) {
+      case 1 * 128 + 16: split_kernel<FMT, 1, 16><<<grid, 512, 0, s>>>(sa); break;
+      case 1 * 128 + 32: split_kernel<FMT, 1, 32><<<grid, 512, 0, s>>>(sa); break;
+      case 1 * 128 + 64: split_kernel<FMT, 1, 64><<<grid, 512, 0, s>>>(sa); break;
+      case 2 * 128 + 16: split_kernel<FMT, 2, 16><<<grid, 512, 0, s>>>(sa); break;
+      case 2 * 128 + 32: split_kernel<FMT, 2, 32><<<grid, 512, 0, s>>>(sa); break;
+      case 2 * 128 + 64: split_kernel<FMT, 2, 64><<<grid, 512, 0, s>>>(sa); break;
+      case 4 * 128 + 16: split_kernel<FMT, 4, 16><<<grid, 512, 0, s>>>(sa); break;
+      case 4 * 128 + 32: split_kernel<FMT, 4, 32><<<grid, 512, 0, s>>>(sa); break;
+      case 4 * 128 + 64: split_kernel<FMT, 4, 64><<<grid, 512, 0, s>>>(sa); break;
+      case 8 * 128 + 16: split_kernel<FMT, 8, 16><<<grid, 512, 0, s>>>(sa); break;
+      case 8 * 128 + 32: split_kernel<FMT, 8, 32><<<grid, 512, 0, s>>>(sa); break;
+      default: split_kernel<FMT, 8, 64><<<grid, 512, 0, s>>>(sa); break;
     }
     return hipGetLastError();
   }
@@ -994,11 +1102,11 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   e = launch_split<FMT>(d, dim3(lay.splits, d.B), sa, s);
   if (e != hipSuccess) return e;
   mark(2);
-  if constexpr (FMT == STARKV_CACHE_Q43)
+  if constexpr (FMT == STARKV_CACHE_F32)
+    merge_kernel<float><<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
+  else   // fp16 partial rows, each divided by its own l
     merge_kernel<_Float16><<<d.B * d.Hq, 256, 0, s>>>(
         reinterpret_cast<const _Float16*>(part_o), part_ml, d, lay.splits, obar);
-  else
-    merge_kernel<float><<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(3);

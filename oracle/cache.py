@@ -7,9 +7,14 @@ byte layout.  This module implements format v1 (tiles of 64 tokens) on its
 own, from the specification below, so that the GPU packer can be checked
 against it to the bit.
 
-fp32 / bf16 caches (elements little-endian):
-  key   [B][Hkv][T_max][r_k]
-  value [B][T_max/64][R_v][64]            (channel-major inside a tile)
+fp32 / bf16 caches (elements little-endian), in the order one GPU load
+instruction reads (64 lanes x 8 consecutive elements):
+  key   [B][Hkv][tile][r_k/8][64 tokens][8 channels]
+  value [B][tile][R_v/32][8 token blocks][32 channels][8 tokens]
+        (element (token u of the tile, channel 32g + m) of group g sits in
+        block u // 8 at [m][u % 8])
+  (shapes the GPU path does not accept -- r_k not a multiple of 8, R_v not
+  a multiple of 32 -- use one chunk of r_k channels / one group of R_v.)
 
 q43 cache (r_k = 32: channels 0-7 at 4 bits, 8-31 at 3 bits; R_v a multiple
 of 128: channels [0, R_v/4) at 4 bits, the rest at 3 bits):
@@ -218,9 +223,16 @@ class Cache:
 
     # -- views -------------------------------------------------------------
     def _elem_views(self):
+        """Element views k [B, H, tile, token, r_k/8, 8] and
+        v [B, tile, block, token-in-block, group, channel-in-group] over the
+        buffers (writes through them land in the buffers)."""
         dt = np.float32 if self.kind == "f32" else np.uint16
-        k = self.buf["key"].view(dt).reshape(self.B, self.H, self.T, self.rk)
-        v = self.buf["value"].view(dt).reshape(self.B, self.nt, self.rv, TT)
+        kw = 8 if self.rk % 8 == 0 else self.rk
+        gw = 32 if self.rv % 32 == 0 else self.rv
+        k = self.buf["key"].view(dt).reshape(
+            self.B, self.H, self.nt, self.rk // kw, TT, kw).transpose(0, 1, 2, 4, 3, 5)
+        v = self.buf["value"].view(dt).reshape(
+            self.B, self.nt, self.rv // gw, 8, gw, 8).transpose(0, 1, 3, 5, 2, 4)
         return k, v
 
     def _q_views(self):
@@ -251,10 +263,10 @@ class Cache:
                 kk, vv = zk, zv
             else:
                 kk, vv = to_bf16_bits(zk), to_bf16_bits(zv)
-            k[:, :, pos:pos + n, :] = np.transpose(kk, (0, 2, 1, 3))
-            for i in range(n):
-                t = pos + i
-                v[:, t // TT, :, t % TT] = vv[:, i, :]
+            t = pos + np.arange(n)
+            k[:, :, t // TT, t % TT] = np.transpose(kk, (0, 2, 1, 3)).reshape(
+                self.B, self.H, n, *k.shape[4:])
+            v[:, t // TT, (t % TT) // 8, t % 8] = vv.reshape(self.B, n, *v.shape[4:])
             return
         if self.rotate:
             zk = hadamard.rotate_latent_f32(zk, self.rk // 4)
@@ -308,7 +320,8 @@ class Cache:
         float64 [seq_len, Hkv, r_k] of batch element b."""
         if self.kind in ("f32", "bf16"):
             k, _ = self._elem_views()
-            x = k[b, :, :seq_len, :]
+            nt = (seq_len + TT - 1) // TT
+            x = k[b, :, :nt].reshape(self.H, nt * TT, self.rk)[:, :seq_len]
             x = x if self.kind == "f32" else from_bf16_bits(x)
             return np.transpose(x, (1, 0, 2)).astype(np.float64)
         kb, km, _, _ = self._q_views()
@@ -326,9 +339,8 @@ class Cache:
         nt = (seq_len + TT - 1) // TT
         if self.kind in ("f32", "bf16"):
             _, v = self._elem_views()
-            x = v[b, :nt]
+            x = v[b, :nt].reshape(nt * TT, self.rv)
             x = x if self.kind == "f32" else from_bf16_bits(x)
-            x = np.transpose(x, (0, 2, 1)).reshape(nt * TT, self.rv)
             return x[:seq_len].astype(np.float64)
         _, _, vb, vm = self._q_views()
         codes = unpack_value_tiles(vb[b, :nt], self.rv)            # [nt,64,R]

@@ -188,3 +188,29 @@ def test_page_printed_numbers():
     assert round(float(1 / f), 2) == e["inverse_approx"]
     # eq. 1 worked by hand: B=1, T=1, L=1, h_kv=1, d_h=1, 16 bits -> K and V
     assert sizes.dense_kv_bytes(1, 1, 1, 1, 1, 16) == 4
+
+
+def test_plain_layout_byte_positions():
+    """bf16 cache, B=2, Hkv=3, r_k=16, R_v=64, T_max=192 (3 tiles): one key
+    and one value element placed by hand.
+    key (b=1, h=2, t=70, c=13): tile 1, token 6, chunk 1, channel-in-chunk 5
+      element ((((1*3 + 2)*3 + 1)*2 + 1)*64 + 6)*8 + 5 = 16949 -> byte 33898
+    value (b=1, t=70, ch=45): tile 1, group 1, channel-in-group 13, block 0,
+      token-in-block 6
+      element ((((1*3 + 1)*2 + 1)*8 + 0)*32 + 13)*8 + 6 = 18542 -> byte 37084
+    1.5 is bf16 0x3FC0 (little-endian bytes C0 3F); -2.25 is 0xC010."""
+    c = oc.Cache(2, 3, 16, 64, 192, "bf16")
+    zk = np.zeros((2, 1, 3, 16), np.float32)
+    zv = np.zeros((2, 1, 64), np.float32)
+    zk[1, 0, 2, 13] = 1.5
+    zv[1, 0, 45] = -2.25
+    c.append(zk, zv, 70, 1)
+    kb, vb = c.buf["key"], c.buf["value"]
+    assert list(kb[33898:33900]) == [0xC0, 0x3F]
+    assert list(vb[37084:37086]) == [0x10, 0xC0]
+    assert np.count_nonzero(kb) == 2 and np.count_nonzero(vb) == 2
+    # the same positions in an fp32 cache hold 4-byte elements
+    c = oc.Cache(2, 3, 16, 64, 192, "f32")
+    c.append(zk, zv, 70, 1)
+    assert c.buf["key"][16949 * 4:16949 * 4 + 4].view(np.float32)[0] == 1.5
+    assert c.buf["value"][18542 * 4:18542 * 4 + 4].view(np.float32)[0] == -2.25
