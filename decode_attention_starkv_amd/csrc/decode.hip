@@ -1005,11 +1005,32 @@ __global__ __launch_bounds__(64 * kVprojWaves) void vproj_kernel(
   const float* arow = obar + ((size_t)min(bb, d.B - 1) * d.Hq + h) * d.rv + ks * 8;
   const size_t brow = ((size_t)g * d.dh + r0 + i16) * d.rv + ks * 8;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-  for (int k0 = w * 32; k0 < d.rv; k0 += 32 * kVprojWaves) {
-    const float4 x0 = *reinterpret_cast<const float4*>(arow + k0);
-    const float4 x1 = *reinterpret_cast<const float4*>(arow + k0 + 4);
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  // this wave's K-steps k0 = 32 (w + 4 s) < rv (s < 8 as rv <= 1024): all
+  // operand loads of all steps are issued before the first product; steps
+  // past rv multiply zeros
+  constexpr int kSteps = 1024 / (32 * kVprojWaves);
+  float4 xa[kSteps], xb[kSteps];
+  bf8 bw[kSteps];
+  f32x4 bwf[kSteps][2];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    const int k0 = 32 * (w + kVprojWaves * st);
+    const bool on = k0 < d.rv;
+    xa[st] = on ? *reinterpret_cast<const float4*>(arow + k0) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    xb[st] = on ? *reinterpret_cast<const float4*>(arow + k0 + 4) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (FMT == STARKV_CACHE_F32) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(bv) + brow + k0);
+      bwf[st][0] = on ? p[0] : f32x4{};
+      bwf[st][1] = on ? p[1] : f32x4{};
+    } else {
+      bw[st] = on ? *reinterpret_cast<const bf8*>(static_cast<const uint16_t*>(bv) + brow + k0)
+                  : bf8{};
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    const float xs[8] = {xa[st].x, xa[st].y, xa[st].z, xa[st].w,
+                         xb[st].x, xb[st].y, xb[st].z, xb[st].w};
     bf8 ah, al;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1018,20 +1039,19 @@ __global__ __launch_bounds__(64 * kVprojWaves) void vproj_kernel(
       al[e] = (__bf16)(x - (float)ah[e]);
     }
     if constexpr (FMT == STARKV_CACHE_F32) {
-      const float* p = static_cast<const float*>(bv) + brow + k0;
       bf8 bh, bl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bh[e] = (__bf16)p[e];
-        bl[e] = (__bf16)(p[e] - (float)bh[e]);
+        const float v = bwf[st][e >> 2][e & 3];
+        bh[e] = (__bf16)v;
+        bl[e] = (__bf16)(v - (float)bh[e]);
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
     } else {
-      const bf8 bw = *reinterpret_cast<const bf8*>(static_cast<const uint16_t*>(bv) + brow + k0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[st], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[st], acc, 0, 0, 0);
     }
   }
   if (w > 0) red[w - 1][l] = acc;
