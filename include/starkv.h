@@ -90,8 +90,11 @@ typedef struct starkv_config {
 
 /* Device buffers of one layer's cache.  Byte layout ("format v1", tiles of
  * 64 tokens):
- *   F32/BF16: key [B][Hkv][T_max][r_k], value [B][T_max/64][R_v][64];
- *             key_meta and value_meta are unused (may be NULL).
+ *   F32/BF16: key [B][Hkv][T_max/64][r_k/8][64 tokens][8 channels],
+ *             value [B][T_max/64][R_v/32][8 token blocks][32 channels]
+ *             [8 tokens] (token u of a tile, channel 32g + m: group g,
+ *             block u/8, [m][u%8]); key_meta and value_meta are unused
+ *             (may be NULL).
  *   Q43:      key  [B][T_max/64][Hkv] blocks of 832 B (4-bit plane u32[64],
  *             3-bit planes u32[64], u32[64], u8[64], token-major);
  *             key_meta [B][T_max/64][Hkv][64][4] fp16 (scale_hi, zero_hi,
