@@ -794,9 +794,10 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z[r], bacc, 0, 0, 0);
       lds_barrier();
     }
+    // zero-point sums of this wave's own columns: one writer per entry
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      if (m >= n0 && m < n0 + NIV) atomicAdd(&bias_l[acc_row(v, lane)][m], bacc[v]);
+      if (m >= n0 && m < n0 + NIV) bias_l[acc_row(v, lane)][m] = bacc[v];
     if (kFour && m == NIV) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -839,7 +840,8 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         const float4 x1 = *reinterpret_cast<const float4*>(st + row * kStageRow + 8 * k + 4);
         const h8 o = {(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
                       (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
-        *reinterpret_cast<h8*>(po + (obase + row) * d.rv + n0 * 32 + 8 * k) = o;
+        // streaming stores: the partials are read once, by the merge
+        __builtin_nontemporal_store(o, reinterpret_cast<h8*>(po + (obase + row) * d.rv + n0 * 32 + 8 * k));
       }
     }
     };
@@ -894,7 +896,8 @@ hipError_t launch_q43(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t
 // fp16 partials: one 8-byte load).
 __device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ inline float4 load4(const _Float16* p) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  // the partials are read exactly once
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   // element picks go through scalars: a bit-cast applied directly to an
   // ext_vector element is lowered as a cast of element 0
   const uint32_t w0 = w[0], w1 = w[1];
