@@ -102,7 +102,9 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
   }
   v *= qscale;
   if (FMT != STARKV_CACHE_Q43) {
-    if (t < d.rk) static_cast<float*>(qt)[(size_t)bh * kPlainRec + t] = v;
+    // the whole record: entries past r_k are zeros (the split kernels read
+    // key rows in 8-channel chunks and may pad them)
+    static_cast<float*>(qt)[(size_t)bh * kPlainRec + t] = t < d.rk ? v : 0.0f;
     return;
   }
   if (t < 32) sq[t] = (_Float16)v;
@@ -193,8 +195,11 @@ __device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
         const u32x4 u = __builtin_nontemporal_load(p), v = __builtin_nontemporal_load(p + 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          z[e] = __builtin_bit_cast(float, u[e]);
-          z[4 + e] = __builtin_bit_cast(float, v[e]);
+          // vector elements go through scalars before the bit-cast (a
+          // bit-cast of an ext_vector element is lowered as one of element 0)
+          const uint32_t wu = u[e], wv = v[e];
+          z[e] = __builtin_bit_cast(float, wu);
+          z[4 + e] = __builtin_bit_cast(float, wv);
         }
       } else {
         const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
@@ -218,7 +223,8 @@ __device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
   uint32_t kw[NC][CW];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const bool live = RK == 64 || RK == 32 || 8 * c < d.rk;
+    // chunks past r_k (when RK rounds it up) are neither read nor used
+    const bool live = 8 * c < d.rk;
     const size_t row = row0 + (size_t)(live ? c : 0) * (kTile * 8);
     if constexpr (FMT == STARKV_CACHE_F32) {
       const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.key) + row);

@@ -98,3 +98,20 @@ def test_deterministic_run_to_run():
     a = gpu_decode(w, cfg, g, 1000, q, 2)
     b = gpu_decode(w, cfg, g, 1000, q, 2)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name,kw", [
+    # one KV head per query head, 8-channel keys (whole rows, values early)
+    ("l2_bf16", dict(n_q_heads=8, n_kv_heads=8, key_rank=8, value_rank=64)),
+    # groups of 2, 24-channel keys in 32-channel registers, R_v 96
+    ("l2_bf16", dict(n_q_heads=8, n_kv_heads=4, key_rank=24, value_rank=96)),
+    # groups of 4, 64-channel keys (chunk loop), R_v 160 (idle value waves)
+    ("l2_bf16", dict(n_q_heads=16, n_kv_heads=4, key_rank=64, value_rank=160)),
+    # fp32, groups of 8, 40-channel keys
+    ("tiny", dict(n_q_heads=16, n_kv_heads=2, head_dim=128, key_rank=40, value_rank=256)),
+])
+def test_plain_cache_shapes(name, kw):
+    """Unquantized caches across the key-row and group-size variants of the
+    plain split kernel, with a ragged tail."""
+    err, _ = run_case(name, 333, q_scale=4.0, **kw)
+    assert err <= TOL
