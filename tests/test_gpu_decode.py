@@ -115,3 +115,18 @@ def test_plain_cache_shapes(name, kw):
     plain split kernel, with a ragged tail."""
     err, _ = run_case(name, 333, q_scale=4.0, **kw)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("kw", [
+    # one KV head (score waves 1-3 idle), groups of 8, d_h 256
+    dict(n_q_heads=8, n_kv_heads=1, head_dim=256, value_rank=256),
+    # two KV heads, groups of 2
+    dict(n_q_heads=4, n_kv_heads=2, value_rank=256),
+    # 16 KV heads in groups of 2, R_v 768 (six value groups per value wave)
+    dict(n_q_heads=32, n_kv_heads=16, value_rank=768),
+])
+def test_q43_shapes(kw):
+    """4/3-bit caches across the score-wave head counts and value-wave group
+    counts of the split kernel, with a ragged tail and a peaked softmax."""
+    err, _ = run_case("l3_gqa_q43", 333, q_scale=4.0, **kw)
+    assert err <= TOL
