@@ -928,13 +928,31 @@ __global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_
   const int bh = blockIdx.x;
   const int b = bh / d.Hq, h = bh % d.Hq;
   const int t = threadIdx.x, lane = t & 63;
+  const int c = 4 * t;
+  const size_t stride = (size_t)d.Hq * d.rv;
+  const PT* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + min(c, d.rv - 4);
+  // (m, l) of split `lane` first, then the rows of the first kPre splits
+  // (clamped addresses: every load is issued, so the wait for (m, l) does
+  // not cover the rows)
+  const float2 ml0 = *reinterpret_cast<const float2*>(
+      part_ml + (((size_t)b * splits + min(lane, splits - 1)) * d.Hq + h) * 2);
+  // (fp32 partials come with one split per row in the prefill: one row)
+  constexpr int kPre = kNormalised ? 16 : 1;
+  float4 xp[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) xp[u] = load4(src + (size_t)min(u, splits - 1) * stride);
   // every wave reduces the same (m, l) values; wave 0 publishes the weights
-  float mx = -INFINITY;
-  for (int s = lane; s < splits; s += 64)
+  float mx = lane < splits ? ml0.x : -INFINITY;
+  for (int s = lane + 64; s < splits; s += 64)
     mx = fmaxf(mx, part_ml[(((size_t)b * splits + s) * d.Hq + h) * 2]);
   mx = wave_max(mx);
   float L = 0.0f;
-  for (int s = lane; s < splits; s += 64) {
+  if (lane < splits) {
+    const float wgt = ml0.y > 0.0f ? exp2f(ml0.x - mx) : 0.0f;
+    if (t < 64) ms[lane] = kNormalised ? wgt * ml0.y : wgt;
+    L = wgt * ml0.y;
+  }
+  for (int s = lane + 64; s < splits; s += 64) {
     const size_t k = (((size_t)b * splits + s) * d.Hq + h) * 2;
     const float l = part_ml[k + 1];
     const float wgt = l > 0.0f ? exp2f(part_ml[k] - mx) : 0.0f;
@@ -943,12 +961,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_
   }
   const float inv = 1.0f / wave_sum(L);
   __syncthreads();
-  const int c = 4 * t;
   float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
   if (c < d.rv) {
-    const size_t stride = (size_t)d.Hq * d.rv;
-    const PT* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + c;
-    int s = 0;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const float wgt = u < splits ? ms[u] : 0.0f;
+      o.x = fmaf(wgt, xp[u].x, o.x);
+      o.y = fmaf(wgt, xp[u].y, o.y);
+      o.z = fmaf(wgt, xp[u].z, o.z);
+      o.w = fmaf(wgt, xp[u].w, o.w);
+    }
+    int s = kPre;
     for (; s + 8 <= splits; s += 8) {
       float4 x[8];
 #pragma unroll
