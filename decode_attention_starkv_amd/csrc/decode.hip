@@ -21,7 +21,10 @@
 // zero are folded outside the inner products:
 //   keys:   q~ . z_hat = s * 2^24 * (q~ . k 2^-24) + z * sum(q~)
 //   values: P Z_hat    = 2^24 * ((P * s) k 2^-24) + P z      (per 32-ch group)
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "device.h"
 
@@ -1187,12 +1190,25 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int decode_groups_per_cu(const Dims& d) {
   if (d.dtype != STARKV_CACHE_Q43) return 1;
   const SplitFn k = q43_kernel(d);
+  if (!k) return 1;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  // asked once per kernel instantiation and device
+  static std::mutex mu;
+  static std::map<std::pair<SplitFn, int>, int> known;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = known.find({k, dev});
+  if (it != known.end()) return it->second;
   int n = 0;
-  if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void*>(k), 512, 0) != hipSuccess || n < 1) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(k), 512, 0) != hipSuccess || n < 1) {
     (void)hipGetLastError();   // no device to ask: one group per unit
     return 1;
   }
+  known[{k, dev}] = n;
   return n;
 }
 
