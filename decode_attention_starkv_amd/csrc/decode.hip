@@ -308,6 +308,10 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   __shared__ float alpha_l[2][32];
   __shared__ int flag_l[2];
   __shared__ float l_row[32];
+  // bf16 caches: per-wave staging of the fp16 partial rows (32 rows of the
+  // wave's NI groups, padded rows) for 16-byte stores
+  constexpr int kStg = kBF ? NI * 32 + 8 : 8;
+  __shared__ __attribute__((aligned(16))) _Float16 stg[kBF ? NW : 1][32][kStg];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -453,21 +457,43 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
     }
   }
   lds_barrier();   // l of every head
+  if constexpr (kBF) {
+    // rows divided by their l, as fp16, through LDS into 16-byte streaming
+    // stores of whole 32-channel group segments
+    float inv_l[16];
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    const int n = wave + ni * NW;
-    if (n < GV) {
+    for (int v = 0; v < 16; ++v) {
+      const float l = l_row[acc_row(v, lane)];
+      inv_l[v] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = acc_row(v, lane);
-        if (row < d.Hq) {
-          const size_t o = (obase + row) * d.rv + n * 32 + m;
-          if constexpr (kBF) {
-            const float l = l_row[row];
-            reinterpret_cast<_Float16*>(a.part_o)[o] = (_Float16)(l > 0.0f ? acc[ni][v] / l : 0.0f);
-          } else {
-            a.part_o[o] = acc[ni][v];
-          }
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        stg[wave][acc_row(v, lane)][ni * 32 + m] = (_Float16)(acc[ni][v] * inv_l[v]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own staging writes done
+    __builtin_amdgcn_wave_barrier();
+    _Float16* po = reinterpret_cast<_Float16*>(a.part_o);
+#pragma unroll
+    for (int k = 0; k < 32 * NI * 4 / 64; ++k) {
+      const int c = lane + 64 * k;
+      const int row = c / (NI * 4), q = c % (NI * 4);
+      const int ni = q >> 2, part = q & 3;
+      const int n = wave + ni * NW;
+      if (row < d.Hq && n < GV) {
+        const h8 o = *reinterpret_cast<const h8*>(&stg[wave][row][ni * 32 + part * 8]);
+        __builtin_nontemporal_store(o, reinterpret_cast<h8*>(po + (obase + row) * d.rv + n * 32 + part * 8));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = wave + ni * NW;
+      if (n < GV) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = acc_row(v, lane);
+          if (row < d.Hq) a.part_o[(obase + row) * d.rv + n * 32 + m] = acc[ni][v];
         }
       }
     }
