@@ -547,17 +547,18 @@ constexpr int ring_bytes(int niv) {
 // 8 waves; waves w and w+4 share a SIMD.
 //   score waves 0-3: wave s owns KV heads s, s+4, ... (KVS of them); lane =
 //     token; key codes (loaded two barrier periods ahead into alternating
-//     register sets) become
-//     fp16 pairs by shift+mask and meet the query pairs in v_dot2_f32_f16;
-//     p = exp2(score - m_ref) goes to a 2-slot LDS ring as the stacked-head
-//     P tile (32 rows, fp16).
+//     register sets) are read in place as fp16 pairs (one AND per field
+//     pair, the field weights carried by the query record) and meet the
+//     query pairs in v_dot2_f32_f16; p = exp2(score - m_ref) goes to a
+//     2-slot LDS ring as the stacked-head P tile (32 rows, fp16).
 //   value waves 4-7: wave v owns the NIV value groups v*NIV .. v*NIV+NIV-1
 //     (32 channels each, one MFMA column tile); since R_v/4 channels are
 //     4-bit, value wave 0 holds exactly the 4-bit groups.  Each value wave
 //     streams its own groups' codes, scales and zeros into a private 4-slot
 //     LDS ring (direct-to-LDS, non-temporal) three tiles ahead, so it waits
-//     on its own loads only.  A = P * scale in fp16, B = codes as fp16 subnormals,
-//     mfma 32x32x16; P x zero adds the zero points.
+//     on its own loads only.  A = P * scale in fp16, B = codes as fp16
+//     subnormals, mfma 32x32x16; P x zero adds the zero points, and a column
+//     of ones in that product gives each head's exp-sum l.
 // One barrier per tile hands P over: while the value waves contract tile t,
 // the score waves already score tile t+1.
 template <int G, int KVS, int NIV>
