@@ -22,6 +22,11 @@ number of steps in which the library records events between its kernels.
 --workload longchat_prefill times the chunked causal prefill instead (one
 starkv_prefill of an 8192-token chunk on 24576 cached tokens per step) and
 reports the attention kernel against the MFMA peak.
+
+--t-sweep runs the default decode workload at T = 8K, 16K, 32K, 64K and 128K
+(one child process each) and prints one JSON line per T plus a line with the
+marginal bandwidth of the split kernel (bytes added / time added between
+successive T) and its fixed cost per launch.
 """
 
 from __future__ import annotations
@@ -57,10 +62,74 @@ def parse():
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    p.add_argument("--t-sweep", action="store_true",
+                   help="decode at T = 8K .. 128K, one JSON line per T")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run one plain 1 GiB device-to-device copy, the "
                         "reference for scaling HBM byte counters")
     return p.parse_args()
+
+
+def percentiles(v):
+    """p10 / p50 / p90 of a list of times (nearest rank)."""
+    s = sorted(v)
+    pick = lambda q: s[min(len(s) - 1, max(0, int(math.ceil(q * len(s))) - 1))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
+def host_info():
+    """What the CPU baseline ran on: CPU model, usable cores, BLAS."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        import numpy  # noqa: F401  (loads the BLAS it reports)
+        from threadpoolctl import threadpool_info
+        blas = sorted({f"{i.get('internal_api')}:{i.get('num_threads')}"
+                       for i in threadpool_info()})
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas": blas}
+
+
+def t_sweep():
+    """Decode at several T (one child process each, this process never
+    touches the GPU) and the split kernel's marginal bandwidth between them."""
+    import subprocess
+    rows = []
+    for T in (8192, 16384, 32768, 65536, 131072):
+        cmd = [sys.executable, os.path.abspath(__file__), "--seq-len", str(T),
+               "--steps", "20", "--warmup", "10", "--no-cpu-baseline"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stderr[-2000:])
+            sys.exit(res.returncode)
+        r = json.loads(res.stdout.strip().splitlines()[-1])
+        split_us = r["kernels_ms"]["split"] * 1e3
+        row = {"t_sweep": True, "seq_len": T, "batch": r["config"]["batch"],
+               "splits": r["config"]["splits"], "ms_per_step": r["ms_per_step"],
+               "tokens_per_s": r["value"], "split_us": split_us,
+               "split_hbm_frac": r["roofline"]["frac"],
+               "cache_bytes": r["algorithmic_bytes"]["cache"]}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    marg = []
+    for a, b in zip(rows, rows[1:]):
+        db = b["cache_bytes"] - a["cache_bytes"]
+        dt = (b["split_us"] - a["split_us"]) * 1e-6
+        marg.append({"from_T": a["seq_len"], "to_T": b["seq_len"],
+                     "marginal_GBps": db / dt / 1e9})
+    last = marg[-1]["marginal_GBps"] if marg else None
+    fixed = (rows[-1]["split_us"] - rows[-1]["cache_bytes"] / (last * 1e9) * 1e6) if last else None
+    print(json.dumps({"t_sweep_summary": True, "marginal": marg,
+                      "fixed_us_per_launch_at_last_rate": fixed}), flush=True)
 
 
 def algorithmic_bytes(w, cfg, seq_len, sk):
@@ -123,7 +192,7 @@ def cpu_baseline(w, seq_len, min_s=10.0, max_reps=30):
         reps += 1
         assert np.isfinite(out).all()
     return {"value": reps * seq_len / dt, "unit": "tokens attended/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "host": host_info(),
             "sample": f"{reps} x decode of 1 sequence x {seq_len} tokens x "
                       f"{w.n_q_heads} heads of the same workload (fp64 numpy, "
                       f"{dt:.1f} s total)"}
@@ -167,6 +236,7 @@ def cpu_baseline_prefill(w, n_rows=64, min_s=10.0, max_reps=30):
         reps += 1
         assert np.isfinite(out).all()
     return {"value": reps * n_rows / dt, "unit": "chunk tokens/s", "cores": threads,
+            "host": host_info(),
             "kind": "oracle",
             "sample": f"{reps} x causal attention of {n_rows} evenly spaced queries "
                       f"x {w.n_q_heads} heads of the {chunk}-token chunk over "
@@ -258,9 +328,12 @@ def run_prefill(args, w, torch, sk, synth):
     print(json.dumps(res))
 
 
-def traffic_from_counters():
+def traffic_from_counters(w, batch, seq_len, splits):
     """HBM bytes per split-kernel launch from committed rocprofv3 counters,
-    or None if the kernel source changed since they were taken."""
+    or None if the kernel source changed since they were taken or the run is
+    not the configuration they were taken on (l2_q43, B 16, T 32768)."""
+    if (w.name, batch, seq_len, splits) != ("l2_q43", 16, 32768, 16):
+        return None
     if not os.path.exists(COUNTERS):
         return None
     rec = json.load(open(COUNTERS))
@@ -276,6 +349,8 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; "
                           "--gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.t_sweep:
+        return t_sweep()
     import torch
 
     if args.calibrate_copy:
@@ -397,8 +472,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "split_kernel",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_from_counters()},
+                     "traffic": traffic_from_counters(w, w.batch, seq_len,
+                                                      sk.starkv_decode_splits(cfg, seq_len))},
         "step_hbm_frac": (cache_bytes + factor_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "ms_per_step_percentiles": percentiles(step_ms),
+        "split_ms_percentiles": percentiles(kern_ms[1]),
         "kernels_ms": {"append": mean(app_ms), "qproj": mean(kern_ms[0]),
                        "split": split_ms, "merge": mean(kern_ms[2]),
                        "vproj": mean(kern_ms[3])},
