@@ -6,10 +6,10 @@
 //   gemm      Z = X [A_key | A_value] (bf16 in, fp32 out) on MFMA 32x32x16
 //   append    the decode-path append kernels (rotation + 4/3-bit packing)
 //   qproj     q~ for every query of the chunk (the decode kernel, rows = B*C)
-//   attn      per (16 queries, 8 query heads, half of R_v): latent scores on
-//             MFMA with an online softmax, then P Z_v on MFMA against an
-//             fp16 value tile dequantized once per workgroup into LDS
-//             (section 5.3, eq. 12)
+//   attn      per (16 queries, 8 query heads, up to 512 value columns):
+//             latent scores on MFMA with a lazy online softmax, then P Z_v
+//             on MFMA with each wave dequantizing its own value groups
+//             straight into MFMA operands (section 5.3, eq. 12)
 //   merge, vproj   the decode kernels with one split per query row
 #include <type_traits>
 
@@ -187,22 +187,17 @@ constexpr int kPQ = 16;       // queries per workgroup
 constexpr int kPH = 8;        // query heads per workgroup
 constexpr int kRows = kPQ * kPH;   // rows of the stacked P tile
 constexpr int kPS = 72;       // P row stride (halves)
-constexpr int kZRow = 128;    // bytes of one dequantized value channel (64 tokens)
 constexpr int kMaxRv = 1024;
-constexpr int kHalfRv = kMaxRv / 2;   // value columns per workgroup (at most)
-// packed value data of one tile and one column half, staged in LDS: codes
-// (at most 8 four-bit + 8 three-bit groups), then scales, then zeros
-constexpr int kVCodeMax = 8 * 1024 + 8 * 768;
-constexpr int kVMetaMax = (kHalfRv / 32) * kTile * 2;
-constexpr int kVSlot = kVCodeMax + 2 * kVMetaMax;
+constexpr int kMaxCols = 512;      // value columns per workgroup (at most)
+// bytes of one tile's value scales (or zeros) over the workgroup's groups
+constexpr int kMetaHalf = (kMaxCols / 32) * kTile * 2;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   Dims d;
-  int ctx, chunk, n_qb, n_qb_pad, n_hg;
-  const uint8_t* key;
-  const u32x2* kmeta;     // per token: (s_hi | z_hi << 16, s_lo | z_lo << 16)
+  int ctx, chunk, n_qb, n_qb_pad, n_hg, n_cb;
   const uint8_t* value;
   const uint16_t* vmeta;
   const uint32_t* qt;     // [B*C][Hq][kQ43Rec]
@@ -211,45 +206,70 @@ struct AttnArgs {
   float* part_ml;         // [B*C][Hq][2]
 };
 
-// Workgroup = (16 consecutive queries, 8 query heads, half of the value
+// One MFMA 32x32x16 B operand of value group run `w` (the lane's channel and
+// 32-token half): tokens 8r .. 8r + 7 of the run as z + s * code, one packed
+// fp16 FMA per token pair.  S, Z: the scales and zeros of those 8 tokens.
+// kMask zeroes tokens past `pmax` (tok: the run's token 8r).
+template <bool kFour, bool kMask>
+__device__ inline h8 value_frag(const u32x4& w, int r, const u32x4& S, const u32x4& Z,
+                                int tok, int pmax) {
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t code = run_pair<kFour>(w, 4 * r + q);
+    // codes as exact fp16 integers: (1024 + k) - 1024
+    const h2 kv = __builtin_bit_cast(h2, code | 0x64006400u) - h2{1024.0f16, 1024.0f16};
+    // element picks go through scalars: a bit-cast applied directly to an
+    // ext_vector element is lowered as a cast of element 0
+    const uint32_t sb = S[q], zb = Z[q];
+    h2 v = __builtin_elementwise_fma(kv, __builtin_bit_cast(h2, sb), __builtin_bit_cast(h2, zb));
+    if constexpr (kMask) {
+      if (tok + 2 * q > pmax) v[0] = (_Float16)0.0f;
+      if (tok + 2 * q + 1 > pmax) v[1] = (_Float16)0.0f;
+    }
+    o[q] = __builtin_bit_cast(uint32_t, v);
+  }
+  return __builtin_bit_cast(h8, u32x4{o[0], o[1], o[2], o[3]});
+}
+
+// Workgroup = (16 consecutive queries, 8 query heads, R_v / n_cb value
 // columns, sequence b), 8 waves.  Rows of the stacked P tile: row = query * 8
-// + head (128 rows = four MFMA row tiles).  Per 64-token tile:
-//   phase A  all threads dequantize the tile's value latents of this
-//            column half into LDS as fp16 (z + s * code: one packed fp16
-//            FMA per token pair; rows of 64 tokens, 16-byte chunks swizzled
-//            by channel so that MFMA operand reads spread over the banks);
-//   barrier
-//   phase B  wave w scores tile t+1 for query head w and all 16 queries on
-//            MFMA 16x16x32 (A = the queries' latent vectors, B = the fp16
-//            key latents a pre-pass dequantized from the packed cache); a
-//            lazy online softmax writes P to the other P slot.  It also
-//            contracts tile t: row tiles 2(w&1),
-//            2(w&1)+1 against its R_v/256 value column tiles on MFMA
-//            32x32x16 f16;
-//   barrier
-// The two column halves compute the same scores; the first writes (m, l).
+// + head (128 rows = four MFMA row tiles).  Wave w
+//   - scores query head w for the 16 queries on MFMA 16x16x32 with the keys
+//     as the A operand (a lane then holds four consecutive tokens of one
+//     query) and a lazy online softmax, writing fp16 probabilities to a P
+//     slot;
+//   - owns value groups 2w and 2w + 1 of the workgroup's columns for all
+//     128 rows: it dequantizes their codes (read from global memory) with
+//     the scales and zeros staged in LDS straight into MFMA B operands and
+//     contracts them with P on MFMA 32x32x16.  MFMA r of a tile takes, in
+//     k-slot j, tokens 32j + 8r .. 32j + 8r + 7: word r of the lane's run.
+// One barrier per 64-token tile: P, alpha and the staged scales and zeros
+// are double-buffered.  Waves 0-3 score tile t+1 and then contract tile t;
+// waves 4-7 (the other wave on each SIMD) contract first, so that one
+// wave's VALU work meets the other's matrix work.
+// The column blocks compute the same scores; the first writes (m, l).
 // Causal mask: query i (absolute position ctx + i) sees cached positions
 // 0 .. ctx + i.  Value tokens past the workgroup's last position are zeroed
 // so that unwritten cache bytes never reach the MFMA operands.
-template <int G, int NCT>
+template <int G>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const Dims& d = a.d;
-  __shared__ __attribute__((aligned(16))) uint8_t zt[kHalfRv * kZRow];
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kRows * kPS];
+  __shared__ __attribute__((aligned(16))) uint8_t meta_l[2][2 * kMetaHalf];
   // the queries' latent vectors in natural channel order (fp16)
-  __shared__ __attribute__((aligned(16))) _Float16 qnat[kPQ * kPH * 32];
-  __shared__ __attribute__((aligned(16))) uint8_t vst[2][kVSlot];
-  __shared__ float alpha_l[2][kRows];
+  __shared__ __attribute__((aligned(16))) _Float16 qnat[kRows * 32];
+  __shared__ __attribute__((aligned(16))) float alpha_l[2][kRows];
   __shared__ int flag_l[2];
 
-  // XCD-aware order: the 8 workgroups of one query block (4 head groups x
-  // 2 column halves for 32 heads) run on one XCD (blockIdx % 8) and share
-  // its L2; the query blocks with the longest causal span start first.
+  // XCD-aware order: the workgroups of one query block (head groups x
+  // column blocks) run on one XCD (blockIdx % 8) and share its L2; the query
+  // blocks with the longest causal span start first.
   const int L = blockIdx.x;
   const int xcd = L & 7, k = L >> 3;
-  const int per_qb = 2 * a.n_hg;
+  const int per_qb = a.n_cb * a.n_hg;
   const int sub = k % per_qb;
-  const int hg = sub % a.n_hg, cs = sub / a.n_hg;
+  const int hg = sub % a.n_hg, cb = sub / a.n_hg;
   const int qb = a.n_qb_pad - 1 - ((k / per_qb) * 8 + xcd);
   if (qb >= a.n_qb) return;   // padding workgroup; uniform, before any barrier
   const int b = blockIdx.y;
@@ -258,33 +278,31 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int pfirst = a.ctx + q0;            // first query's position
   const int pmax = pfirst + nq - 1;         // last position any row may see
   const int tile_last = pmax / kTile;
-  const int cols = d.rv / 2, col0 = cs * cols;
+  const int cols = d.rv / a.n_cb, col0 = cb * cols;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, j = lane >> 5;   // 32x32 operand coordinates
   const int c16 = lane & 15, g16 = lane >> 4;  // 16x16 operand coordinates
 
-  for (int i = tid; i < 2 * kRows * kPS; i += 512) (&p_l[0][0])[i] = (_Float16)0.0f;
   // the query records hold 16 channel pairs (lo half, hi half) in the order
   // of the packed key words; put every channel back in its place
   for (int i = tid; i < kPQ * kPH * 16; i += 512) {
     const int qh = i >> 4, t = i & 15;       // (query, head) and pair
     const int qi = qh / kPH;
-    int ca, cb;
-    if (t < 4) { ca = t; cb = t + 4; }
-    else if (t < 9) { ca = 8 + (t - 4); cb = 18 + (t - 4); }
-    else if (t < 14) { ca = 13 + (t - 9); cb = 23 + (t - 9); }
-    else if (t == 14) { ca = 28; cb = 30; }
-    else { ca = 29; cb = 31; }
+    int ca, cb2;
+    if (t < 4) { ca = t; cb2 = t + 4; }
+    else if (t < 9) { ca = 8 + (t - 4); cb2 = 18 + (t - 4); }
+    else if (t < 14) { ca = 13 + (t - 9); cb2 = 23 + (t - 9); }
+    else if (t == 14) { ca = 28; cb2 = 30; }
+    else { ca = 29; cb2 = 31; }
     const uint32_t pr = qi < nq
         ? a.qt[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH) * kQ43Rec +
                (qh % kPH) * kQ43Rec + t]
         : 0u;
     qnat[qh * 32 + ca] = __builtin_bit_cast(_Float16, (uint16_t)(pr & 0xFFFFu));
-    qnat[qh * 32 + cb] = __builtin_bit_cast(_Float16, (uint16_t)(pr >> 16));
+    qnat[qh * 32 + cb2] = __builtin_bit_cast(_Float16, (uint16_t)(pr >> 16));
   }
-  if (tid < 2 * kRows) (&alpha_l[0][0])[tid] = 1.0f;
   if (tid < 2) flag_l[tid] = -1;
   __syncthreads();
 
@@ -292,260 +310,253 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int hl = wave;                          // query head within the group
   const int h = hg * kPH + hl;
   const int g = h / G;
-  // per lane: queries g16*4 + v (v < 4) of the 16x16 result
-  float m_ref[4], l_lane[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) { m_ref[v] = -INFINITY; l_lane[v] = 0.0f; }
+  // B operand of the score MFMA: query c16, channels 8 g16 .. 8 g16 + 7
+  const h8 bq = *reinterpret_cast<const h8*>(&qnat[(c16 * kPH + hl) * 32 + g16 * 8]);
+  // lazy softmax state of query c16 (the same in its four lanes).  The
+  // running max starts finite so that exp2(x - m) needs no guard: a row's
+  // first real score always moves it (alpha = exp2(-1e30 - m) = 0), and rows
+  // of padding queries only ever see -inf (p = 0).
+  float m_ref = -1e30f, l_lane = 0.0f;
   // P tile: row R, token u stored at chunk (u / 8) ^ (R / 32) of the row, so
   // that the four row tiles' writes fall in different LDS banks
   auto p_at = [&](int slot, int R, int u) -> _Float16* {
     return &p_l[slot][R * kPS + (((u >> 3) ^ (R >> 5)) << 3) + (u & 7)];
   };
-
-  // scores of tile `tile` (index it in the loop) into P slot `slot`: MFMA
-  // 16x16x32 with A = the 16 queries' latent vectors, B = 16 tokens' fp16
-  // key latents, both in natural channel order
-  auto score = [&](int tile, int it, int slot) {
-    const h8 aq = *reinterpret_cast<const h8*>(&qnat[(c16 * kPH + hl) * 32 + g16 * 8]);
-    const bool masked = tile * kTile + kTile - 1 > pfirst;   // uniform
-    const _Float16* kdt = a.kd + (((size_t)b * d.Tmax + tile * kTile) * d.Hkv + g) * 32 + g16 * 8;
-    h8 bk[4];
+  // A operands of the score MFMA: tokens bl * 16 + c16 of a tile, channels
+  // 8 g16 .. 8 g16 + 7 of KV head g
+  const _Float16* kbase = a.kd + ((size_t)b * d.Tmax * d.Hkv + g) * 32 + g16 * 8;
+  auto load_keys = [&](int tile, h8 (&kk)[4]) {
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl)
-      bk[bl] = *reinterpret_cast<const h8*>(kdt + (size_t)(bl * 16 + c16) * d.Hkv * 32);
-    float x[4][4];   // [16-token block][query v]
+      kk[bl] = *reinterpret_cast<const h8*>(
+          kbase + (size_t)(tile * kTile + bl * 16 + c16) * d.Hkv * 32);
+  };
+
+  // scores of tile `tile` (index it in the loop) into P slot `slot`
+  auto score = [&](int tile, int it, int slot, const h8 (&kk)[4]) {
+    float x[4][4];   // [16-token block][token 4 g16 + v], query c16
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl) {
-      const f32x4v dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bk[bl], f32x4v{}, 0, 0, 0);
-      const int tok = tile * kTile + bl * 16 + c16;
+      const f32x4v sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kk[bl], bq, f32x4v{}, 0, 0, 0);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int q = g16 * 4 + v;
-        x[bl][v] = (!masked || (q < nq && tok <= pfirst + q)) ? dq[v] : -INFINITY;
-      }
+      for (int v = 0; v < 4; ++v) x[bl][v] = sc[v];
     }
-    bool big = false;
+    if (tile * kTile + kTile - 1 > pfirst) {   // uniform: some token is hidden
+      // last token of the tile query c16 sees (none for padding queries)
+      const int lim = c16 < nq ? pfirst + c16 - tile * kTile : -1;
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          x[bl][v] = bl * 16 + 4 * g16 + v > lim ? -INFINITY : x[bl][v];
+    }
+    float tmax = x[0][0];
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) big |= x[bl][v] > m_ref[v] + kLazy;
-    if (__builtin_amdgcn_ballot_w64(big) != 0) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float gm = fmaxf(fmaxf(x[0][v], x[1][v]), fmaxf(x[2][v], x[3][v]));
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
-        float alpha = 1.0f;
-        if (gm > m_ref[v] + kLazy) {          // uniform in the 16-lane group
-          alpha = m_ref[v] == -INFINITY ? 0.0f : exp2f(m_ref[v] - gm);
-          m_ref[v] = gm;
-          l_lane[v] *= alpha;
-          if (c16 == 0) flag_l[slot] = it;
-        }
-        if (c16 == 0) alpha_l[slot][(g16 * 4 + v) * kPH + hl] = alpha;
+      for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, x[bl][v]);
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kLazy) != 0) {
+      float gm = fmaxf(tmax, __shfl_xor(tmax, 16));
+      gm = fmaxf(gm, __shfl_xor(gm, 32));
+      if (gm > m_ref + kLazy) {        // the same in the query's four lanes
+        alpha = __builtin_amdgcn_exp2f(m_ref - gm);
+        m_ref = gm;
+        l_lane *= alpha;
+        flag_l[slot] = it;
       }
-    } else if (lane < kPQ) {
-      alpha_l[slot][lane * kPH + hl] = 1.0f;
     }
+    if (lane < kPQ) alpha_l[slot][c16 * kPH + hl] = alpha;
+    float ls = 0.0f;
 #pragma unroll
-    for (int bl = 0; bl < 4; ++bl)
+    for (int bl = 0; bl < 4; ++bl) {
+      float p[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p = x[bl][v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[bl][v] - m_ref[v]);
-        l_lane[v] += p;
-        *p_at(slot, (g16 * 4 + v) * kPH + hl, bl * 16 + c16) = (_Float16)p;
+        p[v] = __builtin_amdgcn_exp2f(x[bl][v] - m_ref);
+        ls += p[v];
       }
+      *reinterpret_cast<h4*>(p_at(slot, c16 * kPH + hl, bl * 16 + 4 * g16)) =
+          h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    }
+    l_lane += ls;
   };
 
-  // ----------------------------------------------------- value dequantize
+  // ------------------------------------------------------------ value setup
   const int NG = d.rv / 32;           // value groups
   const int NH = d.rv / 128;          // 4-bit value groups
+  const int ngrp = cols / 32, g_first = col0 / 32;
   const size_t vtile_bytes = (size_t)26 * d.rv;
   const size_t mtile = (size_t)2 * NG * kTile;     // fp16 elements
-  const int g_first = col0 / 32;      // first value group of this half
-  const int ngh = cols / 32;          // value groups of this half
+  const int meta_bytes = ngrp * kTile * 2;
+  // direct-to-LDS copy of one tile's scales and zeros of the workgroup's
+  // groups into slot `slot`; waves 0-3 move one 1 KB piece each
+  auto stage_meta = [&](int tile, int slot) {
+    if (wave < 4) {
+      const int part = wave >> 1, piece = wave & 1;   // part 0 scales, 1 zeros
+      const int off = piece * 1024 + lane * 16;
+      if (off < meta_bytes) {
+        const uint16_t* mt = a.vmeta + ((size_t)b * d.NT + tile) * mtile +
+                             (size_t)(part * NG + g_first) * kTile;
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const uint8_t*>(mt) + off,
+            (__attribute__((address_space(3))) void*)(&meta_l[slot][part * kMetaHalf + piece * 1024]),
+            16, 0, 0);
+      }
+    }
+  };
+  const int gw = g_first + 2 * wave;          // the wave's first value group
+  const bool active = 2 * wave < ngrp;        // uniform
+  const bool four = gw < NH;                  // both groups: NH is even
   auto goff = [&](int gi) { return gi < NH ? gi * 1024 : NH * 1024 + (gi - NH) * 768; };
-  const int code_lo = goff(g_first), code_bytes = goff(g_first + ngh) - code_lo;
-  const int meta_bytes = ngh * kTile * 2;
-  // direct-to-LDS copy of one tile's codes, scales and zeros of this half
-  // into ring slot `slot`; wave w moves the 1 KB pieces w, w + 8, ...
-  auto stage = [&](int tile, int slot) {
-    const size_t t = (size_t)b * d.NT + tile;
-    const uint8_t* src[3] = {a.value + t * vtile_bytes + code_lo,
-                             reinterpret_cast<const uint8_t*>(a.vmeta + t * mtile + (size_t)g_first * kTile),
-                             reinterpret_cast<const uint8_t*>(a.vmeta + t * mtile + (size_t)(NG + g_first) * kTile)};
-    const int len[3] = {code_bytes, meta_bytes, meta_bytes};
-    const int dst[3] = {0, kVCodeMax, kVCodeMax + kVMetaMax};
+  const int coff0 = goff(gw), coff1 = goff(gw + 1);
+
+  f32x16 acc[4][2];
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
-      for (int piece = wave; piece * 1024 < len[k]; piece += 8) {
-        const int off = piece * 1024 + lane * 16;
-        if (off < len[k])
-          __builtin_amdgcn_global_load_lds(
-              src[k] + off,
-              (__attribute__((address_space(3))) void*)(&vst[slot][dst[k] + piece * 1024]), 16, 0, 0);
-      }
-  };
-  auto dequant = [&](int tile, int slot, auto maskc) {
-    constexpr bool kMask = decltype(maskc)::value;
-    const uint8_t* vb = vst[slot];
-    const uint16_t* vm_s = reinterpret_cast<const uint16_t*>(vb + kVCodeMax);
-    const uint16_t* vm_z = reinterpret_cast<const uint16_t*>(vb + kVCodeMax + kVMetaMax);
-    const int tok_base = tile * kTile;
-    for (int r = tid; r < 2 * cols; r += 512) {
-      const int gl = r >> 6, e = r & 63;          // group in the half; (half, channel)
-      const int gi = g_first + gl;
-      const int jj = e >> 5, c = e & 31;
-      const bool four = gi < NH;                  // uniform per wave
-      const uint8_t* gp = vb + goff(gi) - code_lo;
-      u32x4 w;
-      if (four) {
-        w = *reinterpret_cast<const u32x4*>(gp + e * 16);
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) acc[rt][gp] = f32x16{};
+
+  auto run = [&](auto fourc) {
+    constexpr bool kFour = decltype(fourc)::value;
+    // the lane's runs (channel m, token half j) of its two groups
+    auto load_codes = [&](int tile, u32x4 (&dst)[2]) {
+      const uint8_t* base = a.value + ((size_t)b * d.NT + tile) * vtile_bytes;
+      if constexpr (kFour) {
+        dst[0] = *reinterpret_cast<const u32x4*>(base + coff0 + lane * 16);
+        dst[1] = *reinterpret_cast<const u32x4*>(base + coff1 + lane * 16);
       } else {
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>(gp + e * 12);
-        w = u32x4{pw[0], pw[1], pw[2], 0u};
+        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(base + coff0 + lane * 12);
+        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(base + coff1 + lane * 12);
+        dst[0] = u32x4{p0[0], p0[1], p0[2], 0u};
+        dst[1] = u32x4{p1[0], p1[1], p1[2], 0u};
       }
-      const u32x4* sp = reinterpret_cast<const u32x4*>(vm_s + gl * kTile + 32 * jj);
-      const u32x4* zp = reinterpret_cast<const u32x4*>(vm_z + gl * kTile + 32 * jj);
-      const int ch = gl * 32 + c;                 // column within the half
-      uint8_t* row = zt + (size_t)ch * kZRow;
-      const int t0 = tok_base + 32 * jj;
+    };
+    auto contract = [&](int slot, int it, int tile, const u32x4 (&cw)[2], auto maskc) {
+      constexpr bool kMask = decltype(maskc)::value;
+      if (__builtin_amdgcn_readfirstlane(flag_l[slot]) == it) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const u32x4 S = sp[r4], Z = zp[r4];
-        uint32_t o[4];
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int p = 4 * r4 + q;
-          const uint32_t code = four ? run_pair<true>(w, p) : run_pair<false>(w, p);
-          // codes as exact fp16 integers: (1024 + k) - 1024
-          const h2 kv = __builtin_bit_cast(h2, code | 0x64006400u) - h2{1024.0f16, 1024.0f16};
-          // element picks go through scalars: a bit-cast applied directly
-          // to an ext_vector element is lowered as a cast of element 0
-          const uint32_t sbits = S[q], zbits = Z[q];
-          h2 v = __builtin_elementwise_fma(kv, __builtin_bit_cast(h2, sbits),
-                                           __builtin_bit_cast(h2, zbits));
-          if constexpr (kMask) {
-            const int tk = t0 + 2 * p;
-            if (tk > pmax) v[0] = (_Float16)0.0f;
-            if (tk + 1 > pmax) v[1] = (_Float16)0.0f;
+          for (int k4 = 0; k4 < 4; ++k4) {
+            // rows acc_row(4 k4 + e, lane) = 8 k4 + 4 j + e
+            const f32x4v al = *reinterpret_cast<const f32x4v*>(&alpha_l[slot][rt * 32 + k4 * 8 + j * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[rt][0][4 * k4 + e] *= al[e];
+              acc[rt][1][4 * k4 + e] *= al[e];
+            }
           }
-          o[q] = __builtin_bit_cast(uint32_t, v);
-        }
-        const int chunk = (4 * jj + r4) ^ (ch & 7);
-        *reinterpret_cast<u32x4*>(row + chunk * 16) = u32x4{o[0], o[1], o[2], o[3]};
       }
+      // P row rt * 32 + m, tokens 32 j + 8 r: chunk (4 j + r) ^ rt = 4 j + (r ^ rt)
+      const _Float16* pa = &p_l[slot][m * kPS + 32 * j];
+      const uint8_t* ms = meta_l[slot] + (2 * wave) * (kTile * 2) + 64 * j;
+      const int tok0 = tile * kTile + 32 * j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        h8 A[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          A[rt] = *reinterpret_cast<const h8*>(pa + rt * 32 * kPS + (r ^ rt) * 8);
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int mo = gp * (kTile * 2) + 16 * r;
+          const u32x4 S = *reinterpret_cast<const u32x4*>(ms + mo);
+          const u32x4 Z = *reinterpret_cast<const u32x4*>(ms + kMetaHalf + mo);
+          const h8 Bf = value_frag<kFour, kMask>(cw[gp], r, S, Z, tok0 + 8 * r, pmax);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+            acc[rt][gp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[rt], Bf, acc[rt][gp], 0, 0, 0);
+        }
+        // one k-step's operands live at a time (register budget)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    h8 kk[4];
+    stage_meta(0, 0);
+    load_keys(0, kk);
+    score(0, 0, 0, kk);
+    wait_vmcnt0();
+    __syncthreads();        // P, alpha and the scales of tile 0 in LDS
+    // One tile: contract tile `tile` and score tile + 1.  Codes and keys are
+    // loaded by the step that uses them (no registers held across the
+    // contraction); the other wave of the SIMD runs meanwhile.  Only the
+    // workgroup's last tile can hold tokens past its last position, so only
+    // it takes the masked value operands.
+    auto step = [&](int tile, auto firstc, auto lastc) {
+      constexpr bool kScoreFirst = decltype(firstc)::value;
+      constexpr bool kLast = decltype(lastc)::value;
+      const int it = tile, cur = it & 1, nxt = cur ^ 1;
+      u32x4 cw[2];
+      if constexpr (!kLast) stage_meta(tile + 1, nxt);
+      if (active) load_codes(tile, cw);
+      if constexpr (kScoreFirst) {
+        if constexpr (!kLast) {
+          load_keys(tile + 1, kk);
+          score(tile + 1, it + 1, nxt, kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) contract(cur, it, tile, cw, lastc);
+      } else {
+        if (active) contract(cur, it, tile, cw, lastc);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!kLast) {
+          load_keys(tile + 1, kk);
+          score(tile + 1, it + 1, nxt, kk);
+        }
+      }
+      if constexpr (!kLast) {
+        wait_vmcnt0();      // this wave's staging of tile + 1 landed
+        __syncthreads();    // P slot `cur` free; tile + 1 staged and scored
+      }
+    };
+    if (wave < 4) {
+      for (int tile = 0; tile < tile_last; ++tile) step(tile, std::true_type{}, std::false_type{});
+      step(tile_last, std::true_type{}, std::true_type{});
+    } else {
+      for (int tile = 0; tile < tile_last; ++tile) step(tile, std::false_type{}, std::false_type{});
+      step(tile_last, std::false_type{}, std::true_type{});
     }
   };
-
-  // -------------------------------------------------------------- contract
-  // Wave w: row tiles rt0 = 2 (w & 1) and rt0 + 1, value column tiles
-  // (w >> 1) * NCT .. + NCT - 1 of this half; each value fragment read from
-  // LDS feeds two MFMAs and each P fragment NCT.
-  const int rt0 = 2 * (wave & 1);
-  const int ct0 = (wave >> 1) * NCT;
-  f32x16 acc[2][NCT];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int i = 0; i < NCT; ++i) acc[rt][i] = f32x16{};
-
-  auto contract = [&](int slot, int it) {
-    if (flag_l[slot] == it) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float al = alpha_l[slot][(rt0 + rt) * 32 + acc_row(v, lane)];
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) acc[rt][ct][v] *= al;
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const h8 A0 = *reinterpret_cast<const h8*>(p_at(slot, rt0 * 32 + m, 32 * j + 8 * r));
-      const h8 A1 = *reinterpret_cast<const h8*>(p_at(slot, (rt0 + 1) * 32 + m, 32 * j + 8 * r));
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const uint8_t* row = zt + (size_t)((ct0 + ct) * 32 + m) * kZRow;
-        const h8 Bv = *reinterpret_cast<const h8*>(row + (((4 * j + r) ^ (m & 7)) * 16));
-        acc[0][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, Bv, acc[0][ct], 0, 0, 0);
-        acc[1][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1, Bv, acc[1][ct], 0, 0, 0);
-      }
-    }
-  };
-
-  stage(0, 0);
-  score(0, 0, 0);
-  wait_vmcnt0();
-  __syncthreads();          // packed values of tile 0 in LDS
-  for (int tile = 0, it = 0; tile <= tile_last; ++tile, ++it) {
-    // packed values of the next tile stream in while this one is processed
-    if (tile < tile_last) stage(tile + 1, (it + 1) & 1);
-    // only the workgroup's last tile can hold tokens past its last position
-    if (tile * kTile + kTile - 1 > pmax) dequant(tile, it & 1, std::true_type{});
-    else dequant(tile, it & 1, std::false_type{});
-    lds_barrier();          // value tile and P of this tile visible
-    if (tile < tile_last) score(tile + 1, it + 1, (it + 1) & 1);
-    // keep the scoring and the contraction apart (register pressure); the
-    // other wave of the SIMD overlaps them
-    __builtin_amdgcn_sched_barrier(0);
-    contract(it & 1, it);
-    wait_vmcnt0();          // this wave's pieces of the next tile have landed
-    lds_barrier();          // value tile and this P slot free; next tile staged
-  }
+  if (four) run(std::true_type{});
+  else run(std::false_type{});
 
   // ---------------------------------------------------------------- output
+  if (active) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
+      for (int gp = 0; gp < 2; ++gp)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = (rt0 + rt) * 32 + acc_row(v, lane);
-        const int qi = rr >> 3, hh = rr & 7;
-        if (qi < nq)
-          a.part_o[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + hh) * d.rv +
-                   col0 + (ct0 + ct) * 32 + m] = acc[rt][ct][v];
-      }
-    }
-  if (cs == 0) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float l = l_lane[v];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o);
-      const int q = g16 * 4 + v;
-      if (c16 == 0 && q < nq) {
-        const size_t o = (((size_t)b * a.chunk + q0 + q) * d.Hq + h) * 2;
-        a.part_ml[o] = m_ref[v];
-        a.part_ml[o + 1] = l;
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int rr = rt * 32 + acc_row(v, lane);
+          const int qi = rr >> 3, hh = rr & 7;
+          if (qi < nq)
+            a.part_o[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + hh) * d.rv +
+                     col0 + (2 * wave + gp) * 32 + m] = acc[rt][gp][v];
+        }
+  }
+  if (cb == 0) {
+    float l = l_lane + __shfl_xor(l_lane, 16);
+    l += __shfl_xor(l, 32);
+    if (lane < kPQ && c16 < nq) {
+      const size_t o = (((size_t)b * a.chunk + q0 + c16) * d.Hq + h) * 2;
+      a.part_ml[o] = m_ref;
+      a.part_ml[o + 1] = l;
     }
   }
-}
-
-template <int G>
-hipError_t launch_attn_g(int nct, dim3 grid, const AttnArgs& aa, hipStream_t s) {
-  switch (nct) {
-    case 1: prefill_attn_kernel<G, 1><<<grid, 512, 0, s>>>(aa); break;
-    case 2: prefill_attn_kernel<G, 2><<<grid, 512, 0, s>>>(aa); break;
-    case 3: prefill_attn_kernel<G, 3><<<grid, 512, 0, s>>>(aa); break;
-    case 4: prefill_attn_kernel<G, 4><<<grid, 512, 0, s>>>(aa); break;
-    default: return hipErrorNotSupported;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_attn(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t s) {
-  const int nct = d.rv / 256;
   switch (d.G) {
-    case 1: return launch_attn_g<1>(nct, grid, aa, s);
-    case 2: return launch_attn_g<2>(nct, grid, aa, s);
-    case 4: return launch_attn_g<4>(nct, grid, aa, s);
-    case 8: return launch_attn_g<8>(nct, grid, aa, s);
+    case 1: prefill_attn_kernel<1><<<grid, 512, 0, s>>>(aa); break;
+    case 2: prefill_attn_kernel<2><<<grid, 512, 0, s>>>(aa); break;
+    case 4: prefill_attn_kernel<4><<<grid, 512, 0, s>>>(aa); break;
+    case 8: prefill_attn_kernel<8><<<grid, 512, 0, s>>>(aa); break;
     default: return hipErrorNotSupported;
   }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -646,15 +657,14 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   aa.n_qb = (chunk + kPQ - 1) / kPQ;
   aa.n_qb_pad = (aa.n_qb + 7) / 8 * 8;
   aa.n_hg = d.Hq / kPH;
-  aa.key = static_cast<const uint8_t*>(cache.key);
-  aa.kmeta = static_cast<const u32x2*>(cache.key_meta);
+  aa.n_cb = d.rv > kMaxCols ? 2 : 1;
   aa.value = static_cast<const uint8_t*>(cache.value);
   aa.vmeta = static_cast<const uint16_t*>(cache.value_meta);
   aa.qt = static_cast<const uint32_t*>(qt);
   aa.kd = kd;
   aa.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   aa.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
-  e = launch_attn(d, dim3(aa.n_qb_pad * aa.n_hg * 2, d.B), aa, s);
+  e = launch_attn(d, dim3(aa.n_qb_pad * aa.n_hg * aa.n_cb, d.B), aa, s);
   if (e != hipSuccess) return e;
   mark(4);
 
