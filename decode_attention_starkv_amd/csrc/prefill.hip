@@ -126,7 +126,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     }
 }
 
-__device__ inline void wait_vmcnt0() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // ------------------------------------------------------------- key dequant --
 
@@ -191,6 +197,12 @@ constexpr int kMaxRv = 1024;
 constexpr int kMaxCols = 512;      // value columns per workgroup (at most)
 // bytes of one tile's value scales (or zeros) over the workgroup's groups
 constexpr int kMetaHalf = (kMaxCols / 32) * kTile * 2;
+// bytes of one tile's value codes over the workgroup's groups (at most
+// eight 4-bit and eight 3-bit groups: the 4-bit groups are the first R_v/4
+// channels, so no block of 512 columns holds more)
+constexpr int kCodeSlot = 8 * 1024 + 8 * 768;
+// bytes of one tile's fp16 key latents of the workgroup's KV heads
+constexpr int kKeySlot = kPH * kTile * 64;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -206,19 +218,38 @@ struct AttnArgs {
   float* part_ml;         // [B*C][Hq][2]
 };
 
+// Mask and bias registers of the value unpacking: kept in VGPRs (opaque to
+// the compiler) so that mask-and-bias is one v_and_or_b32.
+struct UnpackRegs {
+  uint32_t m4, m3, bias;
+};
+
+// Codes of token pair p of a value run as the fp16 bit patterns of 1024 + k
+// in both halves (see run_pair for the run layout).
+template <bool kFour>
+__device__ inline uint32_t biased_pair(const u32x4& w, int p, const UnpackRegs& u) {
+  if constexpr (kFour) {
+    return ((w[p >> 2] >> (4 * (p & 3))) & u.m4) | u.bias;
+  } else {
+    if (p < 15) return ((w[p / 5] >> (3 * (p % 5))) & u.m3) | u.bias;
+    return ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
+           ((w[2] >> 13) & 0x00040004u) | u.bias;
+  }
+}
+
 // One MFMA 32x32x16 B operand of value group run `w` (the lane's channel and
 // 32-token half): tokens 8r .. 8r + 7 of the run as z + s * code, one packed
 // fp16 FMA per token pair.  S, Z: the scales and zeros of those 8 tokens.
 // kMask zeroes tokens past `pmax` (tok: the run's token 8r).
 template <bool kFour, bool kMask>
 __device__ inline h8 value_frag(const u32x4& w, int r, const u32x4& S, const u32x4& Z,
-                                int tok, int pmax) {
+                                int tok, int pmax, const UnpackRegs& u) {
   uint32_t o[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t code = run_pair<kFour>(w, 4 * r + q);
     // codes as exact fp16 integers: (1024 + k) - 1024
-    const h2 kv = __builtin_bit_cast(h2, code | 0x64006400u) - h2{1024.0f16, 1024.0f16};
+    const h2 kv = __builtin_bit_cast(h2, biased_pair<kFour>(w, 4 * r + q, u)) -
+                  h2{1024.0f16, 1024.0f16};
     // element picks go through scalars: a bit-cast applied directly to an
     // ext_vector element is lowered as a cast of element 0
     const uint32_t sb = S[q], zb = Z[q];
@@ -240,14 +271,13 @@ __device__ inline h8 value_frag(const u32x4& w, int r, const u32x4& S, const u32
 //     query) and a lazy online softmax, writing fp16 probabilities to a P
 //     slot;
 //   - owns value groups 2w and 2w + 1 of the workgroup's columns for all
-//     128 rows: it dequantizes their codes (read from global memory) with
-//     the scales and zeros staged in LDS straight into MFMA B operands and
-//     contracts them with P on MFMA 32x32x16.  MFMA r of a tile takes, in
-//     k-slot j, tokens 32j + 8r .. 32j + 8r + 7: word r of the lane's run.
-// One barrier per 64-token tile: P, alpha and the staged scales and zeros
-// are double-buffered.  Waves 0-3 score tile t+1 and then contract tile t;
-// waves 4-7 (the other wave on each SIMD) contract first, so that one
-// wave's VALU work meets the other's matrix work.
+//     128 rows: it dequantizes their codes with their scales and zeros
+//     straight into MFMA B operands and contracts them with P on MFMA
+//     32x32x16.  MFMA r of a tile takes, in k-slot j, tokens 32j + 8r ..
+//     32j + 8r + 7: word r of the lane's run.
+// Keys, codes, scales and zeros reach LDS by direct-to-LDS loads issued a
+// step ahead (keys two tiles ahead); P, alpha and every staging buffer are
+// double-buffered, so a tile needs one barrier.
 // The column blocks compute the same scores; the first writes (m, l).
 // Causal mask: query i (absolute position ctx + i) sees cached positions
 // 0 .. ctx + i.  Value tokens past the workgroup's last position are zeroed
@@ -257,6 +287,11 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const Dims& d = a.d;
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kRows * kPS];
   __shared__ __attribute__((aligned(16))) uint8_t meta_l[2][2 * kMetaHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t code_l[2][kCodeSlot];
+  // key latents [KV head][token][4 chunks of 16 B], chunk c of token u at
+  // position c ^ ((u >> 2) & 3) so that a score operand read (16 tokens,
+  // one chunk) touches every bank once
+  __shared__ __attribute__((aligned(16))) uint8_t key_l[2][kKeySlot];
   // the queries' latent vectors in natural channel order (fp16)
   __shared__ __attribute__((aligned(16))) _Float16 qnat[kRows * 32];
   __shared__ __attribute__((aligned(16))) float alpha_l[2][kRows];
@@ -323,13 +358,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
     return &p_l[slot][R * kPS + (((u >> 3) ^ (R >> 5)) << 3) + (u & 7)];
   };
   // A operands of the score MFMA: tokens bl * 16 + c16 of a tile, channels
-  // 8 g16 .. 8 g16 + 7 of KV head g
-  const _Float16* kbase = a.kd + ((size_t)b * d.Tmax * d.Hkv + g) * 32 + g16 * 8;
-  auto load_keys = [&](int tile, h8 (&kk)[4]) {
+  // 8 g16 .. 8 g16 + 7 of KV head g (local head g - g0)
+  const int g0 = hg * kPH / G;
+  const int key_lane = (g - g0) * (kTile * 64) + c16 * 64 + ((g16 ^ (c16 >> 2)) << 4);
+  auto load_keys = [&](int slot, h8 (&kk)[4]) {
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl)
-      kk[bl] = *reinterpret_cast<const h8*>(
-          kbase + (size_t)(tile * kTile + bl * 16 + c16) * d.Hkv * 32);
+      kk[bl] = *reinterpret_cast<const h8*>(&key_l[slot][key_lane + bl * 16 * 64]);
   };
 
   // scores of tile `tile` (index it in the loop) into P slot `slot`
@@ -389,27 +424,52 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const size_t vtile_bytes = (size_t)26 * d.rv;
   const size_t mtile = (size_t)2 * NG * kTile;     // fp16 elements
   const int meta_bytes = ngrp * kTile * 2;
-  // direct-to-LDS copy of one tile's scales and zeros of the workgroup's
-  // groups into slot `slot`; waves 0-3 move one 1 KB piece each
-  auto stage_meta = [&](int tile, int slot) {
-    if (wave < 4) {
-      const int part = wave >> 1, piece = wave & 1;   // part 0 scales, 1 zeros
-      const int off = piece * 1024 + lane * 16;
-      if (off < meta_bytes) {
-        const uint16_t* mt = a.vmeta + ((size_t)b * d.NT + tile) * mtile +
-                             (size_t)(part * NG + g_first) * kTile;
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const uint8_t*>(mt) + off,
-            (__attribute__((address_space(3))) void*)(&meta_l[slot][part * kMetaHalf + piece * 1024]),
-            16, 0, 0);
+  // Direct-to-LDS staging, in 1 KB pieces spread over the waves: the fp16
+  // keys of tile `kt` into key slot kt & 1 (4 pieces per KV head) and the
+  // value codes, scales and zeros of tile `ct` into slot ct & 1.  A key
+  // piece is 16 tokens of one head; lane l moves chunk
+  // (l & 3) ^ ((l >> 4) & 3) of token l >> 2 (the swizzle of key_l).
+  auto goff = [&](int gi) { return gi < NH ? gi * 1024 : NH * 1024 + (gi - NH) * 768; };
+  const int code_lo = goff(g_first), code_bytes = goff(g_first + ngrp) - code_lo;
+  const int nkp = 4 * (kPH / G);               // key pieces
+  const int ncp = (code_bytes + 1023) / 1024;  // code pieces
+  const int nmp = (meta_bytes + 1023) / 1024;  // pieces per scale / zero plane
+  const int key_src_lane = (lane >> 2) * d.Hkv * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  auto dma = [&](const uint8_t* src, uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  auto stage = [&](int kt, int ct) {
+    const int p_key = kt <= tile_last ? nkp : 0;
+    const int p_val = ct <= tile_last ? ncp + 2 * nmp : 0;
+    for (int p = wave; p < p_key + p_val; p += 8) {
+      if (p < p_key) {
+        const int kh = p >> 2, blk = p & 3;
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kd) +
+            (((size_t)b * d.Tmax + kt * kTile + blk * 16) * d.Hkv + g0 + kh) * 64 + key_src_lane;
+        dma(src, &key_l[kt & 1][kh * (kTile * 64) + blk * 1024]);
+      } else if (p < p_key + ncp) {
+        const int q = p - p_key;
+        const int off = q * 1024 + lane * 16;
+        if (off < code_bytes)
+          dma(a.value + ((size_t)b * d.NT + ct) * vtile_bytes + code_lo + off,
+              &code_l[ct & 1][q * 1024]);
+      } else {
+        const int q = p - p_key - ncp;
+        const int part = q / nmp, piece = q - part * nmp;   // part 0 scales, 1 zeros
+        const int off = piece * 1024 + lane * 16;
+        if (off < meta_bytes) {
+          const uint16_t* mt = a.vmeta + ((size_t)b * d.NT + ct) * mtile +
+                               (size_t)(part * NG + g_first) * kTile;
+          dma(reinterpret_cast<const uint8_t*>(mt) + off,
+              &meta_l[ct & 1][part * kMetaHalf + piece * 1024]);
+        }
       }
     }
   };
   const int gw = g_first + 2 * wave;          // the wave's first value group
   const bool active = 2 * wave < ngrp;        // uniform
   const bool four = gw < NH;                  // both groups: NH is even
-  auto goff = [&](int gi) { return gi < NH ? gi * 1024 : NH * 1024 + (gi - NH) * 768; };
-  const int coff0 = goff(gw), coff1 = goff(gw + 1);
+  const int coff0 = goff(gw) - code_lo, coff1 = goff(gw + 1) - code_lo;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -417,11 +477,14 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) acc[rt][gp] = f32x16{};
 
+  UnpackRegs ur{0x000F000Fu, 0x00070007u, 0x64006400u};
+  __asm__ volatile("" : "+v"(ur.m4), "+v"(ur.m3), "+v"(ur.bias));
+
   auto run = [&](auto fourc) {
     constexpr bool kFour = decltype(fourc)::value;
     // the lane's runs (channel m, token half j) of its two groups
-    auto load_codes = [&](int tile, u32x4 (&dst)[2]) {
-      const uint8_t* base = a.value + ((size_t)b * d.NT + tile) * vtile_bytes;
+    auto load_codes = [&](int slot, u32x4 (&dst)[2]) {
+      const uint8_t* base = code_l[slot];
       if constexpr (kFour) {
         dst[0] = *reinterpret_cast<const u32x4*>(base + coff0 + lane * 16);
         dst[1] = *reinterpret_cast<const u32x4*>(base + coff1 + lane * 16);
@@ -432,8 +495,10 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
         dst[1] = u32x4{p1[0], p1[1], p1[2], 0u};
       }
     };
-    auto contract = [&](int slot, int it, int tile, const u32x4 (&cw)[2], auto maskc) {
+    auto contract = [&](int slot, int it, int tile, auto maskc) {
       constexpr bool kMask = decltype(maskc)::value;
+      u32x4 cw[2];
+      load_codes(slot, cw);
       if (__builtin_amdgcn_readfirstlane(flag_l[slot]) == it) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -463,61 +528,43 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
           const int mo = gp * (kTile * 2) + 16 * r;
           const u32x4 S = *reinterpret_cast<const u32x4*>(ms + mo);
           const u32x4 Z = *reinterpret_cast<const u32x4*>(ms + kMetaHalf + mo);
-          const h8 Bf = value_frag<kFour, kMask>(cw[gp], r, S, Z, tok0 + 8 * r, pmax);
+          const h8 Bf = value_frag<kFour, kMask>(cw[gp], r, S, Z, tok0 + 8 * r, pmax, ur);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
             acc[rt][gp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[rt], Bf, acc[rt][gp], 0, 0, 0);
         }
-        // one k-step's operands live at a time (register budget)
-        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    h8 kk[4];
-    stage_meta(0, 0);
-    load_keys(0, kk);
-    score(0, 0, 0, kk);
-    wait_vmcnt0();
-    __syncthreads();        // P, alpha and the scales of tile 0 in LDS
-    // One tile: contract tile `tile` and score tile + 1.  Codes and keys are
-    // loaded by the step that uses them (no registers held across the
-    // contraction); the other wave of the SIMD runs meanwhile.  Only the
-    // workgroup's last tile can hold tokens past its last position, so only
-    // it takes the masked value operands.
-    auto step = [&](int tile, auto firstc, auto lastc) {
-      constexpr bool kScoreFirst = decltype(firstc)::value;
+    // staging runs two tiles ahead for keys, one for values
+    stage(0, 0);
+    stage(1, tile_last + 1);
+    wait_vmcnt<0>();
+    __syncthreads();        // keys of tiles 0, 1 and values of tile 0 in LDS
+    {
+      h8 kk[4];
+      load_keys(0, kk);
+      score(0, 0, 0, kk);
+    }
+    // One tile: contract tile `tile`, then score tile + 1, with the next
+    // stage in flight.  Only the workgroup's last tile can hold tokens past
+    // its last position, so only it takes the masked value operands.
+    auto step = [&](int tile, auto lastc) {
       constexpr bool kLast = decltype(lastc)::value;
       const int it = tile, cur = it & 1, nxt = cur ^ 1;
-      u32x4 cw[2];
-      if constexpr (!kLast) stage_meta(tile + 1, nxt);
-      if (active) load_codes(tile, cw);
-      if constexpr (kScoreFirst) {
-        if constexpr (!kLast) {
-          load_keys(tile + 1, kk);
-          score(tile + 1, it + 1, nxt, kk);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (active) contract(cur, it, tile, cw, lastc);
-      } else {
-        if (active) contract(cur, it, tile, cw, lastc);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!kLast) {
-          load_keys(tile + 1, kk);
-          score(tile + 1, it + 1, nxt, kk);
-        }
-      }
+      lds_barrier();        // P of `tile`, staging of the previous step visible
+      if constexpr (!kLast) stage(tile + 2, tile + 1);
+      if (active) contract(cur, it, tile, lastc);
       if constexpr (!kLast) {
-        wait_vmcnt0();      // this wave's staging of tile + 1 landed
-        __syncthreads();    // P slot `cur` free; tile + 1 staged and scored
+        __builtin_amdgcn_sched_barrier(0);
+        h8 kk[4];
+        load_keys(nxt, kk);
+        score(tile + 1, it + 1, nxt, kk);
+        wait_vmcnt<0>();    // this wave's staging landed
       }
     };
-    if (wave < 4) {
-      for (int tile = 0; tile < tile_last; ++tile) step(tile, std::true_type{}, std::false_type{});
-      step(tile_last, std::true_type{}, std::true_type{});
-    } else {
-      for (int tile = 0; tile < tile_last; ++tile) step(tile, std::false_type{}, std::false_type{});
-      step(tile_last, std::false_type{}, std::true_type{});
-    }
+    for (int tile = 0; tile < tile_last; ++tile) step(tile, std::false_type{});
+    step(tile_last, std::true_type{});
   };
   if (four) run(std::true_type{});
   else run(std::false_type{});
