@@ -49,14 +49,11 @@ struct SplitArgs {
 // One workgroup per (b, h): q is staged in LDS, 256 threads split the d_h
 // contraction into chunks, the chunks are summed, then wave 0 rotates,
 // scales and packs the record.
-// Q43 records come in two layouts:
-//   kFieldRec (decode scores): the 17 fp16 pairs that meet the in-place code
-//     fields of the key words (each entry times 2^-p for a field at bit p;
-//     channel 31 split over three one-bit fields), then sum(q_hi) 2^-24 and
-//     sum(q_lo) 2^-24 as fp32;
-//   otherwise: 16 channel pairs in the order of the key words (prefill puts
-//     them back in channel order), then sum(q_hi), sum(q_lo).
-template <int FMT, bool kFieldRec>
+// A Q43 record holds the 17 fp16 pairs that meet the in-place code fields of
+// the key words (each entry times 2^-p for a field at bit p; channel 31
+// split over three one-bit fields), then sum(q_hi) 2^-24 and
+// sum(q_lo) 2^-24 as fp32.
+template <int FMT>
 __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
                                                     const void* __restrict__ bk,
                                                     Dims d, float qscale,
@@ -114,54 +111,40 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   uint32_t* rec = static_cast<uint32_t*>(qt) + (size_t)bh * kQ43Rec;
-  float qsum_scale = 1.0f;
-  if constexpr (kFieldRec) {
-    qsum_scale = 1.0f / kTwo24;
-    if (t < 17) {
-      int a, cc;        // channels of the low and the high half
-      float sa, sc;     // their field weights (2^-bit position, or the bit's weight)
-      if (t < 4) {
-        // channels 0-3 / 4-7; odd pairs sit at bit 4 of their byte
-        a = t;
-        cc = t + 4;
-        sa = sc = (t & 1) ? 1.0f / 16.0f : 1.0f;
-      } else if (t < 14) {
-        const int i = (t - 4) / 5, f = (t - 4) % 5;
-        a = 8 + 5 * i + f;
-        cc = 18 + 5 * i + f;
-        sa = sc = f == 1 || f == 4 ? 1.0f / 8.0f : f == 2 ? 1.0f / 64.0f : 1.0f;
-      } else if (t == 14) {
-        a = 28; cc = 29; sa = 1.0f; sc = 1.0f / 8.0f;
-      } else if (t == 15) {
-        a = 30; cc = 31; sa = 1.0f / 64.0f; sc = 1.0f / 256.0f;
-      } else {
-        a = 31; cc = 31; sa = 2.0f; sc = 4.0f;
-      }
-      const _Float16 lo = (_Float16)((float)sq[a] * sa);
-      const _Float16 hi = (_Float16)((float)sq[cc] * sc);
-      rec[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  const float qsum_scale = 1.0f / kTwo24;
+  if (t < 17) {
+    int a, cc;        // channels of the low and the high half
+    float sa, sc;     // their field weights (2^-bit position, or the bit's weight)
+    if (t < 4) {
+      // channels 0-3 / 4-7; odd pairs sit at bit 4 of their byte
+      a = t;
+      cc = t + 4;
+      sa = sc = (t & 1) ? 1.0f / 16.0f : 1.0f;
+    } else if (t < 14) {
+      const int i = (t - 4) / 5, f = (t - 4) % 5;
+      a = 8 + 5 * i + f;
+      cc = 18 + 5 * i + f;
+      sa = sc = f == 1 || f == 4 ? 1.0f / 8.0f : f == 2 ? 1.0f / 64.0f : 1.0f;
+    } else if (t == 14) {
+      a = 28; cc = 29; sa = 1.0f; sc = 1.0f / 8.0f;
+    } else if (t == 15) {
+      a = 30; cc = 31; sa = 1.0f / 64.0f; sc = 1.0f / 256.0f;
+    } else {
+      a = 31; cc = 31; sa = 2.0f; sc = 4.0f;
     }
-  } else if (t < 16) {
-    int a, cc;  // channel pair (a -> low half, cc -> high half)
-    if (t < 4) { a = t; cc = t + 4; }
-    else if (t < 9) { a = 8 + (t - 4); cc = 8 + 10 + (t - 4); }
-    else if (t < 14) { a = 8 + 5 + (t - 9); cc = 8 + 15 + (t - 9); }
-    else if (t == 14) { a = 8 + 20; cc = 8 + 22; }
-    else { a = 8 + 21; cc = 8 + 23; }
-    const uint32_t lo = __builtin_bit_cast(uint16_t, sq[a]);
-    const uint32_t hi = __builtin_bit_cast(uint16_t, sq[cc]);
-    rec[t] = lo | (hi << 16);
+    const _Float16 lo = (_Float16)((float)sq[a] * sa);
+    const _Float16 hi = (_Float16)((float)sq[cc] * sc);
+    rec[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
-  const int qs_at = kFieldRec ? 17 : 16;
   if (t == 32) {
     float s = 0.0f;
     for (int k = 0; k < 8; ++k) s += (float)sq[k];
-    rec[qs_at] = __builtin_bit_cast(uint32_t, s * qsum_scale);
+    rec[17] = __builtin_bit_cast(uint32_t, s * qsum_scale);
   } else if (t == 33) {
     float s = 0.0f;
     for (int k = 8; k < 32; ++k) s += (float)sq[k];
-    rec[qs_at + 1] = __builtin_bit_cast(uint32_t, s * qsum_scale);
+    rec[18] = __builtin_bit_cast(uint32_t, s * qsum_scale);
   }
 }
 
@@ -1176,7 +1159,7 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   float* obar = reinterpret_cast<float*>(ws + lay.obar);
   auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], s); };
   mark(0);
-  qproj_kernel<FMT, true><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
+  qproj_kernel<FMT><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(1);
@@ -1253,23 +1236,6 @@ DecodeWs decode_ws_layout(const Dims& d, int splits) {
   off += align256((size_t)d.B * d.Hq * d.rv * 4);
   w.total = off;
   return w;
-}
-
-hipError_t launch_qproj_q43(const Dims& d, const void* q, const void* bk,
-                           float sm_scale, void* qt, hipStream_t s) {
-  qproj_kernel<STARKV_CACHE_Q43, false><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge_vproj_q43(const Dims& d, const float* part_o,
-                                  const float* part_ml, int splits, const void* bv,
-                                  float* obar, float* out, hipStream_t s) {
-  merge_kernel<float><<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, splits, obar);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  vproj_kernel<STARKV_CACHE_Q43><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64 * kVprojWaves, 0, s>>>(
-      obar, bv, d, out);
-  return hipGetLastError();
 }
 
 hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,

@@ -57,17 +57,9 @@ hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,
                          const DecodeWs& lay, hipStream_t s,
                          hipEvent_t* events = nullptr);
 
-// Launchers of decode kernels reused by the prefill path (Q43 caches; d.B
-// may count the chunk's queries as independent rows).
-hipError_t launch_qproj_q43(const Dims& d, const void* q, const void* bk,
-                           float sm_scale, void* qt, hipStream_t s);
-hipError_t launch_merge_vproj_q43(const Dims& d, const float* part_o,
-                                  const float* part_ml, int splits, const void* bv,
-                                  float* obar, float* out, hipStream_t s);
-
 // Workspace carve-up of one prefill call (byte offsets, 256-aligned).
 struct PrefillWs {
-  size_t zk, zv, qt, kd, part_o, part_ml, obar, total;
+  size_t zk, zv, qt, kd, part_o, part_ml, bvr, total;
 };
 PrefillWs prefill_ws_layout(const Dims& d, int chunk);
 hipError_t launch_prefill(const Dims& d, const starkv_cache& cache,

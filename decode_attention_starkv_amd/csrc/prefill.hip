@@ -5,12 +5,13 @@
 //
 //   gemm      Z = X [A_key | A_value] (bf16 in, fp32 out) on MFMA 32x32x16
 //   append    the decode-path append kernels (rotation + 4/3-bit packing)
-//   qproj     q~ for every query of the chunk (the decode kernel, rows = B*C)
+//   qproj     q~ for every query of the chunk on MFMA (natural channel order)
 //   attn      per (16 queries, 8 query heads, up to 512 value columns):
 //             latent scores on MFMA with a lazy online softmax, then P Z_v
 //             on MFMA with each wave dequantizing its own value groups
 //             straight into MFMA operands (section 5.3, eq. 12)
-//   merge, vproj   the decode kernels with one split per query row
+//   vproj     the attention rows times the value factor rotated like the
+//             stored latents, on MFMA, divided by the softmax denominator
 #include <type_traits>
 
 #include "device.h"
@@ -187,6 +188,197 @@ __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restr
                 v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]};
 }
 
+// ------------------------------------------------------------------ qproj --
+
+// q~ = q B_k[g] of every (row, head) of the chunk (eq. 2), rotated by blocks
+// of 8 channels like the stored key latents (eq. 13) and scaled by
+// sm_scale log2(e), as fp16 in natural channel order: [rows][Hq][32].  One
+// workgroup per (128 rows, head): 4 waves of 32 rows on MFMA 32x32x16 bf16,
+// B_k[g] staged channel-major in LDS.
+__global__ __launch_bounds__(256) void prefill_qproj_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ bk,
+                                                            Dims d, int rows, float qscale,
+                                                            _Float16* __restrict__ qn) {
+  __shared__ __attribute__((aligned(16))) uint16_t bt[32 * (256 + 8)];
+  const int h = blockIdx.y, g = h / d.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 31, j = lane >> 5;
+  const int bs = d.dh + 8;    // row stride of bt: operand reads spread over the banks
+  for (int i = tid; i < d.dh * 32; i += 256) {
+    const int k = i >> 5, c = i & 31;
+    bt[c * bs + k] = bk[((size_t)g * d.dh + k) * 32 + c];
+  }
+  __syncthreads();
+  const int r0 = blockIdx.x * 128 + wave * 32;
+  const uint16_t* qrow = q + ((size_t)min(r0 + m, rows - 1) * d.Hq + h) * d.dh + 8 * j;
+  f32x16 acc = f32x16{};
+  for (int k0 = 0; k0 < d.dh; k0 += 16) {
+    const bf8 av = *reinterpret_cast<const bf8*>(qrow + k0);
+    const bf8 bv = *reinterpret_cast<const bf8*>(&bt[m * bs + k0 + 8 * j]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  }
+  // lane: channel m of rows acc_row(v, lane); the rotation pairs channels
+  // m and m ^ s (lanes m ^ s of the same half)
+  const float cst = (d.rotate ? inv_sqrt_pow2(8) : 1.0f) * qscale;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = acc[v];
+    if (d.rotate) {
+#pragma unroll
+      for (int st = 1; st < 8; st <<= 1) {
+        const float p = __shfl_xor(x, st);
+        x = (m & st) ? p - x : x + p;
+      }
+    }
+    const int r = r0 + acc_row(v, lane);
+    if (r < rows) qn[((size_t)r * d.Hq + h) * 32 + m] = (_Float16)(x * cst);
+  }
+}
+
+// ------------------------------------------------------------------ vproj --
+
+// Element (row, head h, channel 32 kb + 16 j + 8 s + 4 i + e) of the
+// attention rows, in the order the up-projection's MFMA A operands are read:
+// planes of `rows` x 32 bytes per (h, kb, s, i), so that an operand load of
+// 32 consecutive rows reads 1 KB of contiguous memory.
+__host__ __device__ inline size_t po_index(const Dims& d, size_t rows, int h, size_t row, int c) {
+  const int kb = c >> 5, j = (c >> 4) & 1, s = (c >> 3) & 1, i = (c >> 2) & 1, e = c & 3;
+  const size_t plane = (((size_t)h * (d.rv / 32) + kb) * 2 + s) * 2 + i;
+  return (plane * rows + row) * 8 + j * 4 + e;
+}
+
+// B_v' = B_v with every row put through the block rotation of the stored
+// value latents (blocks of mb = the largest power of two dividing R_v / 4,
+// scaled by 1/sqrt(mb); the rotation is symmetric), so that
+// (o' H) B_v^T = o' B_v'^T: the up-projection then takes the still rotated
+// attention rows.  Written as bf16 high and low parts in the order the
+// up-projection's MFMA B operands are read (bvr_index), so that every
+// operand load reads 1 KB of contiguous memory.  One workgroup per row of
+// B_v, 4 channels per thread; strides 1 and 2 inside the thread, strides
+// 4 .. mb/2 as lane shuffles (mb <= 256 = one wave).
+// Element (row g d_h + 32 ct + m, channel 32 kb + 16 j + 8 s + e) of part
+// p (0 high, 1 low) of B_v': blocks of 1 KB per (g, kb, p, ct, s), lane
+// (m, j) of a block owning 16 bytes.
+__host__ __device__ inline size_t bvr_index(const Dims& d, int g, int n, int c, int p) {
+  const int ct = n >> 5, m = n & 31;
+  const int kb = c >> 5, j = (c >> 4) & 1, s = (c >> 3) & 1, e = c & 7;
+  const size_t blk = ((((size_t)g * (d.rv / 32) + kb) * 2 + p) * (d.dh / 32) + ct) * 2 + s;
+  return blk * 512 + (m * 2 + j) * 8 + e;
+}
+
+__global__ __launch_bounds__(256) void prefill_rotate_bv_kernel(const uint16_t* __restrict__ bv,
+                                                                Dims d,
+                                                                uint16_t* __restrict__ bvr) {
+  const size_t row = blockIdx.x;
+  const int t = threadIdx.x, c = 4 * t;
+  const int cc = min(c, d.rv - 4);
+  const uint16_t* src = bv + row * d.rv + cc;
+  float o[4] = {bf16v(src[0]), bf16v(src[1]), bf16v(src[2]), bf16v(src[3])};
+  if (d.rotate) {
+    const int mb = pow2_divisor(d.rv / 4);
+    const float a0 = o[0] + o[1], a1 = o[0] - o[1], a2 = o[2] + o[3], a3 = o[2] - o[3];
+    o[0] = a0 + a2; o[1] = a1 + a3; o[2] = a0 - a2; o[3] = a1 - a3;
+    for (int hs = 4; hs < mb; hs <<= 1) {
+      const int dl = hs >> 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __shfl_xor(o[e], dl);
+        o[e] = (c & hs) ? p - o[e] : o[e] + p;
+      }
+    }
+    const float cst = inv_sqrt_pow2(mb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= cst;
+  }
+  if (c < d.rv) {
+    const int g = (int)(row / d.dh), n = (int)(row % d.dh);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const __bf16 hi = (__bf16)o[e];
+      const __bf16 lo = (__bf16)(o[e] - (float)hi);
+      bvr[bvr_index(d, g, n, c + e, 0)] = __builtin_bit_cast(uint16_t, hi);
+      bvr[bvr_index(d, g, n, c + e, 1)] = __builtin_bit_cast(uint16_t, lo);
+    }
+  }
+}
+
+// out[row][h][r] = (sum_c po[row, h, c] B_v'[g d_h + r][c]) / l[row][h]: the
+// attention rows (unnormalised, still rotated, in the order of po_index)
+// times the rotated factor, divided by the softmax denominator.  One workgroup per
+// (128 rows, head): 4 waves of 32 rows x d_h columns on MFMA 32x32x16 bf16
+// over K = R_v in steps of one channel block; lane (m, j) reads channels
+// 16 j .. 16 j + 15 of its row, MFMA s of a step takes channels 16 j + 8 s ..
+// in k-slot j.  The fp32 rows are split into bf16 high and low parts: three
+// products per step (low x low dropped).
+template <int NCT>
+__global__ __launch_bounds__(256) void prefill_vproj_kernel(const float* __restrict__ po,
+                                                            const float* __restrict__ pml,
+                                                            const uint16_t* __restrict__ bvr,
+                                                            Dims d, int rows,
+                                                            float* __restrict__ out) {
+  const int h = blockIdx.y, g = h / d.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 31, j = lane >> 5;
+  const int r0 = blockIdx.x * 128 + wave * 32;
+  // this lane's 16 bytes of every operand plane (kb, s, i) of head h
+  const float* arow = po + po_index(d, rows, h, min(r0 + m, rows - 1), 16 * j);
+  const size_t pstride = (size_t)rows * 8;    // floats from one plane to the next
+  // this lane's 16 bytes of every B_v' operand block of head group g
+  const uint16_t* bg = bvr + (size_t)g * (d.rv / 32) * 2 * NCT * 2 * 512 + (m * 2 + j) * 8;
+  f32x16 acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x16{};
+  for (int k0 = 0; k0 < d.rv; k0 += 32) {
+    f32x4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)   // plane (kb, s = i / 2, i % 2)
+      x[i] = *reinterpret_cast<const f32x4*>(arow + ((size_t)(k0 / 32) * 4 + i) * pstride);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bf8 ah, al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xv = x[2 * st + (e >> 2)][e & 3];
+        ah[e] = (__bf16)xv;
+        al[e] = (__bf16)(xv - (float)ah[e]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        // blocks (kb, p, ct, s) of bvr_index
+        const uint16_t* bo = bg + ((((size_t)(k0 / 32) * 2) * NCT + ct) * 2 + st) * 512;
+        const bf8 bh = *reinterpret_cast<const bf8*>(bo);
+        const bf8 bl = *reinterpret_cast<const bf8*>(bo + (size_t)NCT * 2 * 512);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[ct], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = r0 + acc_row(v, lane);
+    if (r >= rows) continue;
+    const float l = pml[((size_t)r * d.Hq + h) * 2 + 1];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      out[((size_t)r * d.Hq + h) * d.dh + ct * 32 + m] = acc[ct][v] * inv;
+  }
+}
+
+hipError_t launch_prefill_vproj(const Dims& d, int rows, const float* po, const float* pml,
+                                const uint16_t* bvr, float* out, hipStream_t s) {
+  const dim3 grid((rows + 127) / 128, d.Hq);
+  switch (d.dh / 32) {
+    case 2: prefill_vproj_kernel<2><<<grid, 256, 0, s>>>(po, pml, bvr, d, rows, out); break;
+    case 4: prefill_vproj_kernel<4><<<grid, 256, 0, s>>>(po, pml, bvr, d, rows, out); break;
+    case 6: prefill_vproj_kernel<6><<<grid, 256, 0, s>>>(po, pml, bvr, d, rows, out); break;
+    case 8: prefill_vproj_kernel<8><<<grid, 256, 0, s>>>(po, pml, bvr, d, rows, out); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- attn --
 
 constexpr int kPQ = 16;       // queries per workgroup
@@ -212,9 +404,9 @@ struct AttnArgs {
   int ctx, chunk, n_qb, n_qb_pad, n_hg, n_cb;
   const uint8_t* value;
   const uint16_t* vmeta;
-  const uint32_t* qt;     // [B*C][Hq][kQ43Rec]
+  const _Float16* qn;     // [B*C][Hq][32] query latents, natural channel order
   const _Float16* kd;     // [B][T_max][Hkv][32] fp16 key latents
-  float* part_o;          // [B*C][Hq][R_v]
+  float* part_o;          // B*C x Hq rows of R_v, element order of po_index
   float* part_ml;         // [B*C][Hq][2]
 };
 
@@ -320,23 +512,15 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int m = lane & 31, j = lane >> 5;   // 32x32 operand coordinates
   const int c16 = lane & 15, g16 = lane >> 4;  // 16x16 operand coordinates
 
-  // the query records hold 16 channel pairs (lo half, hi half) in the order
-  // of the packed key words; put every channel back in its place
-  for (int i = tid; i < kPQ * kPH * 16; i += 512) {
-    const int qh = i >> 4, t = i & 15;       // (query, head) and pair
+  // the 16 queries' latent vectors of the 8 heads: one 16-byte piece each
+  {
+    const int qh = tid >> 2, piece = tid & 3;    // (query, head), 8 channels
     const int qi = qh / kPH;
-    int ca, cb2;
-    if (t < 4) { ca = t; cb2 = t + 4; }
-    else if (t < 9) { ca = 8 + (t - 4); cb2 = 18 + (t - 4); }
-    else if (t < 14) { ca = 13 + (t - 9); cb2 = 23 + (t - 9); }
-    else if (t == 14) { ca = 28; cb2 = 30; }
-    else { ca = 29; cb2 = 31; }
-    const uint32_t pr = qi < nq
-        ? a.qt[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH) * kQ43Rec +
-               (qh % kPH) * kQ43Rec + t]
-        : 0u;
-    qnat[qh * 32 + ca] = __builtin_bit_cast(_Float16, (uint16_t)(pr & 0xFFFFu));
-    qnat[qh * 32 + cb2] = __builtin_bit_cast(_Float16, (uint16_t)(pr >> 16));
+    h8 v = h8{};
+    if (qi < nq)
+      v = *reinterpret_cast<const h8*>(
+          a.qn + (((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + qh % kPH) * 32 + piece * 8);
+    *reinterpret_cast<h8*>(&qnat[qh * 32 + piece * 8]) = v;
   }
   if (tid < 2) flag_l[tid] = -1;
   __syncthreads();
@@ -580,8 +764,9 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
           const int rr = rt * 32 + acc_row(v, lane);
           const int qi = rr >> 3, hh = rr & 7;
           if (qi < nq)
-            a.part_o[(((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + hh) * d.rv +
-                     col0 + (2 * wave + gp) * 32 + m] = acc[rt][gp][v];
+            a.part_o[po_index(d, (size_t)d.B * a.chunk, hg * kPH + hh,
+                              (size_t)b * a.chunk + q0 + qi,
+                              col0 + (2 * wave + gp) * 32 + m)] = acc[rt][gp][v];
         }
   }
   if (cb == 0) {
@@ -618,16 +803,16 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
   off += align256p(M * d.Hkv * d.rk * 4);
   w.zv = off;
   off += align256p(M * d.rv * 4);
-  w.qt = off;
-  off += align256p(M * d.Hq * kQ43Rec * 4);
+  w.qt = off;   // fp16 query latents [rows][Hq][32]
+  off += align256p(M * d.Hq * 32 * 2);
   w.kd = off;   // fp16 key latents of every cached position, [B][T_max][Hkv][32]
   off += align256p((size_t)d.B * d.Tmax * d.Hkv * 32 * 2);
   w.part_o = off;
   off += align256p(M * d.Hq * d.rv * 4);
   w.part_ml = off;
   off += align256p(M * d.Hq * 2 * 4);
-  w.obar = off;
-  off += align256p(M * d.Hq * d.rv * 4);
+  w.bvr = off;  // rotated value factor, bf16 high then low parts
+  off += align256p((size_t)2 * d.Hkv * d.dh * d.rv * 2);
   w.total = off;
   return w;
 }
@@ -635,7 +820,7 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
 bool prefill_supported(const Dims& d) {
   return d.dtype == STARKV_CACHE_Q43 && d.rk == 32 && d.Hq % kPH == 0 &&
          (d.G == 1 || d.G == 2 || d.G == 4 || d.G == 8) && d.rv % 256 == 0 &&
-         d.rv <= kMaxRv;
+         d.rv <= kMaxRv && d.dh % 64 == 0 && d.dh <= 256;
 }
 
 hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
@@ -688,11 +873,12 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
     if (e != hipSuccess) return e;
   }
 
-  // query records for every (query, head) of the chunk
-  Dims dq = d;
-  dq.B = M;
-  void* qt = ws + lay.qt;
-  e = launch_qproj_q43(dq, q, bk, sm_scale, qt, s);
+  // query latents of every (query, head) of the chunk
+  _Float16* qn = reinterpret_cast<_Float16*>(ws + lay.qt);
+  prefill_qproj_kernel<<<dim3((M + 127) / 128, d.Hq), 256, 0, s>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(bk), d, M,
+      sm_scale * kLog2e, qn);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(3);
 
@@ -707,7 +893,7 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   aa.n_cb = d.rv > kMaxCols ? 2 : 1;
   aa.value = static_cast<const uint8_t*>(cache.value);
   aa.vmeta = static_cast<const uint16_t*>(cache.value_meta);
-  aa.qt = static_cast<const uint32_t*>(qt);
+  aa.qn = qn;
   aa.kd = kd;
   aa.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   aa.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
@@ -715,9 +901,12 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   if (e != hipSuccess) return e;
   mark(4);
 
-  // normalise, undo the value rotation, up-project per head
-  e = launch_merge_vproj_q43(dq, aa.part_o, aa.part_ml, 1, bv,
-                             reinterpret_cast<float*>(ws + lay.obar), out, s);
+  // up-project per head through the rotated factor and normalise
+  uint16_t* bvr = reinterpret_cast<uint16_t*>(ws + lay.bvr);
+  prefill_rotate_bv_kernel<<<d.Hkv * d.dh, 256, 0, s>>>(static_cast<const uint16_t*>(bv), d, bvr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_prefill_vproj(d, M, aa.part_o, aa.part_ml, bvr, out, s);
   mark(5);
   return e;
 }
