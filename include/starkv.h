@@ -191,10 +191,12 @@ STARKV_API int starkv_decode_profiled(const starkv_config* cfg,
  *   z_debug fp32 [B][C][Hkv*r_k + R_v] or NULL: the projected latents
  * Projects Z = x A, appends it at [ctx_len, ctx_len + C) exactly as
  * starkv_append would, then query i (absolute position ctx_len + i) attends
- * to cached positions 0 .. ctx_len + i.  Q43 caches only.  Workspace:
+ * to cached positions 0 .. ctx_len + i.  Workspace:
  * starkv_workspace_bytes(cfg, PREFILL, C).
  * Errors: EINVAL, ECAPACITY (ctx_len + C > max_tokens), EWORKSPACE,
- * EUNSUPPORTED, ELAUNCH. */
+ * ELAUNCH; EUNSUPPORTED unless the cache is Q43 with r_k = 32, Hq a multiple
+ * of 8, Hq / Hkv in {1, 2, 4, 8}, R_v a multiple of 256 up to 1024, d_h a
+ * multiple of 64 up to 256 and D a multiple of 64. */
 STARKV_API int starkv_prefill(const starkv_config* cfg, const starkv_cache* cache,
                    int32_t ctx_len, int32_t chunk, const void* x,
                    int32_t hidden, const void* A_key, const void* A_value,

@@ -142,3 +142,9 @@ def test_call_validation_before_any_hip_call():
     f32 = _cfg(synth.WORKLOADS["tiny"])
     assert lib.starkv_prefill(ctypes.byref(f32), cc, 0, 64, *pargs, 0x8000, 1 << 34,
                               None) == sk.STARKV_EUNSUPPORTED
+    # head dims that decode takes but the prefill's up-projection tiles do not
+    for dh in (96, 160):
+        c = _cfg(pre, head_dim=dh)
+        assert sk.starkv_cache_bytes(c, 0) > 0
+        assert lib.starkv_prefill(ctypes.byref(c), cc, 0, 64, *pargs, 0x8000, 1 << 34,
+                                  None) == sk.STARKV_EUNSUPPORTED, dh
