@@ -626,6 +626,29 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       m_ref[i] = -INFINITY;
       thr[i] = -INFINITY;
     }
+    // Groups of 4 or more query heads per KV head score on MFMA 4x4x4 (16
+    // blocks of 4 tokens): B = the lane's own key fields (column = token),
+    // A = the query records read from LDS (row = query head; lane 4b + i
+    // reads head i of a set of 4), so that a lane receives its token's
+    // scores of the 4 heads in 4 registers.  K step s takes field pairs 2s,
+    // 2s + 1: steps 0-1 the 4-bit part, steps 2-8 the 3-bit part (pair 17
+    // is zero on both sides).
+    constexpr int kSets = G >= 4 ? G / 4 : 0;
+    constexpr int kSetsA = kSets > 0 ? kSets : 1;
+    typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+    float qsh[KVS][kSetsA][4], qsl[KVS][kSetsA][4];
+    if constexpr (kSets > 0) {
+#pragma unroll
+      for (int ki = 0; ki < KVS; ++ki)
+#pragma unroll
+        for (int st = 0; st < kSets; ++st)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t* rv = qrec + ((sw + ki * 4) * G + st * 4 + v) * kQ43Rec;
+            qsh[ki][st][v] = __builtin_bit_cast(float, rv[17]);
+            qsl[ki][st][v] = __builtin_bit_cast(float, rv[18]);
+          }
+    }
 
     // scores of tile `tile` into P slot `slot`; `it` = its index in the split
     auto score = [&](int tile, int it, int slot, const uint32_t (&kc)[KVS][6]) {
@@ -635,10 +658,36 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
         const KeyLane kl = unpack_key_lane(kc[ki]);
+        if constexpr (kSets > 0) {
+          const h2 mh = __builtin_bit_cast(h2, kl.mhi), ml = __builtin_bit_cast(h2, kl.mlo);
 #pragma unroll
-        for (int jj = 0; jj < G; ++jj) {
-          const float sc = key_score(kl, qrec + ((sw + ki * 4) * G + jj) * kQ43Rec);
-          x[ki * G + jj] = valid ? sc : -INFINITY;
+          for (int st = 0; st < kSets; ++st) {
+            const uint32_t* rq = qrec + ((sw + ki * 4) * G + st * 4 + (lane & 3)) * kQ43Rec;
+            f32x4 dh = {0.0f, 0.0f, 0.0f, 0.0f}, dl = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+              const h4v qa = __builtin_bit_cast(
+                  h4v, k < 8 ? *reinterpret_cast<const u32x2*>(rq + 2 * k) : u32x2{rq[16], 0u});
+              const h4v kb = __builtin_bit_cast(
+                  h4v, u32x2{kl.pr[2 * k], k < 8 ? kl.pr[2 * k + 1] : 0u});
+              if (k < 2) dh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa, kb, dh, 0, 0, 0);
+              else dl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa, kb, dl, 0, 0, 0);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float sc =
+                  fmaf((float)mh[0], dh[v],
+                       fmaf((float)ml[0], dl[v],
+                            fmaf((float)mh[1], qsh[ki][st][v], (float)ml[1] * qsl[ki][st][v])));
+              x[ki * G + st * 4 + v] = valid ? sc : -INFINITY;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < G; ++jj) {
+            const float sc = key_score(kl, qrec + ((sw + ki * 4) * G + jj) * kQ43Rec);
+            x[ki * G + jj] = valid ? sc : -INFINITY;
+          }
         }
       }
       bool big = false;
