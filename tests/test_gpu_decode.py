@@ -124,6 +124,9 @@ def test_plain_cache_shapes(name, kw):
     dict(n_q_heads=4, n_kv_heads=2, value_rank=256),
     # 16 KV heads in groups of 2, R_v 768 (six value groups per value wave)
     dict(n_q_heads=32, n_kv_heads=16, value_rank=768),
+    # four KV heads in groups of 4 (MFMA scores, one KV head per score
+    # wave), R_v 512
+    dict(n_q_heads=16, n_kv_heads=4, value_rank=512),
 ])
 def test_q43_shapes(kw):
     """4/3-bit caches across the score-wave head counts and value-wave group
