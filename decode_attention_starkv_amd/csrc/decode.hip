@@ -574,14 +574,10 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   const int GV = 4 * NIV;            // value groups
   const int NH = NIV;                // 4-bit value groups
   // Two workgroups share a compute unit when R_v is small, and issue
-  // arbitration favours the older one; the two halves of the grid (which
-  // land as the first and the second workgroup of each unit) take turns at
-  // the higher wave priority, tile by tile.
-  const int par = (blockIdx.y * gridDim.x + blockIdx.x) >= (gridDim.x * gridDim.y) / 2;
-  auto set_prio = [](bool hi) {
-    if (hi) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-  };
+  // arbitration favours the older one; the grid's second half (which lands
+  // as the second workgroup of each unit) runs at the higher wave priority.
+  if ((blockIdx.y * gridDim.x + blockIdx.x) >= (gridDim.x * gridDim.y) / 2)
+    __builtin_amdgcn_s_setprio(1);
   const int j = lane >> 5, m = lane & 31;
 
   for (int i = tid; i < 2 * 32 * PS / 8; i += 512) reinterpret_cast<h8*>(&p_l[0][0])[i] = h8{};
@@ -733,14 +729,12 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     }
     lds_barrier();
     for (int it = 0; it < n_it; it += 2) {
-      set_prio(par);
       if (it + 1 < n_it && has_keys) {
         score(tile0 + it + 1, it + 1, (it + 1) & 1, kB);
         if (it + 3 < n_it) load_keys(tile0 + it + 3, kB);
       }
       lds_barrier();
       if (it + 1 >= n_it) break;
-      set_prio(!par);
       if (it + 2 < n_it && has_keys) {
         score(tile0 + it + 2, it + 2, (it + 2) & 1, kA);
         if (it + 4 < n_it) load_keys(tile0 + it + 4, kA);
@@ -794,7 +788,6 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     lds_barrier();      // P of the first tile is ready
     for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
       const int pslot = it & 1;
-      set_prio((tile + par) & 1);
       const int vslot = it % kValueSlots;
       if (tile + kValueAhead < tile1) stage(tile + kValueAhead, (it + kValueAhead) % kValueSlots);
       // wait for this tile's stage: the later stages may stay in flight
