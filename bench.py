@@ -328,6 +328,27 @@ def run_prefill(args, w, torch, sk, synth):
     print(json.dumps(res))
 
 
+def stream_read_ceiling(torch, sk, dev, gib=2, reps=10):
+    """Measured streaming-read bandwidth (GB/s): starkv_stream_read over a
+    buffer 8x the Infinity Cache, read once per pass with the split kernel's
+    non-temporal 16-byte loads; the median of `reps` passes."""
+    buf = torch.full((gib << 30,), 7, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sk.starkv_stream_read(buf, sink)
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        sk.starkv_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del buf
+    torch.cuda.empty_cache()
+    ts.sort()
+    return (gib << 30) / (ts[len(ts) // 2] * 1e-3) / 1e9
+
+
 def traffic_from_counters(w, batch, seq_len, splits):
     """HBM bytes per split-kernel launch from committed rocprofv3 counters,
     or None if the kernel source changed since they were taken or the run is
@@ -442,6 +463,7 @@ def main():
               flush=True)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+    stream_gbs = stream_read_ceiling(torch, sk, dev)
 
     mean = lambda v: sum(v) / len(v)
     ms = mean(step_ms)
@@ -474,6 +496,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic_from_counters(w, w.batch, seq_len,
                                                       sk.starkv_decode_splits(cfg, seq_len))},
+        "split_vs_stream_read": {"stream_read_GBps": stream_gbs,
+                                 "frac": achieved / stream_gbs},
         "step_hbm_frac": (cache_bytes + factor_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "ms_per_step_percentiles": percentiles(step_ms),
         "split_ms_percentiles": percentiles(kern_ms[1]),

@@ -30,7 +30,7 @@ OP_DECODE, OP_PREFILL = 0, 1
 ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_decode_splits", "starkv_append", "starkv_decode",
                 "starkv_decode_profiled", "starkv_prefill",
-                "starkv_prefill_profiled", "starkv_strerror")
+                "starkv_prefill_profiled", "starkv_stream_read", "starkv_strerror")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -86,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz,
                                             vp, P(vp)]
     lib.starkv_prefill_profiled.restype = ctypes.c_int
+    lib.starkv_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.starkv_stream_read.restype = ctypes.c_int
     lib.starkv_strerror.argtypes = [ctypes.c_int]
     lib.starkv_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -153,6 +155,15 @@ class LatentCache:
 
     def nbytes(self) -> int:
         return sum(starkv_cache_bytes(self.cfg, w) for w in range(4))
+
+
+def starkv_stream_read(src, sink, stream=None) -> None:
+    """Measurement helper: stream the whole device tensor `src` once (the
+    split kernel's access pattern); `sink` is a device tensor of >= 4 bytes."""
+    st = load_library().starkv_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                           _ptr(sink), _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_stream_read")
 
 
 def starkv_append(cfg, cache: LatentCache, z_key, z_value, pos: int,

@@ -14,7 +14,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libstarkv.so")
-SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "stream.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

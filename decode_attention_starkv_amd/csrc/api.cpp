@@ -221,6 +221,11 @@ int starkv_prefill_profiled(const starkv_config* cfg, const starkv_cache* cache,
                       ws_bytes, stream, events);
 }
 
+int starkv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink || !aligned16(src) || bytes == 0 || bytes % 16 != 0) return STARKV_EINVAL;
+  return launch_stream_read(src, bytes, sink, stream) == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
+}
+
 const char* starkv_strerror(int status) {
   switch (status) {
     case STARKV_OK: return "success";

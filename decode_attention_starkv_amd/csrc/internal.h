@@ -71,6 +71,9 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache,
                           hipEvent_t* events = nullptr);
 bool prefill_supported(const Dims& d);
 
+// Streaming-read measurement pass (stream.hip).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // fp32 value nearest to 1/sqrt(m) for the Walsh-Hadamard block sizes used.
 __host__ __device__ inline float inv_sqrt_pow2(int m) {
   switch (m) {

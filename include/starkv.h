@@ -220,6 +220,17 @@ STARKV_API int starkv_prefill_profiled(const starkv_config* cfg,
                                        void* workspace, size_t ws_bytes,
                                        hipStream_t stream, hipEvent_t* events);
 
+/* Measurement helper, not a step of the method: reads `bytes` bytes of the
+ * device buffer `src` once with non-temporal 16-byte loads, the way the
+ * decode split kernel streams the cache, so that the split kernel's
+ * bandwidth can be set against the measured streaming-read ceiling.
+ * `sink` (device, one uint32) is written only in the rare case that the
+ * XOR of a thread's data equals a fixed value; its content is meaningless.
+ * src 16-byte aligned, bytes a non-zero multiple of 16; EINVAL otherwise,
+ * ELAUNCH if the launch fails.  Async on `stream`. */
+STARKV_API int starkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                                  hipStream_t stream);
+
 /* (host) Static description of a status code. */
 STARKV_API const char* starkv_strerror(int status);
 

@@ -142,6 +142,11 @@ def test_call_validation_before_any_hip_call():
     f32 = _cfg(synth.WORKLOADS["tiny"])
     assert lib.starkv_prefill(ctypes.byref(f32), cc, 0, 64, *pargs, 0x8000, 1 << 34,
                               None) == sk.STARKV_EUNSUPPORTED
+    # stream-read measurement helper: alignment, size and sink checked first
+    assert lib.starkv_stream_read(0x1004, 1 << 20, 0x2000, None) == sk.STARKV_EINVAL
+    assert lib.starkv_stream_read(0x1000, 0, 0x2000, None) == sk.STARKV_EINVAL
+    assert lib.starkv_stream_read(0x1000, 100, 0x2000, None) == sk.STARKV_EINVAL
+    assert lib.starkv_stream_read(0x1000, 1 << 20, None, None) == sk.STARKV_EINVAL
     # head dims that decode takes but the prefill's up-projection tiles do not
     for dh in (96, 160):
         c = _cfg(pre, head_dim=dh)
