@@ -222,7 +222,9 @@ int starkv_prefill_profiled(const starkv_config* cfg, const starkv_cache* cache,
 }
 
 int starkv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
-  if (!src || !sink || !aligned16(src) || bytes == 0 || bytes % 16 != 0) return STARKV_EINVAL;
+  if (!src || !sink || !aligned16(src) || reinterpret_cast<uintptr_t>(sink) % 4 != 0 ||
+      bytes == 0 || bytes % 16 != 0)
+    return STARKV_EINVAL;
   return launch_stream_read(src, bytes, sink, stream) == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
 }
 

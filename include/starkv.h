@@ -226,8 +226,9 @@ STARKV_API int starkv_prefill_profiled(const starkv_config* cfg,
  * bandwidth can be set against the measured streaming-read ceiling.
  * `sink` (device, one uint32) is written only in the rare case that the
  * XOR of a thread's data equals a fixed value; its content is meaningless.
- * src 16-byte aligned, bytes a non-zero multiple of 16; EINVAL otherwise,
- * ELAUNCH if the launch fails.  Async on `stream`. */
+ * src 16-byte aligned, sink 4-byte aligned, bytes a non-zero multiple of
+ * 16; EINVAL otherwise, ELAUNCH if the launch fails (also when bytes / 16
+ * needs more than 2^31 - 1 workgroups of 512).  Async on `stream`. */
 STARKV_API int starkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
                                   hipStream_t stream);
 

@@ -147,6 +147,7 @@ def test_call_validation_before_any_hip_call():
     assert lib.starkv_stream_read(0x1000, 0, 0x2000, None) == sk.STARKV_EINVAL
     assert lib.starkv_stream_read(0x1000, 100, 0x2000, None) == sk.STARKV_EINVAL
     assert lib.starkv_stream_read(0x1000, 1 << 20, None, None) == sk.STARKV_EINVAL
+    assert lib.starkv_stream_read(0x1000, 1 << 20, 0x2002, None) == sk.STARKV_EINVAL
     # head dims that decode takes but the prefill's up-projection tiles do not
     for dh in (96, 160):
         c = _cfg(pre, head_dim=dh)
