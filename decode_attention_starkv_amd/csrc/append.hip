@@ -219,6 +219,30 @@ __device__ inline void append_q43_values(
   const float rc = inv_sqrt_pow2(m);
   uint16_t* vm = vmeta + ((size_t)b * d.NT + tile) * 2 * G * kTile;
 
+  // Words of a 32-token run that this append covers only partly keep the
+  // other tokens' bits: read them now, so that the read overlaps phase 1
+  // instead of following it.  Thread t owns channel cb*256 + t of the tile;
+  // no other thread touches its words.
+  const int ch = cb * 256 + threadIdx.x;
+  const int g = ch / 32, c = ch % 32;
+  const int NH = n_hi / 32;
+  const bool four = g < NH;
+  const int nw = four ? 4 : 3;
+  uint8_t* vt = value + ((size_t)b * d.NT + tile) * 26 * d.rv;
+  uint8_t* grp = four ? vt + (size_t)g * 1024 : vt + (size_t)NH * 1024 + (size_t)(g - NH) * 768;
+  uint32_t old[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int a = max(ulo - 32 * j, 0), e = min(uhi - 32 * j, 32);
+    if (a < e && !(a == 0 && e == 32)) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(grp + (size_t)(32 * j + c) * nw * 4);
+      old[j][0] = src[0];
+      old[j][1] = src[1];
+      old[j][2] = src[2];
+      if (four) old[j][3] = src[3];
+    }
+  }
+
   for (int u = ulo + wave; u < uhi; u += 4) {
     const float* src = zv + ((size_t)b * n + (t0 + u - pos)) * d.rv + cb * 256;
     float x[4];
@@ -253,25 +277,20 @@ __device__ inline void append_q43_values(
         lo = fminf(lo, __shfl_xor(lo, s));
         hi = fmaxf(hi, __shfl_xor(hi, s));
       }
-      int ch = cb * 256 + lane + 64 * r;
-      float levels = ch < n_hi ? 15.0f : 7.0f;
+      const int chr = cb * 256 + lane + 64 * r;
+      float levels = chr < n_hi ? 15.0f : 7.0f;
       QParams p = group_params(lo, hi, levels);
       codes[u][lane + 64 * r] = (uint8_t)code_of(x[r], p, levels);
       if ((lane & 31) == 0) {
-        int g = ch / 32;
-        vm[(size_t)g * kTile + u] = p.sb;
-        vm[(size_t)(G + g) * kTile + u] = p.zb;
+        const int gr = chr / 32;
+        vm[(size_t)gr * kTile + u] = p.sb;
+        vm[(size_t)(G + gr) * kTile + u] = p.zb;
       }
     }
   }
   __syncthreads();
 
-  const int ch = cb * 256 + threadIdx.x;
-  const int g = ch / 32, c = ch % 32;
-  const int NH = n_hi / 32;
-  const bool four = g < NH;
-  uint8_t* vt = value + ((size_t)b * d.NT + tile) * 26 * d.rv;
-  uint8_t* grp = four ? vt + (size_t)g * 1024 : vt + (size_t)NH * 1024 + (size_t)(g - NH) * 768;
+#pragma unroll
   for (int j = 0; j < 2; ++j) {
     int a = max(ulo - 32 * j, 0), e = min(uhi - 32 * j, 32);
     if (a >= e) continue;
@@ -302,13 +321,11 @@ __device__ inline void append_q43_values(
         }
       }
     }
-    const int nw = four ? 4 : 3;
     uint32_t* dst = reinterpret_cast<uint32_t*>(grp + (size_t)(32 * j + c) * nw * 4);
-    bool whole = (a == 0 && e == 32);
-    for (int k = 0; k < nw; ++k) {
-      uint32_t val = whole ? w[k] : ((dst[k] & ~mask[k]) | w[k]);
-      dst[k] = val;
-    }
+    const bool whole = (a == 0 && e == 32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nw) dst[k] = whole ? w[k] : ((old[j][k] & ~mask[k]) | w[k]);
   }
 }
 

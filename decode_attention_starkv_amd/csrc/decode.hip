@@ -46,9 +46,10 @@ struct SplitArgs {
 
 // ------------------------------------------------------------------ qproj --
 
-// One workgroup per (b, h): q is staged in LDS, 256 threads split the d_h
-// contraction into chunks, the chunks are summed, then wave 0 rotates,
-// scales and packs the record.
+// One workgroup per (b, h): 256 threads split the d_h contraction into
+// chunks (each thread loads its q entries and factor entries together, so
+// the kernel makes one round trip to memory), the chunks are summed, then
+// wave 0 rotates, scales and packs the record.
 // A Q43 record holds the 17 fp16 pairs that meet the in-place code fields of
 // the key words (each entry times 2^-p for a field at bit p; channel 31
 // split over three one-bit fields), then sum(q_hi) 2^-24 and
@@ -58,18 +59,12 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
                                                     const void* __restrict__ bk,
                                                     Dims d, float qscale,
                                                     void* __restrict__ qt) {
-  __shared__ float qs[256];
   __shared__ float part[256];
   __shared__ _Float16 sq[32];
   const int bh = blockIdx.x;
-  const int b = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
+  const int g = (bh % d.Hq) / d.G;
   const int t = threadIdx.x;
-  if (t < d.dh) {
-    const size_t qi = ((size_t)b * d.Hq + h) * d.dh + t;
-    qs[t] = FMT == STARKV_CACHE_F32 ? static_cast<const float*>(q)[qi]
-                                    : bf16v(static_cast<const uint16_t*>(q)[qi]);
-  }
-  __syncthreads();
+  const size_t qrow = (size_t)bh * d.dh;
   const int rkp = d.rk <= 32 ? 32 : 64;
   const int c = t % rkp, chunk = t / rkp, nch = 256 / rkp;
   const int klen = (d.dh + nch - 1) / nch;
@@ -81,7 +76,9 @@ __global__ __launch_bounds__(256) void qproj_kernel(const void* __restrict__ q,
       const size_t bi = ((size_t)g * d.dh + k) * d.rk + c;
       const float bv = FMT == STARKV_CACHE_F32 ? static_cast<const float*>(bk)[bi]
                                                : bf16v(static_cast<const uint16_t*>(bk)[bi]);
-      acc = fmaf(qs[k], bv, acc);
+      const float qv = FMT == STARKV_CACHE_F32 ? static_cast<const float*>(q)[qrow + k]
+                                               : bf16v(static_cast<const uint16_t*>(q)[qrow + k]);
+      acc = fmaf(qv, bv, acc);
     }
   }
   part[t] = acc;
@@ -614,7 +611,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
         dst[ki][5] = mt[1];
       }
     };
-    // m_ref: reference max (log2 units); thr = (m_ref + kLazy) 2^-24, the
+    // m_ref: reference max (log2 units); thr = (m_ref + kLazyQ43) 2^-24, the
     // move threshold in the 2^-24 units the scores come in
     float m_ref[KVS * G], thr[KVS * G];
 #pragma unroll
@@ -699,7 +696,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
             const float mt = wave_max(x[i]) * kTwo24;
             alpha = exp2f(m_ref[i] - mt);
             m_ref[i] = mt;
-            thr[i] = (mt + kLazy) * (1.0f / kTwo24);
+            thr[i] = (mt + kLazyQ43) * (1.0f / kTwo24);
             if (lane == 0) flag_l[slot] = it;
           }
           if (lane == 0) alpha_l[slot][h] = alpha;
@@ -823,6 +820,30 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       h8 A[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
+      // zero points of this wave's groups: columns n0 .. n0+NIV-1; the
+      // 4-bit wave (n0 = 0) also sums P into column NIV: l of every head,
+      // rescaled with the accumulators and made of the same fp16 P
+      // (other columns read a row of zeros: no masked loads)
+      {
+        const bool zcol = m >= n0 && m < n0 + NIV;
+        const _Float16* zsrc = zcol ? zr_l + (m - n0) * kTile
+                                    : (kFour && m == NIV) ? zo_l + kTile : zo_l;
+        h8 Z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Z[r] = *reinterpret_cast<const h8*>(zsrc + 32 * j + 8 * r);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z[r], bacc, 0, 0, 0);
+      }
+      // P times the in-place field weights of the token pairs of step r
+      // (powers of two: exact); shared by all groups of the wave
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        h8 F;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) F[e] = (_Float16)run_pair_weight<kFour>(4 * r + e / 2);
+        A[r] = A[r] * F;
+      }
       {
         // two column tiles at a time: their MFMAs are independent
 #pragma unroll
@@ -844,27 +865,16 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
             for (int q = 0; q < 2; ++q) {
               const int ni = n2 + q;
               const h8 S = *reinterpret_cast<const h8*>(sc_l + ni * kTile + 32 * j + 8 * r);
-              const u32x4 bw = {run_pair<kFour>(W[q], 4 * r), run_pair<kFour>(W[q], 4 * r + 1),
-                                run_pair<kFour>(W[q], 4 * r + 2), run_pair<kFour>(W[q], 4 * r + 3)};
+              const u32x4 bw = {run_pair_inplace<kFour>(W[q], 4 * r),
+                                run_pair_inplace<kFour>(W[q], 4 * r + 1),
+                                run_pair_inplace<kFour>(W[q], 4 * r + 2),
+                                run_pair_inplace<kFour>(W[q], 4 * r + 3)};
               acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r] * S, __builtin_bit_cast(h8, bw),
                                                               acc[ni], 0, 0, 0);
             }
           }
         }
       }
-      // zero points of this wave's groups: columns n0 .. n0+NIV-1; the
-      // 4-bit wave (n0 = 0) also sums P into column NIV: l of every head,
-      // rescaled with the accumulators and made of the same fp16 P
-      // (other columns read a row of zeros: no masked loads)
-      const bool zcol = m >= n0 && m < n0 + NIV;
-      const _Float16* zsrc = zcol ? zr_l + (m - n0) * kTile
-                                  : (kFour && m == NIV) ? zo_l + kTile : zo_l;
-      h8 Z[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Z[r] = *reinterpret_cast<const h8*>(zsrc + 32 * j + 8 * r);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        bacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r], Z[r], bacc, 0, 0, 0);
       lds_barrier();
     }
     // zero-point sums of this wave's own columns: one writer per entry
@@ -898,8 +908,9 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = acc_row(v, lane);
+        // products came in units of 2^-20 (4-bit runs) or 2^-18 (3-bit)
         st[row * kStageRow + ni * 32 + m] =
-            fmaf(acc[ni][v], kTwo24, bias_l[row][n]) * inv_l[v];
+            fmaf(acc[ni][v], kFour ? 1048576.0f : 262144.0f, bias_l[row][n]) * inv_l[v];
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own staging writes done

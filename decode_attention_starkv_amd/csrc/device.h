@@ -19,6 +19,10 @@ constexpr float kTwo24 = 16777216.0f;
 // exceeds it by more than this (log2 units), so probabilities stay <= 2^8 and
 // the accumulators are rescaled rarely.
 constexpr float kLazy = 8.0f;
+// The Q43 decode contraction scales P by up to 2^6 (the in-place field
+// weights) before the per-group scale: its running max moves at 2^2, so
+// that P times the weight stays <= 2^8 as elsewhere.
+constexpr float kLazyQ43 = 2.0f;
 constexpr int kQ43Rec = 20;   // dwords per (b, h) query record, Q43
 constexpr int kPlainRec = 64; // floats per (b, h) query record, F32/BF16
 // Cache-policy bits of a non-temporal load.
@@ -60,6 +64,35 @@ __device__ inline uint32_t run_pair(const u32x4& w, int p) {
     return ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
            ((w[2] >> 13) & 0x00040004u);
   }
+}
+
+// The same pairs read in place for the decode contraction: a field at bit
+// p <= 6 of a 16-bit half is the fp16 subnormal c * 2^(p-24) after one AND,
+// and the fields above it are first shifted down by 8 (4-bit runs) or 9
+// (3-bit runs) bits.  The product's other operand carries
+// run_pair_weight(p) = 2^(K-p) for the field's position (K = 4 for 4-bit
+// runs, 6 for 3-bit runs), so every product comes out in units of 2^(K-24).
+// Pair 15 of a 3-bit run (tokens 30, 31) is assembled as in run_pair.
+template <bool kFour>
+__device__ inline uint32_t run_pair_inplace(const u32x4& w, int p) {
+  if constexpr (kFour) {
+    const uint32_t x = (p & 2) ? (w[p >> 2] >> 8) : w[p >> 2];
+    return x & ((p & 1) ? 0x00F000F0u : 0x000F000Fu);
+  } else {
+    if (p < 15) {
+      const int f = p % 5;
+      const uint32_t x = f >= 3 ? (w[p / 5] >> 9) : w[p / 5];
+      return x & (f == 0 || f == 3 ? 0x00070007u : f == 1 || f == 4 ? 0x00380038u : 0x01C001C0u);
+    }
+    return ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
+           ((w[2] >> 13) & 0x00040004u);
+  }
+}
+template <bool kFour>
+__host__ __device__ constexpr float run_pair_weight(int p) {
+  if (kFour) return (p & 1) ? 1.0f : 16.0f;
+  if (p == 15) return 64.0f;
+  return p % 5 == 0 || p % 5 == 3 ? 64.0f : p % 5 == 1 || p % 5 == 4 ? 8.0f : 1.0f;
 }
 
 // One Q43 key tile of one KV head as seen by one lane (= token), as 17 fp16
