@@ -444,7 +444,7 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float l = l_row[acc_row(v, lane)];
-      inv_l[v] = l > 0.0f ? 1.0f / l : 0.0f;
+      inv_l[v] = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;   // rows go out as fp16
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
@@ -900,7 +900,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float l = l_row[acc_row(v, lane)];
-      inv_l[v] = l > 0.0f ? 1.0f / l : 0.0f;
+      inv_l[v] = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;   // rows go out as fp16
     }
 #pragma unroll
     for (int ni = 0; ni < NIV; ++ni) {

@@ -62,6 +62,17 @@ def test_peaked_softmax(name):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("name", ["l2_q43", "l3_gqa_q43"])
+def test_rising_scores(name):
+    """One token per tile with a latent row scaled up tile after tile: the
+    running max of many heads moves again and again along the split, so the
+    rescaling of the value accumulators runs on most tiles."""
+    n = 1100
+    spike = {64 * i + 9: 1.0 + 0.3 * i for i in range(n // 64)}
+    err, _ = run_case(name, n, q_scale=8.0, spike=spike, num_splits=2)
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("splits", [1, 3, 7])
 def test_forced_splits(splits):
     err, _ = run_case("l2_q43", 900, num_splits=splits, q_scale=4.0)
