@@ -1176,6 +1176,144 @@ __global__ __launch_bounds__(64 * kVprojWaves) void vproj_kernel(
   }
 }
 
+// ----------------------------------------------------- merge + vproj --
+
+// Merge and up-projection in one workgroup per (KV head g, sequence b), for
+// fp16 partials, value ranks up to 256 and d_h up to 128: the factor block
+// of one KV head (d_h x R_v bf16, at most 64 KiB) is then read once per
+// sequence from L2 and the two dependent launches become one.
+//   - Wave w merges query heads w, w + 4, .. of the group as merge_kernel
+//     does (lane = split for (m, l); 4 channels per lane; the inverse value
+//     rotation in registers and lane shuffles) and stages each merged row in
+//     LDS as bf16 high and low parts.
+//   - Then wave w takes output columns 16 rb .. 16 rb + 15 (rb = w, w + 4)
+//     on MFMA 16x16x32 bf16: rows = the group's query heads (padded to 16
+//     with zero rows), K = R_v; its factor rows are requested before the
+//     merge starts.
+constexpr int kMvRows = 16;
+constexpr int kMvMaxRv = 256;
+constexpr int kMvPad = 8;
+
+bool merge_vproj_fits(const Dims& d, int splits) {
+  return d.dtype != STARKV_CACHE_F32 && d.rv <= kMvMaxRv && d.rv % 32 == 0 &&
+         d.G <= kMvRows && splits <= 64 && d.dh % 16 == 0 && d.dh <= 128;
+}
+
+__global__ __launch_bounds__(256) void merge_vproj_kernel(
+    const _Float16* __restrict__ part_o, const float* __restrict__ part_ml,
+    const uint16_t* __restrict__ bv, Dims d, int splits, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) __bf16 oh[kMvRows][kMvMaxRv + kMvPad];
+  __shared__ __attribute__((aligned(16))) __bf16 ol[kMvRows][kMvMaxRv + kMvPad];
+  __shared__ float ms[4][64];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int n16 = lane & 15, kq = lane >> 4;
+  const int ksteps = d.rv / 32;
+
+  // factor rows of this wave's output columns: B[k][n] = B_value[g d_h +
+  // 16 rb + n][k], 8 consecutive k per lane
+  bf8 bw[2][kMvMaxRv / 32];
+#pragma unroll
+  for (int ri = 0; ri < 2; ++ri) {
+    const int rb = w + 4 * ri;
+    const bool on = 16 * rb < d.dh;
+    const uint16_t* brow = bv + ((size_t)g * d.dh + 16 * min(rb, d.dh / 16 - 1) + n16) * d.rv + 8 * kq;
+#pragma unroll
+    for (int ks = 0; ks < kMvMaxRv / 32; ++ks)
+      bw[ri][ks] = on && ks < ksteps ? *reinterpret_cast<const bf8*>(brow + 32 * ks) : bf8{};
+  }
+  // zero rows past the group's heads
+  for (int i = t; i < (kMvRows - d.G) * (d.rv / 8); i += 256) {
+    const int row = d.G + i / (d.rv / 8), c8 = 8 * (i % (d.rv / 8));
+    *reinterpret_cast<bf8*>(&oh[row][c8]) = bf8{};
+    *reinterpret_cast<bf8*>(&ol[row][c8]) = bf8{};
+  }
+
+  const size_t stride = (size_t)d.Hq * d.rv;
+  const int c = 4 * lane;
+  for (int i = w; i < d.G; i += 4) {
+    const int h = g * d.G + i;
+    const _Float16* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + min(c, d.rv - 4);
+    const float2 ml0 = *reinterpret_cast<const float2*>(
+        part_ml + (((size_t)b * splits + min(lane, splits - 1)) * d.Hq + h) * 2);
+    float4 xp[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) xp[u] = load4(src + (size_t)min(u, splits - 1) * stride);
+    const float mx = wave_max(lane < splits ? ml0.x : -INFINITY);
+    float wl = 0.0f;
+    if (lane < splits && ml0.y > 0.0f) wl = exp2f(ml0.x - mx) * ml0.y;
+    ms[w][lane] = wl;
+    const float inv = 1.0f / wave_sum(wl);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's weights
+    __builtin_amdgcn_wave_barrier();
+    float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float wgt = u < splits ? ms[w][u] : 0.0f;
+      o.x = fmaf(wgt, xp[u].x, o.x);
+      o.y = fmaf(wgt, xp[u].y, o.y);
+      o.z = fmaf(wgt, xp[u].z, o.z);
+      o.w = fmaf(wgt, xp[u].w, o.w);
+    }
+    for (int s = 16; s < splits; ++s) {
+      const float4 x = load4(src + (size_t)s * stride);
+      const float wgt = ms[w][s];
+      o.x = fmaf(wgt, x.x, o.x);
+      o.y = fmaf(wgt, x.y, o.y);
+      o.z = fmaf(wgt, x.z, o.z);
+      o.w = fmaf(wgt, x.w, o.w);
+    }
+    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+    if (d.dtype == STARKV_CACHE_Q43 && d.rotate) {
+      // undo the block rotation of the stored value latents (eq. 13)
+      const int mb = pow2_divisor(d.rv / 4);
+      float a0 = o.x + o.y, a1 = o.x - o.y, a2 = o.z + o.w, a3 = o.z - o.w;
+      o = float4{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+      for (int hs = 4; hs < mb; hs <<= 1) {
+        const int dl = hs >> 2;
+        const float4 p = {__shfl_xor(o.x, dl), __shfl_xor(o.y, dl), __shfl_xor(o.z, dl),
+                          __shfl_xor(o.w, dl)};
+        if (c & hs) o = float4{p.x - o.x, p.y - o.y, p.z - o.z, p.w - o.w};
+        else o = float4{o.x + p.x, o.y + p.y, o.z + p.z, o.w + p.w};
+      }
+      const float cst = inv_sqrt_pow2(mb);
+      o.x *= cst; o.y *= cst; o.z *= cst; o.w *= cst;
+    }
+    if (c < d.rv) {
+      const float v[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 hi = (__bf16)v[e];
+        oh[i][c + e] = hi;
+        ol[i][c + e] = (__bf16)(v[e] - (float)hi);
+      }
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int ri = 0; ri < 2; ++ri) {
+    const int rb = w + 4 * ri;
+    if (16 * rb >= d.dh) break;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kMvMaxRv / 32; ++ks) {
+      if (ks >= ksteps) break;
+      const bf8 ah = *reinterpret_cast<const bf8*>(&oh[n16][32 * ks + 8 * kq]);
+      const bf8 al = *reinterpret_cast<const bf8*>(&ol[n16][32 * ks + 8 * kq]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[ri][ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[ri][ks], acc, 0, 0, 0);
+    }
+    // C[row = query head 4 kq + v][column = output row 16 rb + n16]
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 4 * kq + v;
+      if (row < d.G)
+        out[((size_t)b * d.Hq + g * d.G + row) * d.dh + 16 * rb + n16] = acc[v];
+    }
+  }
+}
+
 template <int FMT>
 hipError_t launch_split(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t s) {
   if constexpr (FMT == STARKV_CACHE_Q43) {
@@ -1232,6 +1370,16 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   e = launch_split<FMT>(d, dim3(lay.splits, d.B), sa, s);
   if (e != hipSuccess) return e;
   mark(2);
+  if (FMT != STARKV_CACHE_F32 && merge_vproj_fits(d, lay.splits)) {
+    // one kernel for both steps; the up-projection's event pair is empty
+    merge_vproj_kernel<<<dim3(d.Hkv, d.B), 256, 0, s>>>(
+        reinterpret_cast<const _Float16*>(part_o), part_ml, static_cast<const uint16_t*>(bv),
+        d, lay.splits, out);
+    e = hipGetLastError();
+    mark(3);
+    mark(4);
+    return e;
+  }
   if constexpr (FMT == STARKV_CACHE_F32)
     merge_kernel<float><<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
   else   // fp16 partial rows, each divided by its own l

@@ -170,8 +170,11 @@ STARKV_API int starkv_decode(const starkv_config* cfg, const starkv_cache* cache
 /* starkv_decode that also records events[0..4] (host array of created
  * hipEvent_t) on `stream`: before the query projection, before the split
  * kernel, before the merge, before the value up-projection and after it, so
- * a caller can time each kernel on the stream it runs on.  Same arguments,
- * results and errors as starkv_decode; EINVAL if events is NULL. */
+ * a caller can time each kernel on the stream it runs on.  Where the merge
+ * and the up-projection run as one kernel (fp16 partials, R_v <= 256,
+ * d_h <= 128, at most 64 splits), events[3] and events[4] are both recorded
+ * after it.  Same arguments, results and errors as starkv_decode; EINVAL if
+ * events is NULL. */
 STARKV_API int starkv_decode_profiled(const starkv_config* cfg,
                                       const starkv_cache* cache,
                                       int32_t seq_len, const void* q,

@@ -73,6 +73,16 @@ def test_rising_scores(name):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("splits", [40, 64, 65])
+def test_gqa_forced_splits(splits):
+    """Value rank 256: up to 64 splits merge and up-project in one kernel
+    (16 split rows requested up front, the rest in a loop); 65 splits take
+    the separate merge and up-projection kernels."""
+    # one tile per split (the last one ragged), so the split count is exact
+    err, _ = run_case("l3_gqa_q43", 64 * splits - 7, num_splits=splits, q_scale=4.0)
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("splits", [1, 3, 7])
 def test_forced_splits(splits):
     err, _ = run_case("l2_q43", 900, num_splits=splits, q_scale=4.0)
