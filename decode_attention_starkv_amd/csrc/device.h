@@ -53,26 +53,20 @@ __device__ inline int acc_row(int v, int lane) {
   return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
 }
 
-// 16 fp16 pairs (tokens 2p, 2p+1) of one channel's 32-token value run:
-// 4-bit run in 4 words, 3-bit run in 3 words (see the format description).
-template <bool kFour>
-__device__ inline uint32_t run_pair(const u32x4& w, int p) {
-  if constexpr (kFour) {
-    return (w[p >> 2] >> (4 * (p & 3))) & 0x000F000Fu;
-  } else {
-    if (p < 15) return (w[p / 5] >> (3 * (p % 5))) & 0x00070007u;
-    return ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
-           ((w[2] >> 13) & 0x00040004u);
-  }
-}
-
-// The same pairs read in place for the decode contraction: a field at bit
-// p <= 6 of a 16-bit half is the fp16 subnormal c * 2^(p-24) after one AND,
-// and the fields above it are first shifted down by 8 (4-bit runs) or 9
-// (3-bit runs) bits.  The product's other operand carries
-// run_pair_weight(p) = 2^(K-p) for the field's position (K = 4 for 4-bit
-// runs, 6 for 3-bit runs), so every product comes out in units of 2^(K-24).
-// Pair 15 of a 3-bit run (tokens 30, 31) is assembled as in run_pair.
+// fp16 pair p (tokens 2p, 2p + 1 as the two 16-bit halves) of one channel's
+// 32-token value run, read in place for the decode contraction.  Run layout:
+// a 4-bit run is 4 words, word p / 4 holding pair p at bit 4 (p % 4) of
+// each half; a 3-bit run is 3 words, word p / 5 holding pair p < 15 at bit
+// 3 (p % 5) of each half, and pair 15 (tokens 30, 31) has its three bits in
+// bits 15 / 31 of the three words.
+//   - A field at bit b <= 6 of a 16-bit half is the fp16 subnormal
+//     c * 2^(b-24) after one AND; the fields above it are first shifted down
+//     by 8 (4-bit runs) or 9 (3-bit runs) bits.
+//   - The product's other operand carries run_pair_weight(p) = 2^(K-b), b
+//     the bit at which pair p's field is read (K = 4 for 4-bit runs, 6 for
+//     3-bit runs), so every product comes out in units of 2^(K-24).
+//   - Pair 15 of a 3-bit run is assembled from its three one-bit fields
+//     (weight 2^6).
 template <bool kFour>
 __device__ inline uint32_t run_pair_inplace(const u32x4& w, int p) {
   if constexpr (kFour) {

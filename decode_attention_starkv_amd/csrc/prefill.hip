@@ -417,7 +417,7 @@ struct UnpackRegs {
 };
 
 // Codes of token pair p of a value run as the fp16 bit patterns of 1024 + k
-// in both halves (see run_pair for the run layout).
+// in both halves (run layout as described at run_pair_inplace).
 template <bool kFour>
 __device__ inline uint32_t biased_pair(const u32x4& w, int p, const UnpackRegs& u) {
   if constexpr (kFour) {
