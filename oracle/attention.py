@@ -44,15 +44,6 @@ def softmax(a):
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def reconstruct(cache, b, seq_len, bk_eff, bv_eff, g, head_dim):
-    """K_g [T, d_h] and V_g [T, d_h] of KV head g, batch element b."""
-    zk = cache.key_latents(b, seq_len)[:, g, :]
-    zv = cache.value_latents(b, seq_len)
-    k = zk @ bk_eff[g].T
-    v = zv @ bv_eff[g * head_dim:(g + 1) * head_dim].T
-    return k, v
-
-
 def decode(cache, seq_len, q, bk, bv, sm_scale, n_q_heads, rotate,
            batches=None, heads=None):
     """out [len(batches), len(heads), d_h] float64: each query head attends

@@ -327,11 +327,13 @@ class Cache:
         kb, km, _, _ = self._q_views()
         nt = (seq_len + TT - 1) // TT
         codes = unpack_key_tiles(kb[b, :, :nt].reshape(-1, 832)).reshape(
-            self.H, nt * TT, 32)
-        meta = km[b, :, :nt].reshape(self.H, nt * TT, 4)
+            self.H, nt * TT, 32)[:, :seq_len]
+        meta = km[b, :, :nt].reshape(self.H, nt * TT, 4)[:, :seq_len]
+        # only stored tokens are dequantized (slots past seq_len may hold any
+        # bytes, NaN scales included)
         hi = quant.dequantize(codes[..., :8], meta[..., 0], meta[..., 1])
         lo = quant.dequantize(codes[..., 8:], meta[..., 2], meta[..., 3])
-        x = np.concatenate([hi, lo], axis=-1)[:, :seq_len]
+        x = np.concatenate([hi, lo], axis=-1)
         return np.transpose(x, (1, 0, 2))
 
     def value_latents(self, b, seq_len):
@@ -347,5 +349,8 @@ class Cache:
         g = self.rv // 32
         s = np.transpose(vm[b, :nt, 0], (0, 2, 1))                  # [nt,64,G]
         z = np.transpose(vm[b, :nt, 1], (0, 2, 1))
-        x = quant.dequantize(codes.reshape(nt, TT, g, 32), s, z)
-        return x.reshape(nt * TT, self.rv)[:seq_len]
+        codes = codes.reshape(nt * TT, g, 32)[:seq_len]
+        s = s.reshape(nt * TT, g)[:seq_len]
+        z = z.reshape(nt * TT, g)[:seq_len]
+        x = quant.dequantize(codes, s, z)
+        return x.reshape(seq_len, self.rv)

@@ -2,8 +2,9 @@
 
 Per case:
 * z_debug (the GPU's Z = X [A_key | A_value], bf16 inputs, fp32 result) is
-  compared with X A in fp64: max|gpu - ref| / max|ref| <= 1e-4 (bf16
-  products are exact in fp32; the bound covers fp32 accumulation over D);
+  compared with the oracle's projection (X A in fp64, rounded to fp32):
+  max|gpu - ref| / max|ref| <= 1e-4 (bf16 products are exact in fp32; the
+  bound covers fp32 accumulation over D);
 * the cache bytes after the call equal, bit for bit, the oracle packer
   applied to the GPU's z_debug on top of the same context bytes;
 * the output equals oracle causal attention over those same bytes (query i
@@ -80,10 +81,12 @@ def run_prefill(ctx, chunk, batch=1, q_scale=1.0, rows=None, heads=None,
     got = out.cpu().numpy().astype(np.float64)
     z = zdbg.cpu().numpy()
 
-    # projection
-    zref = np.einsum("bcd,dn->bcn", x.astype(np.float64),
-                     np.concatenate([ak, av], axis=1).astype(np.float64))
-    zerr = rel_err(z.astype(np.float64), zref)
+    # projection: the oracle's Z = X A (review Algorithm 2, step 1)
+    zref = []
+    for b in range(batch):
+        zk_ref, zv_ref = oa.project_latents(x[b], ak, av, w.n_kv_heads, w.key_rank)
+        zref.append(np.concatenate([zk_ref.reshape(chunk, nk), zv_ref], axis=1))
+    zerr = rel_err(z.astype(np.float64), np.stack(zref).astype(np.float64))
     # packing of the GPU's latents
     o.append(z[:, :, :nk].reshape(batch, chunk, w.n_kv_heads, w.key_rank),
              z[:, :, nk:], ctx, chunk)

@@ -93,6 +93,9 @@ def test_every_bit_has_exactly_one_owner():
     assert seen.max() == 1
 
 
+# the buffers start as random bytes, read out as (meaningless, often NaN)
+# latents on purpose
+@pytest.mark.filterwarnings("ignore:invalid value encountered in cast")
 @pytest.mark.parametrize("kind", ["f32", "bf16", "q43"])
 def test_append_touches_only_its_tokens(kind):
     w = synth.WORKLOADS["l2_q43"].replace(batch=2, n_q_heads=4, n_kv_heads=4,
