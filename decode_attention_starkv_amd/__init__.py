@@ -36,7 +36,10 @@ ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
 class StarkvConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "key_rank",
-        "value_rank", "max_tokens", "cache_dtype", "rotate", "num_splits")]
+        "value_rank", "max_tokens", "cache_dtype", "hi_bits", "lo_bits",
+        "group_size", "key_hi_channels", "value_hi_channels", "rotate",
+        "num_splits")] + [("rope_theta", ctypes.c_float),
+                          ("key_ranks", ctypes.POINTER(ctypes.c_int32))]
 
 
 class StarkvCache(ctypes.Structure):
@@ -95,11 +98,30 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 def make_config(batch, n_q_heads, n_kv_heads, head_dim, key_rank, value_rank,
-                max_tokens, cache_dtype, rotate=False, num_splits=0) -> StarkvConfig:
+                max_tokens, cache_dtype, rotate=False, num_splits=0, *,
+                hi_bits=None, lo_bits=None, group_size=None,
+                key_hi_channels=None, value_hi_channels=None,
+                rope_theta=0.0, key_ranks=None) -> StarkvConfig:
+    """starkv_config; the quantized cache's layout fields default to the
+    4/3-bit split with the leading quarter of the channels at 4 bits and
+    groups of 32 (zeros for unquantized caches)."""
     dt = DTYPES[cache_dtype] if isinstance(cache_dtype, str) else int(cache_dtype)
-    return StarkvConfig(batch, n_q_heads, n_kv_heads, head_dim, key_rank,
-                        value_rank, max_tokens, dt, int(bool(rotate)),
-                        num_splits)
+    quant = dt == CACHE_Q43
+
+    def pick(v, q_default):
+        return (q_default if quant else 0) if v is None else int(v)
+
+    cfg = StarkvConfig(batch, n_q_heads, n_kv_heads, head_dim, key_rank,
+                       value_rank, max_tokens, dt, pick(hi_bits, 4),
+                       pick(lo_bits, 3), pick(group_size, 32),
+                       pick(key_hi_channels, key_rank // 4),
+                       pick(value_hi_channels, value_rank // 4),
+                       int(bool(rotate)), num_splits, float(rope_theta), None)
+    if key_ranks is not None:
+        arr = (ctypes.c_int32 * len(key_ranks))(*[int(r) for r in key_ranks])
+        cfg._key_ranks_buf = arr          # keeps the host array alive
+        cfg.key_ranks = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return cfg
 
 
 def _ptr(t) -> int | None:

@@ -18,22 +18,62 @@ int check_config(const starkv_config* c) {
       c->max_tokens < kTile || c->max_tokens % kTile != 0 ||
       c->n_q_heads % c->n_kv_heads != 0 || c->num_splits < 0 ||
       c->cache_dtype < STARKV_CACHE_F32 || c->cache_dtype > STARKV_CACHE_Q43 ||
-      (c->rotate != 0 && c->rotate != 1))
+      (c->rotate != 0 && c->rotate != 1) || !(c->rope_theta >= 0.0f) ||
+      c->rope_theta == std::numeric_limits<float>::infinity())
     return STARKV_EINVAL;
+  const bool quant = c->cache_dtype == STARKV_CACHE_Q43;
+  if (quant) {
+    // the precision split of section 6.1: two blocks, each at its own width
+    if (c->hi_bits < 1 || c->hi_bits > 8 || c->lo_bits < 1 || c->lo_bits > 8 ||
+        c->group_size < 1 || c->key_hi_channels < 0 ||
+        c->key_hi_channels > c->key_rank || c->value_hi_channels < 0 ||
+        c->value_hi_channels > c->value_rank)
+      return STARKV_EINVAL;
+  } else if (c->hi_bits != 0 || c->lo_bits != 0 || c->group_size != 0 ||
+             c->key_hi_channels != 0 || c->value_hi_channels != 0) {
+    return STARKV_EINVAL;   // unquantized caches have no precision split
+  }
+  if (c->key_ranks) {
+    for (int g = 0; g < c->n_kv_heads; ++g)
+      if (c->key_ranks[g] < 8 || c->key_ranks[g] % 8 != 0 ||
+          c->key_ranks[g] > c->key_rank)
+        return STARKV_EINVAL;
+    return STARKV_EUNSUPPORTED;
+  }
+  if (c->rope_theta > 0.0f) return STARKV_EUNSUPPORTED;
   const int g = c->n_q_heads / c->n_kv_heads;
   if (c->n_q_heads > kMaxQHeads || (g != 1 && g != 2 && g != 4 && g != 8))
     return STARKV_EUNSUPPORTED;
   if (c->head_dim % 16 != 0 || c->head_dim > 256) return STARKV_EUNSUPPORTED;
   if (c->value_rank % 32 != 0 || c->value_rank > 1024) return STARKV_EUNSUPPORTED;
-  if (c->cache_dtype == STARKV_CACHE_Q43) {
+  if (quant) {
     if (c->key_rank != 32 || c->value_rank % 256 != 0 ||
         (c->n_kv_heads > 4 && c->n_kv_heads % 4 != 0))
+      return STARKV_EUNSUPPORTED;
+    if (c->hi_bits != 4 || c->lo_bits != 3 || c->group_size != 32 ||
+        c->key_hi_channels != c->key_rank / 4 ||
+        c->value_hi_channels != c->value_rank / 4)
+      return STARKV_EUNSUPPORTED;
+    // the rotation blocks (largest power of two dividing each block width)
+    // stay within one wave's 256 channels, where the inverse rotation of
+    // the merge runs in registers
+    if (c->rotate && (pow2_divisor(c->value_hi_channels) > 256 ||
+                      pow2_divisor(c->value_rank - c->value_hi_channels) > 256 ||
+                      pow2_divisor(c->key_hi_channels) > 8 ||
+                      pow2_divisor(c->key_rank - c->key_hi_channels) > 8))
       return STARKV_EUNSUPPORTED;
   } else {
     if (c->rotate) return STARKV_EUNSUPPORTED;
     if (c->key_rank % 8 != 0 || c->key_rank > 64) return STARKV_EUNSUPPORTED;
   }
   return STARKV_OK;
+}
+
+// The configuration is valid and a decode kernel exists for it.
+int check_decode_config(const starkv_config* c) {
+  const int st = check_config(c);
+  if (st != STARKV_OK) return st;
+  return decode_supported(make_dims(*c)) ? STARKV_OK : STARKV_EUNSUPPORTED;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -99,6 +139,7 @@ size_t starkv_workspace_bytes(const starkv_config* cfg, int32_t op,
   if (check_config(cfg) != STARKV_OK || n_tokens < 1) return 0;
   const Dims d = make_dims(*cfg);
   if (op == STARKV_OP_DECODE) {
+    if (!decode_supported(d)) return 0;
     if (n_tokens > cfg->max_tokens) return 0;
     return decode_ws_layout(d, choose_splits(*cfg, n_tokens)).total;
   }
@@ -107,7 +148,7 @@ size_t starkv_workspace_bytes(const starkv_config* cfg, int32_t op,
 }
 
 int32_t starkv_decode_splits(const starkv_config* cfg, int32_t seq_len) {
-  if (check_config(cfg) != STARKV_OK || seq_len < 1) return 0;
+  if (check_decode_config(cfg) != STARKV_OK || seq_len < 1) return 0;
   return choose_splits(*cfg, seq_len);
 }
 
@@ -131,7 +172,7 @@ static int decode_impl(const starkv_config* cfg, const starkv_cache* cache,
                        const void* B_value, float sm_scale, float* out,
                        void* workspace, size_t ws_bytes, hipStream_t stream,
                        hipEvent_t* events) {
-  int st = check_config(cfg);
+  int st = check_decode_config(cfg);
   if (st != STARKV_OK) return st;
   if ((st = check_cache(cfg, cache)) != STARKV_OK) return st;
   if (seq_len < 1) return STARKV_EINVAL;

@@ -7,8 +7,9 @@
 //           (eq. 2 read right to left).
 //   split   per (sequence, token split): latent scores, online softmax, then
 //           the stacked-head probabilities P [Hq x tokens] times the shared
-//           value latent Z_v on MFMA (section 5.3: "Computing P Z_V turns
-//           multiple vector-style reductions into a matrix multiplication").
+//           value latent Z_v on MFMA (section 5.3 / eq. 12: stacking the
+//           heads' probability rows makes the per-head weighted sums one
+//           matrix product against the shared latent).
 //   merge   partial (m, l, o) of the splits combined by the attention
 //           decomposition theorem (CaliDrop review: attention over disjoint
 //           token subsets, weighted by each subset's share of the exp-sum),
@@ -1397,6 +1398,10 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
 }  // namespace
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool decode_supported(const Dims& d) {
+  return d.dtype != STARKV_CACHE_Q43 || q43_kernel(d) != nullptr;
+}
 
 int decode_groups_per_cu(const Dims& d) {
   if (d.dtype != STARKV_CACHE_Q43) return 1;

@@ -18,6 +18,7 @@ constexpr int kMaxSplits = 1024;   // decode token splits per sequence
 // Shape of one call, copied by value into every kernel.
 struct Dims {
   int B, Hq, Hkv, G, dh, rk, rv, Tmax, NT, dtype, rotate;
+  float rope_theta;  // 0: no rotary position embedding
 };
 
 inline Dims make_dims(const starkv_config& c) {
@@ -33,6 +34,7 @@ inline Dims make_dims(const starkv_config& c) {
   d.NT = c.max_tokens / kTile;
   d.dtype = c.cache_dtype;
   d.rotate = c.rotate;
+  d.rope_theta = c.rope_theta;
   return d;
 }
 
@@ -70,11 +72,17 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache,
                           const PrefillWs& lay, hipStream_t s,
                           hipEvent_t* events = nullptr);
 bool prefill_supported(const Dims& d);
+// A decode split kernel exists for the shape (decode.hip).
+bool decode_supported(const Dims& d);
 
 // Streaming-read measurement pass (stream.hip).
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
-// fp32 value nearest to 1/sqrt(m) for the Walsh-Hadamard block sizes used.
+// fp32 value nearest to 1/sqrt(m) for a Walsh-Hadamard block of m channels
+// (m a power of two, 1 <= m <= kMaxRotBlock); 0 otherwise, which the host
+// validation never lets through (a zero would show as an all-zero output,
+// not as a plausible wrong one).
+constexpr int kMaxRotBlock = 1024;
 __host__ __device__ inline float inv_sqrt_pow2(int m) {
   switch (m) {
     case 1: return 1.0f;
@@ -85,7 +93,10 @@ __host__ __device__ inline float inv_sqrt_pow2(int m) {
     case 32: return __builtin_bit_cast(float, 0x3E3504F3u);
     case 64: return 0.125f;
     case 128: return __builtin_bit_cast(float, 0x3DB504F3u);
-    default: return 0.0625f;  // 256
+    case 256: return 0.0625f;
+    case 512: return __builtin_bit_cast(float, 0x3D3504F3u);
+    case 1024: return 0.03125f;
+    default: return 0.0f;
   }
 }
 

@@ -24,8 +24,11 @@
  *   - Pointers marked (host) are host memory; every other pointer is device
  *     memory on the current HIP device, 16-byte aligned.
  *   - The caller allocates and frees everything (cache, inputs, outputs,
- *     workspace).  The library keeps no state between calls and allocates
- *     nothing.
+ *     workspace).  The library allocates no device memory on these calls.
+ *     Its only state is host-side: a memo of the runtime's occupancy answer
+ *     per decode kernel and device (mutex-guarded, filled on first use), from
+ *     which the automatic split count is derived.  (starkv_decode_noalloc
+ *     below is the exception: it uses a fixed device array of the library.)
  *   - Compute calls are asynchronous on `stream` and never synchronize.
  *   - Arguments are validated on the host before any HIP call; a failed
  *     validation returns a negative status and touches no memory.  A kernel
@@ -69,12 +72,26 @@ typedef enum {
                             most 32 channels, fp16 scale and zero per group */
 } starkv_cache_dtype;
 
-/* (host) Shape of one attention layer and its cache. */
+/* (host) Shape of one attention layer and its cache.
+ *
+ * The quantized cache (STARKV_CACHE_Q43) follows section 6.1 of the review:
+ * the retained latent channels split into a leading (outlier) block and a
+ * trailing (inlier) block, each optionally Walsh-Hadamard rotated on its own
+ * (eq. 13) and stored at its own precision (eq. 14), with an asymmetric
+ * fp16 scale and zero per group of at most group_size consecutive channels
+ * of one token inside one block.  The five layout fields below state that
+ * split explicitly; this build has kernels for hi_bits = 4, lo_bits = 3,
+ * group_size = 32, key_hi_channels = key_rank / 4 and value_hi_channels =
+ * value_rank / 4 (the model card's top_fraction = 0.25 recipe, 3.25 bits per
+ * channel on average) and returns STARKV_EUNSUPPORTED for any other
+ * combination.  For F32 / BF16 caches the five fields must be 0. */
 typedef struct starkv_config {
   int32_t batch;       /* B */
   int32_t n_q_heads;   /* Hq <= 32, a multiple of n_kv_heads */
-  int32_t n_kv_heads;  /* Hkv; Hq / Hkv in {1, 2, 4, 8}; Q43 with Hkv > 4
-                          needs Hkv a multiple of 4 */
+  int32_t n_kv_heads;  /* Hkv; Hq / Hkv in {1, 2, 4, 8}; for Q43, Hkv in
+                          {1, 2, 4, 8, 16, 32} with a decode kernel for the
+                          (Hq / Hkv, Hkv) pair (starkv_decode_splits returns
+                          0 when there is none) */
   int32_t head_dim;    /* d_h, a multiple of 16, <= 256 */
   int32_t key_rank;    /* r_k per KV head: <= 64 and a multiple of 8 for
                           F32/BF16; exactly 32 for Q43 */
@@ -82,10 +99,27 @@ typedef struct starkv_config {
                           a multiple of 32, <= 1024 (Q43: multiple of 256) */
   int32_t max_tokens;  /* cache capacity T_max, a multiple of 64 */
   int32_t cache_dtype; /* starkv_cache_dtype */
+  int32_t hi_bits;     /* Q43: bits of the leading block (4) */
+  int32_t lo_bits;     /* Q43: bits of the trailing block (3) */
+  int32_t group_size;  /* Q43: channels per quantization group (32) */
+  int32_t key_hi_channels;   /* Q43: leading key channels per head at
+                                hi_bits (key_rank / 4) */
+  int32_t value_hi_channels; /* Q43: leading value channels at hi_bits
+                                (value_rank / 4) */
   int32_t rotate;      /* Q43 only: 1 = latents are block-Hadamard rotated
                           by starkv_append before quantization (eq. 13); the
                           factors passed to decode/prefill stay unrotated */
   int32_t num_splits;  /* decode token splits per sequence; 0 = automatic */
+  float rope_theta;    /* 0: no rotary position embedding.  > 0: RoPE base
+                          (section 5.3 and Algorithm 2 step 4c: keys stay
+                          pre-RoPE latents, reconstructed and rotated inside
+                          the scoring); see starkv_decode */
+  const int32_t* key_ranks; /* (host) NULL: every KV head has key_rank
+                          channels.  Otherwise n_kv_heads per-head ranks
+                          (section 4 / Fig. 2: learned per-head ranks; eq. 15
+                          sums them), each a multiple of 8 and <= key_rank;
+                          the key cache then stores head g with key_ranks[g]
+                          channels (F32/BF16 caches only) */
 } starkv_config;
 
 /* Device buffers of one layer's cache.  Byte layout ("format v1", tiles of

@@ -99,6 +99,26 @@ def test_config_validation_codes():
         (dict(value_rank=1056), sk.STARKV_EUNSUPPORTED),
         (dict(head_dim=100), sk.STARKV_EUNSUPPORTED),
         (dict(cache_dtype="bf16", rotate=True), sk.STARKV_EUNSUPPORTED),
+        # the precision split of the quantized cache (review section 6.1,
+        # eq. 14): fields out of range are invalid, other splits unsupported
+        (dict(hi_bits=0), sk.STARKV_EINVAL),
+        (dict(lo_bits=9), sk.STARKV_EINVAL),
+        (dict(group_size=0), sk.STARKV_EINVAL),
+        (dict(key_hi_channels=33), sk.STARKV_EINVAL),
+        (dict(value_hi_channels=-1), sk.STARKV_EINVAL),
+        (dict(hi_bits=8), sk.STARKV_EUNSUPPORTED),
+        (dict(lo_bits=2), sk.STARKV_EUNSUPPORTED),
+        (dict(group_size=16), sk.STARKV_EUNSUPPORTED),
+        (dict(key_hi_channels=6), sk.STARKV_EUNSUPPORTED),     # a 20:80 split
+        (dict(value_hi_channels=204), sk.STARKV_EUNSUPPORTED),
+        # unquantized caches have no precision split
+        (dict(cache_dtype="bf16", rotate=False, hi_bits=4), sk.STARKV_EINVAL),
+        (dict(cache_dtype="bf16", rotate=False, group_size=32), sk.STARKV_EINVAL),
+        (dict(rope_theta=-1.0), sk.STARKV_EINVAL),
+        (dict(rope_theta=float("nan")), sk.STARKV_EINVAL),
+        (dict(rope_theta=float("inf")), sk.STARKV_EINVAL),
+        (dict(cache_dtype="bf16", rotate=False, key_ranks=[7] * 32), sk.STARKV_EINVAL),
+        (dict(cache_dtype="bf16", rotate=False, key_ranks=[40] * 32), sk.STARKV_EINVAL),
     ]
     cache = _fake_cache()
     for kw, code in bad:
@@ -107,6 +127,34 @@ def test_config_validation_codes():
         st = lib.starkv_append(ctypes.byref(cfg), ctypes.byref(cache),
                                0x1000, 0x2000, 0, 1, None)
         assert st == code, (kw, st)
+
+
+def test_default_layout_fields_are_the_quarter_split():
+    w = synth.WORKLOADS["l2_q43"]
+    cfg = _cfg(w)
+    assert (cfg.hi_bits, cfg.lo_bits, cfg.group_size, cfg.key_hi_channels,
+            cfg.value_hi_channels) == (4, 3, 32, 8, 256)
+    plain = _cfg(synth.WORKLOADS["l2_bf16"])
+    assert (plain.hi_bits, plain.lo_bits, plain.group_size,
+            plain.key_hi_channels, plain.value_hi_channels) == (0, 0, 0, 0, 0)
+    assert ctypes.sizeof(sk.StarkvConfig) == 72
+
+
+def test_q43_shape_without_decode_kernel_is_rejected_before_launch():
+    """Twelve KV heads (three per score wave) have no decode kernel: the
+    cache and its append are fine, decode says so before any HIP call."""
+    lib = sk.load_library()
+    w = synth.WORKLOADS["l2_q43"]
+    for hq, hkv in ((12, 12), (24, 12), (20, 20), (28, 28)):
+        cfg = _cfg(w, n_q_heads=hq, n_kv_heads=hkv)
+        assert sk.starkv_cache_bytes(cfg, 0) > 0
+        assert sk.starkv_decode_splits(cfg, 1000) == 0
+        assert sk.starkv_workspace_bytes(cfg, sk.OP_DECODE, 1000) == 0
+        cache = _fake_cache()
+        st = lib.starkv_decode(ctypes.byref(cfg), ctypes.byref(cache), 100, 0x1000,
+                               0x2000, 0x3000, ctypes.c_float(0.1), 0x4000,
+                               0x5000, 1 << 30, None)
+        assert st == sk.STARKV_EUNSUPPORTED, (hq, hkv, st)
 
 
 def test_call_validation_before_any_hip_call():
