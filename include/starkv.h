@@ -33,8 +33,18 @@
  *   - Arguments are validated on the host before any HIP call; a failed
  *     validation returns a negative status and touches no memory.  A kernel
  *     launch failure returns STARKV_ELAUNCH.  No C++ exception crosses the ABI.
- *   - Inputs must be finite and latents must lie within the fp16 range for the
- *     quantized cache; otherwise results are unspecified.
+ *   - Inputs must be finite; otherwise results are unspecified.  Decode
+ *     keeps three intermediates in fp16 (the projected query q~, the
+ *     4/3-bit value operand P * 2^k * group scale with P <= 4 and 2^k <= 64,
+ *     and each split's partial rows divided by their exp-sum), so:
+ *       - quantized caches: latents within the fp16 range (their scale and
+ *         zero are fp16), and value group scales below 256 (a 3-bit group's
+ *         range below ~1.8e3, a 4-bit group's below ~1.5e4);
+ *       - BF16 caches: softmax-weighted averages of the value latents (the
+ *         partial rows) within the fp16 range, |.| < 65504.
+ *     Measured within these limits (value latents scaled 1e-3 .. 1e5, key
+ *     latents 1e-2 .. 1e3, queries sharpened 32x) the output stays within
+ *     2e-3 of the fp64 oracle relative to its largest entry.
  *   - Calls that overlap on the same cache buffers race; calls on disjoint
  *     buffers may run concurrently on different streams.
  */
