@@ -1435,7 +1435,8 @@ DecodeWs decode_ws_layout(const Dims& d, int splits) {
   w.qt = off;
   off += align256((size_t)d.B * d.Hq * kPlainRec * 4);
   w.part_o = off;
-  off += align256((size_t)d.B * splits * d.Hq * d.rv * 4);
+  // partial rows: fp32 for an F32 cache, fp16 (divided by l) otherwise
+  off += align256((size_t)d.B * splits * d.Hq * d.rv * (d.dtype == STARKV_CACHE_F32 ? 4 : 2));
   w.part_ml = off;
   off += align256((size_t)d.B * splits * d.Hq * 2 * 4);
   w.obar = off;
