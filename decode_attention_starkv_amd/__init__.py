@@ -30,7 +30,8 @@ OP_DECODE, OP_PREFILL = 0, 1
 ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_decode_splits", "starkv_append", "starkv_decode",
                 "starkv_decode_profiled", "starkv_prefill",
-                "starkv_prefill_profiled", "starkv_stream_read", "starkv_strerror")
+                "starkv_prefill_profiled", "starkv_stream_read", "starkv_strerror",
+                "starkv_decode_noalloc", "starkv_noalloc_scratch_bytes")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -91,6 +92,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.starkv_prefill_profiled.restype = ctypes.c_int
     lib.starkv_stream_read.argtypes = [vp, sz, vp, vp]
     lib.starkv_stream_read.restype = ctypes.c_int
+    lib.starkv_decode_noalloc.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp,
+                                          vp, f32, vp, vp]
+    lib.starkv_decode_noalloc.restype = ctypes.c_int
+    lib.starkv_noalloc_scratch_bytes.argtypes = []
+    lib.starkv_noalloc_scratch_bytes.restype = sz
     lib.starkv_strerror.argtypes = [ctypes.c_int]
     lib.starkv_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -209,6 +215,21 @@ def starkv_decode(cfg, cache: LatentCache, seq_len: int, q, B_key, B_value,
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != STARKV_OK:
         raise StarkvError(st, "starkv_decode")
+
+
+def starkv_decode_noalloc(cfg, cache: LatentCache, seq_len: int, q, B_key,
+                          B_value, sm_scale: float, out, stream=None) -> None:
+    """starkv_decode with the library's fixed scratch array as workspace."""
+    cs = cache.struct
+    st = load_library().starkv_decode_noalloc(
+        ctypes.byref(cfg), ctypes.byref(cs), seq_len, _ptr(q), _ptr(B_key),
+        _ptr(B_value), sm_scale, _ptr(out), _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_decode_noalloc")
+
+
+def starkv_noalloc_scratch_bytes() -> int:
+    return load_library().starkv_noalloc_scratch_bytes()
 
 
 def starkv_decode_profiled(cfg, cache: LatentCache, seq_len: int, q, B_key,

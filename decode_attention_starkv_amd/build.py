@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libstarkv.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "stream.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "stream.hip",
+           "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

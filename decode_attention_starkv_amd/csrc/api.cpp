@@ -167,11 +167,14 @@ int starkv_append(const starkv_config* cfg, const starkv_cache* cache,
   return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
 }
 
-static int decode_impl(const starkv_config* cfg, const starkv_cache* cache,
-                       int32_t seq_len, const void* q, const void* B_key,
-                       const void* B_value, float sm_scale, float* out,
-                       void* workspace, size_t ws_bytes, hipStream_t stream,
-                       hipEvent_t* events) {
+}  // extern "C"
+
+namespace starkv {
+
+// Everything starkv_decode checks before it looks at the workspace.
+int validate_decode(const starkv_config* cfg, const starkv_cache* cache,
+                    int32_t seq_len, const void* q, const void* B_key,
+                    const void* B_value, const float* out, DecodeWs* lay) {
   int st = check_decode_config(cfg);
   if (st != STARKV_OK) return st;
   if ((st = check_cache(cfg, cache)) != STARKV_OK) return st;
@@ -180,13 +183,27 @@ static int decode_impl(const starkv_config* cfg, const starkv_cache* cache,
   if (!q || !B_key || !B_value || !out || !aligned16(q) || !aligned16(B_key) ||
       !aligned16(B_value) || !aligned16(out))
     return STARKV_EINVAL;
-  const Dims d = make_dims(*cfg);
-  const DecodeWs lay = decode_ws_layout(d, choose_splits(*cfg, seq_len));
+  *lay = decode_ws_layout(make_dims(*cfg), choose_splits(*cfg, seq_len));
+  return STARKV_OK;
+}
+
+}  // namespace starkv
+
+extern "C" {
+
+static int decode_impl(const starkv_config* cfg, const starkv_cache* cache,
+                       int32_t seq_len, const void* q, const void* B_key,
+                       const void* B_value, float sm_scale, float* out,
+                       void* workspace, size_t ws_bytes, hipStream_t stream,
+                       hipEvent_t* events) {
+  DecodeWs lay;
+  const int st = validate_decode(cfg, cache, seq_len, q, B_key, B_value, out, &lay);
+  if (st != STARKV_OK) return st;
   if (!workspace || !aligned16(workspace) || ws_bytes < lay.total)
     return STARKV_EWORKSPACE;
-  hipError_t e = launch_decode(d, *cache, seq_len, q, B_key, B_value, sm_scale,
-                               out, static_cast<char*>(workspace), lay, stream,
-                               events);
+  hipError_t e = launch_decode(make_dims(*cfg), *cache, seq_len, q, B_key, B_value,
+                               sm_scale, out, static_cast<char*>(workspace), lay,
+                               stream, events);
   return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
 }
 

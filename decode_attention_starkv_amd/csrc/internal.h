@@ -48,6 +48,11 @@ DecodeWs decode_ws_layout(const Dims& d, int splits);
 // (1 when it cannot be asked, e.g. without a device).
 int decode_groups_per_cu(const Dims& d);
 int choose_splits(const starkv_config& c, int seq_len);
+// Host validation of a decode call short of the workspace (api.cpp): status,
+// and on success the workspace layout the call needs.
+int validate_decode(const starkv_config* cfg, const starkv_cache* cache,
+                    int32_t seq_len, const void* q, const void* B_key,
+                    const void* B_value, const float* out, DecodeWs* lay);
 
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_append(const Dims& d, const starkv_cache& cache,

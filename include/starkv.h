@@ -227,6 +227,31 @@ STARKV_API int starkv_decode_profiled(const starkv_config* cfg,
                                       void* workspace, size_t ws_bytes,
                                       hipStream_t stream, hipEvent_t* events);
 
+/* For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * starkv_decode -- same arguments except the workspace, same kernels, same
+ * results and errors -- but the workspace is a fixed array of the library,
+ * starkv_noalloc_scratch_bytes() = 64 MiB per device, held from the first
+ * call on a device until the process ends.  The call allocates nothing.
+ * Its first call on a device asks the runtime for that device's array
+ * address (a HIP call, done once per device).  Every call on one device
+ * shares its array: calls that overlap on one device (different streams, or
+ * different threads) race and give undefined results; calls on one stream
+ * are ordered.  Nothing in the array needs to start at zero: each call
+ * writes everything it reads.
+ * Errors: as starkv_decode; STARKV_EWORKSPACE when the shape needs more than
+ * starkv_noalloc_scratch_bytes() (starkv_workspace_bytes(cfg, DECODE,
+ * seq_len) tells), checked on the host before any HIP call. */
+STARKV_API int starkv_decode_noalloc(const starkv_config* cfg,
+                                     const starkv_cache* cache,
+                                     int32_t seq_len, const void* q,
+                                     const void* B_key, const void* B_value,
+                                     float sm_scale, float* out,
+                                     hipStream_t stream);
+
+/* (host) Size of the fixed scratch array starkv_decode_noalloc uses. */
+STARKV_API size_t starkv_noalloc_scratch_bytes(void);
+
 /* Chunked causal prefill of one chunk (review Algorithm 2, steps 1-3, then
  * causal attention over the stored cache):
  *   x       bf16 [B][C][D]          hidden states of the chunk

@@ -62,7 +62,7 @@ def test_workspace_and_splits():
     s = sk.starkv_decode_splits(cfg, w.seq_len)
     assert s == 16                      # 16 sequences x 16 splits = 256 groups
     ws = sk.starkv_workspace_bytes(cfg, sk.OP_DECODE, w.seq_len)
-    assert ws >= w.batch * s * w.n_q_heads * w.value_rank * 4
+    assert ws >= w.batch * s * w.n_q_heads * w.value_rank * 2   # fp16 rows
     assert sk.starkv_decode_splits(_cfg(w, num_splits=5), w.seq_len) == 5
     assert sk.starkv_decode_splits(cfg, 1) == 1
     assert sk.starkv_decode_splits(cfg, 65) == 2
@@ -155,6 +155,28 @@ def test_q43_shape_without_decode_kernel_is_rejected_before_launch():
                                0x2000, 0x3000, ctypes.c_float(0.1), 0x4000,
                                0x5000, 1 << 30, None)
         assert st == sk.STARKV_EUNSUPPORTED, (hq, hkv, st)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_hip_call():
+    lib = sk.load_library()
+    assert sk.starkv_noalloc_scratch_bytes() == 64 << 20
+    w = synth.WORKLOADS["l2_q43"]
+    big = _cfg(w, batch=512, max_tokens=4096)
+    assert sk.starkv_workspace_bytes(big, sk.OP_DECODE, 4096) > 64 << 20
+    cache = _fake_cache()
+    args = (0x1000, 0x2000, 0x3000, ctypes.c_float(0.1), 0x4000, None)
+    assert lib.starkv_decode_noalloc(ctypes.byref(big), ctypes.byref(cache), 4096,
+                                     *args) == sk.STARKV_EWORKSPACE
+    cfg = _cfg(w)
+    assert lib.starkv_decode_noalloc(ctypes.byref(cfg), ctypes.byref(cache), 0,
+                                     *args) == sk.STARKV_EINVAL
+    assert lib.starkv_decode_noalloc(ctypes.byref(cfg), ctypes.byref(cache),
+                                     w.max_tokens + 1, *args) == sk.STARKV_ECAPACITY
+    assert lib.starkv_decode_noalloc(ctypes.byref(cfg), ctypes.byref(cache), 100,
+                                     None, 0x2000, 0x3000, ctypes.c_float(0.1), 0x4000,
+                                     None) == sk.STARKV_EINVAL
+    # the metric shape fits
+    assert sk.starkv_workspace_bytes(cfg, sk.OP_DECODE, w.seq_len) <= 64 << 20
 
 
 def test_call_validation_before_any_hip_call():
