@@ -31,7 +31,8 @@ ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_decode_splits", "starkv_append", "starkv_decode",
                 "starkv_decode_profiled", "starkv_prefill",
                 "starkv_prefill_profiled", "starkv_stream_read", "starkv_strerror",
-                "starkv_decode_noalloc", "starkv_noalloc_scratch_bytes")
+                "starkv_decode_noalloc", "starkv_noalloc_scratch_bytes",
+                "starkv_decode_step", "starkv_decode_step_profiled")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -92,6 +93,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.starkv_prefill_profiled.restype = ctypes.c_int
     lib.starkv_stream_read.argtypes = [vp, sz, vp, vp]
     lib.starkv_stream_read.restype = ctypes.c_int
+    lib.starkv_decode_step.argtypes = [P(StarkvConfig), P(StarkvCache), vp, vp, i32, i32,
+                                       vp, vp, vp, f32, vp, vp, sz, vp]
+    lib.starkv_decode_step.restype = ctypes.c_int
+    lib.starkv_decode_step_profiled.argtypes = [P(StarkvConfig), P(StarkvCache), vp, vp,
+                                                i32, i32, vp, vp, vp, f32, vp, vp, sz,
+                                                vp, P(vp)]
+    lib.starkv_decode_step_profiled.restype = ctypes.c_int
     lib.starkv_decode_noalloc.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp,
                                           vp, f32, vp, vp]
     lib.starkv_decode_noalloc.restype = ctypes.c_int
@@ -215,6 +223,26 @@ def starkv_decode(cfg, cache: LatentCache, seq_len: int, q, B_key, B_value,
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != STARKV_OK:
         raise StarkvError(st, "starkv_decode")
+
+
+def starkv_decode_step(cfg, cache: LatentCache, z_key, z_value, pos: int, q,
+                       B_key, B_value, sm_scale: float, out, workspace,
+                       n: int | None = None, stream=None, events=None) -> None:
+    """Append tokens [pos, pos+n) then decode over pos + n tokens (one
+    call); `events`: five timing events (the profiled variant)."""
+    n = z_key.shape[1] if n is None else n
+    cs = cache.struct
+    args = (ctypes.byref(cfg), ctypes.byref(cs), _ptr(z_key), _ptr(z_value), pos, n,
+            _ptr(q), _ptr(B_key), _ptr(B_value), sm_scale, _ptr(out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    lib = load_library()
+    if events is None:
+        st = lib.starkv_decode_step(*args)
+    else:
+        handles = (ctypes.c_void_p * 5)(*(e.cuda_event for e in events))
+        st = lib.starkv_decode_step_profiled(*args, handles)
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_decode_step")
 
 
 def starkv_decode_noalloc(cfg, cache: LatentCache, seq_len: int, q, B_key,

@@ -207,6 +207,62 @@ static int decode_impl(const starkv_config* cfg, const starkv_cache* cache,
   return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
 }
 
+static int decode_step_impl(const starkv_config* cfg, const starkv_cache* cache,
+                            const float* z_key, const float* z_value, int32_t pos,
+                            int32_t n, const void* q, const void* B_key,
+                            const void* B_value, float sm_scale, float* out,
+                            void* workspace, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t* events) {
+  if (pos < 0 || n < 0) return STARKV_EINVAL;
+  if ((int64_t)pos + n > std::numeric_limits<int32_t>::max()) return STARKV_ECAPACITY;
+  DecodeWs lay;
+  const int st = validate_decode(cfg, cache, pos + n, q, B_key, B_value, out, &lay);
+  if (st != STARKV_OK) return st;
+  if (n > 0 && (!z_key || !z_value || !aligned16(z_key) || !aligned16(z_value)))
+    return STARKV_EINVAL;
+  if (!workspace || !aligned16(workspace) || ws_bytes < lay.total)
+    return STARKV_EWORKSPACE;
+  const Dims d = make_dims(*cfg);
+  char* ws = static_cast<char*>(workspace);
+  if (events) (void)hipEventRecord(events[0], stream);
+  hipError_t e = hipSuccess;
+  bool fused = false;
+  if (n > 0) {
+    if (d.dtype == STARKV_CACHE_Q43) {
+      e = launch_append_qproj(d, *cache, z_key, z_value, pos, n, q, B_key,
+                              sm_scale * 1.4426950408889634f, ws + lay.qt, stream);
+      fused = true;
+    } else {
+      e = launch_append(d, *cache, z_key, z_value, pos, n, stream);
+    }
+    if (e != hipSuccess) return STARKV_ELAUNCH;
+  }
+  e = launch_decode(d, *cache, pos + n, q, B_key, B_value, sm_scale, out, ws, lay,
+                    stream, events, fused, true);
+  return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
+}
+
+int starkv_decode_step(const starkv_config* cfg, const starkv_cache* cache,
+                       const float* z_key, const float* z_value, int32_t pos,
+                       int32_t n, const void* q, const void* B_key,
+                       const void* B_value, float sm_scale, float* out,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return decode_step_impl(cfg, cache, z_key, z_value, pos, n, q, B_key, B_value,
+                          sm_scale, out, workspace, ws_bytes, stream, nullptr);
+}
+
+int starkv_decode_step_profiled(const starkv_config* cfg, const starkv_cache* cache,
+                                const float* z_key, const float* z_value,
+                                int32_t pos, int32_t n, const void* q,
+                                const void* B_key, const void* B_value,
+                                float sm_scale, float* out, void* workspace,
+                                size_t ws_bytes, hipStream_t stream,
+                                hipEvent_t* events) {
+  if (!events) return STARKV_EINVAL;
+  return decode_step_impl(cfg, cache, z_key, z_value, pos, n, q, B_key, B_value,
+                          sm_scale, out, workspace, ws_bytes, stream, events);
+}
+
 int starkv_decode(const starkv_config* cfg, const starkv_cache* cache,
                   int32_t seq_len, const void* q, const void* B_key,
                   const void* B_value, float sm_scale, float* out,

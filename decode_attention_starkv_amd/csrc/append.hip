@@ -10,6 +10,7 @@
 //   zero  = fp16(min) rounded toward -inf, scale = fp16((max - zero) / L)
 //           rounded toward +inf, code = clamp(rint((x - zero) / scale), 0, L).
 #include "internal.h"
+#include "qproj.h"   // before the pragma: the query projection keeps its own FP rules
 
 #pragma clang fp contract(off)
 
@@ -349,7 +350,51 @@ __global__ __launch_bounds__(256) void append_q43_kernel(
   append_q43_values(zv, value, vmeta, d, pos, n, cb, rest % tiles, rest / tiles, codes);
 }
 
+// A decode step's first launch: the append of the new tokens (blocks
+// [0, append_blocks), exactly append_q43_kernel's work) and the query
+// projection (one block per (b, h) after them) are independent, so they
+// share one launch and their memory latencies overlap.
+__global__ __launch_bounds__(256) void step_q43_kernel(
+    const float* __restrict__ zk, const float* __restrict__ zv,
+    uint8_t* __restrict__ key, uint16_t* __restrict__ kmeta,
+    uint8_t* __restrict__ value, uint16_t* __restrict__ vmeta, Dims d, int pos,
+    int n, int key_blocks, int tiles, int append_blocks,
+    const void* __restrict__ q, const void* __restrict__ bk, float qscale,
+    void* __restrict__ qt) {
+  __shared__ uint8_t codes[kTile][256];
+  const int blk = blockIdx.x;
+  if (blk >= append_blocks) {
+    qproj_block<STARKV_CACHE_Q43>(q, bk, d, qscale, qt, blk - append_blocks);
+    return;
+  }
+  if (blk < key_blocks) {
+    append_q43_keys(zk, key, kmeta, d, pos, n, (size_t)blk * 256 + threadIdx.x);
+    return;
+  }
+  const int vb = blk - key_blocks;
+  const int ncb = d.rv / 256;
+  const int cb = vb % ncb, rest = vb / ncb;
+  append_q43_values(zv, value, vmeta, d, pos, n, cb, rest % tiles, rest / tiles, codes);
+}
+
 }  // namespace
+
+hipError_t launch_append_qproj(const Dims& d, const starkv_cache& cache,
+                               const float* zk, const float* zv, int pos, int n,
+                               const void* q, const void* bk, float qscale,
+                               void* qt, hipStream_t s) {
+  const int T = 256;
+  const size_t nk = (size_t)d.B * n * d.Hkv;
+  const size_t key_blocks = (nk + T - 1) / T;
+  const int tiles = (pos + n - 1) / kTile - pos / kTile + 1;
+  const size_t append_blocks = key_blocks + (size_t)(d.rv / 256) * tiles * d.B;
+  const size_t blocks = append_blocks + (size_t)d.B * d.Hq;
+  step_q43_kernel<<<(unsigned)blocks, T, 0, s>>>(
+      zk, zv, static_cast<uint8_t*>(cache.key), static_cast<uint16_t*>(cache.key_meta),
+      static_cast<uint8_t*>(cache.value), static_cast<uint16_t*>(cache.value_meta), d,
+      pos, n, (int)key_blocks, tiles, (int)append_blocks, q, bk, qscale, qt);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const Dims& d, const starkv_cache& cache,
                          const float* zk, const float* zv, int pos, int n,

@@ -58,11 +58,21 @@ int validate_decode(const starkv_config* cfg, const starkv_cache* cache,
 hipError_t launch_append(const Dims& d, const starkv_cache& cache,
                          const float* zk, const float* zv, int pos, int n,
                          hipStream_t s);
+// Decode launches.  With `qproj_done` the query records are already in the
+// workspace (written by launch_append_qproj) and the query projection is not
+// launched again; with `first_mark_done` the caller has recorded events[0].
 hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,
                          const void* q, const void* bk, const void* bv,
                          float sm_scale, float* out, char* ws,
                          const DecodeWs& lay, hipStream_t s,
-                         hipEvent_t* events = nullptr);
+                         hipEvent_t* events = nullptr, bool qproj_done = false,
+                         bool first_mark_done = false);
+// One launch for the append of tokens [pos, pos+n) of a 4/3-bit cache and the
+// decode query projection into `qt` (the workspace's query records).
+hipError_t launch_append_qproj(const Dims& d, const starkv_cache& cache,
+                               const float* zk, const float* zv, int pos, int n,
+                               const void* q, const void* bk, float qscale,
+                               void* qt, hipStream_t s);
 
 // Workspace carve-up of one prefill call (byte offsets, 256-aligned).
 struct PrefillWs {

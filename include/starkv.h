@@ -211,6 +211,32 @@ STARKV_API int starkv_decode(const starkv_config* cfg, const starkv_cache* cache
                   const void* B_value, float sm_scale, float* out,
                   void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* One decode step (review Algorithm 2, steps 3-7): append tokens [pos,
+ * pos + n) of every sequence, then decode over seq_len = pos + n tokens --
+ * exactly starkv_append followed by starkv_decode (same bytes, same output),
+ * but for the 4/3-bit cache the append and the query projection share one
+ * launch (they are independent), which saves a launch and overlaps their
+ * memory latencies.  Arguments as in those two calls; n == 0 decodes only.
+ * Workspace: starkv_workspace_bytes(cfg, DECODE, pos + n).
+ * Errors: EINVAL (pos < 0, n < 0, null or misaligned pointer), ECAPACITY
+ * (pos + n > max_tokens), EWORKSPACE, EUNSUPPORTED, ELAUNCH. */
+STARKV_API int starkv_decode_step(const starkv_config* cfg,
+                                  const starkv_cache* cache, const float* z_key,
+                                  const float* z_value, int32_t pos, int32_t n,
+                                  const void* q, const void* B_key,
+                                  const void* B_value, float sm_scale,
+                                  float* out, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* starkv_decode_step that also records events[0..4] on `stream`: before the
+ * append (and query projection), before the split kernel, before the merge,
+ * before the up-projection and after it (as starkv_decode_profiled). */
+STARKV_API int starkv_decode_step_profiled(
+    const starkv_config* cfg, const starkv_cache* cache, const float* z_key,
+    const float* z_value, int32_t pos, int32_t n, const void* q,
+    const void* B_key, const void* B_value, float sm_scale, float* out,
+    void* workspace, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
 /* starkv_decode that also records events[0..4] (host array of created
  * hipEvent_t) on `stream`: before the query projection, before the split
  * kernel, before the merge, before the value up-projection and after it, so

@@ -179,6 +179,25 @@ def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_hip_call():
     assert sk.starkv_workspace_bytes(cfg, sk.OP_DECODE, w.seq_len) <= 64 << 20
 
 
+def test_decode_step_validation_before_any_hip_call():
+    lib = sk.load_library()
+    w = synth.WORKLOADS["l2_q43"]
+    cfg = _cfg(w)
+    cp, cc = ctypes.byref(cfg), ctypes.byref(_fake_cache())
+    tail = (0x3000, 0x4000, 0x5000, ctypes.c_float(0.1), 0x6000, 0x7000, 1 << 30, None)
+    step = lambda zk, zv, pos, n, *t: lib.starkv_decode_step(cp, cc, zk, zv, pos, n, *t)
+    assert step(0x1000, 0x2000, -1, 1, *tail) == sk.STARKV_EINVAL
+    assert step(0x1000, 0x2000, 5, -1, *tail) == sk.STARKV_EINVAL
+    assert step(0x1000, 0x2000, w.max_tokens, 1, *tail) == sk.STARKV_ECAPACITY
+    assert step(0x1000, 0x2000, 0, 0, *tail) == sk.STARKV_EINVAL          # seq_len 0
+    assert step(None, 0x2000, 5, 1, *tail) == sk.STARKV_EINVAL
+    assert step(0x1004, 0x2000, 5, 1, *tail) == sk.STARKV_EINVAL
+    small = tail[:6] + (16, None)
+    assert step(0x1000, 0x2000, 5, 1, *small) == sk.STARKV_EWORKSPACE
+    assert lib.starkv_decode_step_profiled(cp, cc, 0x1000, 0x2000, 5, 1, *tail,
+                                           None) == sk.STARKV_EINVAL
+
+
 def test_call_validation_before_any_hip_call():
     w = synth.WORKLOADS["l2_q43"]
     lib = sk.load_library()
