@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    p.add_argument("--hidden", type=int, default=0,
+                   help="decode through the fused value/output factor into a "
+                        "hidden size of this width (starkv_decode_hidden)")
     p.add_argument("--t-sweep", action="store_true",
                    help="decode at T = 8K .. 128K, one JSON line per T")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -329,6 +332,100 @@ def run_prefill(args, w, torch, sk, synth):
     print(json.dumps(res))
 
 
+def run_hidden(args, w, torch, sk, synth):
+    """Decode that ends in the hidden size through the fused factor
+    F_h = B_value[g(h)]^T O_h (review section 5.3, eq. 12; Algorithm 2, steps
+    7-8).  One step = one starkv_decode_hidden call; the roofline is the
+    hidden GEMM's (it streams F once)."""
+    seq_len = args.seq_len or w.seq_len
+    D = args.hidden
+    cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                         w.key_rank, w.value_rank, ((seq_len + 63) // 64) * 64,
+                         w.cache, w.rotate, args.splits)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# workload {w.name} B={w.batch} T={seq_len} hidden={D}", file=sys.stderr,
+          flush=True)
+    cache = sk.LatentCache(cfg)
+    fill_cache(w, cfg, cache, seq_len, sk, torch)
+    bk, bv = synth.factors(w)
+    bf = torch.bfloat16
+    bk_t = torch.from_numpy(bk).to(dev, bf)
+    bv_t = torch.from_numpy(bv).to(dev, bf)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 7)
+    w_o = (torch.randn((w.n_q_heads * w.head_dim, D), device=dev, generator=gen)
+           / math.sqrt(w.n_q_heads * w.head_dim)).to(bf)
+    F = torch.empty(sk.starkv_fused_factor_bytes(cfg, D), dtype=torch.uint8, device=dev)
+    sk.starkv_fuse_value_output(cfg, bv_t, w_o, D, F)
+    q_t = torch.from_numpy(synth.queries(w)).to(dev, bf)
+    y = torch.empty((w.batch, D), device=dev)
+    ws = torch.empty(sk.starkv_decode_hidden_workspace_bytes(cfg, seq_len, D),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+
+    def step(i, profiled):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        ev[6].record()
+        sk.starkv_decode_hidden(cfg, cache, seq_len, q_t, bk_t, F, D, scale, y, ws,
+                                events=ev[:6] if profiled else None)
+        ev[7].record()
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    step_ms, kern = [], [[] for _ in range(5)]
+    for i in range(args.steps):
+        step(i, False)
+        torch.cuda.synchronize()
+        step_ms.append(ev[6].elapsed_time(ev[7]))
+    for i in range(args.steps):
+        step(i, True)
+        torch.cuda.synchronize()
+        for k in range(5):
+            kern[k].append(ev[k].elapsed_time(ev[k + 1]))
+        print(f"# profiled step {i}: hidden gemm {kern[3][-1]:.4f} ms", file=sys.stderr,
+              flush=True)
+    assert torch.isfinite(y).all()
+    mean = lambda v: sum(v) / len(v)
+    ms = mean(step_ms)
+    gemm_ms = mean(kern[3])
+    f_bytes = F.numel()
+    gemm_bytes = f_bytes + w.batch * w.n_q_heads * w.value_rank * 4 + w.batch * D * 4
+    cache_bytes, _ = algorithmic_bytes(w, cfg, seq_len, sk)
+    achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    res = {
+        "metric": "latent-KV decode into the hidden size through the fused "
+                  "value/output factor: tokens attended/s",
+        "value": w.batch * seq_len / (ms * 1e-3), "unit": "tokens attended/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{w.name} decode_hidden", "batch": w.batch,
+                   "seq_len": seq_len, "hidden": D, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "key_rank": w.key_rank, "value_rank": w.value_rank,
+                   "cache": w.cache + (" rotated" if w.rotate else ""),
+                   "fused_factor_bytes": f_bytes,
+                   "cache_flushed_before_step": not args.no_flush},
+        "roofline": {"bound": "hbm", "kernel": "hidden_gemm_kernel",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "step_hbm_frac": (cache_bytes + gemm_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms": {"qproj": mean(kern[0]), "split": mean(kern[1]),
+                       "merge": mean(kern[2]), "hidden_gemm": gemm_ms,
+                       "k_slice_reduce": mean(kern[4])},
+        "algorithmic_bytes": {"cache": cache_bytes, "hidden_gemm": gemm_bytes},
+    }
+    print(json.dumps(res))
+
+
 def stream_read_ceiling(torch, sk, dev, gib=2, reps=10):
     """Measured streaming-read bandwidth (GB/s): starkv_stream_read over a
     buffer 8x the Infinity Cache, read once per pass with the split kernel's
@@ -393,6 +490,8 @@ def main():
         w = w.replace(batch=args.batch)
     if w.chunk:
         return run_prefill(args, w, torch, sk, synth)
+    if args.hidden:
+        return run_hidden(args, w, torch, sk, synth)
     seq_len = args.seq_len or w.seq_len
     cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
                          w.key_rank, w.value_rank, ((seq_len + 63) // 64) * 64,

@@ -32,7 +32,10 @@ ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_decode_profiled", "starkv_prefill",
                 "starkv_prefill_profiled", "starkv_stream_read", "starkv_strerror",
                 "starkv_decode_noalloc", "starkv_noalloc_scratch_bytes",
-                "starkv_decode_step", "starkv_decode_step_profiled")
+                "starkv_decode_step", "starkv_decode_step_profiled",
+                "starkv_fused_factor_bytes", "starkv_fuse_value_output",
+                "starkv_decode_hidden_workspace_bytes", "starkv_decode_hidden",
+                "starkv_decode_hidden_profiled")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -100,6 +103,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 i32, i32, vp, vp, vp, f32, vp, vp, sz,
                                                 vp, P(vp)]
     lib.starkv_decode_step_profiled.restype = ctypes.c_int
+    lib.starkv_fused_factor_bytes.argtypes = [P(StarkvConfig), i32]
+    lib.starkv_fused_factor_bytes.restype = sz
+    lib.starkv_fuse_value_output.argtypes = [P(StarkvConfig), vp, vp, i32, vp, vp]
+    lib.starkv_fuse_value_output.restype = ctypes.c_int
+    lib.starkv_decode_hidden_workspace_bytes.argtypes = [P(StarkvConfig), i32, i32]
+    lib.starkv_decode_hidden_workspace_bytes.restype = sz
+    lib.starkv_decode_hidden.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp, vp,
+                                         i32, f32, vp, vp, sz, vp]
+    lib.starkv_decode_hidden.restype = ctypes.c_int
+    lib.starkv_decode_hidden_profiled.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp,
+                                                  vp, vp, i32, f32, vp, vp, sz, vp, P(vp)]
+    lib.starkv_decode_hidden_profiled.restype = ctypes.c_int
     lib.starkv_decode_noalloc.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp,
                                           vp, f32, vp, vp]
     lib.starkv_decode_noalloc.restype = ctypes.c_int
@@ -243,6 +258,42 @@ def starkv_decode_step(cfg, cache: LatentCache, z_key, z_value, pos: int, q,
         st = lib.starkv_decode_step_profiled(*args, handles)
     if st != STARKV_OK:
         raise StarkvError(st, "starkv_decode_step")
+
+
+def starkv_fused_factor_bytes(cfg, hidden: int) -> int:
+    return load_library().starkv_fused_factor_bytes(ctypes.byref(cfg), hidden)
+
+
+def starkv_fuse_value_output(cfg, B_value, W_o, hidden: int, F, stream=None) -> None:
+    """F_h = B_value[g(h)]^T O_h into the device buffer F (bf16, opaque)."""
+    st = load_library().starkv_fuse_value_output(
+        ctypes.byref(cfg), _ptr(B_value), _ptr(W_o), hidden, _ptr(F), _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_fuse_value_output")
+
+
+def starkv_decode_hidden_workspace_bytes(cfg, seq_len: int, hidden: int) -> int:
+    return load_library().starkv_decode_hidden_workspace_bytes(ctypes.byref(cfg),
+                                                               seq_len, hidden)
+
+
+def starkv_decode_hidden(cfg, cache: LatentCache, seq_len: int, q, B_key, F,
+                         hidden: int, sm_scale: float, y, workspace,
+                         stream=None, events=None) -> None:
+    """y fp32 [B, hidden] = sum_h obar_h F_h (decode through the fused
+    value/output factor); `events`: six timing events (profiled variant)."""
+    cs = cache.struct
+    args = (ctypes.byref(cfg), ctypes.byref(cs), seq_len, _ptr(q), _ptr(B_key), _ptr(F),
+            hidden, sm_scale, _ptr(y), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    lib = load_library()
+    if events is None:
+        st = lib.starkv_decode_hidden(*args)
+    else:
+        handles = (ctypes.c_void_p * 6)(*(e.cuda_event for e in events))
+        st = lib.starkv_decode_hidden_profiled(*args, handles)
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_decode_hidden")
 
 
 def starkv_decode_noalloc(cfg, cache: LatentCache, seq_len: int, q, B_key,

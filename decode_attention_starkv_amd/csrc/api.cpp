@@ -263,6 +263,83 @@ int starkv_decode_step_profiled(const starkv_config* cfg, const starkv_cache* ca
                           sm_scale, out, workspace, ws_bytes, stream, events);
 }
 
+// ------------------------------------------- value/output fusion, head sum
+
+static bool hidden_ok(const starkv_config* cfg, int32_t hidden) {
+  return cfg->cache_dtype != STARKV_CACHE_F32 && hidden >= 128 && hidden % 128 == 0;
+}
+
+size_t starkv_fused_factor_bytes(const starkv_config* cfg, int32_t hidden) {
+  if (check_config(cfg) != STARKV_OK || !hidden_ok(cfg, hidden)) return 0;
+  return (size_t)cfg->n_q_heads * cfg->value_rank * hidden * 2;
+}
+
+int starkv_fuse_value_output(const starkv_config* cfg, const void* B_value,
+                             const void* W_o, int32_t hidden, void* F,
+                             hipStream_t stream) {
+  const int st = check_config(cfg);
+  if (st != STARKV_OK) return st;
+  if (hidden < 1) return STARKV_EINVAL;
+  if (!hidden_ok(cfg, hidden)) return STARKV_EUNSUPPORTED;
+  if (!B_value || !W_o || !F || !aligned16(B_value) || !aligned16(W_o) || !aligned16(F))
+    return STARKV_EINVAL;
+  return launch_fuse_vo(make_dims(*cfg), B_value, W_o, hidden, F, stream) == hipSuccess
+             ? STARKV_OK : STARKV_ELAUNCH;
+}
+
+static size_t hidden_extra(const Dims& d, int32_t hidden) {
+  return (size_t)hidden_k_slices(d, hidden) * d.B * hidden * 4;
+}
+
+size_t starkv_decode_hidden_workspace_bytes(const starkv_config* cfg,
+                                            int32_t seq_len, int32_t hidden) {
+  const size_t base = starkv_workspace_bytes(cfg, STARKV_OP_DECODE, seq_len);
+  if (base == 0 || !hidden_ok(cfg, hidden)) return 0;
+  return base + hidden_extra(make_dims(*cfg), hidden);
+}
+
+static int decode_hidden_impl(const starkv_config* cfg, const starkv_cache* cache,
+                              int32_t seq_len, const void* q, const void* B_key,
+                              const void* F, int32_t hidden, float sm_scale, float* y,
+                              void* workspace, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t* events) {
+  DecodeWs lay;
+  // F stands in for B_value in the common checks
+  int st = validate_decode(cfg, cache, seq_len, q, B_key, F, y, &lay);
+  if (st != STARKV_OK) return st;
+  if (hidden < 1) return STARKV_EINVAL;
+  if (!hidden_ok(cfg, hidden)) return STARKV_EUNSUPPORTED;
+  const Dims d = make_dims(*cfg);
+  const size_t need = lay.total + hidden_extra(d, hidden);
+  if (!workspace || !aligned16(workspace) || ws_bytes < need) return STARKV_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = launch_decode(d, *cache, seq_len, q, B_key, nullptr, sm_scale, nullptr,
+                               ws, lay, stream, events, false, false, true);
+  if (e != hipSuccess) return STARKV_ELAUNCH;
+  e = launch_hidden(d, reinterpret_cast<const float*>(ws + lay.obar), F, hidden,
+                    reinterpret_cast<float*>(ws + lay.total), y, stream,
+                    events ? events + 4 : nullptr);
+  return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
+}
+
+int starkv_decode_hidden(const starkv_config* cfg, const starkv_cache* cache,
+                         int32_t seq_len, const void* q, const void* B_key,
+                         const void* F, int32_t hidden, float sm_scale, float* y,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return decode_hidden_impl(cfg, cache, seq_len, q, B_key, F, hidden, sm_scale, y,
+                            workspace, ws_bytes, stream, nullptr);
+}
+
+int starkv_decode_hidden_profiled(const starkv_config* cfg, const starkv_cache* cache,
+                                  int32_t seq_len, const void* q, const void* B_key,
+                                  const void* F, int32_t hidden, float sm_scale,
+                                  float* y, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream, hipEvent_t* events) {
+  if (!events) return STARKV_EINVAL;
+  return decode_hidden_impl(cfg, cache, seq_len, q, B_key, F, hidden, sm_scale, y,
+                            workspace, ws_bytes, stream, events);
+}
+
 int starkv_decode(const starkv_config* cfg, const starkv_cache* cache,
                   int32_t seq_len, const void* q, const void* B_key,
                   const void* B_value, float sm_scale, float* out,

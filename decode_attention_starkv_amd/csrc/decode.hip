@@ -1255,7 +1255,7 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
                       const void* q, const void* bk, const void* bv,
                       float sm_scale, float* out, char* ws, const DecodeWs& lay,
                       hipStream_t s, hipEvent_t* ev, bool qproj_done,
-                      bool first_mark_done) {
+                      bool first_mark_done, bool latent_only) {
   void* qt = ws + lay.qt;
   float* part_o = reinterpret_cast<float*>(ws + lay.part_o);
   float* part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
@@ -1286,7 +1286,7 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   e = launch_split<FMT>(d, dim3(lay.splits, d.B), sa, s);
   if (e != hipSuccess) return e;
   mark(2);
-  if (FMT != STARKV_CACHE_F32 && merge_vproj_fits(d, lay.splits)) {
+  if (FMT != STARKV_CACHE_F32 && !latent_only && merge_vproj_fits(d, lay.splits)) {
     // one kernel for both steps; the up-projection's event pair is empty
     merge_vproj_kernel<<<dim3(d.Hkv, d.B), 256, 0, s>>>(
         reinterpret_cast<const _Float16*>(part_o), part_ml, static_cast<const uint16_t*>(bv),
@@ -1304,6 +1304,7 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(3);
+  if (latent_only) return hipSuccess;   // obar (unrotated) is the result
   vproj_kernel<FMT><<<dim3(d.Hq, d.dh / 16, (d.B + 15) / 16), 64 * kVprojWaves, 0, s>>>(obar, bv, d, out);
   e = hipGetLastError();
   mark(4);
@@ -1364,14 +1365,14 @@ hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,
                          const void* q, const void* bk, const void* bv,
                          float sm_scale, float* out, char* ws,
                          const DecodeWs& lay, hipStream_t s, hipEvent_t* ev,
-                         bool qproj_done, bool first_mark_done) {
+                         bool qproj_done, bool first_mark_done, bool latent_only) {
   switch (d.dtype) {
     case STARKV_CACHE_F32:
-      return decode_fmt<STARKV_CACHE_F32>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev, qproj_done, first_mark_done);
+      return decode_fmt<STARKV_CACHE_F32>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev, qproj_done, first_mark_done, latent_only);
     case STARKV_CACHE_BF16:
-      return decode_fmt<STARKV_CACHE_BF16>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev, qproj_done, first_mark_done);
+      return decode_fmt<STARKV_CACHE_BF16>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev, qproj_done, first_mark_done, latent_only);
     default:
-      return decode_fmt<STARKV_CACHE_Q43>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev, qproj_done, first_mark_done);
+      return decode_fmt<STARKV_CACHE_Q43>(d, cache, seq_len, q, bk, bv, sm_scale, out, ws, lay, s, ev, qproj_done, first_mark_done, latent_only);
   }
 }
 

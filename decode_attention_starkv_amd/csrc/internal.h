@@ -60,13 +60,23 @@ hipError_t launch_append(const Dims& d, const starkv_cache& cache,
                          hipStream_t s);
 // Decode launches.  With `qproj_done` the query records are already in the
 // workspace (written by launch_append_qproj) and the query projection is not
-// launched again; with `first_mark_done` the caller has recorded events[0].
+// launched again; with `first_mark_done` the caller has recorded events[0];
+// with `latent_only` the call stops after the merge, leaving the merged,
+// unrotated rows obar [B][Hq][R_v] fp32 at ws + lay.obar (no up-projection).
 hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,
                          const void* q, const void* bk, const void* bv,
                          float sm_scale, float* out, char* ws,
                          const DecodeWs& lay, hipStream_t s,
                          hipEvent_t* events = nullptr, bool qproj_done = false,
-                         bool first_mark_done = false);
+                         bool first_mark_done = false, bool latent_only = false);
+// Value/output factor fusion and the head sum (oproj.hip).
+int hidden_k_slices(const Dims& d, int D);
+hipError_t launch_fuse_vo(const Dims& d, const void* bv, const void* w_o, int D,
+                          void* F, hipStream_t s);
+// events (optional): [0] after the GEMM, [1] after the K-slice reduction.
+hipError_t launch_hidden(const Dims& d, const float* obar, const void* F, int D,
+                         float* part_y, float* y, hipStream_t s,
+                         hipEvent_t* events = nullptr);
 // One launch for the append of tokens [pos, pos+n) of a 4/3-bit cache and the
 // decode query projection into `qt` (the workspace's query records).
 hipError_t launch_append_qproj(const Dims& d, const starkv_cache& cache,

@@ -253,6 +253,65 @@ STARKV_API int starkv_decode_profiled(const starkv_config* cfg,
                                       void* workspace, size_t ws_bytes,
                                       hipStream_t stream, hipEvent_t* events);
 
+/* ---- value/output factor fusion and the head sum (review section 5.3,
+ * eq. 12 read right to left; Algorithm 2, steps 7-8) ---------------------
+ * eq. 12: p_h (Z_V U_h^T) O_h = (p_h Z_V)(U_h^T O_h).  The right-hand factor
+ * F_h = B_value[g(h)]^T O_h (R_v x hidden per query head, O_h = rows h*d_h
+ * .. h*d_h + d_h - 1 of the output projection W_o [Hq*d_h][hidden], row-vector
+ * convention y = o W_o) is prepared once; decode then ends in the hidden
+ * size: y[b] = sum_h obar[b, h] F_h, obar[b, h] = softmax_t(scores) Z_v the
+ * per-head attention row in the (unrotated) value latent.
+ * Shapes: BF16 or Q43 caches (bf16 factors), hidden a multiple of 128;
+ * EUNSUPPORTED otherwise.  F's layout is opaque to callers: it is written by
+ * starkv_fuse_value_output and read by starkv_decode_hidden only (bf16,
+ * [hidden/16][Hq*R_v/8][16][8]). */
+
+/* (host) Bytes of the fused factor F for `hidden`; 0 if unsupported. */
+STARKV_API size_t starkv_fused_factor_bytes(const starkv_config* cfg,
+                                            int32_t hidden);
+
+/* F_h = B_value[g(h)]^T O_h for every query head, fp32 accumulation of bf16
+ * products, rounded to bf16 (nearest even).  B_value [Hkv*d_h][R_v] bf16
+ * (unrotated, as in starkv_decode), W_o [Hq*d_h][hidden] bf16, F device
+ * buffer of starkv_fused_factor_bytes(cfg, hidden) bytes.
+ * Errors: EINVAL (null / misaligned pointer, hidden < 1), EUNSUPPORTED,
+ * ELAUNCH. */
+STARKV_API int starkv_fuse_value_output(const starkv_config* cfg,
+                                        const void* B_value, const void* W_o,
+                                        int32_t hidden, void* F,
+                                        hipStream_t stream);
+
+/* (host) Workspace bytes of starkv_decode_hidden; 0 if unsupported. */
+STARKV_API size_t starkv_decode_hidden_workspace_bytes(const starkv_config* cfg,
+                                                       int32_t seq_len,
+                                                       int32_t hidden);
+
+/* Decode that ends in the hidden size: the query projection, split scores
+ * and online softmax, P Z_v on MFMA and the split merge of starkv_decode,
+ * then y = obar_flat [B][Hq*R_v] x F [Hq*R_v][hidden] (the per-head value
+ * factors and the sum over heads as one GEMM; obar fp32 split into bf16 high
+ * and low parts, fp32 accumulation, K slices summed in a fixed order).
+ *   q, B_key as in starkv_decode; F from starkv_fuse_value_output;
+ *   y fp32 [B][hidden].
+ * Errors: as starkv_decode; EUNSUPPORTED for the shapes above. */
+STARKV_API int starkv_decode_hidden(const starkv_config* cfg,
+                                    const starkv_cache* cache, int32_t seq_len,
+                                    const void* q, const void* B_key,
+                                    const void* F, int32_t hidden,
+                                    float sm_scale, float* y, void* workspace,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/* starkv_decode_hidden that also records events[0..5] (host array of
+ * created hipEvent_t) on `stream`: before the query projection, before the
+ * split kernel, before the merge, before the hidden GEMM, before the K-slice
+ * reduction and after it.  Same arguments, results and errors; EINVAL if
+ * events is NULL. */
+STARKV_API int starkv_decode_hidden_profiled(
+    const starkv_config* cfg, const starkv_cache* cache, int32_t seq_len,
+    const void* q, const void* B_key, const void* F, int32_t hidden,
+    float sm_scale, float* y, void* workspace, size_t ws_bytes,
+    hipStream_t stream, hipEvent_t* events);
+
 /* For callers that cannot allocate device memory (code under stream
  * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
  * starkv_decode -- same arguments except the workspace, same kernels, same

@@ -143,3 +143,59 @@ def causal_attention(cache, ctx_len, q, bk, bv, sm_scale, n_q_heads, rotate,
         a = np.where(pos[None, :] <= (ctx_len + rows)[:, None], a, -np.inf)
         out[:, hi] = softmax(a) @ v
     return out
+
+
+def fuse_value_output(bv, w_o, n_q_heads, n_kv_heads, head_dim):
+    """Per-query-head fused value/output factor F_h = B_value[g(h)]^T O_h
+    (review section 5.3, eq. 12: the right-hand factor U_h^T O_h prepared
+    offline; Algorithm 2, step 7).  bv [Hkv*d_h, R_v]; w_o [Hq*d_h, D] with
+    O_h its rows h*d_h .. (h+1)*d_h - 1 (row-vector convention: y = o W_o).
+    Returns F [Hq, R_v, D] float64."""
+    bv = np.asarray(bv, np.float64)
+    w_o = np.asarray(w_o, np.float64)
+    group = n_q_heads // n_kv_heads
+    out = []
+    for h in range(n_q_heads):
+        g = h // group
+        bvg = bv[g * head_dim:(g + 1) * head_dim]           # [d_h, R_v]
+        out.append(bvg.T @ w_o[h * head_dim:(h + 1) * head_dim])
+    return np.stack(out)
+
+
+def decode_hidden(cache, seq_len, q, bk, bv, w_o, sm_scale, n_q_heads, rotate,
+                  batches=None):
+    """Decode that ends in the hidden size (review Algorithm 2, steps 7-8):
+    y[b] = sum_h o_h O_h, o_h the per-head attention output of `decode` and
+    O_h the rows h*d_h .. (h+1)*d_h - 1 of w_o [Hq*d_h, D].  float64."""
+    o = decode(cache, seq_len, q, bk, bv, sm_scale, n_q_heads, rotate, batches)
+    w_o = np.asarray(w_o, np.float64)
+    d_h = o.shape[-1]
+    return sum(o[:, h] @ w_o[h * d_h:(h + 1) * d_h] for h in range(n_q_heads))
+
+
+def decode_latent_rows(cache, seq_len, q, bk, sm_scale, n_q_heads, rotate,
+                       batches=None, unrotated=False):
+    """The per-head attention rows in the (stored) value latent,
+    obar_h = softmax(a_h) Z_v [len(batches), Hq, R_v] float64 -- the left-hand
+    factor p_h Z_V of eq. 12, before any value factor is applied.  With a
+    rotated cache Z_v is the stored rotated latent (Z H); a fused factor for
+    it is F_h with its R_v rows rotated the same way.  `unrotated` returns
+    obar_h H instead (the rows in the unrotated latent: H H = I, eq. 13)."""
+    q = np.asarray(q, np.float64)
+    n_kv = cache.H
+    group = n_q_heads // n_kv
+    bk_e, _ = effective_factors(bk, np.zeros((1, cache.rv)), rotate, cache.rk,
+                                cache.rv)
+    batches = range(q.shape[0]) if batches is None else batches
+    out = np.zeros((len(batches), n_q_heads, cache.rv))
+    for bi, b in enumerate(batches):
+        zk = cache.key_latents(b, seq_len)
+        zv = cache.value_latents(b, seq_len)
+        for h in range(n_q_heads):
+            g = h // group
+            p = softmax(sm_scale * ((zk[:, g, :] @ bk_e[g].T) @ q[b, h]))
+            out[bi, h] = p @ zv
+    if unrotated and rotate:
+        rv = hadamard.rotation_matrix(cache.rv // 4, cache.rv - cache.rv // 4)
+        out = out @ rv
+    return out

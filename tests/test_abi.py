@@ -198,6 +198,28 @@ def test_decode_step_validation_before_any_hip_call():
                                            None) == sk.STARKV_EINVAL
 
 
+def test_hidden_decode_validation():
+    lib = sk.load_library()
+    w = synth.WORKLOADS["l2_q43"]
+    cfg = _cfg(w)
+    assert sk.starkv_fused_factor_bytes(cfg, 4096) == 32 * 1024 * 4096 * 2
+    assert sk.starkv_fused_factor_bytes(cfg, 100) == 0            # not a multiple of 128
+    assert sk.starkv_fused_factor_bytes(_cfg(synth.WORKLOADS["tiny"]), 256) == 0   # fp32
+    assert sk.starkv_decode_hidden_workspace_bytes(cfg, 1000, 4096) > \
+        sk.starkv_workspace_bytes(cfg, sk.OP_DECODE, 1000)
+    cp, cc = ctypes.byref(cfg), ctypes.byref(_fake_cache())
+    assert lib.starkv_fuse_value_output(cp, 0x1000, 0x2000, 0, 0x3000, None) == sk.STARKV_EINVAL
+    assert lib.starkv_fuse_value_output(cp, 0x1000, 0x2000, 100, 0x3000, None) == \
+        sk.STARKV_EUNSUPPORTED
+    assert lib.starkv_fuse_value_output(cp, None, 0x2000, 256, 0x3000, None) == sk.STARKV_EINVAL
+    args = (0x1000, 0x2000, 0x3000, 256, ctypes.c_float(0.1), 0x4000)
+    assert lib.starkv_decode_hidden(cp, cc, 100, *args, 0x5000, 16, None) == sk.STARKV_EWORKSPACE
+    assert lib.starkv_decode_hidden(cp, cc, 0, *args, 0x5000, 1 << 30, None) == sk.STARKV_EINVAL
+    bad = (0x1000, 0x2000, 0x3000, 200, ctypes.c_float(0.1), 0x4000)
+    assert lib.starkv_decode_hidden(cp, cc, 100, *bad, 0x5000, 1 << 30, None) == \
+        sk.STARKV_EUNSUPPORTED
+
+
 def test_call_validation_before_any_hip_call():
     w = synth.WORKLOADS["l2_q43"]
     lib = sk.load_library()
