@@ -44,10 +44,34 @@ def softmax(a):
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
+def rope(x, pos, theta):
+    """Rotary position embedding of the rows x [..., d_h] at positions pos
+    [...] (review section 5.3: keys stay pre-RoPE latents and are rotated
+    after reconstruction; Algorithm 2, step 4c).  The pages fix no variant;
+    the one taken is the half-split pairing of LLaMA-family checkpoints:
+    channel i < d_h/2 pairs with i + d_h/2, and the pair turns by the angle
+    pos * theta^(-2i/d_h):
+        (x_i, x_{i+d/2}) -> (x_i cos a - x_{i+d/2} sin a,
+                             x_i sin a + x_{i+d/2} cos a).   float64."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    inv = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(pos, np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
 def decode(cache, seq_len, q, bk, bv, sm_scale, n_q_heads, rotate,
-           batches=None, heads=None):
+           batches=None, heads=None, rope_theta=0.0, q_pos=None):
     """out [len(batches), len(heads), d_h] float64: each query head attends
-    to the first seq_len cached tokens of its batch element."""
+    to the first seq_len cached tokens of its batch element.
+
+    rope_theta > 0: the query (at position q_pos, by default seq_len - 1, the
+    token just appended) and every reconstructed key (at its own position
+    0 .. seq_len - 1) are rotated by `rope` before the scores; values are
+    not rotated."""
     q = np.asarray(q, np.float64)
     n_kv = cache.H
     group = n_q_heads // n_kv
@@ -56,6 +80,7 @@ def decode(cache, seq_len, q, bk, bv, sm_scale, n_q_heads, rotate,
     batches = range(q.shape[0]) if batches is None else batches
     heads = range(n_q_heads) if heads is None else heads
     out = np.zeros((len(batches), len(heads), d_h))
+    t = seq_len - 1 if q_pos is None else q_pos
     for bi, b in enumerate(batches):
         zk = cache.key_latents(b, seq_len)
         zv = cache.value_latents(b, seq_len)
@@ -63,7 +88,11 @@ def decode(cache, seq_len, q, bk, bv, sm_scale, n_q_heads, rotate,
             g = h // group
             k = zk[:, g, :] @ bk_e[g].T
             v = zv @ bv_e[g * d_h:(g + 1) * d_h].T
-            p = softmax(sm_scale * (k @ q[b, h]))
+            qh = q[b, h]
+            if rope_theta:
+                k = rope(k, np.arange(seq_len), rope_theta)
+                qh = rope(qh, t, rope_theta)
+            p = softmax(sm_scale * (k @ qh))
             out[bi, hi] = p @ v
     return out
 
