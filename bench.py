@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    p.add_argument("--rope-theta", type=float, default=0.0,
+                   help="rotary position embedding of the keys (base theta), "
+                        "fused into the latent-key scoring")
     p.add_argument("--hidden", type=int, default=0,
                    help="decode through the fused value/output factor into a "
                         "hidden size of this width (starkv_decode_hidden)")
@@ -495,10 +498,10 @@ def main():
     seq_len = args.seq_len or w.seq_len
     cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
                          w.key_rank, w.value_rank, ((seq_len + 63) // 64) * 64,
-                         w.cache, w.rotate, args.splits)
+                         w.cache, w.rotate, args.splits, rope_theta=args.rope_theta)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"# workload {w.name} B={w.batch} T={seq_len} splits="
+    print(f"# workload {w.name} B={w.batch} T={seq_len} rope_theta={args.rope_theta} splits="
           f"{sk.starkv_decode_splits(cfg, seq_len)}", file=sys.stderr, flush=True)
 
     cache = sk.LatentCache(cfg)
@@ -595,7 +598,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name} decode", "batch": w.batch,
+        "config": {"workload": f"{w.name} decode" + (" rope" if args.rope_theta else ""),
+                   "batch": w.batch, "rope_theta": args.rope_theta,
                    "seq_len": seq_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "key_rank": w.key_rank, "value_rank": w.value_rank,
@@ -618,7 +622,10 @@ def main():
                                 / HBM_PEAK_GBS,
         "ms_per_step_percentiles": percentiles(step_ms),
         "split_ms_percentiles": percentiles(kern_ms[1]),
-        "kernels_ms": {"append_and_qproj": mean(kern_ms[0]),
+        # with rotary keys the first interval also holds the rotary score
+        # kernels (trig table, query coefficients, scores)
+        "kernels_ms": {("append_and_rope_scores" if args.rope_theta
+                        else "append_and_qproj"): mean(kern_ms[0]),
                        "split": split_ms, "merge": mean(kern_ms[2]),
                        "vproj": mean(kern_ms[3])},
         "algorithmic_bytes": {"cache": cache_bytes, "factors": factor_bytes},

@@ -40,7 +40,10 @@ int check_config(const starkv_config* c) {
         return STARKV_EINVAL;
     return STARKV_EUNSUPPORTED;
   }
-  if (c->rope_theta > 0.0f) return STARKV_EUNSUPPORTED;
+  // rotary keys: the 4/3-bit cache's decode only (rope.hip), head_dim 64 or 128
+  if (c->rope_theta > 0.0f &&
+      (!quant || (c->head_dim != 64 && c->head_dim != 128)))
+    return STARKV_EUNSUPPORTED;
   const int g = c->n_q_heads / c->n_kv_heads;
   if (c->n_q_heads > kMaxQHeads || (g != 1 && g != 2 && g != 4 && g != 8))
     return STARKV_EUNSUPPORTED;
@@ -141,7 +144,7 @@ size_t starkv_workspace_bytes(const starkv_config* cfg, int32_t op,
   if (op == STARKV_OP_DECODE) {
     if (!decode_supported(d)) return 0;
     if (n_tokens > cfg->max_tokens) return 0;
-    return decode_ws_layout(d, choose_splits(*cfg, n_tokens)).total;
+    return decode_ws_layout(d, choose_splits(*cfg, n_tokens), n_tokens).total;
   }
   if (op == STARKV_OP_PREFILL) return prefill_ws_layout(d, n_tokens).total;
   return 0;
@@ -183,7 +186,7 @@ int validate_decode(const starkv_config* cfg, const starkv_cache* cache,
   if (!q || !B_key || !B_value || !out || !aligned16(q) || !aligned16(B_key) ||
       !aligned16(B_value) || !aligned16(out))
     return STARKV_EINVAL;
-  *lay = decode_ws_layout(make_dims(*cfg), choose_splits(*cfg, seq_len));
+  *lay = decode_ws_layout(make_dims(*cfg), choose_splits(*cfg, seq_len), seq_len);
   return STARKV_OK;
 }
 
@@ -228,7 +231,7 @@ static int decode_step_impl(const starkv_config* cfg, const starkv_cache* cache,
   hipError_t e = hipSuccess;
   bool fused = false;
   if (n > 0) {
-    if (d.dtype == STARKV_CACHE_Q43) {
+    if (d.dtype == STARKV_CACHE_Q43 && d.rope_theta == 0.0f) {
       e = launch_append_qproj(d, *cache, z_key, z_value, pos, n, q, B_key,
                               sm_scale * 1.4426950408889634f, ws + lay.qt, stream);
       fused = true;
@@ -375,7 +378,8 @@ static int prefill_impl(const starkv_config* cfg, const starkv_cache* cache,
       !aligned16(out) || (z_debug && !aligned16(z_debug)))
     return STARKV_EINVAL;
   const Dims d = make_dims(*cfg);
-  if (hidden % 64 != 0 || !prefill_supported(d)) return STARKV_EUNSUPPORTED;
+  if (hidden % 64 != 0 || !prefill_supported(d) || cfg->rope_theta > 0.0f)
+    return STARKV_EUNSUPPORTED;
   const PrefillWs lay = prefill_ws_layout(d, chunk);
   if (!workspace || !aligned16(workspace) || ws_bytes < lay.total)
     return STARKV_EWORKSPACE;

@@ -38,12 +38,17 @@ inline Dims make_dims(const starkv_config& c) {
   return d;
 }
 
+// Workspace of the rotary-key scores (offsets from DecodeWs::rope_off).
+struct RopeWs {
+  size_t mrec, trig, s_rel, m_tile, m_split, total;
+};
 // Workspace carve-up of one decode call (byte offsets, 256-aligned).
 struct DecodeWs {
-  size_t qt, part_o, part_ml, obar, total;
+  size_t qt, part_o, part_ml, obar, rope_off, total;
+  RopeWs rope;
   int splits;
 };
-DecodeWs decode_ws_layout(const Dims& d, int splits);
+DecodeWs decode_ws_layout(const Dims& d, int splits, int seq_len);
 // Decode split workgroups that stay resident on one compute unit together
 // (1 when it cannot be asked, e.g. without a device).
 int decode_groups_per_cu(const Dims& d);
@@ -69,6 +74,24 @@ hipError_t launch_decode(const Dims& d, const starkv_cache& cache, int seq_len,
                          const DecodeWs& lay, hipStream_t s,
                          hipEvent_t* events = nullptr, bool qproj_done = false,
                          bool first_mark_done = false, bool latent_only = false);
+// Rotary-key scores (rope.hip).
+struct RopeArgs {
+  Dims d;
+  int seq_len, splits, tiles_per_split;
+  const void* key;
+  const uint16_t* kmeta;
+  const void* mrec;      // fp16 query coefficient fragments
+  const void* trig;      // fp16 position trig fragments
+  void* s_rel;           // fp16 [B][Hq][NT*64]
+  float* m_tile;         // [B][Hq][NT]
+  float* m_split;        // [B][splits][Hq]
+};
+bool rope_supported(const Dims& d);
+size_t rope_ws_bytes(const Dims& d, int seq_len, int splits, RopeWs* w);
+hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_len,
+                              const void* q, const void* bk, float sm_scale,
+                              char* ws, const RopeWs& rw, int splits,
+                              int tiles_per_split, hipStream_t s);
 // Value/output factor fusion and the head sum (oproj.hip).
 int hidden_k_slices(const Dims& d, int D);
 hipError_t launch_fuse_vo(const Dims& d, const void* bv, const void* w_o, int D,

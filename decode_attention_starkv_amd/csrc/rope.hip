@@ -1,0 +1,366 @@
+// Rotary position embedding fused into latent-key scoring -- the technical
+// review of arXiv 2606.08382, section 5.3 ("keys are harder"): the stored
+// keys stay pre-RoPE latents, and reconstruction, rotation and scoring are
+// fused at runtime (Algorithm 2, steps 4b-4d), with no key ever written out.
+//
+// RoPE variant: channel i < d_h/2 pairs with i + d_h/2 and turns by the angle
+// pos * theta^(-2i/d_h).  With q' = R_t q (the query at its position t) and
+// k_j = B z_j (B = the KV head's key factor), the score is
+//   q' . R_j k_j = sum_{i < d_h/2} cos(j w_i) (A_i . z_j) + sin(j w_i) (C_i . z_j),
+//   A_i = q'_i B_i + q'_{i'} B_{i'},   C_i = q'_{i'} B_i - q'_i B_{i'}   (i' = i + d_h/2),
+// i.e. per token q~_j = Trig_j M (M = [A; C], d_h x r_k per query head) and
+// score_j = q~_j . z_j.  Per call:
+//   rope_trig_kernel   Trig for positions 0 .. seq_len-1, fp16, already in the
+//                      MFMA B-operand order (angles reduced in fp64);
+//   rope_qproj_kernel  M per (sequence, query head): q rotated to its own
+//                      position, A and C, the key latent's block rotation and
+//                      sm_scale * log2(e) folded in, fp16 in A-operand order;
+//   rope_score_kernel  per (split, group of 8 query heads, sequence): q~ for a
+//                      64-token tile on MFMA 32x32x16 (K = d_h), transposed
+//                      through LDS so lane = token, then the 32-term dot with
+//                      the dequantized latent.  Scores leave as fp16 relative
+//                      to the running (exact) max of their head, with that
+//                      max per tile and the split's final max.
+// The 4/3-bit split kernel then reads those scores instead of computing
+// latent ones (exp2(s_rel + m_tile - m_split) <= 1) and runs its value
+// contraction unchanged.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "device.h"
+
+namespace starkv {
+namespace {
+
+constexpr int kRopeHeads = 8;     // query heads per score workgroup (4 waves x 2)
+constexpr int kQtStride = 36;     // floats per token row of the transpose buffer
+
+// sin / cos of pos * theta^(-2 p / dh), the angle reduced modulo 2 pi in fp64
+__device__ inline void rope_angle(int pos, int p, int dh, double log2_theta, float* c,
+                                  float* s) {
+  const double w = exp2(-2.0 * p / dh * log2_theta);
+  const double a = (double)pos * w;
+  const double turns = a * 0.15915494309189535;     // 1 / (2 pi)
+  const float phi = (float)((turns - floor(turns)) * 6.283185307179586);
+  *c = cosf(phi);
+  *s = sinf(phi);
+}
+
+// Trig[tile][s][j][lane][e] = T[i = 16 s + 8 (lane / 32) + e][token 64 tile +
+// 32 j + lane % 32], T[i][pos] = cos(pos w_i) (i < dh/2), sin(pos w_{i-dh/2}).
+__global__ __launch_bounds__(256) void rope_trig_kernel(int dh, int n_tiles,
+                                                        double log2_theta,
+                                                        _Float16* __restrict__ trig) {
+  const int per_tile = dh * 64;               // halves per tile
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)n_tiles * per_tile) return;
+  const int tile = (int)(idx / per_tile);
+  int r = (int)(idx % per_tile);
+  const int e = r & 7;
+  r >>= 3;
+  const int lane = r & 63;
+  r >>= 6;
+  const int j = r & 1, s = r >> 1;
+  const int i = 16 * s + 8 * (lane >> 5) + e;
+  const int pos = tile * kTile + 32 * j + (lane & 31);
+  float c, sn;
+  rope_angle(pos, i % (dh / 2), dh, log2_theta, &c, &sn);
+  trig[idx] = (_Float16)(i < dh / 2 ? c : sn);
+}
+
+// M for one (sequence, query head) = blockIdx.x, in A-operand order
+// frag[s][lane][e] = M[i = 16 s + 8 (lane / 32) + e][r = lane % 32].
+__global__ __launch_bounds__(256) void rope_qproj_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ bk,
+                                                         Dims d, int q_pos,
+                                                         double log2_theta, float qscale,
+                                                         _Float16* __restrict__ mrec) {
+  __shared__ float qr[256];
+  __shared__ float Mf[256][33];
+  const int bh = blockIdx.x, h = bh % d.Hq, g = h / d.G;
+  const int t = threadIdx.x;
+  const int half = d.dh / 2;
+  const float* dummy = nullptr;
+  (void)dummy;
+  // q' = R_t q
+  if (t < half) {
+    float c, s;
+    rope_angle(q_pos, t, d.dh, log2_theta, &c, &s);
+    const float a = bf16v(q[(size_t)bh * d.dh + t]);
+    const float b = bf16v(q[(size_t)bh * d.dh + t + half]);
+    qr[t] = a * c - b * s;
+    qr[t + half] = a * s + b * c;
+  }
+  __syncthreads();
+  // A (rows i < half) and C (rows half + i), 32 latent channels each
+  for (int x = t; x < half * 32; x += 256) {
+    const int i = x / 32, r = x % 32;
+    const float b0 = bf16v(bk[((size_t)g * d.dh + i) * 32 + r]);
+    const float b1 = bf16v(bk[((size_t)g * d.dh + i + half) * 32 + r]);
+    Mf[i][r] = qr[i] * b0 + qr[i + half] * b1;
+    Mf[half + i][r] = qr[i + half] * b0 - qr[i] * b1;
+  }
+  __syncthreads();
+  // stored key latents rotated by blocks of 8 channels (eq. 13): M H
+  if (d.rotate) {
+    for (int x = t; x < d.dh * 4; x += 256) {
+      const int i = x / 4, blk = x % 4;
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = Mf[i][8 * blk + k];
+#pragma unroll
+      for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (!(k & st)) {
+            const float a = v[k], b = v[k + st];
+            v[k] = a + b;
+            v[k + st] = a - b;
+          }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) Mf[i][8 * blk + k] = v[k] * inv_sqrt_pow2(8);
+    }
+    __syncthreads();
+  }
+  const int ks = d.dh / 16;
+  for (int x = t; x < ks * 64 * 8; x += 256) {
+    const int e = x & 7, lane = (x >> 3) & 63, s = x >> 9;
+    const int i = 16 * s + 8 * (lane >> 5) + e;
+    mrec[(size_t)bh * ks * 512 + x] = (_Float16)(Mf[i][lane & 31] * qscale);
+  }
+}
+
+template <int N>
+__device__ inline void rope_wait_vmcnt() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Scores of one (split, group of 8 query heads, sequence).  Wave w owns
+// query heads 8 hg + 2 w and 8 hg + 2 w + 1.  Per 64-token tile: the trig
+// fragments come through a 2-slot LDS ring (direct-to-LDS loads one tile
+// ahead), each lane loads its own token's key words one tile ahead.
+template <int DH>
+__global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
+  constexpr int KS = DH / 16;
+  constexpr int kChunks = KS * 2;              // 1 KB trig chunks per tile
+  constexpr int kChunksPerWave = kChunks / 4;
+  const Dims& d = a.d;
+  __shared__ __attribute__((aligned(16))) h8 trig_l[2][kChunks * 64];
+  __shared__ __attribute__((aligned(16))) float qt_l[4][kTile * kQtStride];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const int sp = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int n_tiles = (a.seq_len + kTile - 1) / kTile;
+  const int tile0 = sp * a.tiles_per_split;
+  const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
+  const int h0 = hg * kRopeHeads + 2 * w;
+  const bool on0 = h0 < d.Hq, on1 = h0 + 1 < d.Hq;
+  const int g0 = min(h0, d.Hq - 1) / d.G, g1 = min(h0 + 1, d.Hq - 1) / d.G;
+  const bool two_kv = g0 != g1;
+
+  // this wave's M fragments (registers for the whole split)
+  h8 mf[2][KS];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int h = min(h0 + hh, d.Hq - 1);
+    const h8* src = static_cast<const h8*>(a.mrec) + ((size_t)b * d.Hq + h) * KS * 64;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) mf[hh][s] = src[s * 64 + l];
+  }
+
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.key);
+  const u32x2* kmeta = reinterpret_cast<const u32x2*>(a.kmeta);
+  const uint8_t* tbase = static_cast<const uint8_t*>(a.trig);
+  _Float16* srel = static_cast<_Float16*>(a.s_rel);
+  auto stage = [&](int tile, int slot) {
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+      const int k = w * kChunksPerWave + c;
+      __builtin_amdgcn_global_load_lds(
+          tbase + ((size_t)tile * kChunks + k) * 1024 + l * 16,
+          (__attribute__((address_space(3))) void*)(&trig_l[slot][k * 64]), 16, 0, 0);
+    }
+  };
+  // the lane's token: 4-bit word, two 3-bit words, remainder byte, meta
+  uint32_t kc[2][2][6];
+  auto load_keys = [&](int tile, int set) {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const int g = kv == 0 ? g0 : g1;
+      const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + g;
+      const uint8_t* kb = kbase + blk * kKeyBlock;
+      kc[set][kv][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + l);
+      kc[set][kv][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + l);
+      kc[set][kv][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + l);
+      kc[set][kv][3] = __builtin_nontemporal_load(kb + 768 + l);
+      const u32x2 mt = __builtin_nontemporal_load(kmeta + blk * kTile + l);
+      kc[set][kv][4] = mt[0];
+      kc[set][kv][5] = mt[1];
+    }
+  };
+  // loads per tile and wave: trig chunks + 5 per KV head (always both sets,
+  // the second a duplicate when the wave's heads share a KV head)
+  constexpr int kLoadsPerTile = kChunksPerWave + 10;
+
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float* qt = &qt_l[w][0];
+  const size_t tpad = (size_t)d.NT * kTile;
+
+  stage(tile0, 0);
+  load_keys(tile0, 0);
+  for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
+    const int slot = it & 1, set = it & 1;
+    if (tile + 1 < tile1) {
+      stage(tile + 1, slot ^ 1);
+      load_keys(tile + 1, set ^ 1);
+      rope_wait_vmcnt<kLoadsPerTile>();
+    } else {
+      rope_wait_vmcnt<0>();
+    }
+    lds_barrier();   // every wave's trig chunks of this tile are in LDS
+
+    // dequantized latents of the lane's token, per KV head of the wave
+    float zf[2][32];
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint32_t* k = kc[set][kv];
+      const uint32_t hi = k[0], lo0 = k[1], lo1 = k[2];
+      const uint32_t rem = (k[3] & 0xFFu) | (((lo0 >> 15) & 1u) << 8) |
+                           (((lo0 >> 31) & 1u) << 9) | (((lo1 >> 15) & 1u) << 10) |
+                           (((lo1 >> 31) & 1u) << 11);
+      const h2 mh = __builtin_bit_cast(h2, k[4]), ml = __builtin_bit_cast(h2, k[5]);
+      const float sh = (float)mh[0], zh = (float)mh[1], sl = (float)ml[0], zl = (float)ml[1];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) zf[kv][c] = fmaf(sh, (float)((hi >> (4 * c)) & 15u), zh);
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        uint32_t code;
+        if (i < 5) code = (lo0 >> (3 * i)) & 7u;
+        else if (i < 10) code = (lo1 >> (3 * (i - 5))) & 7u;
+        else if (i < 15) code = (lo0 >> (16 + 3 * (i - 10))) & 7u;
+        else if (i < 20) code = (lo1 >> (16 + 3 * (i - 15))) & 7u;
+        else code = (rem >> (3 * (i - 20))) & 7u;
+        zf[kv][8 + i] = fmaf(sl, (float)code, zl);
+      }
+    }
+
+    const h8* tr = &trig_l[slot][0];
+    const bool valid = tile * kTile + l < a.seq_len;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bool on = hh == 0 ? on0 : on1;
+      if (!on) continue;
+      const int h = h0 + hh;
+      const int kv = (hh == 1 && two_kv) ? 1 : 0;
+      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const h8 t0 = tr[(2 * s) * 64 + l], t1 = tr[(2 * s + 1) * 64 + l];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s], t0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s], t1, acc1, 0, 0, 0);
+      }
+      // D[r][token]: lane l holds token l % 32 (acc0) and 32 + l % 32 (acc1),
+      // rows acc_row(v, l); through LDS so that lane = token
+#pragma unroll
+      for (int v = 0; v < 16; v += 4) {
+        const int r = acc_row(v, l);
+        *reinterpret_cast<float4*>(qt + (l & 31) * kQtStride + r) =
+            float4{acc0[v], acc0[v + 1], acc0[v + 2], acc0[v + 3]};
+        *reinterpret_cast<float4*>(qt + (32 + (l & 31)) * kQtStride + r) =
+            float4{acc1[v], acc1[v + 1], acc1[v + 2], acc1[v + 3]};
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      float sc = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 32; r += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(qt + l * kQtStride + r);
+        sc = fmaf(x.x, zf[kv][r], sc);
+        sc = fmaf(x.y, zf[kv][r + 1], sc);
+        sc = fmaf(x.z, zf[kv][r + 2], sc);
+        sc = fmaf(x.w, zf[kv][r + 3], sc);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next head writes
+      __builtin_amdgcn_wave_barrier();
+      sc = valid ? sc : -INFINITY;
+      const float mt = wave_max(sc);
+      const float mn = fmaxf(m_run[hh], mt);
+      m_run[hh] = mn;
+      const float rel = valid ? sc - mn : -INFINITY;
+      srel[((size_t)b * d.Hq + h) * tpad + (size_t)tile * kTile + l] = (_Float16)rel;
+      if (l == 0) a.m_tile[((size_t)b * d.Hq + h) * d.NT + tile] = mn;
+    }
+    lds_barrier();   // the slot read here is restaged next iteration
+  }
+  if (l == 0) {
+    if (on0) a.m_split[((size_t)b * a.splits + sp) * d.Hq + h0] = m_run[0];
+    if (on1) a.m_split[((size_t)b * a.splits + sp) * d.Hq + h0 + 1] = m_run[1];
+  }
+}
+
+}  // namespace
+
+bool rope_supported(const Dims& d) {
+  return d.dtype == STARKV_CACHE_Q43 && d.rk == 32 && (d.dh == 64 || d.dh == 128);
+}
+
+size_t rope_ws_bytes(const Dims& d, int seq_len, int splits, RopeWs* w) {
+  const size_t nt = (size_t)(seq_len + kTile - 1) / kTile;
+  auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 0;
+  RopeWs r;
+  r.mrec = off;
+  off += a256((size_t)d.B * d.Hq * d.dh * 32 * 2);
+  r.trig = off;
+  off += a256(nt * d.dh * kTile * 2);
+  r.s_rel = off;
+  off += a256((size_t)d.B * d.Hq * d.NT * kTile * 2);
+  r.m_tile = off;
+  off += a256((size_t)d.B * d.Hq * d.NT * 4);
+  r.m_split = off;
+  off += a256((size_t)d.B * splits * d.Hq * 4);
+  r.total = off;
+  if (w) *w = r;
+  return off;
+}
+
+hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_len,
+                              const void* q, const void* bk, float sm_scale,
+                              char* ws, const RopeWs& rw, int splits,
+                              int tiles_per_split, hipStream_t s) {
+  const double log2_theta = log2((double)d.rope_theta);
+  const int n_tiles = (seq_len + kTile - 1) / kTile;
+  const size_t n_trig = (size_t)n_tiles * d.dh * kTile;
+  _Float16* trig = reinterpret_cast<_Float16*>(ws + rw.trig);
+  _Float16* mrec = reinterpret_cast<_Float16*>(ws + rw.mrec);
+  rope_trig_kernel<<<(unsigned)((n_trig + 255) / 256), 256, 0, s>>>(d.dh, n_tiles,
+                                                                     log2_theta, trig);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  rope_qproj_kernel<<<d.B * d.Hq, 256, 0, s>>>(static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(bk), d,
+                                                seq_len - 1, log2_theta,
+                                                sm_scale * kLog2e, mrec);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  RopeArgs a;
+  a.d = d;
+  a.seq_len = seq_len;
+  a.splits = splits;
+  a.tiles_per_split = tiles_per_split;
+  a.key = cache.key;
+  a.kmeta = static_cast<const uint16_t*>(cache.key_meta);
+  a.mrec = mrec;
+  a.trig = trig;
+  a.s_rel = ws + rw.s_rel;
+  a.m_tile = reinterpret_cast<float*>(ws + rw.m_tile);
+  a.m_split = reinterpret_cast<float*>(ws + rw.m_split);
+  const dim3 grid(splits, (d.Hq + kRopeHeads - 1) / kRopeHeads, d.B);
+  if (d.dh == 64)
+    rope_score_kernel<64><<<grid, 256, 0, s>>>(a);
+  else
+    rope_score_kernel<128><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace starkv

@@ -220,6 +220,30 @@ def test_hidden_decode_validation():
         sk.STARKV_EUNSUPPORTED
 
 
+def test_rope_support_and_workspace():
+    lib = sk.load_library()
+    w = synth.WORKLOADS["l2_q43"]
+    plain = _cfg(w)
+    rope = _cfg(w, rope_theta=10000.0)
+    assert sk.starkv_cache_bytes(rope, 0) == sk.starkv_cache_bytes(plain, 0)
+    # the rotary scores need their own workspace on top of decode's
+    assert sk.starkv_workspace_bytes(rope, sk.OP_DECODE, 4096) > \
+        sk.starkv_workspace_bytes(plain, sk.OP_DECODE, 4096)
+    assert sk.starkv_decode_splits(rope, 4096) > 0
+    cache = _fake_cache()
+    args = (0x1000, 0x2000, 0x3000, ctypes.c_float(0.1), 0x4000, 0x5000, 1 << 30, None)
+    for cfg in (_cfg(synth.WORKLOADS["l2_bf16"], rope_theta=10000.0),   # plain caches
+                _cfg(w, head_dim=256, rope_theta=10000.0)):             # head dim 256
+        assert lib.starkv_decode(ctypes.byref(cfg), ctypes.byref(cache), 100,
+                                 *args) == sk.STARKV_EUNSUPPORTED
+    # prefill with rotary keys is not built
+    pre = _cfg(synth.WORKLOADS["longchat_prefill"], rope_theta=10000.0)
+    pargs = (0x1000, 4096, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000,
+             ctypes.c_float(0.1), 0x7000, None)
+    assert lib.starkv_prefill(ctypes.byref(pre), ctypes.byref(cache), 0, 64, *pargs,
+                              0x8000, 1 << 34, None) == sk.STARKV_EUNSUPPORTED
+
+
 def test_call_validation_before_any_hip_call():
     w = synth.WORKLOADS["l2_q43"]
     lib = sk.load_library()
