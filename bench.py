@@ -585,6 +585,23 @@ def main():
     cache_bytes, factor_bytes = algorithmic_bytes(w, cfg, seq_len, sk)
     achieved = cache_bytes / (split_ms * 1e-3) / 1e9
     tokens = w.batch * seq_len
+    roofline = {"bound": "hbm", "kernel": "split_kernel",
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic_from_counters(w, w.batch, seq_len,
+                                                 sk.starkv_decode_splits(cfg, seq_len))}
+    if args.rope_theta:
+        # rotary keys: the dominant kernel is the rotary score kernel, timed
+        # alone by events[0..1]; its work is 2 d_h r_k flop per (token, query
+        # head) for q~ = Trig M plus 2 r_k for the dot with the latent
+        rope_ms = mean(kern_ms[0])
+        flops = tokens * w.n_q_heads * (2 * w.head_dim * w.key_rank + 2 * w.key_rank)
+        tf = flops / (rope_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "rope_score_kernel", "achieved": tf,
+                    "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tf / MFMA_PEAK_TFLOPS, "traffic": None,
+                    "key_bytes_GBps": tokens * w.n_kv_heads * 21 / (rope_ms * 1e-3) / 1e9}
+        achieved = None
     res = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -606,13 +623,10 @@ def main():
                    "cache": w.cache + (" rotated" if w.rotate else ""),
                    "splits": sk.starkv_decode_splits(cfg, seq_len),
                    "cache_flushed_before_step": not args.no_flush},
-        "roofline": {"bound": "hbm", "kernel": "split_kernel",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_from_counters(w, w.batch, seq_len,
-                                                      sk.starkv_decode_splits(cfg, seq_len))},
-        "split_vs_stream_read": {"stream_read_GBps": stream_gbs,
-                                 "frac": achieved / stream_gbs},
+        "roofline": roofline,
+        "split_vs_stream_read": ({"stream_read_GBps": stream_gbs,
+                                  "frac": achieved / stream_gbs} if achieved else
+                                 {"stream_read_GBps": stream_gbs}),
         # whole step (append + the decode attention call) and the decode
         # attention call alone (query projection, split, merge, up-projection)
         # against the HBM peak; roofline.frac above is the split kernel alone
@@ -622,9 +636,8 @@ def main():
                                 / HBM_PEAK_GBS,
         "ms_per_step_percentiles": percentiles(step_ms),
         "split_ms_percentiles": percentiles(kern_ms[1]),
-        # with rotary keys the first interval also holds the rotary score
-        # kernels (trig table, query coefficients, scores)
-        "kernels_ms": {("append_and_rope_scores" if args.rope_theta
+        # with rotary keys the first interval is the rotary score kernel
+        "kernels_ms": {("rope_scores" if args.rope_theta
                         else "append_and_qproj"): mean(kern_ms[0]),
                        "split": split_ms, "merge": mean(kern_ms[2]),
                        "vproj": mean(kern_ms[3])},

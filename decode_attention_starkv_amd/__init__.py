@@ -35,7 +35,8 @@ ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_decode_step", "starkv_decode_step_profiled",
                 "starkv_fused_factor_bytes", "starkv_fuse_value_output",
                 "starkv_decode_hidden_workspace_bytes", "starkv_decode_hidden",
-                "starkv_decode_hidden_profiled")
+                "starkv_decode_hidden_profiled", "starkv_append_paged",
+                "starkv_decode_paged")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -115,6 +116,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.starkv_decode_hidden_profiled.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp,
                                                   vp, vp, i32, f32, vp, vp, sz, vp, P(vp)]
     lib.starkv_decode_hidden_profiled.restype = ctypes.c_int
+    lib.starkv_append_paged.argtypes = [P(StarkvConfig), P(StarkvCache), vp, i32, vp, vp,
+                                        vp, vp]
+    lib.starkv_append_paged.restype = ctypes.c_int
+    lib.starkv_decode_paged.argtypes = [P(StarkvConfig), P(StarkvCache), vp, i32, vp, i32,
+                                        vp, vp, vp, f32, vp, vp, sz, vp]
+    lib.starkv_decode_paged.restype = ctypes.c_int
     lib.starkv_decode_noalloc.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp,
                                           vp, f32, vp, vp]
     lib.starkv_decode_noalloc.restype = ctypes.c_int
@@ -294,6 +301,33 @@ def starkv_decode_hidden(cfg, cache: LatentCache, seq_len: int, q, B_key, F,
         st = lib.starkv_decode_hidden_profiled(*args, handles)
     if st != STARKV_OK:
         raise StarkvError(st, "starkv_decode_hidden")
+
+
+def starkv_append_paged(cfg, cache: LatentCache, page_table, positions, z_key,
+                        z_value, stream=None) -> None:
+    """One token per sequence at positions[b] of a paged pool.
+    page_table int32 [B, pages_per_seq], positions int32 [B] (device);
+    z_key fp32 [B, Hkv, r_k], z_value fp32 [B, R_v]."""
+    cs = cache.struct
+    st = load_library().starkv_append_paged(
+        ctypes.byref(cfg), ctypes.byref(cs), _ptr(page_table), page_table.shape[1],
+        _ptr(positions), _ptr(z_key), _ptr(z_value), _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_append_paged")
+
+
+def starkv_decode_paged(cfg, cache: LatentCache, page_table, seq_lens,
+                        max_seq_len: int, q, B_key, B_value, sm_scale: float, out,
+                        workspace, stream=None) -> None:
+    """Decode over a paged pool with ragged lengths seq_lens int32 [B]."""
+    cs = cache.struct
+    st = load_library().starkv_decode_paged(
+        ctypes.byref(cfg), ctypes.byref(cs), _ptr(page_table), page_table.shape[1],
+        _ptr(seq_lens), max_seq_len, _ptr(q), _ptr(B_key), _ptr(B_value), sm_scale,
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_decode_paged")
 
 
 def starkv_decode_noalloc(cfg, cache: LatentCache, seq_len: int, q, B_key,

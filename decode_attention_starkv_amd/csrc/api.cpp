@@ -343,6 +343,55 @@ int starkv_decode_hidden_profiled(const starkv_config* cfg, const starkv_cache* 
                             workspace, ws_bytes, stream, events);
 }
 
+// ------------------------------------------------ paged and ragged caches
+
+int starkv_append_paged(const starkv_config* cfg, const starkv_cache* cache,
+                        const int32_t* page_table, int32_t pages_per_seq,
+                        const int32_t* positions, const float* z_key,
+                        const float* z_value, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != STARKV_OK) return st;
+  if ((st = check_cache(cfg, cache)) != STARKV_OK) return st;
+  if (cfg->cache_dtype != STARKV_CACHE_Q43) return STARKV_EUNSUPPORTED;
+  if (!page_table || !positions || pages_per_seq < 1 || !z_key || !z_value ||
+      !aligned16(z_key) || !aligned16(z_value) ||
+      reinterpret_cast<uintptr_t>(page_table) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(positions) % 4 != 0)
+    return STARKV_EINVAL;
+  Dims d = make_dims(*cfg);
+  d.pages = page_table;
+  d.pages_per_seq = pages_per_seq;
+  d.positions = positions;
+  hipError_t e = launch_append(d, *cache, z_key, z_value, 0, 1, stream);
+  return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
+}
+
+int starkv_decode_paged(const starkv_config* cfg, const starkv_cache* cache,
+                        const int32_t* page_table, int32_t pages_per_seq,
+                        const int32_t* seq_lens, int32_t max_seq_len, const void* q,
+                        const void* B_key, const void* B_value, float sm_scale,
+                        float* out, void* workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+  DecodeWs lay;
+  int st = validate_decode(cfg, cache, max_seq_len, q, B_key, B_value, out, &lay);
+  if (st != STARKV_OK) return st;
+  if (cfg->cache_dtype != STARKV_CACHE_Q43) return STARKV_EUNSUPPORTED;
+  if (!page_table || !seq_lens || pages_per_seq < 1 ||
+      (int64_t)pages_per_seq * kTile < max_seq_len ||
+      reinterpret_cast<uintptr_t>(page_table) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(seq_lens) % 4 != 0)
+    return STARKV_EINVAL;
+  if (!workspace || !aligned16(workspace) || ws_bytes < lay.total)
+    return STARKV_EWORKSPACE;
+  Dims d = make_dims(*cfg);
+  d.pages = page_table;
+  d.pages_per_seq = pages_per_seq;
+  d.lens = seq_lens;
+  hipError_t e = launch_decode(d, *cache, max_seq_len, q, B_key, B_value, sm_scale, out,
+                               static_cast<char*>(workspace), lay, stream);
+  return e == hipSuccess ? STARKV_OK : STARKV_ELAUNCH;
+}
+
 int starkv_decode(const starkv_config* cfg, const starkv_cache* cache,
                   int32_t seq_len, const void* q, const void* B_key,
                   const void* B_value, float sm_scale, float* out,

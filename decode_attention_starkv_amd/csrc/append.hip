@@ -142,7 +142,9 @@ __device__ inline void append_q43_keys(const float* __restrict__ zk,
   int h = idx % d.Hkv;
   int i = (idx / d.Hkv) % n;
   int b = idx / ((size_t)d.Hkv * n);
-  int t = pos + i;
+  // per-sequence positions (paged caches, one token each, clamped into the
+  // sequence's pages) or the common one
+  int t = (d.positions ? min(max(d.positions[b], 0), d.pages_per_seq * kTile - 1) : pos) + i;
   int tile = t / kTile, u = t % kTile;
 
   float x[32];
@@ -188,7 +190,7 @@ __device__ inline void append_q43_keys(const float* __restrict__ zk,
   lo1 |= ((R >> 10) & 1u) << 15;
   lo1 |= ((R >> 11) & 1u) << 31;
 
-  size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + h;
+  size_t blk = tile_index(d, b, tile) * d.Hkv + h;
   uint8_t* kb = key + blk * kKeyBlock;
   reinterpret_cast<uint32_t*>(kb)[u] = whi;
   reinterpret_cast<uint32_t*>(kb + 256)[u] = lo0;
@@ -209,6 +211,8 @@ __device__ inline void append_q43_values(
     const float* __restrict__ zv, uint8_t* __restrict__ value,
     uint16_t* __restrict__ vmeta, const Dims& d, int pos, int n, int cb,
     int tile_off, int b, uint8_t (*codes)[256]) {
+  // paged caches: one token per sequence, at its own (clamped) position
+  if (d.positions) pos = min(max(d.positions[b], 0), d.pages_per_seq * kTile - 1);
   const int tile = pos / kTile + tile_off;
   const int t0 = tile * kTile;
   const int ulo = max(pos, t0) - t0;
@@ -218,7 +222,7 @@ __device__ inline void append_q43_values(
   const int G = d.rv / 32;
   const int m = pow2_divisor(n_hi);  // rotation block size
   const float rc = inv_sqrt_pow2(m);
-  uint16_t* vm = vmeta + ((size_t)b * d.NT + tile) * 2 * G * kTile;
+  uint16_t* vm = vmeta + tile_index(d, b, tile) * 2 * G * kTile;
 
   // Words of a 32-token run that this append covers only partly keep the
   // other tokens' bits: read them now, so that the read overlaps phase 1
@@ -229,7 +233,7 @@ __device__ inline void append_q43_values(
   const int NH = n_hi / 32;
   const bool four = g < NH;
   const int nw = four ? 4 : 3;
-  uint8_t* vt = value + ((size_t)b * d.NT + tile) * 26 * d.rv;
+  uint8_t* vt = value + tile_index(d, b, tile) * 26 * d.rv;
   uint8_t* grp = four ? vt + (size_t)g * 1024 : vt + (size_t)NH * 1024 + (size_t)(g - NH) * 768;
   uint32_t old[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll

@@ -456,7 +456,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_
     if (t < 64) ms[s] = kNormalised ? wgt * l : wgt;
     L = fmaf(wgt, l, L);
   }
-  const float inv = 1.0f / wave_sum(L);
+  // a sequence with no token in any split (ragged batches, length 0) gives 0
+  const float Lt = wave_sum(L);
+  const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
   __syncthreads();
   float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
   if (c < d.rv) {
@@ -662,7 +664,8 @@ __global__ __launch_bounds__(256) void merge_vproj_kernel(
     float wl = 0.0f;
     if (lane < splits && ml0.y > 0.0f) wl = exp2f(ml0.x - mx) * ml0.y;
     ms[w][lane] = wl;
-    const float inv = 1.0f / wave_sum(wl);
+    const float wt = wave_sum(wl);
+    const float inv = wt > 0.0f ? 1.0f / wt : 0.0f;
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's weights
     __builtin_amdgcn_wave_barrier();
     float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -778,8 +781,10 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   if (rope) {
     // rotary keys: position trig table, rotated query coefficients and the
     // scores of every head and token (rope.hip), read by the split kernel
+    // (profiled calls: events[0] is re-recorded right before the score
+    // kernel, so that events[0..1] time it alone)
     e = launch_rope_scores(d, cache, seq_len, q, bk, sm_scale, ws + lay.rope_off, lay.rope,
-                           lay.splits, tiles_per_split, s);
+                           lay.splits, tiles_per_split, s, ev ? ev[0] : nullptr);
     if (e != hipSuccess) return e;
   } else if (!qproj_done) {
     qproj_kernel<FMT><<<d.B * d.Hq, 256, 0, s>>>(q, bk, d, sm_scale * kLog2e, qt);

@@ -19,7 +19,32 @@ constexpr int kMaxSplits = 1024;   // decode token splits per sequence
 struct Dims {
   int B, Hq, Hkv, G, dh, rk, rv, Tmax, NT, dtype, rotate;
   float rope_theta;  // 0: no rotary position embedding
+  // Paged / ragged 4/3-bit caches (all null / 0 for the contiguous layout):
+  const int32_t* pages = nullptr;  // device [B][pages_per_seq]: tile -> pool page
+  int pages_per_seq = 0;
+  const int32_t* lens = nullptr;   // device [B]: tokens of each sequence (decode)
+  const int32_t* positions = nullptr;  // device [B]: append position of each sequence
 };
+
+// Index of the 64-token tile `tile` of sequence b in the cache buffers: the
+// contiguous layout b * NT + tile, or the page the table maps it to (clamped
+// into the pool of B * NT pages, so a bad table entry selects a wrong page but
+// never an address outside the buffers).
+__host__ __device__ inline size_t tile_index(const Dims& d, int b, int tile) {
+  if (!d.pages) return (size_t)b * d.NT + tile;
+  const int t = tile < 0 ? 0 : (tile < d.pages_per_seq ? tile : d.pages_per_seq - 1);
+  int p = d.pages[(size_t)b * d.pages_per_seq + t];
+  const int n_pages = d.B * d.NT;
+  p = p < 0 ? 0 : (p >= n_pages ? n_pages - 1 : p);
+  return (size_t)p;
+}
+// Tokens of sequence b: its own length (ragged batches, clamped to
+// [0, max_len]) or the call's common length.
+__host__ __device__ inline int seq_len_of(const Dims& d, int b, int max_len) {
+  if (!d.lens) return max_len;
+  const int n = d.lens[b];
+  return n < 0 ? 0 : (n > max_len ? max_len : n);
+}
 
 inline Dims make_dims(const starkv_config& c) {
   Dims d;
@@ -91,7 +116,8 @@ size_t rope_ws_bytes(const Dims& d, int seq_len, int splits, RopeWs* w);
 hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_len,
                               const void* q, const void* bk, float sm_scale,
                               char* ws, const RopeWs& rw, int splits,
-                              int tiles_per_split, hipStream_t s);
+                              int tiles_per_split, hipStream_t s,
+                              hipEvent_t before_scores = nullptr);
 // Value/output factor fusion and the head sum (oproj.hip).
 int hidden_k_slices(const Dims& d, int D);
 hipError_t launch_fuse_vo(const Dims& d, const void* bv, const void* w_o, int D,

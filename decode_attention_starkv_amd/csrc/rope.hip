@@ -80,6 +80,8 @@ __global__ __launch_bounds__(256) void rope_qproj_kernel(const uint16_t* __restr
   const int bh = blockIdx.x, h = bh % d.Hq, g = h / d.G;
   const int t = threadIdx.x;
   const int half = d.dh / 2;
+  // the query sits at its sequence's last position (ragged batches: its own)
+  if (d.lens) q_pos = seq_len_of(d, bh / d.Hq, q_pos + 1) - 1;
   const float* dummy = nullptr;
   (void)dummy;
   // q' = R_t q
@@ -150,7 +152,8 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int sp = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
-  const int n_tiles = (a.seq_len + kTile - 1) / kTile;
+  const int seq_len = seq_len_of(d, b, a.seq_len);
+  const int n_tiles = (seq_len + kTile - 1) / kTile;
   const int tile0 = sp * a.tiles_per_split;
   const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
   const int h0 = hg * kRopeHeads + 2 * w;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const int g = kv == 0 ? g0 : g1;
-      const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + g;
+      const size_t blk = tile_index(d, b, tile) * d.Hkv + g;
       const uint8_t* kb = kbase + blk * kKeyBlock;
       kc[set][kv][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + l);
       kc[set][kv][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + l);
@@ -206,8 +209,12 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
   float* qt = &qt_l[w][0];
   const size_t tpad = (size_t)d.NT * kTile;
 
-  stage(tile0, 0);
-  load_keys(tile0, 0);
+  // (a split may hold no tile of a shorter sequence: then nothing is loaded,
+  // and no direct-to-LDS load is left in flight when the workgroup ends)
+  if (tile0 < tile1) {
+    stage(tile0, 0);
+    load_keys(tile0, 0);
+  }
   for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
     const int slot = it & 1, set = it & 1;
     if (tile + 1 < tile1) {
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
     }
 
     const h8* tr = &trig_l[slot][0];
-    const bool valid = tile * kTile + l < a.seq_len;
+    const bool valid = tile * kTile + l < seq_len;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const bool on = hh == 0 ? on0 : on1;
@@ -327,7 +334,8 @@ size_t rope_ws_bytes(const Dims& d, int seq_len, int splits, RopeWs* w) {
 hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_len,
                               const void* q, const void* bk, float sm_scale,
                               char* ws, const RopeWs& rw, int splits,
-                              int tiles_per_split, hipStream_t s) {
+                              int tiles_per_split, hipStream_t s,
+                              hipEvent_t before_scores) {
   const double log2_theta = log2((double)d.rope_theta);
   const int n_tiles = (seq_len + kTile - 1) / kTile;
   const size_t n_trig = (size_t)n_tiles * d.dh * kTile;
@@ -356,6 +364,7 @@ hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_
   a.m_tile = reinterpret_cast<float*>(ws + rw.m_tile);
   a.m_split = reinterpret_cast<float*>(ws + rw.m_split);
   const dim3 grid(splits, (d.Hq + kRopeHeads - 1) / kRopeHeads, d.B);
+  if (before_scores) (void)hipEventRecord(before_scores, s);
   if (d.dh == 64)
     rope_score_kernel<64><<<grid, 256, 0, s>>>(a);
   else

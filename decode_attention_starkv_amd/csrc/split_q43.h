@@ -121,7 +121,10 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int b = blockIdx.y, sp = blockIdx.x;
-  const int n_tiles = (a.seq_len + kTile - 1) / kTile;
+  // this sequence's tokens (ragged batches: its own length; the splits are
+  // laid out for the longest, so a split may hold no tile of it)
+  const int seq_len = seq_len_of(d, b, a.seq_len);
+  const int n_tiles = (seq_len + kTile - 1) / kTile;
   const int tile0 = sp * a.tiles_per_split;
   const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
   const int GV = 4 * NIV;            // value groups
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     };
     auto score_pre = [&](int tile, int slot, const uint32_t (&sr)[KVS * G],
                          const float (&mt)[KVS * G]) {
-      const bool valid = lane < a.seq_len - tile * kTile;
+      const bool valid = lane < seq_len - tile * kTile;
 #pragma unroll
       for (int i = 0; i < KVS * G; ++i) {
         const float x = valid ? f16v(sr[i]) + (mt[i] - msplit[i]) : -INFINITY;
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
         const int kh = sw + ki * 4;
-        const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + kh;
+        const size_t blk = tile_index(d, b, tile) * d.Hkv + kh;
         const uint8_t* kb = kbase + blk * kKeyBlock;
         dst[ki][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + lane);
         dst[ki][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + lane);
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 
     // scores of tile `tile` into P slot `slot`; `it` = its index in the split
     auto score = [&](int tile, int it, int slot, const uint32_t (&kc)[KVS][6]) {
-      const int rem = a.seq_len - tile * kTile;
+      const int rem = seq_len - tile * kTile;
       const bool valid = lane < rem;
       float x[KVS * G];   // scores times 2^-24
 #pragma unroll
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     uint8_t* ring = vring + (four ? 0 : kHiRegion + (vw - 1) * kLoRegion);
 
     auto stage = [&](int tile, int slot) {
-      const size_t t = (size_t)b * d.NT + tile;
+      const size_t t = tile_index(d, b, tile);
       uint8_t* dst = ring + slot * kSlotBytes;
       wave_dma(vbase + t * tile_bytes + code_off, dst, code_bytes, lane);
       wave_dma(vmbase + t * meta_tile + (size_t)n0 * kTile * 2, dst + code_bytes, meta_bytes, lane);
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       uint8_t* vt = ring + vslot * kSlotBytes;
       _Float16* sc_l = reinterpret_cast<_Float16*>(vt + code_bytes);
       _Float16* zr_l = sc_l + NIV * kTile;
-      const int rem = a.seq_len - tile * kTile;
+      const int rem = seq_len - tile * kTile;
       if (rem < kTile) {
         // last, partial tile: zero the missing tokens' scales and zeros so
         // unused cache bytes never reach the MFMA operands

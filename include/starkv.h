@@ -243,8 +243,10 @@ STARKV_API int starkv_decode_step_profiled(
  * a caller can time each kernel on the stream it runs on.  Where the merge
  * and the up-projection run as one kernel (fp16 partials, R_v <= 256,
  * d_h <= 128, at most 64 splits), events[3] and events[4] are both recorded
- * after it.  Same arguments, results and errors as starkv_decode; EINVAL if
- * events is NULL. */
+ * after it.  With rotary keys (rope_theta > 0) events[0] is recorded right
+ * before the rotary score kernel instead (after the position table and the
+ * query coefficients), so events[0..1] time that kernel alone.  Same
+ * arguments, results and errors as starkv_decode; EINVAL if events is NULL. */
 STARKV_API int starkv_decode_profiled(const starkv_config* cfg,
                                       const starkv_cache* cache,
                                       int32_t seq_len, const void* q,
@@ -252,6 +254,47 @@ STARKV_API int starkv_decode_profiled(const starkv_config* cfg,
                                       float sm_scale, float* out,
                                       void* workspace, size_t ws_bytes,
                                       hipStream_t stream, hipEvent_t* events);
+
+/* ---- paged and ragged 4/3-bit caches (vLLM-style KV blocks) -----------
+ * The cache buffers are a pool of B * (max_tokens / 64) pages, each holding
+ * one 64-token tile of every KV head (the tile layout of the Q43 format
+ * above: key [page][Hkv][832 B], key_meta [page][Hkv][64][4], value
+ * [page][26 R_v B], value_meta [page][2][R_v/32][64]); starkv_cache_bytes
+ * gives their sizes.  page_table (device, int32 [B][pages_per_seq]) maps tile
+ * t of sequence b to its page; the contiguous cache is the table
+ * page(b, t) = b * (max_tokens / 64) + t.  Table entries are clamped into the
+ * pool on the device (a bad entry reads or writes a wrong page, never outside
+ * the buffers).  Q43 caches only; EUNSUPPORTED otherwise. */
+
+/* Append one token per sequence, each at its own position positions[b]
+ * (device int32 [B], clamped on the device to [0, pages_per_seq * 64)):
+ *   z_key fp32 [B][Hkv][r_k], z_value fp32 [B][R_v]; quantized, rotated and
+ *   packed exactly as starkv_append does.
+ * Errors: EINVAL (null / misaligned pointer, pages_per_seq < 1), EUNSUPPORTED,
+ * ELAUNCH. */
+STARKV_API int starkv_append_paged(const starkv_config* cfg,
+                                   const starkv_cache* cache,
+                                   const int32_t* page_table,
+                                   int32_t pages_per_seq,
+                                   const int32_t* positions, const float* z_key,
+                                   const float* z_value, hipStream_t stream);
+
+/* starkv_decode over a paged pool with ragged lengths: sequence b attends to
+ * its first seq_lens[b] tokens (device int32 [B], clamped on the device to
+ * [0, max_seq_len]; a length of 0 gives an all-zero output row).  The splits
+ * are laid out for max_seq_len (host), which must be <= max_tokens and
+ * <= pages_per_seq * 64.  With rotary keys the query of sequence b sits at
+ * position seq_lens[b] - 1.  Workspace: starkv_workspace_bytes(cfg, DECODE,
+ * max_seq_len).  Other arguments, results and errors as starkv_decode. */
+STARKV_API int starkv_decode_paged(const starkv_config* cfg,
+                                   const starkv_cache* cache,
+                                   const int32_t* page_table,
+                                   int32_t pages_per_seq,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   const void* q, const void* B_key,
+                                   const void* B_value, float sm_scale,
+                                   float* out, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* ---- value/output factor fusion and the head sum (review section 5.3,
  * eq. 12 read right to left; Algorithm 2, steps 7-8) ---------------------

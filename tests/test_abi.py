@@ -244,6 +244,29 @@ def test_rope_support_and_workspace():
                               0x8000, 1 << 34, None) == sk.STARKV_EUNSUPPORTED
 
 
+def test_paged_validation():
+    lib = sk.load_library()
+    w = synth.WORKLOADS["l2_q43"]
+    cfg = _cfg(w)
+    cp, cc = ctypes.byref(cfg), ctypes.byref(_fake_cache())
+    # append: table / positions / latents required, one page at least
+    assert lib.starkv_append_paged(cp, cc, None, 4, 0x100, 0x1000, 0x2000, None) == sk.STARKV_EINVAL
+    assert lib.starkv_append_paged(cp, cc, 0x100, 0, 0x200, 0x1000, 0x2000, None) == sk.STARKV_EINVAL
+    assert lib.starkv_append_paged(cp, cc, 0x102, 4, 0x200, 0x1000, 0x2000, None) == sk.STARKV_EINVAL
+    bf = _cfg(synth.WORKLOADS["l2_bf16"])
+    assert lib.starkv_append_paged(ctypes.byref(bf), cc, 0x100, 4, 0x200, 0x1000, 0x2000,
+                                   None) == sk.STARKV_EUNSUPPORTED
+    tail = (0x1000, 0x2000, 0x3000, ctypes.c_float(0.1), 0x4000, 0x5000, 1 << 30, None)
+    # decode: the pages must cover max_seq_len; max_seq_len within capacity
+    assert lib.starkv_decode_paged(cp, cc, 0x100, 4, 0x200, 257, *tail) == sk.STARKV_EINVAL
+    assert lib.starkv_decode_paged(cp, cc, 0x100, 4096, 0x200, w.max_tokens + 1,
+                                   *tail) == sk.STARKV_ECAPACITY
+    assert lib.starkv_decode_paged(cp, cc, None, 4, 0x200, 100, *tail) == sk.STARKV_EINVAL
+    assert lib.starkv_decode_paged(cp, cc, 0x100, 4, None, 100, *tail) == sk.STARKV_EINVAL
+    short = tail[:6] + (16, None)
+    assert lib.starkv_decode_paged(cp, cc, 0x100, 4, 0x200, 100, *short) == sk.STARKV_EWORKSPACE
+
+
 def test_call_validation_before_any_hip_call():
     w = synth.WORKLOADS["l2_q43"]
     lib = sk.load_library()
