@@ -53,13 +53,17 @@ TT = 64
 
 # ------------------------------------------------------------------ sizes --
 
-def layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache):
-    """Byte sizes of the four cache buffers."""
+def layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache,
+           key_ranks=None):
+    """Byte sizes of the four cache buffers.  key_ranks (fp32 / bf16 caches):
+    per-KV-head key ranks; the key buffer then holds sum(key_ranks) channels
+    per token (the technical review's eq. 15 sums the per-head ranks)."""
     assert max_tokens % TT == 0
     nt = max_tokens // TT
     if cache in ("f32", "bf16"):
         es = 4 if cache == "f32" else 2
-        return dict(key=batch * n_kv_heads * max_tokens * key_rank * es,
+        rsum = n_kv_heads * key_rank if key_ranks is None else int(sum(key_ranks))
+        return dict(key=batch * max_tokens * rsum * es,
                     key_meta=0,
                     value=batch * nt * value_rank * TT * es,
                     value_meta=0)
@@ -207,11 +211,16 @@ class Cache:
     """Byte-exact image of the four cache buffers, with append and read-out."""
 
     def __init__(self, batch, n_kv_heads, key_rank, value_rank, max_tokens,
-                 cache, rotate=False, fill=0):
+                 cache, rotate=False, fill=0, key_ranks=None):
         self.B, self.H, self.rk, self.rv = batch, n_kv_heads, key_rank, value_rank
         self.T, self.kind, self.rotate = max_tokens, cache, rotate
         self.nt = max_tokens // TT
-        sz = layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache)
+        # per-head key ranks (fp32 / bf16 caches): head g keeps key_ranks[g]
+        # channels; key_rank is the largest, the width of the latent rows
+        self.kr = None if key_ranks is None else [int(r) for r in key_ranks]
+        assert self.kr is None or (cache in ("f32", "bf16") and
+                                   all(r % 8 == 0 and 0 < r <= key_rank for r in self.kr))
+        sz = layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache, key_ranks)
         self.buf = {k: np.full(v, fill, np.uint8) for k, v in sz.items()}
 
     @classmethod
@@ -229,11 +238,27 @@ class Cache:
         dt = np.float32 if self.kind == "f32" else np.uint16
         kw = 8 if self.rk % 8 == 0 else self.rk
         gw = 32 if self.rv % 32 == 0 else self.rv
-        k = self.buf["key"].view(dt).reshape(
+        k = None if self.kr is not None else self.buf["key"].view(dt).reshape(
             self.B, self.H, self.nt, self.rk // kw, TT, kw).transpose(0, 1, 2, 4, 3, 5)
         v = self.buf["value"].view(dt).reshape(
             self.B, self.nt, self.rv // gw, 8, gw, 8).transpose(0, 1, 3, 5, 2, 4)
         return k, v
+
+    def _key_head_view(self, g):
+        """Per-head key view [B, tile, token, r_g/8, 8] of a cache with
+        per-head ranks: sequence b's key region holds the heads one after the
+        other, head g as [tile][r_g/8][64 tokens][8 channels] (writes through
+        the view land in the buffer)."""
+        dt = np.float32 if self.kind == "f32" else np.uint16
+        e = self.buf["key"].view(dt)
+        rg, rs = self.kr[g], sum(self.kr)
+        base = self.nt * TT * sum(self.kr[:g])
+        it = e.itemsize
+        v = np.lib.stride_tricks.as_strided(
+            e[base:], shape=(self.B, self.nt, rg // 8, TT, 8),
+            strides=(self.nt * TT * rs * it, (rg // 8) * TT * 8 * it, TT * 8 * it, 8 * it, it),
+            writeable=True)
+        return v.transpose(0, 1, 3, 2, 4)
 
     def _q_views(self):
         """Key views with axes (batch, head, tile, ...) over the tile-major
@@ -264,8 +289,13 @@ class Cache:
             else:
                 kk, vv = to_bf16_bits(zk), to_bf16_bits(zv)
             t = pos + np.arange(n)
-            k[:, :, t // TT, t % TT] = np.transpose(kk, (0, 2, 1, 3)).reshape(
-                self.B, self.H, n, *k.shape[4:])
+            if self.kr is None:
+                k[:, :, t // TT, t % TT] = np.transpose(kk, (0, 2, 1, 3)).reshape(
+                    self.B, self.H, n, *k.shape[4:])
+            else:
+                for g, rg in enumerate(self.kr):
+                    hv = self._key_head_view(g)
+                    hv[:, t // TT, t % TT] = kk[:, :, g, :rg].reshape(self.B, n, rg // 8, 8)
             v[:, t // TT, (t % TT) // 8, t % 8] = vv.reshape(self.B, n, *v.shape[4:])
             return
         if self.rotate:
@@ -318,6 +348,15 @@ class Cache:
     def key_latents(self, b, seq_len):
         """Dequantized (stored, i.e. rotated if enabled) key latents
         float64 [seq_len, Hkv, r_k] of batch element b."""
+        if self.kind in ("f32", "bf16") and self.kr is not None:
+            # channels past a head's rank read as 0
+            nt = (seq_len + TT - 1) // TT
+            out = np.zeros((seq_len, self.H, self.rk))
+            for g, rg in enumerate(self.kr):
+                x = self._key_head_view(g)[b, :nt].reshape(nt * TT, rg)[:seq_len]
+                x = x if self.kind == "f32" else from_bf16_bits(x)
+                out[:, g, :rg] = x
+            return out
         if self.kind in ("f32", "bf16"):
             k, _ = self._elem_views()
             nt = (seq_len + TT - 1) // TT
