@@ -34,11 +34,14 @@ int check_config(const starkv_config* c) {
     return STARKV_EINVAL;   // unquantized caches have no precision split
   }
   if (c->key_ranks) {
+    if (c->n_kv_heads > kMaxQHeads) return STARKV_EUNSUPPORTED;
     for (int g = 0; g < c->n_kv_heads; ++g)
       if (c->key_ranks[g] < 8 || c->key_ranks[g] % 8 != 0 ||
           c->key_ranks[g] > c->key_rank)
         return STARKV_EINVAL;
-    return STARKV_EUNSUPPORTED;
+    // per-head ranks: the unquantized caches (the 4/3-bit key tile is built
+    // for 32 channels)
+    if (quant) return STARKV_EUNSUPPORTED;
   }
   // rotary keys: the 4/3-bit cache's decode only (rope.hip), head_dim 64 or 128
   if (c->rope_theta > 0.0f &&
@@ -104,8 +107,13 @@ size_t cache_bytes(const starkv_config& c, int which) {
     }
   }
   const size_t es = c.cache_dtype == STARKV_CACHE_F32 ? 4 : 2;
+  size_t rsum = H * rk;   // eq. 15: the sum of the per-head key ranks
+  if (c.key_ranks) {
+    rsum = 0;
+    for (int g = 0; g < c.n_kv_heads; ++g) rsum += c.key_ranks[g];
+  }
   switch (which) {
-    case STARKV_BUF_KEY: return B * H * T * rk * es;
+    case STARKV_BUF_KEY: return B * T * rsum * es;
     case STARKV_BUF_VALUE: return B * NT * rv * kTile * es;
     default: return 0;
   }

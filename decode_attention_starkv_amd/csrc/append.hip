@@ -97,10 +97,11 @@ __global__ void append_plain_keys(const float* __restrict__ zk, void* key,
   r /= d.Hkv;
   int i = r % n;
   int b = r / n;
-  // [B][Hkv][tile][r_k/8][64 tokens][8 channels]
+  // per-head regions [NT][r_g/8][64 tokens][8 channels]; z_key rows are
+  // r_k (the largest rank) wide, channels past the head's rank are skipped
+  if (c >= d.krank[h]) return;
   const int t = pos + i;
-  size_t dst = (((((size_t)b * d.Hkv + h) * d.NT + t / kTile) * (d.rk / 8) + c / 8) * kTile +
-                t % kTile) * 8 + c % 8;
+  const size_t dst = plain_key_offset(d, b, h, t / kTile, c / 8, t % kTile) + c % 8;
   if (kBf16)
     static_cast<uint16_t*>(key)[dst] = bf16_bits_rn(zk[idx]);
   else

@@ -58,7 +58,8 @@ __device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
                                         float* sc) {
   const Dims& d = a.d;
   // chunk c of this token's key row: [b][kh][tile][c][lane][8 channels]
-  const size_t row0 = (((size_t)b * d.Hkv + kh) * d.NT + tile) * (d.rk / 8) * (kTile * 8) + lane * 8;
+  const size_t row0 = plain_key_offset(d, b, kh, tile, 0, lane);
+  const int rank = d.krank[kh];            // this KV head's key rank
   // the record offset is made opaque per call so the records are read from
   // LDS where they are used instead of being held in registers across tiles
   int rec_off = kh * G * kPlainRec;
@@ -72,7 +73,7 @@ __device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.0f;
 #pragma unroll 1
-    for (int c = 0; c < NC && 8 * c < d.rk; ++c) {
+    for (int c = 0; c < NC && 8 * c < rank; ++c) {
       float z[8];
       const size_t row = row0 + (size_t)c * (kTile * 8);
       if constexpr (FMT == STARKV_CACHE_F32) {
@@ -108,8 +109,9 @@ __device__ inline void score_tile_plain(const SplitArgs& a, const float* qrec,
   uint32_t kw[NC][CW];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    // chunks past r_k (when RK rounds it up) are neither read nor used
-    const bool live = 8 * c < d.rk;
+    // chunks past the head's rank (RK rounds the largest up) are neither
+    // read nor used
+    const bool live = 8 * c < rank;
     const size_t row = row0 + (size_t)(live ? c : 0) * (kTile * 8);
     if constexpr (FMT == STARKV_CACHE_F32) {
       const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.key) + row);

@@ -24,7 +24,23 @@ struct Dims {
   int pages_per_seq = 0;
   const int32_t* lens = nullptr;   // device [B]: tokens of each sequence (decode)
   const int32_t* positions = nullptr;  // device [B]: append position of each sequence
+  // Key rank of each KV head and the channel offset of its key region
+  // (per-head ranks; for uniform ranks krank[g] = rk, kpre[g] = g * rk);
+  // kpre[Hkv] = sum of the ranks.
+  uint8_t krank[kMaxQHeads];
+  uint16_t kpre[kMaxQHeads + 1];
 };
+
+// Element offset, in an unquantized key buffer, of the 8-channel chunk c of
+// token u of tile `tile` of KV head g of sequence b.  Layout: per sequence,
+// the KV heads' regions one after the other, head g's region
+// [NT][r_g/8][64 tokens][8 channels] (with uniform ranks this is
+// [B][Hkv][NT][r_k/8][64][8]).
+__host__ __device__ inline size_t plain_key_offset(const Dims& d, int b, int g, int tile,
+                                                   int c, int u) {
+  return (size_t)d.NT * kTile * ((size_t)b * d.kpre[d.Hkv] + d.kpre[g]) +
+         ((size_t)tile * (d.krank[g] / 8) + c) * (kTile * 8) + (size_t)u * 8;
+}
 
 // Index of the 64-token tile `tile` of sequence b in the cache buffers: the
 // contiguous layout b * NT + tile, or the page the table maps it to (clamped
@@ -60,6 +76,15 @@ inline Dims make_dims(const starkv_config& c) {
   d.dtype = c.cache_dtype;
   d.rotate = c.rotate;
   d.rope_theta = c.rope_theta;
+  int off = 0;
+  for (int g = 0; g < kMaxQHeads; ++g) {
+    const int r = g < c.n_kv_heads ? (c.key_ranks ? c.key_ranks[g] : c.key_rank) : 0;
+    d.krank[g] = (uint8_t)r;
+    d.kpre[g] = (uint16_t)off;
+    off += r;
+  }
+  d.kpre[kMaxQHeads] = (uint16_t)off;
+  if (c.n_kv_heads < kMaxQHeads) d.kpre[c.n_kv_heads] = (uint16_t)off;
   return d;
 }
 

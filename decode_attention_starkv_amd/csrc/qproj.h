@@ -32,7 +32,8 @@ __device__ inline void qproj_block(const void* __restrict__ q,
   const int c = t % rkp, chunk = t / rkp, nch = 256 / rkp;
   const int klen = (d.dh + nch - 1) / nch;
   float acc = 0.0f;
-  if (c < d.rk) {
+  const int rank = d.krank[g];       // B_key is [Hkv][d_h][r_k] with r_k the largest rank
+  if (c < rank) {
     const int k0 = chunk * klen, k1 = min(d.dh, k0 + klen);
 #pragma unroll 16
     for (int k = k0; k < k1; ++k) {
@@ -64,7 +65,7 @@ __device__ inline void qproj_block(const void* __restrict__ q,
   if (FMT != STARKV_CACHE_Q43) {
     // the whole record: entries past r_k are zeros (the split kernels read
     // key rows in 8-channel chunks and may pad them)
-    static_cast<float*>(qt)[(size_t)bh * kPlainRec + t] = t < d.rk ? v : 0.0f;
+    static_cast<float*>(qt)[(size_t)bh * kPlainRec + t] = t < rank ? v : 0.0f;
     return;
   }
   if (t < 32) sq[t] = (_Float16)v;

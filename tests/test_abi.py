@@ -267,6 +267,20 @@ def test_paged_validation():
     assert lib.starkv_decode_paged(cp, cc, 0x100, 4, 0x200, 100, *short) == sk.STARKV_EWORKSPACE
 
 
+def test_per_head_key_ranks_cache_bytes():
+    w = synth.WORKLOADS["l2_bf16"]
+    ranks = [8, 64, 24, 40] * 8
+    cfg = _cfg(w, key_rank=64, key_ranks=ranks)
+    lay = oc.layout(w.batch, w.n_kv_heads, 64, w.value_rank, w.max_tokens, "bf16",
+                    key_ranks=ranks)
+    assert sk.starkv_cache_bytes(cfg, sk.BUF_KEY) == lay["key"] == \
+        w.batch * w.max_tokens * sum(ranks) * 2
+    assert sk.starkv_decode_splits(cfg, 1000) > 0
+    # the 4/3-bit key tile is built for 32 channels: no per-head ranks there
+    q = _cfg(synth.WORKLOADS["l2_q43"], key_ranks=[32] * 32)
+    assert sk.starkv_cache_bytes(q, 0) == 0
+
+
 def test_call_validation_before_any_hip_call():
     w = synth.WORKLOADS["l2_q43"]
     lib = sk.load_library()
