@@ -327,6 +327,11 @@ def run_prefill(args, w, torch, sk, synth):
         "kernels_ms": {"gemm": mean(kern[0]), "append": mean(kern[1]),
                        "qproj": mean(kern[2]), "attention": attn_ms,
                        "merge_vproj": mean(kern[4])},
+        # the latent projection Z = X A (Algorithm 2, step 1) on MFMA
+        "projection_gemm_mfma": {
+            "flop": gemm_flops,
+            "tflops": gemm_flops / (mean(kern[0]) * 1e-3) / 1e12,
+            "frac": gemm_flops / (mean(kern[0]) * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS},
         "algorithmic_flops": {"attention": attn_flops, "projection": gemm_flops},
     }
     if not args.no_cpu_baseline:
@@ -634,6 +639,15 @@ def main():
         "decode_call_ms": mean(call_ms),
         "decode_call_hbm_frac": (cache_bytes + factor_bytes) / (mean(call_ms) * 1e-3) / 1e9
                                 / HBM_PEAK_GBS,
+        # the joint-value contraction P Z_v on MFMA inside the split kernel:
+        # 2 B T Hq R_v flop against the dense fp16 MFMA peak (the kernel is
+        # bound by HBM, so this is low by design; it is the step the pages
+        # move onto matrix units)
+        "pzv_mfma": {"flop": 2.0 * tokens * w.n_q_heads * w.value_rank,
+                     "tflops": 2.0 * tokens * w.n_q_heads * w.value_rank
+                               / (split_ms * 1e-3) / 1e12,
+                     "frac": 2.0 * tokens * w.n_q_heads * w.value_rank
+                             / (split_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS},
         "ms_per_step_percentiles": percentiles(step_ms),
         "split_ms_percentiles": percentiles(kern_ms[1]),
         # with rotary keys the first interval is the rotary score kernel
