@@ -217,10 +217,12 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     const u32x2* kmeta = reinterpret_cast<const u32x2*>(a.kmeta);
     uint32_t kA[KVS][6], kB[KVS][6];
     auto load_keys = [&](int tile, uint32_t (&dst)[KVS][6]) {
+      // the tile's slot (page) once per tile, not once per KV head
+      const size_t tix = tile_index(d, b, tile) * d.Hkv;
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
         const int kh = sw + ki * 4;
-        const size_t blk = tile_index(d, b, tile) * d.Hkv + kh;
+        const size_t blk = tix + kh;
         const uint8_t* kb = kbase + blk * kKeyBlock;
         dst[ki][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + lane);
         dst[ki][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + lane);
