@@ -184,87 +184,83 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
           (__attribute__((address_space(3))) void*)(&trig_l[slot][k * 64]), 16, 0, 0);
     }
   };
-  // the lane's token: 4-bit word, two 3-bit words, remainder byte, meta
-  uint32_t kc[2][2][6];
-  auto load_keys = [&](int tile, int set) {
+  // the lane's token: 4-bit word, two 3-bit words, remainder byte, meta;
+  // three register sets: keys are loaded two tiles ahead
+  uint32_t kc[3][2][6];
+  auto load_keys = [&](int tile, uint32_t (&dst)[2][6]) {
+    const size_t tix = tile_index(d, b, tile) * d.Hkv;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
-      const int g = kv == 0 ? g0 : g1;
-      const size_t blk = tile_index(d, b, tile) * d.Hkv + g;
+      const size_t blk = tix + (kv == 0 ? g0 : g1);
       const uint8_t* kb = kbase + blk * kKeyBlock;
-      kc[set][kv][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + l);
-      kc[set][kv][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + l);
-      kc[set][kv][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + l);
-      kc[set][kv][3] = __builtin_nontemporal_load(kb + 768 + l);
+      dst[kv][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + l);
+      dst[kv][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + l);
+      dst[kv][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + l);
+      dst[kv][3] = __builtin_nontemporal_load(kb + 768 + l);
       const u32x2 mt = __builtin_nontemporal_load(kmeta + blk * kTile + l);
-      kc[set][kv][4] = mt[0];
-      kc[set][kv][5] = mt[1];
+      dst[kv][4] = mt[0];
+      dst[kv][5] = mt[1];
     }
   };
-  // loads per tile and wave: trig chunks + 5 per KV head (always both sets,
-  // the second a duplicate when the wave's heads share a KV head)
-  constexpr int kLoadsPerTile = kChunksPerWave + 10;
+  // loads per issue: 5 per KV head (both sets, the second a duplicate when
+  // the wave's heads share one) and the wave's trig chunks
+  constexpr int kKeyLoads = 10;
 
   float m_run[2] = {-INFINITY, -INFINITY};
   float* qt = &qt_l[w][0];
   const size_t tpad = (size_t)d.NT * kTile;
 
-  // (a split may hold no tile of a shorter sequence: then nothing is loaded,
-  // and no direct-to-LDS load is left in flight when the workgroup ends)
-  if (tile0 < tile1) {
-    stage(tile0, 0);
-    load_keys(tile0, 0);
-  }
-  for (int tile = tile0, it = 0; tile < tile1; ++tile, ++it) {
-    const int slot = it & 1, set = it & 1;
-    if (tile + 1 < tile1) {
-      stage(tile + 1, slot ^ 1);
-      load_keys(tile + 1, set ^ 1);
-      rope_wait_vmcnt<kLoadsPerTile>();
-    } else {
-      rope_wait_vmcnt<0>();
-    }
+  // one tile: issue the trig of tile + 1 and the keys of tile + 2, wait for
+  // this tile's trig (older loads -- its keys included -- are then done),
+  // score both heads
+  auto step = [&](int tile, int it, const uint32_t (&cur)[2][6], uint32_t (&ahead)[2][6]) {
+    const int slot = it & 1;
+    const bool more1 = tile + 1 < tile1, more2 = tile + 2 < tile1;
+    if (more1) stage(tile + 1, slot ^ 1);
+    if (more2) load_keys(tile + 2, ahead);
+    // loads issued after this tile's trig: keys(tile+1) [last step],
+    // trig(tile+1) and keys(tile+2) [this step]
+    if (more2) rope_wait_vmcnt<2 * kKeyLoads + kChunksPerWave>();
+    else if (more1) rope_wait_vmcnt<kKeyLoads + kChunksPerWave>();
+    else rope_wait_vmcnt<0>();
     lds_barrier();   // every wave's trig chunks of this tile are in LDS
-
-    // dequantized latents of the lane's token, per KV head of the wave
-    float zf[2][32];
-#pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-      const uint32_t* k = kc[set][kv];
-      const uint32_t hi = k[0], lo0 = k[1], lo1 = k[2];
-      const uint32_t rem = (k[3] & 0xFFu) | (((lo0 >> 15) & 1u) << 8) |
-                           (((lo0 >> 31) & 1u) << 9) | (((lo1 >> 15) & 1u) << 10) |
-                           (((lo1 >> 31) & 1u) << 11);
-      const h2 mh = __builtin_bit_cast(h2, k[4]), ml = __builtin_bit_cast(h2, k[5]);
-      const float sh = (float)mh[0], zh = (float)mh[1], sl = (float)ml[0], zl = (float)ml[1];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) zf[kv][c] = fmaf(sh, (float)((hi >> (4 * c)) & 15u), zh);
-#pragma unroll
-      for (int i = 0; i < 24; ++i) {
-        uint32_t code;
-        if (i < 5) code = (lo0 >> (3 * i)) & 7u;
-        else if (i < 10) code = (lo1 >> (3 * (i - 5))) & 7u;
-        else if (i < 15) code = (lo0 >> (16 + 3 * (i - 10))) & 7u;
-        else if (i < 20) code = (lo1 >> (16 + 3 * (i - 15))) & 7u;
-        else code = (rem >> (3 * (i - 20))) & 7u;
-        zf[kv][8 + i] = fmaf(sl, (float)code, zl);
-      }
-    }
 
     const h8* tr = &trig_l[slot][0];
     const bool valid = tile * kTile + l < seq_len;
+    float zf[32];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const bool on = hh == 0 ? on0 : on1;
       if (!on) continue;
       const int h = h0 + hh;
-      const int kv = (hh == 1 && two_kv) ? 1 : 0;
+      if (hh == 0 || two_kv) {
+        // dequantized latent of the lane's token for this head's KV head
+        const uint32_t* k = cur[hh == 1 && two_kv ? 1 : 0];
+        const uint32_t hi = k[0], lo0 = k[1], lo1 = k[2];
+        const uint32_t rem = (k[3] & 0xFFu) | (((lo0 >> 15) & 1u) << 8) |
+                             (((lo0 >> 31) & 1u) << 9) | (((lo1 >> 15) & 1u) << 10) |
+                             (((lo1 >> 31) & 1u) << 11);
+        const h2 mh = __builtin_bit_cast(h2, k[4]), ml = __builtin_bit_cast(h2, k[5]);
+        const float sh = (float)mh[0], zh = (float)mh[1], sl = (float)ml[0], zl = (float)ml[1];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) zf[c] = fmaf(sh, (float)((hi >> (4 * c)) & 15u), zh);
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+          uint32_t code;
+          if (i < 5) code = (lo0 >> (3 * i)) & 7u;
+          else if (i < 10) code = (lo1 >> (3 * (i - 5))) & 7u;
+          else if (i < 15) code = (lo0 >> (16 + 3 * (i - 10))) & 7u;
+          else if (i < 20) code = (lo1 >> (16 + 3 * (i - 15))) & 7u;
+          else code = (rem >> (3 * (i - 20))) & 7u;
+          zf[8 + i] = fmaf(sl, (float)code, zl);
+        }
+      }
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const h8 t0 = tr[(2 * s) * 64 + l], t1 = tr[(2 * s + 1) * 64 + l];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s], t0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s], t1, acc1, 0, 0, 0);
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const h8 t0 = tr[(2 * s2) * 64 + l], t1 = tr[(2 * s2 + 1) * 64 + l];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s2], t0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s2], t1, acc1, 0, 0, 0);
       }
       // D[r][token]: lane l holds token l % 32 (acc0) and 32 + l % 32 (acc1),
       // rows acc_row(v, l); through LDS so that lane = token
@@ -282,10 +278,10 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
 #pragma unroll
       for (int r = 0; r < 32; r += 4) {
         const float4 x = *reinterpret_cast<const float4*>(qt + l * kQtStride + r);
-        sc = fmaf(x.x, zf[kv][r], sc);
-        sc = fmaf(x.y, zf[kv][r + 1], sc);
-        sc = fmaf(x.z, zf[kv][r + 2], sc);
-        sc = fmaf(x.w, zf[kv][r + 3], sc);
+        sc = fmaf(x.x, zf[r], sc);
+        sc = fmaf(x.y, zf[r + 1], sc);
+        sc = fmaf(x.z, zf[r + 2], sc);
+        sc = fmaf(x.w, zf[r + 3], sc);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next head writes
       __builtin_amdgcn_wave_barrier();
@@ -297,7 +293,23 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
       srel[((size_t)b * d.Hq + h) * tpad + (size_t)tile * kTile + l] = (_Float16)rel;
       if (l == 0) a.m_tile[((size_t)b * d.Hq + h) * d.NT + tile] = mn;
     }
-    lds_barrier();   // the slot read here is restaged next iteration
+    lds_barrier();   // the slot read here is restaged next step
+  };
+
+  // (a split may hold no tile of a shorter sequence: then nothing is loaded,
+  // and no direct-to-LDS load is left in flight when the workgroup ends)
+  if (tile0 < tile1) {
+    load_keys(tile0, kc[0]);
+    stage(tile0, 0);
+    if (tile0 + 1 < tile1) load_keys(tile0 + 1, kc[1]);
+  }
+  // three steps per round so that the register sets are named statically
+  for (int tile = tile0, it = 0; tile < tile1; tile += 3, it += 3) {
+    step(tile, it, kc[0], kc[2]);
+    if (tile + 1 >= tile1) break;
+    step(tile + 1, it + 1, kc[1], kc[0]);
+    if (tile + 2 >= tile1) break;
+    step(tile + 2, it + 2, kc[2], kc[1]);
   }
   if (l == 0) {
     if (on0) a.m_split[((size_t)b * a.splits + sp) * d.Hq + h0] = m_run[0];
