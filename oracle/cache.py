@@ -38,6 +38,15 @@ of 128: channels [0, R_v/4) at 4 bits, the rest at 3 bits):
         3-bit, u = 30: code bit k is bit 15 of word k; u = 31: bit 31 of word k
   value meta [B][tile][2][R_v/32][64] fp16: plane 0 scales, plane 1 zeros.
 
+uniform 4-bit cache (lo_bits = 4; the 4-bit cache of the review's speed
+figures, section 6.1 after eq. 14): the same precision blocks, groups and
+rotation, both blocks at 4 bits:
+  key codes  [B][tile][Hkv] blocks of 1024 B: four u32[64] planes, plane p
+      holding key channels 8p .. 8p+7 of each token as nibbles (channel 8p+c
+      at bits 4c, the layout of the q43 hi plane);
+  value codes [B][tile] blocks of 32*R_v B: every group in the 4-bit run
+      layout above.  Metadata as for q43.
+
 Appending tokens [pos, pos+n) changes only the bits and metadata of those
 tokens; every other bit of the buffers keeps its previous value.
 """
@@ -53,8 +62,18 @@ TT = 64
 
 # ------------------------------------------------------------------ sizes --
 
+def key_block_bytes(lo_bits=3):
+    """Bytes of one packed key tile of one KV head."""
+    return 832 if lo_bits == 3 else 1024
+
+
+def value_tile_bytes(value_rank, lo_bits=3):
+    """Bytes of one packed value tile (all groups of one 64-token tile)."""
+    return (26 if lo_bits == 3 else 32) * value_rank
+
+
 def layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache,
-           key_ranks=None):
+           key_ranks=None, lo_bits=3):
     """Byte sizes of the four cache buffers.  key_ranks (fp32 / bf16 caches):
     per-KV-head key ranks; the key buffer then holds sum(key_ranks) channels
     per token (the technical review's eq. 15 sums the per-head ranks)."""
@@ -68,9 +87,10 @@ def layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache,
                     value=batch * nt * value_rank * TT * es,
                     value_meta=0)
     assert cache == "q43" and key_rank == 32 and value_rank % 128 == 0
-    return dict(key=batch * n_kv_heads * nt * 832,
+    assert lo_bits in (3, 4)
+    return dict(key=batch * n_kv_heads * nt * key_block_bytes(lo_bits),
                 key_meta=batch * n_kv_heads * nt * TT * 8,
-                value=batch * nt * value_rank * 26,
+                value=batch * nt * value_tile_bytes(value_rank, lo_bits),
                 value_meta=batch * nt * 2 * (value_rank // 32) * TT * 2)
 
 
@@ -106,9 +126,19 @@ def _key_lo_bit(i: int, k: int):
 
 # ------------------------------------------------------------ pack/unpack --
 
-def pack_key_tiles(codes: np.ndarray) -> np.ndarray:
-    """codes uint8 [N, 64, 32] -> bytes uint8 [N, 832]."""
+def pack_key_tiles(codes: np.ndarray, lo_bits: int = 3) -> np.ndarray:
+    """codes uint8 [N, 64, 32] -> bytes uint8 [N, 832] (lo_bits 3) or
+    [N, 1024] (lo_bits 4: four nibble planes)."""
     n = codes.shape[0]
+    if lo_bits == 4:
+        c = codes.astype(np.uint32)
+        out = np.empty((n, 1024), np.uint8)
+        for p in range(4):
+            w = np.zeros((n, TT), np.uint32)
+            for ch in range(8):
+                w |= (c[:, :, 8 * p + ch] & 15) << (4 * ch)
+            out[:, 256 * p:256 * (p + 1)] = w.astype("<u4").view(np.uint8).reshape(n, 256)
+        return out
     c = codes.astype(np.uint32)
     hi = np.zeros((n, TT), np.uint32)
     for ch in range(8):
@@ -126,10 +156,18 @@ def pack_key_tiles(codes: np.ndarray) -> np.ndarray:
     return out
 
 
-def unpack_key_tiles(blob: np.ndarray) -> np.ndarray:
-    """bytes uint8 [N, 832] -> codes uint8 [N, 64, 32]."""
+def unpack_key_tiles(blob: np.ndarray, lo_bits: int = 3) -> np.ndarray:
+    """bytes uint8 [N, 832] (or [N, 1024], lo_bits 4) -> codes uint8
+    [N, 64, 32]."""
     n = blob.shape[0]
     blob = np.ascontiguousarray(blob)
+    if lo_bits == 4:
+        codes = np.zeros((n, TT, 32), np.uint32)
+        for p in range(4):
+            w = blob[:, 256 * p:256 * (p + 1)].copy().view("<u4").astype(np.uint32)
+            for ch in range(8):
+                codes[:, :, 8 * p + ch] = (w >> (4 * ch)) & 15
+        return codes.astype(np.uint8)
     hi = blob[:, 0:256].copy().view("<u4").astype(np.uint32)
     lo0 = blob[:, 256:512].copy().view("<u4").astype(np.uint32)
     lo1 = blob[:, 512:768].copy().view("<u4").astype(np.uint32)
@@ -145,24 +183,25 @@ def unpack_key_tiles(blob: np.ndarray) -> np.ndarray:
     return codes.astype(np.uint8)
 
 
-def _value_regions(value_rank: int):
+def _value_regions(value_rank: int, lo_bits: int = 3):
     """[(first channel, bits, byte offset, words per run)] per 32-ch group."""
     n_hi = value_rank // 4
     regs, off = [], 0
     for g in range(value_rank // 32):
-        bits = 4 if 32 * g < n_hi else 3
+        bits = 4 if 32 * g < n_hi else lo_bits
         regs.append((32 * g, bits, off, bits))
         off += 2 * 32 * bits * 4
-    assert off == 26 * value_rank
+    assert off == value_tile_bytes(value_rank, lo_bits)
     return regs
 
 
-def pack_value_tiles(codes: np.ndarray) -> np.ndarray:
-    """codes uint8 [N, 64, R_v] -> bytes uint8 [N, 26*R_v]."""
+def pack_value_tiles(codes: np.ndarray, lo_bits: int = 3) -> np.ndarray:
+    """codes uint8 [N, 64, R_v] -> bytes uint8 [N, 26*R_v] (32*R_v with
+    lo_bits 4)."""
     n, _, rv = codes.shape
-    out = np.empty((n, 26 * rv), np.uint8)
+    out = np.empty((n, value_tile_bytes(rv, lo_bits)), np.uint8)
     c = codes.astype(np.uint32)
-    for c0, bits, off, nw in _value_regions(rv):
+    for c0, bits, off, nw in _value_regions(rv, lo_bits):
         words = np.zeros((n, 2, 32, nw), np.uint32)   # [tile, half, ch, word]
         grp = c[:, :, c0:c0 + 32]                      # [tile, token, ch]
         for j in range(2):
@@ -176,11 +215,12 @@ def pack_value_tiles(codes: np.ndarray) -> np.ndarray:
     return out
 
 
-def unpack_value_tiles(blob: np.ndarray, value_rank: int) -> np.ndarray:
-    """bytes uint8 [N, 26*R_v] -> codes uint8 [N, 64, R_v]."""
+def unpack_value_tiles(blob: np.ndarray, value_rank: int, lo_bits: int = 3) -> np.ndarray:
+    """bytes uint8 [N, 26*R_v] (32*R_v with lo_bits 4) -> codes uint8
+    [N, 64, R_v]."""
     n = blob.shape[0]
     codes = np.zeros((n, TT, value_rank), np.uint32)
-    for c0, bits, off, nw in _value_regions(value_rank):
+    for c0, bits, off, nw in _value_regions(value_rank, lo_bits):
         size = 2 * 32 * nw * 4
         words = np.ascontiguousarray(blob[:, off:off + size]).view("<u4")
         words = words.astype(np.uint32).reshape(n, 2, 32, nw)
@@ -211,16 +251,18 @@ class Cache:
     """Byte-exact image of the four cache buffers, with append and read-out."""
 
     def __init__(self, batch, n_kv_heads, key_rank, value_rank, max_tokens,
-                 cache, rotate=False, fill=0, key_ranks=None):
+                 cache, rotate=False, fill=0, key_ranks=None, lo_bits=3):
         self.B, self.H, self.rk, self.rv = batch, n_kv_heads, key_rank, value_rank
         self.T, self.kind, self.rotate = max_tokens, cache, rotate
+        self.lob = lo_bits        # bits of the trailing precision block (q43)
         self.nt = max_tokens // TT
         # per-head key ranks (fp32 / bf16 caches): head g keeps key_ranks[g]
         # channels; key_rank is the largest, the width of the latent rows
         self.kr = None if key_ranks is None else [int(r) for r in key_ranks]
         assert self.kr is None or (cache in ("f32", "bf16") and
                                    all(r % 8 == 0 and 0 < r <= key_rank for r in self.kr))
-        sz = layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache, key_ranks)
+        sz = layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache, key_ranks,
+                    lo_bits)
         self.buf = {k: np.full(v, fill, np.uint8) for k, v in sz.items()}
 
     @classmethod
@@ -228,7 +270,7 @@ class Cache:
         return cls(w.batch if batch is None else batch, w.n_kv_heads,
                    w.key_rank, w.value_rank,
                    w.max_tokens if max_tokens is None else max_tokens,
-                   w.cache, w.rotate, fill)
+                   w.cache, w.rotate, fill, lo_bits=getattr(w, "lo_bits", 3))
 
     # -- views -------------------------------------------------------------
     def _elem_views(self):
@@ -263,10 +305,11 @@ class Cache:
     def _q_views(self):
         """Key views with axes (batch, head, tile, ...) over the tile-major
         buffers (writes through the views land in the buffers)."""
-        k = self.buf["key"].reshape(self.B, self.nt, self.H, 832).transpose(0, 2, 1, 3)
+        kb = key_block_bytes(self.lob)
+        k = self.buf["key"].reshape(self.B, self.nt, self.H, kb).transpose(0, 2, 1, 3)
         km = self.buf["key_meta"].view(np.uint16).reshape(
             self.B, self.nt, self.H, TT, 4).transpose(0, 2, 1, 3, 4)
-        v = self.buf["value"].reshape(self.B, self.nt, 26 * self.rv)
+        v = self.buf["value"].reshape(self.B, self.nt, value_tile_bytes(self.rv, self.lob))
         vm = self.buf["value_meta"].view(np.uint16).reshape(
             self.B, self.nt, 2, self.rv // 32, TT)
         return k, km, v, vm
@@ -302,11 +345,11 @@ class Cache:
             zk = hadamard.rotate_latent_f32(zk, self.rk // 4)
             zv = hadamard.rotate_latent_f32(zv, self.rv // 4)
         kq_hi = quant.quantize(zk[..., :8], 4)
-        kq_lo = quant.quantize(zk[..., 8:], 3)
+        kq_lo = quant.quantize(zk[..., 8:], self.lob)
         nhi = self.rv // 4
         vgr = zv.reshape(self.B, n, self.rv // 32, 32)
         vq4 = quant.quantize(vgr[:, :, :nhi // 32], 4)
-        vq3 = quant.quantize(vgr[:, :, nhi // 32:], 3)
+        vq3 = quant.quantize(vgr[:, :, nhi // 32:], self.lob)
         kcodes = np.concatenate([kq_hi[0], kq_lo[0]], axis=-1)     # [B,n,H,32]
         vcodes = np.concatenate([vq4[0], vq3[0]], axis=2).reshape(self.B, n, self.rv)
         vscale = np.concatenate([vq4[1], vq3[1]], axis=2)          # [B,n,G]
@@ -319,23 +362,24 @@ class Cache:
         sel = (win >= 0) & (win < n)
         src = np.clip(win, 0, max(n - 1, 0))
         # keys: unpack the touched tiles, overwrite the appended tokens, repack
-        cur = unpack_key_tiles(kb[:, :, ta:tb].reshape(-1, 832)).reshape(
-            self.B, self.H, nt * TT, 32)
+        cur = unpack_key_tiles(kb[:, :, ta:tb].reshape(-1, key_block_bytes(self.lob)),
+                               self.lob).reshape(self.B, self.H, nt * TT, 32)
         newk = np.transpose(kcodes, (0, 2, 1, 3))[:, :, src]
         cur = np.where(sel[None, None, :, None], newk, cur)
-        kb[:, :, ta:tb] = pack_key_tiles(cur.reshape(-1, TT, 32)).reshape(
-            self.B, self.H, nt, 832)
+        kb[:, :, ta:tb] = pack_key_tiles(cur.reshape(-1, TT, 32), self.lob).reshape(
+            self.B, self.H, nt, key_block_bytes(self.lob))
         meta = np.stack([kq_hi[1], kq_hi[2], kq_lo[1], kq_lo[2]], axis=-1)
         oldm = km[:, :, ta:tb].reshape(self.B, self.H, nt * TT, 4)
         newm = np.transpose(meta, (0, 2, 1, 3))[:, :, src]
         km[:, :, ta:tb] = np.where(sel[None, None, :, None], newm, oldm).reshape(
             self.B, self.H, nt, TT, 4)
         # values
-        curv = unpack_value_tiles(vb[:, ta:tb].reshape(-1, 26 * self.rv),
-                                  self.rv).reshape(self.B, nt * TT, self.rv)
+        vtb = value_tile_bytes(self.rv, self.lob)
+        curv = unpack_value_tiles(vb[:, ta:tb].reshape(-1, vtb),
+                                  self.rv, self.lob).reshape(self.B, nt * TT, self.rv)
         curv = np.where(sel[None, :, None], vcodes[:, src], curv)
-        vb[:, ta:tb] = pack_value_tiles(curv.reshape(-1, TT, self.rv)).reshape(
-            self.B, nt, 26 * self.rv)
+        vb[:, ta:tb] = pack_value_tiles(curv.reshape(-1, TT, self.rv), self.lob).reshape(
+            self.B, nt, vtb)
         for plane, arr in ((0, vscale), (1, vzero)):
             old_ = np.transpose(vm[:, ta:tb, plane], (0, 2, 1, 3)).reshape(
                 self.B, -1, nt * TT)                       # [B, G, nt*64]
@@ -365,8 +409,8 @@ class Cache:
             return np.transpose(x, (1, 0, 2)).astype(np.float64)
         kb, km, _, _ = self._q_views()
         nt = (seq_len + TT - 1) // TT
-        codes = unpack_key_tiles(kb[b, :, :nt].reshape(-1, 832)).reshape(
-            self.H, nt * TT, 32)[:, :seq_len]
+        codes = unpack_key_tiles(kb[b, :, :nt].reshape(-1, key_block_bytes(self.lob)),
+                                 self.lob).reshape(self.H, nt * TT, 32)[:, :seq_len]
         meta = km[b, :, :nt].reshape(self.H, nt * TT, 4)[:, :seq_len]
         # only stored tokens are dequantized (slots past seq_len may hold any
         # bytes, NaN scales included)
@@ -384,7 +428,7 @@ class Cache:
             x = x if self.kind == "f32" else from_bf16_bits(x)
             return x[:seq_len].astype(np.float64)
         _, _, vb, vm = self._q_views()
-        codes = unpack_value_tiles(vb[b, :nt], self.rv)            # [nt,64,R]
+        codes = unpack_value_tiles(vb[b, :nt], self.rv, self.lob)  # [nt,64,R]
         g = self.rv // 32
         s = np.transpose(vm[b, :nt, 0], (0, 2, 1))                  # [nt,64,G]
         z = np.transpose(vm[b, :nt, 1], (0, 2, 1))

@@ -54,6 +54,7 @@ class Workload:
     decaying_latents: bool = True
     hidden: int = 0       # prefill only: D
     chunk: int = 0        # prefill only: C
+    lo_bits: int = 3      # q43 caches: bits of the trailing block (4 = uniform 4-bit)
 
     @property
     def group(self) -> int:
@@ -82,6 +83,11 @@ WORKLOADS = {
     "l2_q43": Workload("l2_q43", batch=16, n_q_heads=32, n_kv_heads=32,
                        head_dim=128, key_rank=32, value_rank=1024,
                        seq_len=32768, cache="q43", rotate=True, seed=20260300),
+    # Same shape with the uniform 4-bit cache of the pages' speed figures.
+    "l2_q4": Workload("l2_q4", batch=16, n_q_heads=32, n_kv_heads=32,
+                      head_dim=128, key_rank=32, value_rank=1024,
+                      seq_len=32768, cache="q43", rotate=True, seed=20260600,
+                      lo_bits=4),
     # LLaMA-3-8B-shaped GQA decode: 32 query heads over 8 KV heads.
     "l3_gqa_q43": Workload("l3_gqa_q43", batch=32, n_q_heads=32, n_kv_heads=8,
                            head_dim=128, key_rank=32, value_rank=256,
