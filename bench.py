@@ -51,6 +51,17 @@ COUNTERS = os.path.join(ROOT, "profiles", "split_kernel_l2_q43_counters.json")
 DECODE_SRC = os.path.join(ROOT, "decode_attention_starkv_amd", "csrc", "decode.hip")
 
 
+
+def cache_label(w):
+    kind = "u4" if w.cache == "q43" and w.lo_bits == 4 else w.cache
+    return kind + (" rotated" if w.rotate else "")
+
+
+def qbits(w):
+    """make_config keywords of a quantized workload's precision split (the
+    trailing block's width: 3 bits, or 4 for a uniform 4-bit cache)."""
+    return dict(lo_bits=w.lo_bits) if w.cache == "q43" else {}
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -254,7 +265,7 @@ def run_prefill(args, w, torch, sk, synth):
     ctx, chunk = (args.seq_len or w.seq_len), w.chunk
     T = ((ctx + chunk + 63) // 64) * 64
     cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
-                         w.key_rank, w.value_rank, T, w.cache, w.rotate)
+                         w.key_rank, w.value_rank, T, w.cache, w.rotate, **qbits(w))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# workload {w.name} B={w.batch} ctx={ctx} chunk={chunk}", file=sys.stderr,
@@ -319,7 +330,7 @@ def run_prefill(args, w, torch, sk, synth):
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "key_rank": w.key_rank,
                    "value_rank": w.value_rank,
-                   "cache": w.cache + (" rotated" if w.rotate else "")},
+                   "cache": cache_label(w)},
         "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel",
                      "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS,
@@ -349,7 +360,7 @@ def run_hidden(args, w, torch, sk, synth):
     D = args.hidden
     cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
                          w.key_rank, w.value_rank, ((seq_len + 63) // 64) * 64,
-                         w.cache, w.rotate, args.splits)
+                         w.cache, w.rotate, args.splits, **qbits(w))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# workload {w.name} B={w.batch} T={seq_len} hidden={D}", file=sys.stderr,
@@ -419,7 +430,7 @@ def run_hidden(args, w, torch, sk, synth):
                    "seq_len": seq_len, "hidden": D, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "key_rank": w.key_rank, "value_rank": w.value_rank,
-                   "cache": w.cache + (" rotated" if w.rotate else ""),
+                   "cache": cache_label(w),
                    "fused_factor_bytes": f_bytes,
                    "cache_flushed_before_step": not args.no_flush},
         "roofline": {"bound": "hbm", "kernel": "hidden_gemm_kernel",
@@ -503,7 +514,8 @@ def main():
     seq_len = args.seq_len or w.seq_len
     cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
                          w.key_rank, w.value_rank, ((seq_len + 63) // 64) * 64,
-                         w.cache, w.rotate, args.splits, rope_theta=args.rope_theta)
+                         w.cache, w.rotate, args.splits, rope_theta=args.rope_theta,
+                         **qbits(w))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# workload {w.name} B={w.batch} T={seq_len} rope_theta={args.rope_theta} splits="
@@ -625,7 +637,7 @@ def main():
                    "seq_len": seq_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "key_rank": w.key_rank, "value_rank": w.value_rank,
-                   "cache": w.cache + (" rotated" if w.rotate else ""),
+                   "cache": cache_label(w),
                    "splits": sk.starkv_decode_splits(cfg, seq_len),
                    "cache_flushed_before_step": not args.no_flush},
         "roofline": roofline,

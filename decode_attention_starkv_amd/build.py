@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libstarkv.so")
 OBJ = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "stream.hip",
-           "noalloc.hip", "oproj.hip", "rope.hip", "decode_rope.hip"]
+           "noalloc.hip", "oproj.hip", "rope.hip", "decode_rope.hip",
+           "decode_u4.hip", "decode_u4_rope.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -56,7 +56,8 @@ int check_config(const starkv_config* c) {
     if (c->key_rank != 32 || c->value_rank % 256 != 0 ||
         (c->n_kv_heads > 4 && c->n_kv_heads % 4 != 0))
       return STARKV_EUNSUPPORTED;
-    if (c->hi_bits != 4 || c->lo_bits != 3 || c->group_size != 32 ||
+    // the 4/3-bit split, or both blocks at 4 bits (uniform 4-bit cache)
+    if (c->hi_bits != 4 || (c->lo_bits != 3 && c->lo_bits != 4) || c->group_size != 32 ||
         c->key_hi_channels != c->key_rank / 4 ||
         c->value_hi_channels != c->value_rank / 4)
       return STARKV_EUNSUPPORTED;
@@ -99,9 +100,9 @@ size_t cache_bytes(const starkv_config& c, int which) {
   const size_t rk = c.key_rank, rv = c.value_rank;
   if (c.cache_dtype == STARKV_CACHE_Q43) {
     switch (which) {
-      case STARKV_BUF_KEY: return B * H * NT * kKeyBlock;
+      case STARKV_BUF_KEY: return B * H * NT * key_block_bytes(c.lo_bits);
       case STARKV_BUF_KEY_META: return B * H * NT * kTile * 8;
-      case STARKV_BUF_VALUE: return B * NT * rv * 26;
+      case STARKV_BUF_VALUE: return B * NT * value_tile_bytes((int)rv, c.lo_bits);
       case STARKV_BUF_VALUE_META: return B * NT * 2 * (rv / 32) * kTile * 2;
       default: return 0;
     }
@@ -154,7 +155,10 @@ size_t starkv_workspace_bytes(const starkv_config* cfg, int32_t op,
     if (n_tokens > cfg->max_tokens) return 0;
     return decode_ws_layout(d, choose_splits(*cfg, n_tokens), n_tokens).total;
   }
-  if (op == STARKV_OP_PREFILL) return prefill_ws_layout(d, n_tokens).total;
+  if (op == STARKV_OP_PREFILL) {
+    if (!prefill_supported(d) || cfg->rope_theta > 0.0f) return 0;
+    return prefill_ws_layout(d, n_tokens).total;
+  }
   return 0;
 }
 

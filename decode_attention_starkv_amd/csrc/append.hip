@@ -165,14 +165,33 @@ __device__ inline void append_q43_keys(const float* __restrict__ zk,
   lo = x[8]; hi = x[8];
 #pragma unroll
   for (int c = 9; c < 32; ++c) { lo = fminf(lo, x[c]); hi = fmaxf(hi, x[c]); }
-  QParams pl = group_params(lo, hi, 7.0f);
+  const bool u4 = d.lob == 4;
+  const float lo_levels = u4 ? 15.0f : 7.0f;
+  QParams pl = group_params(lo, hi, lo_levels);
 
   uint32_t whi = 0;
 #pragma unroll
   for (int c = 0; c < 8; ++c) whi |= code_of(x[c], ph, 15.0f) << (4 * c);
   uint32_t q[24];
 #pragma unroll
-  for (int c = 0; c < 24; ++c) q[c] = code_of(x[8 + c], pl, 7.0f);
+  for (int c = 0; c < 24; ++c) q[c] = code_of(x[8 + c], pl, lo_levels);
+  size_t blk = tile_index(d, b, tile) * d.Hkv + h;
+  uint16_t* km = kmeta + (blk * kTile + u) * 4;
+  if (u4) {
+    // uniform 4-bit: four nibble planes, plane p holding channels 8p .. 8p+7
+    // at bits 4c (the layout of the 4-bit plane above)
+    uint8_t* kb = key + blk * key_block_bytes(4);
+    reinterpret_cast<uint32_t*>(kb)[u] = whi;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) w |= q[8 * p + c] << (4 * c);
+      reinterpret_cast<uint32_t*>(kb + 256 * (p + 1))[u] = w;
+    }
+    km[0] = ph.sb; km[1] = ph.zb; km[2] = pl.sb; km[3] = pl.zb;
+    return;
+  }
   // lo channel i: i<5 -> lo0 bit 3i; 5<=i<10 -> lo1 bit 3(i-5);
   // 10<=i<15 -> lo0 bit 16+3(i-10); 15<=i<20 -> lo1 bit 16+3(i-15);
   // 20<=i<24 -> remainder R bit 3(i-20): R[0:8] = lo2,
@@ -191,13 +210,11 @@ __device__ inline void append_q43_keys(const float* __restrict__ zk,
   lo1 |= ((R >> 10) & 1u) << 15;
   lo1 |= ((R >> 11) & 1u) << 31;
 
-  size_t blk = tile_index(d, b, tile) * d.Hkv + h;
-  uint8_t* kb = key + blk * kKeyBlock;
+  uint8_t* kb = key + blk * key_block_bytes(3);
   reinterpret_cast<uint32_t*>(kb)[u] = whi;
   reinterpret_cast<uint32_t*>(kb + 256)[u] = lo0;
   reinterpret_cast<uint32_t*>(kb + 512)[u] = lo1;
   kb[768 + u] = (uint8_t)(R & 0xFFu);
-  uint16_t* km = kmeta + (blk * kTile + u) * 4;
   km[0] = ph.sb; km[1] = ph.zb; km[2] = pl.sb; km[3] = pl.zb;
 }
 
@@ -231,10 +248,11 @@ __device__ inline void append_q43_values(
   // no other thread touches its words.
   const int ch = cb * 256 + threadIdx.x;
   const int g = ch / 32, c = ch % 32;
-  const int NH = n_hi / 32;
+  // leading groups at 4 bits (every group in a uniform 4-bit cache)
+  const int NH = d.lob == 4 ? G : n_hi / 32;
   const bool four = g < NH;
   const int nw = four ? 4 : 3;
-  uint8_t* vt = value + tile_index(d, b, tile) * 26 * d.rv;
+  uint8_t* vt = value + tile_index(d, b, tile) * value_tile_bytes(d.rv, d.lob);
   uint8_t* grp = four ? vt + (size_t)g * 1024 : vt + (size_t)NH * 1024 + (size_t)(g - NH) * 768;
   uint32_t old[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
@@ -284,7 +302,7 @@ __device__ inline void append_q43_values(
         hi = fmaxf(hi, __shfl_xor(hi, s));
       }
       const int chr = cb * 256 + lane + 64 * r;
-      float levels = chr < n_hi ? 15.0f : 7.0f;
+      float levels = chr < n_hi || d.lob == 4 ? 15.0f : 7.0f;
       QParams p = group_params(lo, hi, levels);
       codes[u][lane + 64 * r] = (uint8_t)code_of(x[r], p, levels);
       if ((lane & 31) == 0) {

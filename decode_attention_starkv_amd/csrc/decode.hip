@@ -385,7 +385,8 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
 }
 
 SplitFn q43_kernel(const Dims& d) {
-  return d.rope_theta > 0.0f ? q43_rope_kernel(d) : q43_kernel_select<false>(d);
+  if (d.lob == 4) return d.rope_theta > 0.0f ? u4_rope_kernel(d) : u4_kernel(d);
+  return d.rope_theta > 0.0f ? q43_rope_kernel(d) : q43_kernel_select<false, false>(d);
 }
 
 hipError_t launch_q43(const Dims& d, dim3 grid, const SplitArgs& sa, hipStream_t s) {

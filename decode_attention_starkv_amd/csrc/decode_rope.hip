@@ -5,6 +5,6 @@
 
 namespace starkv {
 
-SplitFn q43_rope_kernel(const Dims& d) { return q43_kernel_select<true>(d); }
+SplitFn q43_rope_kernel(const Dims& d) { return q43_kernel_select<true, false>(d); }
 
 }  // namespace starkv

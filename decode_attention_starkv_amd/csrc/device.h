@@ -135,6 +135,26 @@ __device__ inline KeyLane unpack_key_lane(const uint32_t (&kc)[6]) {
   return k;
 }
 
+// The same for a uniform 4-bit key tile: kc holds the lane's four nibble
+// planes (plane p: channels 8p .. 8p+3 in the low half, 8p+4 .. 8p+7 in the
+// high half) and its two meta words; pair 4p + k is read like pair k of the
+// 4-bit plane above, and pair 16 is zero.
+__device__ inline KeyLane unpack_key_lane_u4(const uint32_t (&kc)[6]) {
+  KeyLane k;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w = kc[p], w8 = w >> 8;
+    k.pr[4 * p] = w & 0x000F000Fu;
+    k.pr[4 * p + 1] = w & 0x00F000F0u;
+    k.pr[4 * p + 2] = w8 & 0x000F000Fu;
+    k.pr[4 * p + 3] = w8 & 0x00F000F0u;
+  }
+  k.pr[16] = 0u;
+  k.mhi = kc[4];
+  k.mlo = kc[5];
+  return k;
+}
+
 // Latent score of one key lane against one Q43 query record (17 fp16
 // pairs, then the sums of the hi and lo query parts times 2^-24), in units
 // of 2^-24 (log2 domain, pre-scaled):

@@ -10,7 +10,14 @@
 namespace starkv {
 
 constexpr int kTile = 64;          // tokens per cache tile (format v1)
-constexpr int kKeyBlock = 832;     // bytes of one Q43 key tile of one KV head
+// Bytes of one quantized key tile of one KV head: 4/3-bit (832: a 4-bit
+// plane, two 3-bit planes and a remainder byte per token) or uniform 4-bit
+// (1024: four 4-bit planes), and of one value tile (26 or 32 bytes per
+// latent channel).
+__host__ __device__ constexpr int key_block_bytes(int lo_bits) { return lo_bits == 4 ? 1024 : 832; }
+__host__ __device__ constexpr int value_tile_bytes(int rv, int lo_bits) {
+  return (lo_bits == 4 ? 32 : 26) * rv;
+}
 constexpr int kMaxQHeads = 32;     // rows of the stacked-head P operand
 constexpr int kDecodeWaves = 8;    // waves per decode workgroup
 constexpr int kMaxSplits = 1024;   // decode token splits per sequence
@@ -18,6 +25,7 @@ constexpr int kMaxSplits = 1024;   // decode token splits per sequence
 // Shape of one call, copied by value into every kernel.
 struct Dims {
   int B, Hq, Hkv, G, dh, rk, rv, Tmax, NT, dtype, rotate;
+  int lob;           // quantized caches: bits of the trailing block (3 or 4)
   float rope_theta;  // 0: no rotary position embedding
   // Paged / ragged 4/3-bit caches (all null / 0 for the contiguous layout):
   const int32_t* pages = nullptr;  // device [B][pages_per_seq]: tile -> pool page
@@ -75,6 +83,7 @@ inline Dims make_dims(const starkv_config& c) {
   d.NT = c.max_tokens / kTile;
   d.dtype = c.cache_dtype;
   d.rotate = c.rotate;
+  d.lob = c.cache_dtype == STARKV_CACHE_Q43 ? c.lo_bits : 0;
   d.rope_theta = c.rope_theta;
   int off = 0;
   for (int g = 0; g < kMaxQHeads; ++g) {

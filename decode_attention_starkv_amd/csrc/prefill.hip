@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restr
   const int b = idx / ((size_t)d.Hkv * n);
   const int tile = t / kTile, u = t % kTile;
   const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + h;
-  const uint8_t* kb = key + blk * kKeyBlock;
+  const uint8_t* kb = key + blk * key_block_bytes(3);
   const uint32_t whi = reinterpret_cast<const uint32_t*>(kb)[u];
   const uint32_t w0 = reinterpret_cast<const uint32_t*>(kb + 256)[u];
   const uint32_t w1 = reinterpret_cast<const uint32_t*>(kb + 512)[u];
@@ -818,7 +818,9 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
 }
 
 bool prefill_supported(const Dims& d) {
-  return d.dtype == STARKV_CACHE_Q43 && d.rk == 32 && d.Hq % kPH == 0 &&
+  // the 4/3-bit cache (the prefill's attention tiles read its key and value
+  // layout; a uniform 4-bit cache is decode-only)
+  return d.dtype == STARKV_CACHE_Q43 && d.lob == 3 && d.rk == 32 && d.Hq % kPH == 0 &&
          (d.G == 1 || d.G == 2 || d.G == 4 || d.G == 8) && d.rv % 256 == 0 &&
          d.rv <= kMaxRv && d.dh % 64 == 0 && d.dh <= 256;
 }

@@ -18,7 +18,9 @@ namespace starkv {
 // A Q43 record holds the 17 fp16 pairs that meet the in-place code fields of
 // the key words (each entry times 2^-p for a field at bit p; channel 31
 // split over three one-bit fields), then sum(q_hi) 2^-24 and
-// sum(q_lo) 2^-24 as fp32.
+// sum(q_lo) 2^-24 as fp32.  For a uniform 4-bit cache the pairs are those
+// of the four nibble planes (pair 4p + k: channels 8p + k and 8p + k + 4),
+// and pair 16 is zero.
 template <int FMT>
 __device__ inline void qproj_block(const void* __restrict__ q,
                                    const void* __restrict__ bk, const Dims& d,
@@ -76,7 +78,13 @@ __device__ inline void qproj_block(const void* __restrict__ q,
   if (t < 17) {
     int a, cc;        // channels of the low and the high half
     float sa, sc;     // their field weights (2^-bit position, or the bit's weight)
-    if (t < 4) {
+    if (d.lob == 4) {
+      // pair k of plane p = t / 4 as in the 4-bit plane below; pair 16
+      // meets no field and is stored as zero
+      a = t < 16 ? 8 * (t >> 2) + (t & 3) : 0;
+      cc = a + 4;
+      sa = sc = (t & 1) ? 1.0f / 16.0f : 1.0f;
+    } else if (t < 4) {
       // channels 0-3 / 4-7; odd pairs sit at bit 4 of their byte
       a = t;
       cc = t + 4;
@@ -95,8 +103,9 @@ __device__ inline void qproj_block(const void* __restrict__ q,
     }
     const _Float16 lo = (_Float16)((float)sq[a] * sa);
     const _Float16 hi = (_Float16)((float)sq[cc] * sc);
-    rec[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    rec[t] = d.lob == 4 && t == 16 ? 0u
+                                   : (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
   if (t == 32) {
     float s = 0.0f;

@@ -21,9 +21,9 @@
 //                      the dequantized latent.  Scores leave as fp16 relative
 //                      to the running (exact) max of their head, with that
 //                      max per tile and the split's final max.
-// The 4/3-bit split kernel then reads those scores instead of computing
-// latent ones (exp2(s_rel + m_tile - m_split) <= 1) and runs its value
-// contraction unchanged.
+// The quantized split kernel (4/3-bit or uniform 4-bit) then reads those
+// scores instead of computing latent ones (exp2(s_rel + m_tile - m_split)
+// <= 1) and runs its value contraction unchanged.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -140,8 +140,9 @@ __device__ inline void rope_wait_vmcnt() {
 // Scores of one (split, group of 8 query heads, sequence).  Wave w owns
 // query heads 8 hg + 2 w and 8 hg + 2 w + 1.  Per 64-token tile: the trig
 // fragments come through a 2-slot LDS ring (direct-to-LDS loads one tile
-// ahead), each lane loads its own token's key words one tile ahead.
-template <int DH>
+// ahead), each lane loads its own token's key words two tiles ahead.  kU4:
+// a uniform 4-bit key tile (four nibble planes) instead of a 4/3-bit one.
+template <int DH, bool kU4>
 __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
   constexpr int KS = DH / 16;
   constexpr int kChunks = KS * 2;              // 1 KB trig chunks per tile
@@ -184,19 +185,23 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
           (__attribute__((address_space(3))) void*)(&trig_l[slot][k * 64]), 16, 0, 0);
     }
   };
-  // the lane's token: 4-bit word, two 3-bit words, remainder byte, meta;
-  // three register sets: keys are loaded two tiles ahead
+  // the lane's token: 4-bit word, two 3-bit words, remainder byte (kU4:
+  // four 4-bit words), meta; three register sets: keys are loaded two tiles
+  // ahead
   uint32_t kc[3][2][6];
   auto load_keys = [&](int tile, uint32_t (&dst)[2][6]) {
     const size_t tix = tile_index(d, b, tile) * d.Hkv;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const size_t blk = tix + (kv == 0 ? g0 : g1);
-      const uint8_t* kb = kbase + blk * kKeyBlock;
+      const uint8_t* kb = kbase + blk * key_block_bytes(kU4 ? 4 : 3);
       dst[kv][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + l);
       dst[kv][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + l);
       dst[kv][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + l);
-      dst[kv][3] = __builtin_nontemporal_load(kb + 768 + l);
+      if constexpr (kU4)
+        dst[kv][3] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 768) + l);
+      else
+        dst[kv][3] = __builtin_nontemporal_load(kb + 768 + l);
       const u32x2 mt = __builtin_nontemporal_load(kmeta + blk * kTile + l);
       dst[kv][4] = mt[0];
       dst[kv][5] = mt[1];
@@ -236,23 +241,30 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
       if (hh == 0 || two_kv) {
         // dequantized latent of the lane's token for this head's KV head
         const uint32_t* k = cur[hh == 1 && two_kv ? 1 : 0];
-        const uint32_t hi = k[0], lo0 = k[1], lo1 = k[2];
-        const uint32_t rem = (k[3] & 0xFFu) | (((lo0 >> 15) & 1u) << 8) |
-                             (((lo0 >> 31) & 1u) << 9) | (((lo1 >> 15) & 1u) << 10) |
-                             (((lo1 >> 31) & 1u) << 11);
         const h2 mh = __builtin_bit_cast(h2, k[4]), ml = __builtin_bit_cast(h2, k[5]);
         const float sh = (float)mh[0], zh = (float)mh[1], sl = (float)ml[0], zl = (float)ml[1];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) zf[c] = fmaf(sh, (float)((hi >> (4 * c)) & 15u), zh);
+        for (int c = 0; c < 8; ++c) zf[c] = fmaf(sh, (float)((k[0] >> (4 * c)) & 15u), zh);
+        if constexpr (kU4) {
+          // channel 8p + c at bits 4c of plane p
 #pragma unroll
-        for (int i = 0; i < 24; ++i) {
-          uint32_t code;
-          if (i < 5) code = (lo0 >> (3 * i)) & 7u;
-          else if (i < 10) code = (lo1 >> (3 * (i - 5))) & 7u;
-          else if (i < 15) code = (lo0 >> (16 + 3 * (i - 10))) & 7u;
-          else if (i < 20) code = (lo1 >> (16 + 3 * (i - 15))) & 7u;
-          else code = (rem >> (3 * (i - 20))) & 7u;
-          zf[8 + i] = fmaf(sl, (float)code, zl);
+          for (int i = 0; i < 24; ++i)
+            zf[8 + i] = fmaf(sl, (float)((k[1 + i / 8] >> (4 * (i % 8))) & 15u), zl);
+        } else {
+          const uint32_t lo0 = k[1], lo1 = k[2];
+          const uint32_t rem = (k[3] & 0xFFu) | (((lo0 >> 15) & 1u) << 8) |
+                               (((lo0 >> 31) & 1u) << 9) | (((lo1 >> 15) & 1u) << 10) |
+                               (((lo1 >> 31) & 1u) << 11);
+#pragma unroll
+          for (int i = 0; i < 24; ++i) {
+            uint32_t code;
+            if (i < 5) code = (lo0 >> (3 * i)) & 7u;
+            else if (i < 10) code = (lo1 >> (3 * (i - 5))) & 7u;
+            else if (i < 15) code = (lo0 >> (16 + 3 * (i - 10))) & 7u;
+            else if (i < 20) code = (lo1 >> (16 + 3 * (i - 15))) & 7u;
+            else code = (rem >> (3 * (i - 20))) & 7u;
+            zf[8 + i] = fmaf(sl, (float)code, zl);
+          }
         }
       }
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
@@ -377,10 +389,14 @@ hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_
   a.m_split = reinterpret_cast<float*>(ws + rw.m_split);
   const dim3 grid(splits, (d.Hq + kRopeHeads - 1) / kRopeHeads, d.B);
   if (before_scores) (void)hipEventRecord(before_scores, s);
-  if (d.dh == 64)
-    rope_score_kernel<64><<<grid, 256, 0, s>>>(a);
-  else
-    rope_score_kernel<128><<<grid, 256, 0, s>>>(a);
+  const bool u4 = d.lob == 4;
+  if (d.dh == 64) {
+    if (u4) rope_score_kernel<64, true><<<grid, 256, 0, s>>>(a);
+    else rope_score_kernel<64, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (u4) rope_score_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    else rope_score_kernel<128, false><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

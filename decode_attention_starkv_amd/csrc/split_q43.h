@@ -1,9 +1,11 @@
-// The 4/3-bit decode split kernel (rows a-3 and a-4 of the decode path:
+// The quantized decode split kernel (rows a-3 and a-4 of the decode path:
 // split-T latent scores with an online softmax, and the stacked-head joint
-// value contraction P Z_v on MFMA), shared by two translation units:
-// decode.hip instantiates the latent-score kernels, decode_rope.hip the
-// variants that read precomputed rotary scores.  Each unit gets its own copy
-// of the kernels (anonymous namespace); SplitArgs and SplitFn are common.
+// value contraction P Z_v on MFMA), shared by four translation units:
+// decode.hip instantiates the 4/3-bit latent-score kernels, decode_rope.hip
+// the 4/3-bit variants that read precomputed rotary scores, decode_u4.hip
+// and decode_u4_rope.hip the same two for the uniform 4-bit cache.  Each
+// unit gets its own copy of the kernels (anonymous namespace); SplitArgs and
+// SplitFn are common.
 #pragma once
 
 #include <type_traits>
@@ -33,6 +35,9 @@ using SplitFn = void (*)(SplitArgs);
 // The 4/3-bit split kernel reading precomputed rotary scores for the
 // shape, or nullptr (decode_rope.hip).
 SplitFn q43_rope_kernel(const Dims& d);
+// The uniform 4-bit split kernels (decode_u4.hip, decode_u4_rope.hip).
+SplitFn u4_kernel(const Dims& d);
+SplitFn u4_rope_kernel(const Dims& d);
 
 namespace {
 
@@ -59,23 +64,25 @@ __device__ inline void wave_dma(const uint8_t* src, uint8_t* lds_dst, int bytes,
   }
 }
 
-constexpr int kValueSlots = 4;     // LDS ring slots per value wave
-constexpr int kValueAhead = kValueSlots - 1;   // tiles staged ahead of use
 // Value ring of a kernel whose value waves own NIV groups each (R_v = 128 NIV,
 // NIV <= 8); sized per NIV so that small value ranks leave room for a second
 // workgroup on the compute unit.
-// one slot: the 4-bit wave's codes + scales + zeros, then the three 3-bit
-// waves' (1024 + 128 + 128 and 768 + 128 + 128 bytes per group)
+// one slot: the 4-bit wave's codes + scales + zeros, then the three other
+// waves' (1024 + 128 + 128 bytes per 4-bit group, 768 + 128 + 128 per 3-bit
+// group; in a uniform 4-bit cache every wave's groups are 4-bit)
 constexpr int hi_region(int niv) { return niv * 1280; }
-constexpr int lo_region(int niv) { return niv * 1024; }
-constexpr int slot_bytes(int niv) { return hi_region(niv) + 3 * lo_region(niv); }
+constexpr int lo_region(int niv, bool u4) { return niv * (u4 ? 1280 : 1024); }
+constexpr int slot_bytes(int niv, bool u4) { return hi_region(niv) + 3 * lo_region(niv, u4); }
+// LDS ring slots per value wave: 4 (tiles staged three ahead of use), 3 where
+// four slots would not fit in LDS (uniform 4-bit, R_v = 1024)
+constexpr int value_slots(int niv, bool u4) { return u4 && niv == 8 ? 3 : 4; }
 // fp32 row stride of the epilogue's per-wave staging of partial rows (kept
 // in the value ring): 32 rows of 32 NIV columns, padded so the two row halves
 // a store instruction writes fall in different LDS banks
 constexpr int stage_row(int niv) { return niv * 32 + 8; }
-constexpr int ring_bytes(int niv) {
-  return kValueSlots * slot_bytes(niv) > 4 * 32 * stage_row(niv) * 4
-             ? kValueSlots * slot_bytes(niv)
+constexpr int ring_bytes(int niv, bool u4) {
+  return value_slots(niv, u4) * slot_bytes(niv, u4) > 4 * 32 * stage_row(niv) * 4
+             ? value_slots(niv, u4) * slot_bytes(niv, u4)
              : 4 * 32 * stage_row(niv) * 4;
 }
 
@@ -89,26 +96,27 @@ constexpr int ring_bytes(int niv) {
 //     2-slot LDS ring as the stacked-head P tile (32 rows, fp16).
 //   value waves 4-7: wave v owns the NIV value groups v*NIV .. v*NIV+NIV-1
 //     (32 channels each, one MFMA column tile); since R_v/4 channels are
-//     4-bit, value wave 0 holds exactly the 4-bit groups.  Each value wave
-//     streams its own groups' codes, scales and zeros into a private 4-slot
-//     LDS ring (direct-to-LDS, non-temporal) three tiles ahead, so it waits
-//     on its own loads only.  A = P * scale in fp16, B = codes as fp16
+//     4-bit, value wave 0 holds exactly the 4-bit groups (kU4: every group
+//     is 4-bit).  Each value wave streams its own groups' codes, scales and
+//     zeros into a private LDS ring (direct-to-LDS, non-temporal) two or
+//     three tiles ahead, so it waits on its own loads only.  A = P * scale in fp16, B = codes as fp16
 //     subnormals, mfma 32x32x16; P x zero adds the zero points, and a column
 //     of ones in that product gives each head's exp-sum l.
 // One barrier per tile hands P over: while the value waves contract tile t,
 // the score waves already score tile t+1.
-template <int G, int KVS, int NIV, bool kRope>
+template <int G, int KVS, int NIV, bool kRope, bool kU4>
 __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   constexpr int PS = 72;                        // P row stride (halves)
-  constexpr bool kFourW0 = true;                // value wave 0: 4-bit groups
   constexpr int kDmaHi = NIV + 2 * ((NIV * 128 + 1023) / 1024);
   constexpr int kDmaLo = (NIV * 768 + 1023) / 1024 + 2 * ((NIV * 128 + 1023) / 1024);
-  (void)kFourW0;
+  constexpr int kValueSlots = value_slots(NIV, kU4);
+  constexpr int kValueAhead = kValueSlots - 1;   // tiles staged ahead of use
+  constexpr int kKeyBlockBytes = key_block_bytes(kU4 ? 4 : 3);
   const Dims& d = a.d;
 
-  constexpr int kHiRegion = hi_region(NIV), kLoRegion = lo_region(NIV);
-  constexpr int kSlotBytes = slot_bytes(NIV), kStageRow = stage_row(NIV);
-  __shared__ __attribute__((aligned(16))) uint8_t vring[ring_bytes(NIV)];
+  constexpr int kHiRegion = hi_region(NIV), kLoRegion = lo_region(NIV, kU4);
+  constexpr int kSlotBytes = slot_bytes(NIV, kU4), kStageRow = stage_row(NIV);
+  __shared__ __attribute__((aligned(16))) uint8_t vring[ring_bytes(NIV, kU4)];
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][32 * PS];
   __shared__ __attribute__((aligned(16))) uint32_t qrec[kMaxQHeads * kQ43Rec];
   __shared__ float alpha_l[2][32];
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   const int tile0 = sp * a.tiles_per_split;
   const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
   const int GV = 4 * NIV;            // value groups
-  const int NH = NIV;                // 4-bit value groups
+  const int NH = kU4 ? GV : NIV;     // 4-bit value groups
   // Two workgroups share a compute unit when R_v is small, and issue
   // arbitration favours the older one; the grid's second half (which lands
   // as the second workgroup of each unit) runs at the higher wave priority.
@@ -223,11 +231,15 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       for (int ki = 0; ki < KVS; ++ki) {
         const int kh = sw + ki * 4;
         const size_t blk = tix + kh;
-        const uint8_t* kb = kbase + blk * kKeyBlock;
+        const uint8_t* kb = kbase + blk * kKeyBlockBytes;
         dst[ki][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + lane);
         dst[ki][1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 256) + lane);
         dst[ki][2] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 512) + lane);
-        dst[ki][3] = __builtin_nontemporal_load(kb + 768 + lane);
+        // the remainder byte (4/3-bit) or the fourth nibble plane (kU4)
+        if constexpr (kU4)
+          dst[ki][3] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + 768) + lane);
+        else
+          dst[ki][3] = __builtin_nontemporal_load(kb + 768 + lane);
         const u32x2 mt = __builtin_nontemporal_load(kmeta + blk * kTile + lane);
         dst[ki][4] = mt[0];
         dst[ki][5] = mt[1];
@@ -246,8 +258,9 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     // A = the query records read from LDS (row = query head; lane 4b + i
     // reads head i of a set of 4), so that a lane receives its token's
     // scores of the 4 heads in 4 registers.  K step s takes field pairs 2s,
-    // 2s + 1: steps 0-1 the 4-bit part, steps 2-8 the 3-bit part (pair 17
-    // is zero on both sides).
+    // 2s + 1: steps 0-1 the leading block, steps 2-8 the trailing block
+    // (pair 17 is zero on both sides; kU4 has no pair 16 either and stops
+    // after step 7).
     constexpr int kSets = G >= 4 ? G / 4 : 0;
     constexpr int kSetsA = kSets > 0 ? kSets : 1;
     typedef _Float16 h4v __attribute__((ext_vector_type(4)));
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       float x[KVS * G];   // scores times 2^-24
 #pragma unroll
       for (int ki = 0; ki < KVS; ++ki) {
-        const KeyLane kl = unpack_key_lane(kc[ki]);
+        const KeyLane kl = kU4 ? unpack_key_lane_u4(kc[ki]) : unpack_key_lane(kc[ki]);
         if constexpr (kSets > 0) {
           const h2 mh = __builtin_bit_cast(h2, kl.mhi), ml = __builtin_bit_cast(h2, kl.mlo);
 #pragma unroll
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
             const uint32_t* rq = qrec + ((sw + ki * 4) * G + st * 4 + (lane & 3)) * kQ43Rec;
             f32x4 dh = {0.0f, 0.0f, 0.0f, 0.0f}, dl = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int k = 0; k < 9; ++k) {
+            for (int k = 0; k < (kU4 ? 8 : 9); ++k) {
               const h4v qa = __builtin_bit_cast(
                   h4v, k < 8 ? *reinterpret_cast<const u32x2*>(rq + 2 * k) : u32x2{rq[16], 0u});
               const h4v kb = __builtin_bit_cast(
@@ -376,15 +389,16 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
     // ================================================================ values
     const int vw = wave - 4;
     const int n0 = vw * NIV;                 // first value group of this wave
-    const bool four = vw == 0;
+    const bool four = kU4 || vw == 0;
     const int code_bytes = NIV * (four ? 1024 : 768);
-    const int code_off = four ? 0 : NH * 1024 + (n0 - NH) * 768;
+    const int code_off = four ? n0 * 1024 : NH * 1024 + (n0 - NH) * 768;
     const int meta_bytes = NIV * kTile * 2;   // one plane of this wave's groups
     const uint8_t* vbase = static_cast<const uint8_t*>(a.value);
     const uint8_t* vmbase = reinterpret_cast<const uint8_t*>(a.vmeta);
-    const size_t tile_bytes = (size_t)26 * 32 * GV;
+    const size_t tile_bytes = value_tile_bytes(32 * GV, kU4 ? 4 : 3);
     const size_t meta_tile = (size_t)2 * GV * kTile * 2;
-    uint8_t* ring = vring + (four ? 0 : kHiRegion + (vw - 1) * kLoRegion);
+    // this wave's region of each slot: value wave 0's groups (4-bit) first
+    uint8_t* ring = vring + (vw == 0 ? 0 : kHiRegion + (vw - 1) * kLoRegion);
 
     auto stage = [&](int tile, int slot) {
       const size_t t = tile_index(d, b, tile);
@@ -442,14 +456,14 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
       h8 A[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) A[r] = *reinterpret_cast<const h8*>(prow + 8 * r);
-      // zero points of this wave's groups: columns n0 .. n0+NIV-1; the
-      // 4-bit wave (n0 = 0) also sums P into column NIV: l of every head,
+      // zero points of this wave's groups: columns n0 .. n0+NIV-1; value
+      // wave 0 (n0 = 0) also sums P into column NIV: l of every head,
       // rescaled with the accumulators and made of the same fp16 P
       // (other columns read a row of zeros: no masked loads)
       {
         const bool zcol = m >= n0 && m < n0 + NIV;
         const _Float16* zsrc = zcol ? zr_l + (m - n0) * kTile
-                                    : (kFour && m == NIV) ? zo_l + kTile : zo_l;
+                                    : (vw == 0 && m == NIV) ? zo_l + kTile : zo_l;
         h8 Z[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) Z[r] = *reinterpret_cast<const h8*>(zsrc + 32 * j + 8 * r);
@@ -503,7 +517,7 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (m >= n0 && m < n0 + NIV) bias_l[acc_row(v, lane)][m] = bacc[v];
-    if (kFour && m == NIV) {
+    if (vw == 0 && m == NIV) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = acc_row(v, lane);
@@ -556,35 +570,36 @@ __global__ __launch_bounds__(512) void split_q43_kernel(SplitArgs a) {
   }
 }
 
-// The Q43 split kernel for a shape: G query heads per KV head, KVS KV heads
-// per score wave, NIV value groups per value wave; kRope reads precomputed
-// (rotary) scores instead of scoring latent keys.
-template <int G, int KVS, bool kRope>
+// The quantized split kernel for a shape: G query heads per KV head, KVS KV
+// heads per score wave, NIV value groups per value wave; kRope reads
+// precomputed (rotary) scores instead of scoring latent keys; kU4 reads a
+// uniform 4-bit cache.
+template <int G, int KVS, bool kRope, bool kU4>
 SplitFn q43_kernel_niv(int NIV) {
   switch (NIV) {
-    case 2: return split_q43_kernel<G, KVS, 2, kRope>;
-    case 4: return split_q43_kernel<G, KVS, 4, kRope>;
-    case 6: return split_q43_kernel<G, KVS, 6, kRope>;
-    case 8: return split_q43_kernel<G, KVS, 8, kRope>;
+    case 2: return split_q43_kernel<G, KVS, 2, kRope, kU4>;
+    case 4: return split_q43_kernel<G, KVS, 4, kRope, kU4>;
+    case 6: return split_q43_kernel<G, KVS, 6, kRope, kU4>;
+    case 8: return split_q43_kernel<G, KVS, 8, kRope, kU4>;
     default: return nullptr;
   }
 }
 
-template <bool kRope>
+template <bool kRope, bool kU4>
 SplitFn q43_kernel_select(const Dims& d) {
   const int NIV = d.rv / 128;
   const int KVS = d.Hkv >= 4 ? d.Hkv / 4 : 1;
   switch (d.G * 16 + KVS) {
-    case 1 * 16 + 1: return q43_kernel_niv<1, 1, kRope>(NIV);
-    case 1 * 16 + 2: return q43_kernel_niv<1, 2, kRope>(NIV);
-    case 1 * 16 + 4: return q43_kernel_niv<1, 4, kRope>(NIV);
-    case 1 * 16 + 8: return q43_kernel_niv<1, 8, kRope>(NIV);
-    case 2 * 16 + 1: return q43_kernel_niv<2, 1, kRope>(NIV);
-    case 2 * 16 + 2: return q43_kernel_niv<2, 2, kRope>(NIV);
-    case 2 * 16 + 4: return q43_kernel_niv<2, 4, kRope>(NIV);
-    case 4 * 16 + 1: return q43_kernel_niv<4, 1, kRope>(NIV);
-    case 4 * 16 + 2: return q43_kernel_niv<4, 2, kRope>(NIV);
-    case 8 * 16 + 1: return q43_kernel_niv<8, 1, kRope>(NIV);
+    case 1 * 16 + 1: return q43_kernel_niv<1, 1, kRope, kU4>(NIV);
+    case 1 * 16 + 2: return q43_kernel_niv<1, 2, kRope, kU4>(NIV);
+    case 1 * 16 + 4: return q43_kernel_niv<1, 4, kRope, kU4>(NIV);
+    case 1 * 16 + 8: return q43_kernel_niv<1, 8, kRope, kU4>(NIV);
+    case 2 * 16 + 1: return q43_kernel_niv<2, 1, kRope, kU4>(NIV);
+    case 2 * 16 + 2: return q43_kernel_niv<2, 2, kRope, kU4>(NIV);
+    case 2 * 16 + 4: return q43_kernel_niv<2, 4, kRope, kU4>(NIV);
+    case 4 * 16 + 1: return q43_kernel_niv<4, 1, kRope, kU4>(NIV);
+    case 4 * 16 + 2: return q43_kernel_niv<4, 2, kRope, kU4>(NIV);
+    case 8 * 16 + 1: return q43_kernel_niv<8, 1, kRope, kU4>(NIV);
     default: return nullptr;
   }
 }

@@ -93,8 +93,11 @@ typedef enum {
  * split explicitly; this build has kernels for hi_bits = 4, lo_bits = 3,
  * group_size = 32, key_hi_channels = key_rank / 4 and value_hi_channels =
  * value_rank / 4 (the model card's top_fraction = 0.25 recipe, 3.25 bits per
- * channel on average) and returns STARKV_EUNSUPPORTED for any other
- * combination.  For F32 / BF16 caches the five fields must be 0. */
+ * channel on average), and for the same fields with lo_bits = 4 (a uniform
+ * 4-bit cache: the 4-bit cache of the review's speed figures, section 6.1
+ * after eq. 14; decode only, starkv_prefill returns STARKV_EUNSUPPORTED),
+ * and returns STARKV_EUNSUPPORTED for any other combination (a 20:80 split
+ * among them).  For F32 / BF16 caches the five fields must be 0. */
 typedef struct starkv_config {
   int32_t batch;       /* B */
   int32_t n_q_heads;   /* Hq <= 32, a multiple of n_kv_heads */
@@ -110,7 +113,8 @@ typedef struct starkv_config {
   int32_t max_tokens;  /* cache capacity T_max, a multiple of 64 */
   int32_t cache_dtype; /* starkv_cache_dtype */
   int32_t hi_bits;     /* Q43: bits of the leading block (4) */
-  int32_t lo_bits;     /* Q43: bits of the trailing block (3) */
+  int32_t lo_bits;     /* Q43: bits of the trailing block (3, or 4 for a
+                          uniform 4-bit cache) */
   int32_t group_size;  /* Q43: channels per quantization group (32) */
   int32_t key_hi_channels;   /* Q43: leading key channels per head at
                                 hi_bits (key_rank / 4) */
@@ -146,6 +150,11 @@ typedef struct starkv_config {
  *             value [B][T_max/64] blocks of 26*R_v B (per 32-channel group,
  *             channel-major runs of 32 tokens, 4-bit groups first);
  *             value_meta [B][T_max/64][2][R_v/32][64] fp16 (scales, zeros).
+ *   Q43 with lo_bits = 4 (uniform 4-bit): key blocks of 1024 B (four 4-bit
+ *             planes u32[64], plane p holding channels 8p .. 8p+7 of each
+ *             token at bits 4c, the layout of the 4/3-bit cache's 4-bit
+ *             plane); value blocks of 32*R_v B (every group in the 4-bit
+ *             run layout); metadata as above.
  * Sizes are returned by starkv_cache_bytes. */
 typedef struct starkv_cache {
   void* key;
@@ -162,13 +171,15 @@ enum { STARKV_OP_DECODE = 0, STARKV_OP_PREFILL = 1 };
 
 /* (host) Bytes of one cache buffer for `cfg`; 0 if cfg is invalid or the
  * buffer is unused.  The quantized payload equals eq. 15 of the review
- * (B T b_bar / 8 (Hkv r_k + R_v) with b_bar = 3.25) with no padding term; the
+ * (B T b_bar / 8 (Hkv r_k + R_v) with b_bar = 3.25, or 4 for a uniform 4-bit
+ * cache) with no padding term; the
  * metadata is 4 bytes per (token, group). */
 STARKV_API size_t starkv_cache_bytes(const starkv_config* cfg, int32_t buffer);
 
 /* (host) Workspace bytes needed by starkv_decode (op STARKV_OP_DECODE,
  * n_tokens = largest seq_len that will be passed) or starkv_prefill (op
- * STARKV_OP_PREFILL, n_tokens = chunk length).  0 on invalid arguments. */
+ * STARKV_OP_PREFILL, n_tokens = chunk length).  0 on invalid arguments or
+ * for a configuration the operation has no kernel for. */
 STARKV_API size_t starkv_workspace_bytes(const starkv_config* cfg, int32_t op,
                               int32_t n_tokens);
 

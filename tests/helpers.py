@@ -19,12 +19,18 @@ def sk():
     return mod
 
 
-def config_for(w, batch=None, max_tokens=None, num_splits=0, rotate=None):
+def qbits(w):
+    """make_config keywords of the workload's precision split (quantized
+    caches: the trailing block's width, 3 or 4 bits)."""
+    return dict(lo_bits=w.lo_bits) if w.cache == "q43" else {}
+
+
+def config_for(w, batch=None, max_tokens=None, num_splits=0, rotate=None, **kw):
     return sk().make_config(
         w.batch if batch is None else batch, w.n_q_heads, w.n_kv_heads,
         w.head_dim, w.key_rank, w.value_rank,
         w.max_tokens if max_tokens is None else max_tokens, w.cache,
-        w.rotate if rotate is None else rotate, num_splits)
+        w.rotate if rotate is None else rotate, num_splits, **qbits(w), **kw)
 
 
 def dev(a, dtype=None):

@@ -27,6 +27,8 @@ def _cfg(w, **kw):
                 value_rank=w.value_rank, max_tokens=w.max_tokens,
                 cache_dtype=w.cache, rotate=w.rotate)
     base.update(kw)
+    if base["cache_dtype"] == "q43" and "lo_bits" not in kw:
+        base["lo_bits"] = w.lo_bits
     return sk.make_config(**base)
 
 
@@ -44,7 +46,7 @@ def test_cache_bytes_match_oracle_layout(name):
     w = synth.WORKLOADS[name]
     cfg = _cfg(w)
     lay = oc.layout(w.batch, w.n_kv_heads, w.key_rank, w.value_rank,
-                    w.max_tokens, w.cache)
+                    w.max_tokens, w.cache, lo_bits=w.lo_bits)
     got = [sk.starkv_cache_bytes(cfg, i) for i in range(4)]
     assert got == [lay["key"], lay["key_meta"], lay["value"], lay["value_meta"]]
 
@@ -138,6 +140,42 @@ def test_default_layout_fields_are_the_quarter_split():
     assert (plain.hi_bits, plain.lo_bits, plain.group_size,
             plain.key_hi_channels, plain.value_hi_channels) == (0, 0, 0, 0, 0)
     assert ctypes.sizeof(sk.StarkvConfig) == 72
+
+
+def test_uniform_4bit_support():
+    """Both precision blocks at 4 bits (the 4-bit cache of the review's speed
+    figures, section 6.1): accepted for decode (latent and rotary scores),
+    1024 key bytes per tile-head and 32 value bytes per channel and tile,
+    refused by the prefill before any HIP call."""
+    lib = sk.load_library()
+    w = synth.WORKLOADS["l2_q4"]
+    cfg = _cfg(w)
+    assert cfg.lo_bits == 4
+    nt = w.max_tokens // 64
+    assert sk.starkv_cache_bytes(cfg, 0) == w.batch * w.n_kv_heads * nt * 1024
+    assert sk.starkv_cache_bytes(cfg, 2) == w.batch * nt * 32 * w.value_rank
+    # per token: 32 heads x (16 B codes + 8 B meta) keys, 512 B codes +
+    # 128 B meta values
+    total = sum(sk.starkv_cache_bytes(cfg, i) for i in range(4))
+    assert total == w.batch * w.max_tokens * 1408
+    assert sk.starkv_decode_splits(cfg, w.seq_len) > 0
+    assert sk.starkv_workspace_bytes(cfg, sk.OP_DECODE, w.seq_len) > 0
+    rope = _cfg(w, rope_theta=10000.0)
+    assert sk.starkv_workspace_bytes(rope, sk.OP_DECODE, w.seq_len) > 0
+    for hq, hkv, rv in ((32, 8, 256), (16, 2, 512), (16, 4, 768), (8, 8, 1024)):
+        c = _cfg(w, n_q_heads=hq, n_kv_heads=hkv, value_rank=rv)
+        assert sk.starkv_decode_splits(c, 1000) > 0, (hq, hkv, rv)
+    # the prefill reads the 4/3-bit layout only
+    small = _cfg(w, max_tokens=256)
+    assert sk.starkv_workspace_bytes(small, sk.OP_PREFILL, 64) == 0
+    cache = _fake_cache()
+    st = lib.starkv_prefill(ctypes.byref(small), ctypes.byref(cache), 0, 64, 0x1000, 4096,
+                            0x2000, 0x3000, 0x4000, 0x5000, 0x6000, ctypes.c_float(0.1),
+                            0x7000, None, 0x8000, 1 << 30, None)
+    assert st == sk.STARKV_EUNSUPPORTED
+    # other trailing widths stay unsupported
+    assert sk.starkv_cache_bytes(_cfg(w, lo_bits=2), 0) == 0
+    assert sk.starkv_cache_bytes(_cfg(w, lo_bits=5), 0) == 0
 
 
 def test_q43_shape_without_decode_kernel_is_rejected_before_launch():

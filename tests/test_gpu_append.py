@@ -22,6 +22,8 @@ CASES = [
     ("l2_q43", dict(batch=2)),
     ("l2_q43", dict(batch=2, rotate=False)),
     ("l3_gqa_q43", dict(batch=3)),
+    ("l2_q4", dict(batch=2)),
+    ("l2_q4", dict(batch=2, rotate=False, value_rank=256)),
 ]
 
 

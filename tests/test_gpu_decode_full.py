@@ -81,6 +81,11 @@ def test_full_q43_b16_t32768():
     assert run_full("l2_q43", 16, 32768, [0, 15]) <= TOL
 
 
+def test_full_u4_b16_t32768():
+    """The measured workload's shape with a uniform 4-bit cache."""
+    assert run_full("l2_q4", 16, 32768, [0, 15]) <= TOL
+
+
 def test_full_gqa_q43_b32_t16384():
     assert run_full("l3_gqa_q43", 32, 16384, [0, 31]) <= TOL
 

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("name,batch,ctx,n", [
     ("l2_q43", 3, 700, 1), ("l2_q43", 2, 125, 5), ("l3_gqa_q43", 4, 1000, 1),
-    ("l2_q43", 2, 640, 0), ("l2_bf16", 2, 300, 2), ("tiny", 1, 255, 1)])
+    ("l2_q43", 2, 640, 0), ("l2_bf16", 2, 300, 2), ("tiny", 1, 255, 1),
+    ("l2_q4", 2, 700, 1)])
 def test_decode_step_equals_append_then_decode(name, batch, ctx, n):
     import torch
     w = synth.WORKLOADS[name].replace(batch=batch)

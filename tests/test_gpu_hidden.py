@@ -44,6 +44,7 @@ def make_wo(w, D, seed):
     ("l2_bf16", 2, 300, 256, dict(n_q_heads=8, n_kv_heads=4, value_rank=512)),
     ("l2_q43", 17, 333, 128, dict(n_q_heads=4, n_kv_heads=4, value_rank=256)),
     ("l2_q43", 70, 100, 256, dict(n_q_heads=4, n_kv_heads=4, value_rank=256)),
+    ("l2_q4", 2, 500, 256, dict(n_q_heads=8, n_kv_heads=8, value_rank=512)),
 ])
 def test_fused_factor_and_hidden_decode(name, batch, seq_len, D, kw):
     import torch

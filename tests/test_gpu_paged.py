@@ -19,7 +19,7 @@ import synth
 from oracle import cache as oc
 from oracle import paged
 
-from helpers import TOL, append_both, config_for, dev, fill_random, rel_err, sk
+from helpers import TOL, append_both, config_for, dev, fill_random, qbits, rel_err, sk
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,8 @@ def run_paged(name, batch, ctx, lens, rope=0.0, seed=0, **kw):
     w = synth.WORKLOADS[name].replace(batch=batch, **kw)
     T = ((ctx + 1 + 63) // 64 + 1) * 64
     cfg = sk().make_config(batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.key_rank,
-                           w.value_rank, T, w.cache, w.rotate, rope_theta=rope)
+                           w.value_rank, T, w.cache, w.rotate, rope_theta=rope,
+                           **qbits(w))
     g = sk().LatentCache(cfg)
     o = oc.Cache.for_workload(w, max_tokens=T)
     fill_random(g, o, seed=ctx + seed)
@@ -106,3 +107,8 @@ def test_paged_ragged_gqa():
 def test_paged_ragged_rope():
     assert run_paged("l2_q43", 3, 500, [500, 200, 65], rope=10000.0, n_q_heads=8,
                      n_kv_heads=8, value_rank=256, seed=2) <= TOL
+
+
+def test_paged_ragged_uniform_4bit():
+    assert run_paged("l2_q4", 3, 700, [700, 1, 300], n_q_heads=8, n_kv_heads=8,
+                     value_rank=256, seed=3) <= TOL

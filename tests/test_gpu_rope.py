@@ -19,7 +19,8 @@ import synth
 from oracle import attention as oa
 from oracle import cache as oc
 
-from helpers import TOL, append_both, config_for, dev, fill_byte, fill_random, rel_err, sk
+from helpers import (TOL, append_both, config_for, dev, fill_byte, fill_random, qbits,
+                     rel_err, sk)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +32,11 @@ def run_rope(name, seq_len, theta, batch=2, q_scale=4.0, num_splits=0, fill="ran
     T = max_tokens or ((seq_len + 63) // 64 + 1) * 64
     rot = w.rotate if rotate is None else rotate
     cfg = sk().make_config(batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.key_rank,
-                           w.value_rank, T, w.cache, rot, num_splits, rope_theta=theta)
+                           w.value_rank, T, w.cache, rot, num_splits, rope_theta=theta,
+                           **qbits(w))
     g = sk().LatentCache(cfg)
-    o = oc.Cache(batch, w.n_kv_heads, w.key_rank, w.value_rank, T, w.cache, rot)
+    o = oc.Cache(batch, w.n_kv_heads, w.key_rank, w.value_rank, T, w.cache, rot,
+                 lo_bits=w.lo_bits)
     if fill == "random":
         fill_random(g, o, seed=seq_len + 11)
     else:
@@ -81,6 +84,13 @@ def test_rope_head_dim_64_rotation_off_peaked():
 def test_rope_nan_unused_slots():
     assert run_rope("l2_q43", 333, 10000.0, fill=0xFF, n_q_heads=4, n_kv_heads=4,
                     value_rank=512) <= TOL
+
+
+@pytest.mark.parametrize("hq,hkv,dh,rv", [(8, 8, 128, 256), (8, 4, 64, 256)])
+def test_rope_uniform_4bit(hq, hkv, dh, rv):
+    """Uniform 4-bit keys (four nibble planes) under the rotary scoring."""
+    assert run_rope("l2_q4", 700, 10000.0, n_q_heads=hq, n_kv_heads=hkv, head_dim=dh,
+                    value_rank=rv) <= TOL
 
 
 def test_rope_gqa_full_shape_groups():
