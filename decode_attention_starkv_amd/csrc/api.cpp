@@ -39,9 +39,8 @@ int check_config(const starkv_config* c) {
       if (c->key_ranks[g] < 8 || c->key_ranks[g] % 8 != 0 ||
           c->key_ranks[g] > c->key_rank)
         return STARKV_EINVAL;
-    // per-head ranks: the unquantized caches (the 4/3-bit key tile is built
-    // for 32 channels)
-    if (quant) return STARKV_EUNSUPPORTED;
+    // quantized caches pad every head to the 32-channel key tile (eq. 15's
+    // padding term): ranks are checked against key_rank = 32 above
   }
   // rotary keys: the 4/3-bit cache's decode only (rope.hip), head_dim 64 or 128
   if (c->rope_theta > 0.0f &&

@@ -155,6 +155,13 @@ __device__ inline void append_q43_keys(const float* __restrict__ zk,
     float4 v = src[k];
     x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
   }
+  // per-head ranks: the head's latent is padded with zeros to the 32-channel
+  // tile (whole blocks of 8, so the rotation never mixes them with its
+  // channels)
+  const int rank = d.krank[h];
+#pragma unroll
+  for (int c = 8; c < 32; ++c)
+    if (c >= rank) x[c] = 0.0f;
   if (d.rotate) {
     fwht8(x); fwht8(x + 8); fwht8(x + 16); fwht8(x + 24);
   }

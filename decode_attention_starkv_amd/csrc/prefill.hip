@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256) void prefill_qproj_kernel(const uint16_t* __re
   const int bs = d.dh + 8;    // row stride of bt: operand reads spread over the banks
   for (int i = tid; i < d.dh * 32; i += 256) {
     const int k = i >> 5, c = i & 31;
-    bt[c * bs + k] = bk[((size_t)g * d.dh + k) * 32 + c];
+    // channels past the head's key rank have no factor column (zero)
+    bt[c * bs + k] = c < d.krank[g] ? bk[((size_t)g * d.dh + k) * 32 + c] : (uint16_t)0;
   }
   __syncthreads();
   const int r0 = blockIdx.x * 128 + wave * 32;

@@ -82,8 +82,6 @@ __global__ __launch_bounds__(256) void rope_qproj_kernel(const uint16_t* __restr
   const int half = d.dh / 2;
   // the query sits at its sequence's last position (ragged batches: its own)
   if (d.lens) q_pos = seq_len_of(d, bh / d.Hq, q_pos + 1) - 1;
-  const float* dummy = nullptr;
-  (void)dummy;
   // q' = R_t q
   if (t < half) {
     float c, s;
@@ -95,10 +93,12 @@ __global__ __launch_bounds__(256) void rope_qproj_kernel(const uint16_t* __restr
   }
   __syncthreads();
   // A (rows i < half) and C (rows half + i), 32 latent channels each
+  // (channels past the head's key rank have no factor column: zero)
+  const int rank = d.krank[g];
   for (int x = t; x < half * 32; x += 256) {
     const int i = x / 32, r = x % 32;
-    const float b0 = bf16v(bk[((size_t)g * d.dh + i) * 32 + r]);
-    const float b1 = bf16v(bk[((size_t)g * d.dh + i + half) * 32 + r]);
+    const float b0 = r < rank ? bf16v(bk[((size_t)g * d.dh + i) * 32 + r]) : 0.0f;
+    const float b1 = r < rank ? bf16v(bk[((size_t)g * d.dh + i + half) * 32 + r]) : 0.0f;
     Mf[i][r] = qr[i] * b0 + qr[i + half] * b1;
     Mf[half + i][r] = qr[i + half] * b0 - qr[i] * b1;
   }

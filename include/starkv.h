@@ -131,9 +131,15 @@ typedef struct starkv_config {
   const int32_t* key_ranks; /* (host) NULL: every KV head has key_rank
                           channels.  Otherwise n_kv_heads per-head ranks
                           (section 4 / Fig. 2: learned per-head ranks; eq. 15
-                          sums them), each a multiple of 8 and <= key_rank;
-                          the key cache then stores head g with key_ranks[g]
-                          channels (F32/BF16 caches only) */
+                          sums them), each a multiple of 8 and <= key_rank.
+                          F32/BF16: the key cache stores head g with
+                          key_ranks[g] channels.  Q43: every head keeps its
+                          32-channel key tile, the channels past its rank
+                          zero (section 6.2: rank rounding to a supported
+                          kernel tile, eq. 15's padding term).  Either way
+                          z_key rows stay key_rank wide and B_key stays
+                          [Hkv][d_h][key_rank]; entries past a head's rank
+                          are ignored */
 } starkv_config;
 
 /* Device buffers of one layer's cache.  Byte layout ("format v1", tiles of

@@ -25,11 +25,18 @@ import numpy as np
 from . import hadamard
 
 
-def effective_factors(bk, bv, rotate, key_rank, value_rank):
+def effective_factors(bk, bv, rotate, key_rank, value_rank, key_ranks=None):
     """Factors that reconstruct from the stored latents: B (no rotation) or
-    B H (rotated cache, eq. 13), float64."""
-    bk = np.asarray(bk, np.float64)
+    B H (rotated cache, eq. 13), float64.  key_ranks: KV head g's key factor
+    has key_ranks[g] columns (review section 4, learned per-head ranks); the
+    columns past it do not exist and are taken as zero, so whatever a cache
+    holds in those channels (a 4/3-bit tile's padding) never reaches a
+    score."""
+    bk = np.array(bk, np.float64)
     bv = np.asarray(bv, np.float64)
+    if key_ranks is not None:
+        for g, r in enumerate(key_ranks):
+            bk[g, :, r:] = 0.0
     if not rotate:
         return bk, bv
     rk = hadamard.rotation_matrix(key_rank // 4, key_rank - key_rank // 4)
@@ -76,7 +83,7 @@ def decode(cache, seq_len, q, bk, bv, sm_scale, n_q_heads, rotate,
     n_kv = cache.H
     group = n_q_heads // n_kv
     d_h = q.shape[-1]
-    bk_e, bv_e = effective_factors(bk, bv, rotate, cache.rk, cache.rv)
+    bk_e, bv_e = effective_factors(bk, bv, rotate, cache.rk, cache.rv, cache.kr)
     batches = range(q.shape[0]) if batches is None else batches
     heads = range(n_q_heads) if heads is None else heads
     out = np.zeros((len(batches), len(heads), d_h))
@@ -157,7 +164,7 @@ def causal_attention(cache, ctx_len, q, bk, bv, sm_scale, n_q_heads, rotate,
     q = np.asarray(q, np.float64)
     d_h = q.shape[-1]
     group = n_q_heads // cache.H
-    bk_e, bv_e = effective_factors(bk, bv, rotate, cache.rk, cache.rv)
+    bk_e, bv_e = effective_factors(bk, bv, rotate, cache.rk, cache.rv, cache.kr)
     rows = np.arange(c) if rows is None else np.asarray(rows)
     heads = range(n_q_heads) if heads is None else heads
     zkl = cache.key_latents(batch, total)
@@ -214,7 +221,7 @@ def decode_latent_rows(cache, seq_len, q, bk, sm_scale, n_q_heads, rotate,
     n_kv = cache.H
     group = n_q_heads // n_kv
     bk_e, _ = effective_factors(bk, np.zeros((1, cache.rv)), rotate, cache.rk,
-                                cache.rv)
+                                cache.rv, cache.kr)
     batches = range(q.shape[0]) if batches is None else batches
     out = np.zeros((len(batches), n_q_heads, cache.rv))
     for bi, b in enumerate(batches):

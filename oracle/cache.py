@@ -74,9 +74,10 @@ def value_tile_bytes(value_rank, lo_bits=3):
 
 def layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache,
            key_ranks=None, lo_bits=3):
-    """Byte sizes of the four cache buffers.  key_ranks (fp32 / bf16 caches):
-    per-KV-head key ranks; the key buffer then holds sum(key_ranks) channels
-    per token (the technical review's eq. 15 sums the per-head ranks)."""
+    """Byte sizes of the four cache buffers.  key_ranks: per-KV-head key
+    ranks; an fp32 / bf16 key buffer then holds sum(key_ranks) channels per
+    token (the technical review's eq. 15 sums the per-head ranks), a q43 one
+    keeps its 32-channel tiles (eq. 15's padding term)."""
     assert max_tokens % TT == 0
     nt = max_tokens // TT
     if cache in ("f32", "bf16"):
@@ -256,21 +257,25 @@ class Cache:
         self.T, self.kind, self.rotate = max_tokens, cache, rotate
         self.lob = lo_bits        # bits of the trailing precision block (q43)
         self.nt = max_tokens // TT
-        # per-head key ranks (fp32 / bf16 caches): head g keeps key_ranks[g]
-        # channels; key_rank is the largest, the width of the latent rows
+        # per-head key ranks: head g keeps key_ranks[g] channels; key_rank is
+        # the largest, the width of the latent rows.  fp32 / bf16 caches
+        # store exactly those channels; a q43 cache keeps every head's
+        # 32-channel tile with the channels past its rank zero (the review's
+        # section 6.2: rank rounding to a supported kernel tile, eq. 15's
+        # padding term)
         self.kr = None if key_ranks is None else [int(r) for r in key_ranks]
-        assert self.kr is None or (cache in ("f32", "bf16") and
-                                   all(r % 8 == 0 and 0 < r <= key_rank for r in self.kr))
+        assert self.kr is None or all(r % 8 == 0 and 0 < r <= key_rank for r in self.kr)
         sz = layout(batch, n_kv_heads, key_rank, value_rank, max_tokens, cache, key_ranks,
                     lo_bits)
         self.buf = {k: np.full(v, fill, np.uint8) for k, v in sz.items()}
 
     @classmethod
-    def for_workload(cls, w, fill=0, batch=None, max_tokens=None):
+    def for_workload(cls, w, fill=0, batch=None, max_tokens=None, key_ranks=None):
         return cls(w.batch if batch is None else batch, w.n_kv_heads,
                    w.key_rank, w.value_rank,
                    w.max_tokens if max_tokens is None else max_tokens,
-                   w.cache, w.rotate, fill, lo_bits=getattr(w, "lo_bits", 3))
+                   w.cache, w.rotate, fill, key_ranks=key_ranks,
+                   lo_bits=getattr(w, "lo_bits", 3))
 
     # -- views -------------------------------------------------------------
     def _elem_views(self):
@@ -341,6 +346,10 @@ class Cache:
                     hv[:, t // TT, t % TT] = kk[:, :, g, :rg].reshape(self.B, n, rg // 8, 8)
             v[:, t // TT, (t % TT) // 8, t % 8] = vv.reshape(self.B, n, *v.shape[4:])
             return
+        if self.kr is not None:
+            zk = zk.copy()
+            for g, rg in enumerate(self.kr):
+                zk[:, :, g, rg:] = 0.0
         if self.rotate:
             zk = hadamard.rotate_latent_f32(zk, self.rk // 4)
             zv = hadamard.rotate_latent_f32(zv, self.rv // 4)

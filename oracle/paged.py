@@ -27,7 +27,7 @@ def gather(pool, table, b, n_tiles):
     t < n_tiles."""
     assert pool.kind == "q43"
     c = oc.Cache(1, pool.H, pool.rk, pool.rv, n_tiles * oc.TT, "q43", pool.rotate,
-                 lo_bits=pool.lob)
+                 key_ranks=pool.kr, lo_bits=pool.lob)
     src, dst = _tile_views(pool), _tile_views(c)
     for t in range(n_tiles):
         for k in src:

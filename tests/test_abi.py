@@ -314,9 +314,19 @@ def test_per_head_key_ranks_cache_bytes():
     assert sk.starkv_cache_bytes(cfg, sk.BUF_KEY) == lay["key"] == \
         w.batch * w.max_tokens * sum(ranks) * 2
     assert sk.starkv_decode_splits(cfg, 1000) > 0
-    # the 4/3-bit key tile is built for 32 channels: no per-head ranks there
-    q = _cfg(synth.WORKLOADS["l2_q43"], key_ranks=[32] * 32)
-    assert sk.starkv_cache_bytes(q, 0) == 0
+    # quantized caches keep every head's 32-channel key tile (section 6.2:
+    # rank rounding to a supported kernel tile, eq. 15's padding term)
+    qw = synth.WORKLOADS["l2_q43"]
+    plain = _cfg(qw)
+    for lob in (3, 4):
+        q = _cfg(qw, key_ranks=[8, 16, 24, 32] * 8, lo_bits=lob)
+        for i in range(4):
+            assert sk.starkv_cache_bytes(q, i) == sk.starkv_cache_bytes(
+                _cfg(qw, lo_bits=lob), i) > 0
+        assert sk.starkv_decode_splits(q, 1000) == sk.starkv_decode_splits(plain, 1000)
+    # ranks past the tile, or not a multiple of 8, are invalid
+    assert sk.starkv_cache_bytes(_cfg(qw, key_ranks=[40] * 32), 0) == 0
+    assert sk.starkv_cache_bytes(_cfg(qw, key_ranks=[12] * 32), 0) == 0
 
 
 def test_call_validation_before_any_hip_call():

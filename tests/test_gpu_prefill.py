@@ -45,13 +45,14 @@ def chunk_inputs(w, chunk, batch, q_scale):
 
 
 def run_prefill(ctx, chunk, batch=1, q_scale=1.0, rows=None, heads=None,
-                fill="random", oracle_context=True, name="longchat_prefill", **kw):
+                fill="random", oracle_context=True, name="longchat_prefill",
+                key_ranks=None, **kw):
     import torch
     w = synth.WORKLOADS[name].replace(batch=batch, **kw)
     T = ((ctx + chunk + 63) // 64 + 1) * 64
-    cfg = config_for(w, max_tokens=T)
+    cfg = config_for(w, max_tokens=T, key_ranks=key_ranks)
     g = sk().LatentCache(cfg)
-    o = oc.Cache.for_workload(w, max_tokens=T)
+    o = oc.Cache.for_workload(w, max_tokens=T, key_ranks=key_ranks)
     if fill == "random":
         fill_random(g, o, seed=ctx * 7 + chunk)
     else:
@@ -131,6 +132,16 @@ def test_prefill_gqa_and_ranks(hq, hkv, dh, rv):
 
 def test_prefill_batch_rotation_off_and_peaked():
     zerr, err, _ = run_prefill(70, 45, batch=2, q_scale=8.0, rotate=False, **SMALL)
+    assert zerr <= 1e-4
+    assert err <= TOL
+
+
+def test_prefill_per_head_key_ranks():
+    """Per-head key ranks on the quantized cache (heads padded to the
+    32-channel key tile): the appended chunk's padded channels are zero and
+    the query side drops the factor columns past each head's rank."""
+    ranks = [8, 32, 16, 24, 8, 16, 32, 24]
+    zerr, err, _ = run_prefill(100, 70, key_ranks=ranks, **SMALL)
     assert zerr <= 1e-4
     assert err <= TOL
 
