@@ -48,7 +48,17 @@ METRIC = ("latent-KV decode attention: tokens attended/s and % HBM roofline "
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published peak
 COUNTERS = os.path.join(ROOT, "profiles", "split_kernel_l2_q43_counters.json")
-DECODE_SRC = os.path.join(ROOT, "decode_attention_starkv_amd", "csrc", "decode.hip")
+# sources of the split kernel the counters describe: a change to any of them
+# invalidates the committed traffic figure
+SPLIT_SRCS = [os.path.join(ROOT, "decode_attention_starkv_amd", "csrc", f)
+              for f in ("decode.hip", "split_q43.h", "device.h", "internal.h")]
+
+
+def split_sources_sha256():
+    h = hashlib.sha256()
+    for f in SPLIT_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 
@@ -475,8 +485,7 @@ def traffic_from_counters(w, batch, seq_len, splits):
     if not os.path.exists(COUNTERS):
         return None
     rec = json.load(open(COUNTERS))
-    src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if rec.get("decode_hip_sha256") != src:
+    if rec.get("split_sources_sha256") != split_sources_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
 
