@@ -623,31 +623,38 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   auto dma = [&](const uint8_t* src, uint8_t* dst) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   };
+  // Pieces are numbered keys first (nkp), then codes (ncp), then scales and
+  // zeros (nmp each); wave w issues the pieces p with p % 8 == w.  Each kind
+  // has its own loop with its base address set up once per call, so a piece
+  // costs an address add and the load.
+  auto first_piece = [&](int p0) { return p0 + ((wave - p0) & 7); };
   auto stage = [&](int kt, int ct) {
-    const int p_key = kt <= tile_last ? nkp : 0;
-    const int p_val = ct <= tile_last ? ncp + 2 * nmp : 0;
-    for (int p = wave; p < p_key + p_val; p += 8) {
-      if (p < p_key) {
+    if (kt <= tile_last) {
+      // piece p: KV head g0 + p / 4, tokens 16 (p % 4) .. + 15 of tile kt
+      const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kd) +
+          (((size_t)b * d.Tmax + (size_t)kt * kTile) * d.Hkv + g0) * 64 + key_src_lane;
+      uint8_t* kdst = &key_l[kt & 1][0];
+      for (int p = wave; p < nkp; p += 8) {
         const int kh = p >> 2, blk = p & 3;
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kd) +
-            (((size_t)b * d.Tmax + kt * kTile + blk * 16) * d.Hkv + g0 + kh) * 64 + key_src_lane;
-        dma(src, &key_l[kt & 1][kh * (kTile * 64) + blk * 1024]);
-      } else if (p < p_key + ncp) {
-        const int q = p - p_key;
-        const int off = q * 1024 + lane * 16;
-        if (off < code_bytes)
-          dma(a.value + ((size_t)b * d.NT + ct) * vtile_bytes + code_lo + off,
-              &code_l[ct & 1][q * 1024]);
-      } else {
-        const int q = p - p_key - ncp;
-        const int part = q / nmp, piece = q - part * nmp;   // part 0 scales, 1 zeros
-        const int off = piece * 1024 + lane * 16;
-        if (off < meta_bytes) {
-          const uint16_t* mt = a.vmeta + ((size_t)b * d.NT + ct) * mtile +
-                               (size_t)(part * NG + g_first) * kTile;
-          dma(reinterpret_cast<const uint8_t*>(mt) + off,
-              &meta_l[ct & 1][part * kMetaHalf + piece * 1024]);
-        }
+        dma(kbase + ((size_t)blk * 16 * d.Hkv + kh) * 64, kdst + kh * (kTile * 64) + blk * 1024);
+      }
+    }
+    if (ct <= tile_last) {
+      const uint8_t* cbase = a.value + ((size_t)b * d.NT + ct) * vtile_bytes + code_lo + lane * 16;
+      uint8_t* cdst = &code_l[ct & 1][0];
+      for (int p = first_piece(nkp); p < nkp + ncp; p += 8) {
+        const int q = p - nkp;
+        if (q * 1024 + lane * 16 < code_bytes) dma(cbase + q * 1024, cdst + q * 1024);
+      }
+      const uint8_t* mbase = reinterpret_cast<const uint8_t*>(
+          a.vmeta + ((size_t)b * d.NT + ct) * mtile + (size_t)g_first * kTile) + lane * 16;
+      uint8_t* mdst = &meta_l[ct & 1][0];
+      for (int p = first_piece(nkp + ncp); p < nkp + ncp + 2 * nmp; p += 8) {
+        const int q = p - nkp - ncp;
+        const int part = q >= nmp ? 1 : 0, piece = q - part * nmp;   // 0 scales, 1 zeros
+        if (piece * 1024 + lane * 16 < meta_bytes)
+          dma(mbase + (size_t)part * NG * kTile * 2 + piece * 1024,
+              mdst + part * kMetaHalf + piece * 1024);
       }
     }
   };
