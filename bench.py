@@ -54,11 +54,34 @@ SPLIT_SRCS = [os.path.join(ROOT, "decode_attention_starkv_amd", "csrc", f)
               for f in ("decode.hip", "split_q43.h", "device.h", "internal.h")]
 
 
-def split_sources_sha256():
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_attn_longchat_counters.json")
+PREFILL_SRCS = [os.path.join(ROOT, "decode_attention_starkv_amd", "csrc", f)
+                for f in ("prefill.hip", "device.h", "internal.h")]
+
+
+def sources_sha256(paths):
     h = hashlib.sha256()
-    for f in SPLIT_SRCS:
+    for f in paths:
         h.update(open(f, "rb").read())
     return h.hexdigest()
+
+
+def split_sources_sha256():
+    return sources_sha256(SPLIT_SRCS)
+
+
+def prefill_traffic_from_counters(w, ctx, chunk):
+    """HBM bytes per prefill attention launch from committed rocprofv3
+    counters, or None if its sources changed since they were taken or the run
+    is not the configuration they were taken on (longchat_prefill defaults)."""
+    if (w.name, w.batch, ctx, chunk) != ("longchat_prefill", 1, 24576, 8192):
+        return None
+    if not os.path.exists(PREFILL_COUNTERS):
+        return None
+    rec = json.load(open(PREFILL_COUNTERS))
+    if rec.get("prefill_sources_sha256") != sources_sha256(PREFILL_SRCS):
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 
@@ -344,7 +367,7 @@ def run_prefill(args, w, torch, sk, synth):
         "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel",
                      "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS,
-                     "traffic": None},
+                     "traffic": prefill_traffic_from_counters(w, ctx, chunk)},
         "kernels_ms": {"gemm": mean(kern[0]), "append": mean(kern[1]),
                        "qproj": mean(kern[2]), "attention": attn_ms,
                        "merge_vproj": mean(kern[4])},
