@@ -139,8 +139,9 @@ __device__ inline void wait_vmcnt() {
 
 // fp16 key latents z + s * code of positions [0, n) of every sequence and KV
 // head, channels in their natural order: [B][T_max][Hkv][32] (64 bytes per
-// token and head).  One thread per (sequence, position, KV head).  The
-// attention kernel reads them as MFMA operands.
+// token and head), from a 4/3-bit or a uniform 4-bit key tile.  One thread
+// per (sequence, position, KV head).  The attention kernel reads them as
+// MFMA operands.
 __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restrict__ key,
                                                           const u32x2* __restrict__ kmeta,
                                                           Dims d, int n,
@@ -152,11 +153,13 @@ __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restr
   const int b = idx / ((size_t)d.Hkv * n);
   const int tile = t / kTile, u = t % kTile;
   const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + h;
-  const uint8_t* kb = key + blk * key_block_bytes(3);
+  const uint8_t* kb = key + blk * key_block_bytes(d.lob);
   const uint32_t whi = reinterpret_cast<const uint32_t*>(kb)[u];
   const uint32_t w0 = reinterpret_cast<const uint32_t*>(kb + 256)[u];
   const uint32_t w1 = reinterpret_cast<const uint32_t*>(kb + 512)[u];
-  const uint32_t R = kb[768 + u] | (((w0 >> 15) & 1u) << 8) | ((w0 >> 31) << 9) |
+  // the remainder byte (4/3-bit) or the fourth 4-bit plane
+  const uint32_t w2 = d.lob == 4 ? reinterpret_cast<const uint32_t*>(kb + 768)[u] : kb[768 + u];
+  const uint32_t R = w2 | (((w0 >> 15) & 1u) << 8) | ((w0 >> 31) << 9) |
                      (((w1 >> 15) & 1u) << 10) | ((w1 >> 31) << 11);
   const u32x2 mt = kmeta[blk * kTile + u];
   const uint32_t m0 = mt[0], m1 = mt[1];
@@ -168,18 +171,27 @@ __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restr
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     v[c] = (_Float16)fmaf((float)s_hi, (float)((whi >> (4 * c)) & 15u), (float)z_hi);
-  // 3-bit channel i (= key channel 8 + i): i < 5 lo0 bits 3i, i < 10 lo1
-  // bits 3(i-5), i < 15 lo0 bits 16+3(i-10), i < 20 lo1 bits 16+3(i-15),
-  // else bits 3(i-20) of the 12-bit remainder
+  if (d.lob == 4) {
+    // uniform 4-bit: channel 8p + c at bits 4c of plane p
+    const uint32_t pl[3] = {w0, w1, w2};
 #pragma unroll
-  for (int i = 0; i < 24; ++i) {
-    uint32_t code;
-    if (i < 5) code = (w0 >> (3 * i)) & 7u;
-    else if (i < 10) code = (w1 >> (3 * (i - 5))) & 7u;
-    else if (i < 15) code = (w0 >> (16 + 3 * (i - 10))) & 7u;
-    else if (i < 20) code = (w1 >> (16 + 3 * (i - 15))) & 7u;
-    else code = (R >> (3 * (i - 20))) & 7u;
-    v[8 + i] = (_Float16)fmaf((float)s_lo, (float)code, (float)z_lo);
+    for (int i = 0; i < 24; ++i)
+      v[8 + i] = (_Float16)fmaf((float)s_lo, (float)((pl[i / 8] >> (4 * (i % 8))) & 15u),
+                                (float)z_lo);
+  } else {
+    // 3-bit channel i (= key channel 8 + i): i < 5 lo0 bits 3i, i < 10 lo1
+    // bits 3(i-5), i < 15 lo0 bits 16+3(i-10), i < 20 lo1 bits 16+3(i-15),
+    // else bits 3(i-20) of the 12-bit remainder
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      uint32_t code;
+      if (i < 5) code = (w0 >> (3 * i)) & 7u;
+      else if (i < 10) code = (w1 >> (3 * (i - 5))) & 7u;
+      else if (i < 15) code = (w0 >> (16 + 3 * (i - 10))) & 7u;
+      else if (i < 20) code = (w1 >> (16 + 3 * (i - 15))) & 7u;
+      else code = (R >> (3 * (i - 20))) & 7u;
+      v[8 + i] = (_Float16)fmaf((float)s_lo, (float)code, (float)z_lo);
+    }
   }
   h8* dst = reinterpret_cast<h8*>(kd + (((size_t)b * d.Tmax + t) * d.Hkv + h) * 32);
 #pragma unroll
@@ -390,10 +402,10 @@ constexpr int kMaxRv = 1024;
 constexpr int kMaxCols = 512;      // value columns per workgroup (at most)
 // bytes of one tile's value scales (or zeros) over the workgroup's groups
 constexpr int kMetaHalf = (kMaxCols / 32) * kTile * 2;
-// bytes of one tile's value codes over the workgroup's groups (at most
-// eight 4-bit and eight 3-bit groups: the 4-bit groups are the first R_v/4
-// channels, so no block of 512 columns holds more)
-constexpr int kCodeSlot = 8 * 1024 + 8 * 768;
+// bytes of one tile's value codes over the workgroup's groups: at most 16
+// groups of 1024 B (a uniform 4-bit cache; a 4/3-bit block of 512 columns
+// holds at most eight 4-bit and eight 3-bit groups, 14 KB)
+constexpr int kCodeSlot = 16 * 1024;
 // bytes of one tile's fp16 key latents of the workgroup's KV heads
 constexpr int kKeySlot = kPH * kTile * 64;
 
@@ -604,9 +616,9 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
 
   // ------------------------------------------------------------ value setup
   const int NG = d.rv / 32;           // value groups
-  const int NH = d.rv / 128;          // 4-bit value groups
+  const int NH = d.lob == 4 ? NG : d.rv / 128;   // 4-bit value groups
   const int ngrp = cols / 32, g_first = col0 / 32;
-  const size_t vtile_bytes = (size_t)26 * d.rv;
+  const size_t vtile_bytes = value_tile_bytes(d.rv, d.lob);
   const size_t mtile = (size_t)2 * NG * kTile;     // fp16 elements
   const int meta_bytes = ngrp * kTile * 2;
   // Direct-to-LDS staging, in 1 KB pieces spread over the waves: the fp16
@@ -826,9 +838,7 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
 }
 
 bool prefill_supported(const Dims& d) {
-  // the 4/3-bit cache (the prefill's attention tiles read its key and value
-  // layout; a uniform 4-bit cache is decode-only)
-  return d.dtype == STARKV_CACHE_Q43 && d.lob == 3 && d.rk == 32 && d.Hq % kPH == 0 &&
+  return d.dtype == STARKV_CACHE_Q43 && d.rk == 32 && d.Hq % kPH == 0 &&
          (d.G == 1 || d.G == 2 || d.G == 4 || d.G == 8) && d.rv % 256 == 0 &&
          d.rv <= kMaxRv && d.dh % 64 == 0 && d.dh <= 256;
 }

@@ -95,8 +95,8 @@ typedef enum {
  * value_rank / 4 (the model card's top_fraction = 0.25 recipe, 3.25 bits per
  * channel on average), and for the same fields with lo_bits = 4 (a uniform
  * 4-bit cache: the 4-bit cache of the review's speed figures, section 6.1
- * after eq. 14; decode only, starkv_prefill returns STARKV_EUNSUPPORTED),
- * and returns STARKV_EUNSUPPORTED for any other combination (a 20:80 split
+ * after eq. 14), and returns STARKV_EUNSUPPORTED for any other combination
+ * (a 20:80 split
  * among them).  For F32 / BF16 caches the five fields must be 0. */
 typedef struct starkv_config {
   int32_t batch;       /* B */

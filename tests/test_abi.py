@@ -144,9 +144,9 @@ def test_default_layout_fields_are_the_quarter_split():
 
 def test_uniform_4bit_support():
     """Both precision blocks at 4 bits (the 4-bit cache of the review's speed
-    figures, section 6.1): accepted for decode (latent and rotary scores),
-    1024 key bytes per tile-head and 32 value bytes per channel and tile,
-    refused by the prefill before any HIP call."""
+    figures, section 6.1): accepted for decode (latent and rotary scores) and
+    prefill, 1024 key bytes per tile-head and 32 value bytes per channel and
+    tile."""
     lib = sk.load_library()
     w = synth.WORKLOADS["l2_q4"]
     cfg = _cfg(w)
@@ -165,13 +165,17 @@ def test_uniform_4bit_support():
     for hq, hkv, rv in ((32, 8, 256), (16, 2, 512), (16, 4, 768), (8, 8, 1024)):
         c = _cfg(w, n_q_heads=hq, n_kv_heads=hkv, value_rank=rv)
         assert sk.starkv_decode_splits(c, 1000) > 0, (hq, hkv, rv)
-    # the prefill reads the 4/3-bit layout only
+    # the prefill reads both layouts; with rotary keys it is refused (decode
+    # only) before any HIP call
     small = _cfg(w, max_tokens=256)
-    assert sk.starkv_workspace_bytes(small, sk.OP_PREFILL, 64) == 0
+    assert sk.starkv_workspace_bytes(small, sk.OP_PREFILL, 64) > 0
+    assert sk.starkv_workspace_bytes(_cfg(w, max_tokens=256, rope_theta=1e4),
+                                     sk.OP_PREFILL, 64) == 0
     cache = _fake_cache()
-    st = lib.starkv_prefill(ctypes.byref(small), ctypes.byref(cache), 0, 64, 0x1000, 4096,
-                            0x2000, 0x3000, 0x4000, 0x5000, 0x6000, ctypes.c_float(0.1),
-                            0x7000, None, 0x8000, 1 << 30, None)
+    st = lib.starkv_prefill(ctypes.byref(_cfg(w, max_tokens=256, rope_theta=1e4)),
+                            ctypes.byref(cache), 0, 64, 0x1000, 4096, 0x2000, 0x3000,
+                            0x4000, 0x5000, 0x6000, ctypes.c_float(0.1), 0x7000, None,
+                            0x8000, 1 << 30, None)
     assert st == sk.STARKV_EUNSUPPORTED
     # other trailing widths stay unsupported
     assert sk.starkv_cache_bytes(_cfg(w, lo_bits=2), 0) == 0

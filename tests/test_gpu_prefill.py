@@ -146,6 +146,24 @@ def test_prefill_per_head_key_ranks():
     assert err <= TOL
 
 
+@pytest.mark.parametrize("rotate", [True, False])
+def test_prefill_uniform_4bit(rotate):
+    """A uniform 4-bit cache (both precision blocks at 4 bits): the key
+    pre-pass reads four nibble planes, every value group takes the 4-bit
+    operand path."""
+    zerr, err, _ = run_prefill(100, 77, lo_bits=4, rotate=rotate, **SMALL)
+    assert zerr <= 1e-4
+    assert err <= TOL
+
+
+def test_prefill_uniform_4bit_gqa_wide():
+    """G 4, R_v 1024 (two column blocks of sixteen 4-bit groups each)."""
+    kw = dict(SMALL, n_q_heads=16, n_kv_heads=4, head_dim=256, value_rank=1024)
+    zerr, err, _ = run_prefill(64, 130, lo_bits=4, **kw)
+    assert zerr <= 1e-4
+    assert err <= TOL
+
+
 def test_prefill_nan_unused_slots():
     """Unused cache bytes are 0xFF (NaN scales and zeros): masking keeps
     them out of every operand."""
