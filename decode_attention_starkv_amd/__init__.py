@@ -36,7 +36,7 @@ ENTRY_POINTS = ("starkv_cache_bytes", "starkv_workspace_bytes",
                 "starkv_fused_factor_bytes", "starkv_fuse_value_output",
                 "starkv_decode_hidden_workspace_bytes", "starkv_decode_hidden",
                 "starkv_decode_hidden_profiled", "starkv_append_paged",
-                "starkv_decode_paged")
+                "starkv_decode_paged", "starkv_prefill_paged")
 
 
 class StarkvConfig(ctypes.Structure):
@@ -122,6 +122,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.starkv_decode_paged.argtypes = [P(StarkvConfig), P(StarkvCache), vp, i32, vp, i32,
                                         vp, vp, vp, f32, vp, vp, sz, vp]
     lib.starkv_decode_paged.restype = ctypes.c_int
+    lib.starkv_prefill_paged.argtypes = [P(StarkvConfig), P(StarkvCache), vp, i32, i32, i32,
+                                         vp, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz,
+                                         vp]
+    lib.starkv_prefill_paged.restype = ctypes.c_int
     lib.starkv_decode_noalloc.argtypes = [P(StarkvConfig), P(StarkvCache), i32, vp, vp,
                                           vp, f32, vp, vp]
     lib.starkv_decode_noalloc.restype = ctypes.c_int
@@ -328,6 +332,21 @@ def starkv_decode_paged(cfg, cache: LatentCache, page_table, seq_lens,
         _stream(stream))
     if st != STARKV_OK:
         raise StarkvError(st, "starkv_decode_paged")
+
+
+def starkv_prefill_paged(cfg, cache: LatentCache, page_table, ctx_len: int, chunk: int,
+                         x, hidden: int, A_key, A_value, q, B_key, B_value,
+                         sm_scale: float, out, workspace, z_debug=None,
+                         stream=None) -> None:
+    """starkv_prefill over a paged pool (page_table int32 [B, pages_per_seq])."""
+    cs = cache.struct
+    st = load_library().starkv_prefill_paged(
+        ctypes.byref(cfg), ctypes.byref(cs), _ptr(page_table), page_table.shape[1],
+        ctx_len, chunk, _ptr(x), hidden, _ptr(A_key), _ptr(A_value), _ptr(q),
+        _ptr(B_key), _ptr(B_value), sm_scale, _ptr(out), _ptr(z_debug), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != STARKV_OK:
+        raise StarkvError(st, "starkv_prefill_paged")
 
 
 def starkv_decode_noalloc(cfg, cache: LatentCache, seq_len: int, q, B_key,

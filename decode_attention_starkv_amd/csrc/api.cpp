@@ -426,7 +426,8 @@ static int prefill_impl(const starkv_config* cfg, const starkv_cache* cache,
                         int32_t hidden, const void* A_key, const void* A_value,
                         const void* q, const void* B_key, const void* B_value,
                         float sm_scale, float* out, float* z_debug, void* workspace,
-                        size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+                        size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                        const int32_t* page_table = nullptr, int32_t pages_per_seq = 0) {
   int st = check_config(cfg);
   if (st != STARKV_OK) return st;
   if ((st = check_cache(cfg, cache)) != STARKV_OK) return st;
@@ -437,9 +438,17 @@ static int prefill_impl(const starkv_config* cfg, const starkv_cache* cache,
       !aligned16(q) || !aligned16(B_key) || !aligned16(B_value) ||
       !aligned16(out) || (z_debug && !aligned16(z_debug)))
     return STARKV_EINVAL;
-  const Dims d = make_dims(*cfg);
+  Dims d = make_dims(*cfg);
   if (hidden % 64 != 0 || !prefill_supported(d) || cfg->rope_theta > 0.0f)
     return STARKV_EUNSUPPORTED;
+  if (page_table) {
+    // every sequence's positions [0, ctx_len + chunk) must have pages
+    if (pages_per_seq < 1 || (int64_t)pages_per_seq * kTile < (int64_t)ctx_len + chunk ||
+        reinterpret_cast<uintptr_t>(page_table) % 4 != 0)
+      return STARKV_EINVAL;
+    d.pages = page_table;
+    d.pages_per_seq = pages_per_seq;
+  }
   const PrefillWs lay = prefill_ws_layout(d, chunk);
   if (!workspace || !aligned16(workspace) || ws_bytes < lay.total)
     return STARKV_EWORKSPACE;
@@ -474,6 +483,19 @@ int starkv_prefill_profiled(const starkv_config* cfg, const starkv_cache* cache,
   return prefill_impl(cfg, cache, ctx_len, chunk, x, hidden, A_key, A_value, q,
                       B_key, B_value, sm_scale, out, z_debug, workspace,
                       ws_bytes, stream, events);
+}
+
+int starkv_prefill_paged(const starkv_config* cfg, const starkv_cache* cache,
+                         const int32_t* page_table, int32_t pages_per_seq,
+                         int32_t ctx_len, int32_t chunk, const void* x, int32_t hidden,
+                         const void* A_key, const void* A_value, const void* q,
+                         const void* B_key, const void* B_value, float sm_scale,
+                         float* out, float* z_debug, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!page_table) return STARKV_EINVAL;
+  return prefill_impl(cfg, cache, ctx_len, chunk, x, hidden, A_key, A_value, q,
+                      B_key, B_value, sm_scale, out, z_debug, workspace, ws_bytes,
+                      stream, nullptr, page_table, pages_per_seq);
 }
 
 int starkv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {

@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restr
   const int t = (idx / d.Hkv) % n;
   const int b = idx / ((size_t)d.Hkv * n);
   const int tile = t / kTile, u = t % kTile;
-  const size_t blk = ((size_t)b * d.NT + tile) * d.Hkv + h;
+  // the tile's slot: b * NT + tile, or its page in a paged pool
+  const size_t blk = tile_index(d, b, tile) * d.Hkv + h;
   const uint8_t* kb = key + blk * key_block_bytes(d.lob);
   const uint32_t whi = reinterpret_cast<const uint32_t*>(kb)[u];
   const uint32_t w0 = reinterpret_cast<const uint32_t*>(kb + 256)[u];
@@ -652,14 +653,15 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
       }
     }
     if (ct <= tile_last) {
-      const uint8_t* cbase = a.value + ((size_t)b * d.NT + ct) * vtile_bytes + code_lo + lane * 16;
+      const size_t ctix = tile_index(d, b, ct);   // the tile's slot or page
+      const uint8_t* cbase = a.value + ctix * vtile_bytes + code_lo + lane * 16;
       uint8_t* cdst = &code_l[ct & 1][0];
       for (int p = first_piece(nkp); p < nkp + ncp; p += 8) {
         const int q = p - nkp;
         if (q * 1024 + lane * 16 < code_bytes) dma(cbase + q * 1024, cdst + q * 1024);
       }
       const uint8_t* mbase = reinterpret_cast<const uint8_t*>(
-          a.vmeta + ((size_t)b * d.NT + ct) * mtile + (size_t)g_first * kTile) + lane * 16;
+          a.vmeta + ctix * mtile + (size_t)g_first * kTile) + lane * 16;
       uint8_t* mdst = &meta_l[ct & 1][0];
       for (int p = first_piece(nkp + ncp); p < nkp + ncp + 2 * nmp; p += 8) {
         const int q = p - nkp - ncp;

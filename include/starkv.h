@@ -313,6 +313,26 @@ STARKV_API int starkv_decode_paged(const starkv_config* cfg,
                                    float* out, void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
 
+/* starkv_prefill over a paged pool (same page layout as starkv_append_paged):
+ * every sequence b has the same ctx_len and chunk, and its tile t lives in
+ * pool page page_table[b * pages_per_seq + t] (device int32, clamped on the
+ * device into the pool).  The chunk's latents are appended at [ctx_len,
+ * ctx_len + chunk) of each sequence's pages, then attended to as in
+ * starkv_prefill.  pages_per_seq * 64 must cover ctx_len + chunk.
+ * Workspace: starkv_workspace_bytes(cfg, PREFILL, chunk).  Other arguments,
+ * results and errors as starkv_prefill; EINVAL also for a null or
+ * misaligned page table or too few pages per sequence. */
+STARKV_API int starkv_prefill_paged(const starkv_config* cfg,
+                                    const starkv_cache* cache,
+                                    const int32_t* page_table,
+                                    int32_t pages_per_seq, int32_t ctx_len,
+                                    int32_t chunk, const void* x, int32_t hidden,
+                                    const void* A_key, const void* A_value,
+                                    const void* q, const void* B_key,
+                                    const void* B_value, float sm_scale,
+                                    float* out, float* z_debug, void* workspace,
+                                    size_t ws_bytes, hipStream_t stream);
+
 /* ---- value/output factor fusion and the head sum (review section 5.3,
  * eq. 12 read right to left; Algorithm 2, steps 7-8) ---------------------
  * eq. 12: p_h (Z_V U_h^T) O_h = (p_h Z_V)(U_h^T O_h).  The right-hand factor

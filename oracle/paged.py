@@ -71,3 +71,25 @@ def decode_paged(pool, table, seq_lens, q, bk, bv, sm_scale, n_q_heads, rotate,
         out[bi] = attention.decode(c, n, q[b:b + 1], bk, bv, sm_scale, n_q_heads,
                                    rotate, rope_theta=rope_theta)[0]
     return out
+
+
+def prefill_paged(pool, table, ctx_len, z_key, z_value, q, bk, bv, sm_scale,
+                  n_q_heads, rotate, rows=None, heads=None):
+    """Chunked causal prefill of every sequence b of a paged pool: the
+    chunk's latents z_key [B, C, Hkv, r_k], z_value [B, C, R_v] are appended
+    at [ctx_len, ctx_len + C) of sequence b's pages (technical review of
+    arXiv 2606.08382, Algorithm 2 step 3), then query i of q [B, C, Hq, d_h]
+    (absolute position ctx_len + i) attends to positions 0 .. ctx_len + i of
+    the stored cache.  Returns out [B, len(rows), len(heads), d_h] float64."""
+    z_key = np.asarray(z_key, np.float32)
+    z_value = np.asarray(z_value, np.float32)
+    n = z_key.shape[1]
+    n_tiles = (ctx_len + n + oc.TT - 1) // oc.TT
+    outs = []
+    for b in range(z_key.shape[0]):
+        c = gather(pool, table, b, n_tiles)
+        c.append(z_key[b:b + 1], z_value[b:b + 1], ctx_len, n)
+        outs.append(attention.causal_attention(c, ctx_len, q[b], bk, bv, sm_scale,
+                                               n_q_heads, rotate, rows, heads))
+        scatter(pool, table, b, c)
+    return np.stack(outs)

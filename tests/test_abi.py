@@ -307,6 +307,18 @@ def test_paged_validation():
     assert lib.starkv_decode_paged(cp, cc, 0x100, 4, None, 100, *tail) == sk.STARKV_EINVAL
     short = tail[:6] + (16, None)
     assert lib.starkv_decode_paged(cp, cc, 0x100, 4, 0x200, 100, *short) == sk.STARKV_EWORKSPACE
+    # prefill: a table is required, its pages must cover ctx_len + chunk,
+    # rotary keys are decode-only; all before any HIP call
+    pre = (0x1000, 4096, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, ctypes.c_float(0.1),
+           0x7000, None, 0x8000, 1 << 40, None)
+    assert lib.starkv_prefill_paged(cp, cc, None, 8, 0, 64, *pre) == sk.STARKV_EINVAL
+    assert lib.starkv_prefill_paged(cp, cc, 0x100, 2, 100, 64, *pre) == sk.STARKV_EINVAL
+    assert lib.starkv_prefill_paged(cp, cc, 0x102, 8, 100, 64, *pre) == sk.STARKV_EINVAL
+    rope = _cfg(w, rope_theta=1e4)
+    assert lib.starkv_prefill_paged(ctypes.byref(rope), cc, 0x100, 8, 100, 64,
+                                    *pre) == sk.STARKV_EUNSUPPORTED
+    assert lib.starkv_prefill_paged(cp, cc, 0x100, 8, 100, 64,
+                                    *(pre[:11] + (16, None))) == sk.STARKV_EWORKSPACE
 
 
 def test_per_head_key_ranks_cache_bytes():

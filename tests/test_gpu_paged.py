@@ -112,3 +112,65 @@ def test_paged_ragged_rope():
 def test_paged_ragged_uniform_4bit():
     assert run_paged("l2_q4", 3, 700, [700, 1, 300], n_q_heads=8, n_kv_heads=8,
                      value_rank=256, seed=3) <= TOL
+
+
+@pytest.mark.parametrize("name,ctx,chunk", [("longchat_prefill", 100, 70),
+                                            ("longchat_prefill", 64, 129)])
+def test_paged_prefill(name, ctx, chunk):
+    """starkv_prefill_paged over a permuted pool of two sequences: the pool's
+    bytes after the call equal oracle.paged.prefill_paged's (fed the GPU's
+    own chunk latents, whose projection test_gpu_prefill checks), and so do
+    the outputs, to the decode bound."""
+    run_paged_prefill(name, ctx, chunk, lo_bits=3)
+
+
+def test_paged_prefill_uniform_4bit():
+    run_paged_prefill("longchat_prefill", 90, 60, lo_bits=4)
+
+
+def run_paged_prefill(name, ctx, chunk, lo_bits):
+    import torch
+    B = 2
+    w = synth.WORKLOADS[name].replace(batch=B, n_q_heads=8, n_kv_heads=8, head_dim=64,
+                                      value_rank=256, hidden=128, lo_bits=lo_bits)
+    T = ((ctx + chunk + 63) // 64 + 1) * 64
+    cfg = config_for(w, max_tokens=T)
+    g = sk().LatentCache(cfg)
+    o = oc.Cache.for_workload(w, max_tokens=T)
+    fill_random(g, o, seed=ctx + chunk)
+    print(f"paged prefill B={B} ctx={ctx} C={chunk} lo_bits={lo_bits}", flush=True)
+    append_both(w, cfg, g, o, 0, ctx, B)
+    rng = np.random.default_rng(ctx)
+    table = rng.permutation(B * o.nt).reshape(B, o.nt).astype(np.int32)
+    permute(g, o, table)
+    xs, qs = [], []
+    ak = av = None
+    for b in range(B):
+        x, a_k, a_v, q = synth.prefill_inputs(w.replace(seed=w.seed + 1000 * b), chunk)
+        if b == 0:
+            _, ak, av, _ = synth.prefill_inputs(w, chunk)
+        xs.append(x)
+        qs.append(synth.round_to_bf16(q))
+    x, q = np.stack(xs), np.stack(qs)
+    bk, bv = synth.factors(w)
+    nk = w.n_kv_heads * w.key_rank
+    bf = torch.bfloat16
+    out = torch.empty((B, chunk, w.n_q_heads, w.head_dim), device="cuda")
+    zdbg = torch.empty((B, chunk, nk + w.value_rank), device="cuda")
+    ws = sk().workspace(cfg, sk().OP_PREFILL, chunk)
+    s = 1.0 / math.sqrt(w.head_dim)
+    sk().starkv_prefill_paged(cfg, g, torch.from_numpy(table).cuda(), ctx, chunk, dev(x, bf),
+                              w.hidden, dev(ak, bf), dev(av, bf), dev(q, bf), dev(bk, bf),
+                              dev(bv, bf), s, out, ws, z_debug=zdbg)
+    torch.cuda.synchronize()
+    z = zdbg.cpu().numpy()
+    ref = paged.prefill_paged(o, table, ctx, z[:, :, :nk].reshape(B, chunk, w.n_kv_heads,
+                                                                   w.key_rank),
+                              z[:, :, nk:], q, bk, bv, s, w.n_q_heads, w.rotate)
+    for i, k in enumerate(KEYS):
+        assert np.array_equal(g.buffers[i][:o.buf[k].size].cpu().numpy(), o.buf[k]), k
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = rel_err(got, ref)
+    print(f"  rel err {err:.3e}", flush=True)
+    assert err <= TOL

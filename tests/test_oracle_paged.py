@@ -96,3 +96,37 @@ def test_paged_append_lands_in_the_named_page():
         g = paged.gather(pool, table, b, c.nt)
         for k in g.buf:
             assert np.array_equal(g.buf[k], one.buf[k]), (b, k)
+
+
+def test_paged_prefill_is_plain_prefill_per_sequence():
+    """Chunked prefill over a permuted pool: each sequence's output and bytes
+    equal the plain prefill of that sequence's contiguous cache (the chunk
+    crosses a tile boundary; the identity table gives the contiguous cache's
+    own result)."""
+    w, c, bk, bv, q = _setup(seed=8, seq=100)
+    pool, table = _permuted_pool(c, np.random.default_rng(9))
+    rng = np.random.default_rng(10)
+    C = 50
+    zk = rng.standard_normal((3, C, 4, 32)).astype(np.float32)
+    zv = (rng.standard_normal((3, C, 256)) * 0.3).astype(np.float32)
+    qc = rng.standard_normal((3, C, 4, w.head_dim)) * 4 / math.sqrt(w.head_dim)
+    s = 1 / math.sqrt(w.head_dim)
+    got = paged.prefill_paged(pool, table, 100, zk, zv, qc, bk, bv, s, 4, True)
+    for b in range(3):
+        one = oc.Cache(1, c.H, c.rk, c.rv, c.T, "q43", c.rotate)
+        for k in one.buf:
+            n = one.buf[k].size
+            one.buf[k][:] = c.buf[k][b * n:(b + 1) * n]
+        one.append(zk[b:b + 1], zv[b:b + 1], 100, C)
+        ref = oa.causal_attention(one, 100, qc[b], bk, bv, s, 4, True)
+        assert np.array_equal(got[b], ref)
+        g = paged.gather(pool, table, b, c.nt)
+        for k in g.buf:
+            assert np.array_equal(g.buf[k], one.buf[k]), (b, k)
+    # identity table: the contiguous cache prefilled in place
+    c2 = oc.Cache(3, c.H, c.rk, c.rv, c.T, "q43", c.rotate)
+    for k in c.buf:
+        c2.buf[k][:] = c.buf[k]
+    ident = np.arange(3 * c.nt).reshape(3, c.nt)
+    got2 = paged.prefill_paged(c2, ident, 100, zk, zv, qc, bk, bv, s, 4, True)
+    assert np.array_equal(got2, got)
