@@ -516,7 +516,7 @@ def traffic_from_counters(w, batch, seq_len, splits):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; "
+        print(json.dumps({"error": "the decode path runs on one GPU only; "
                           "--gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
     if args.t_sweep:

@@ -69,7 +69,7 @@ extern "C" {
 typedef enum {
   STARKV_OK = 0,
   STARKV_EINVAL = -1,       /* bad pointer, size, range or enum value */
-  STARKV_EUNSUPPORTED = -2, /* valid shape this build has no kernel for */
+  STARKV_EUNSUPPORTED = -2, /* valid shape the library has no kernel for */
   STARKV_ECAPACITY = -3,    /* tokens past max_tokens */
   STARKV_EWORKSPACE = -4,   /* workspace missing or too small */
   STARKV_ELAUNCH = -5       /* a HIP launch or query failed */
@@ -90,7 +90,7 @@ typedef enum {
  * (eq. 13) and stored at its own precision (eq. 14), with an asymmetric
  * fp16 scale and zero per group of at most group_size consecutive channels
  * of one token inside one block.  The five layout fields below state that
- * split explicitly; this build has kernels for hi_bits = 4, lo_bits = 3,
+ * split explicitly; the library has kernels for hi_bits = 4, lo_bits = 3,
  * group_size = 32, key_hi_channels = key_rank / 4 and value_hi_channels =
  * value_rank / 4 (the model card's top_fraction = 0.25 recipe, 3.25 bits per
  * channel on average), and for the same fields with lo_bits = 4 (a uniform
