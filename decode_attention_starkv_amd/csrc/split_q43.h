@@ -73,9 +73,11 @@ __device__ inline void wave_dma(const uint8_t* src, uint8_t* lds_dst, int bytes,
 constexpr int hi_region(int niv) { return niv * 1280; }
 constexpr int lo_region(int niv, bool u4) { return niv * (u4 ? 1280 : 1024); }
 constexpr int slot_bytes(int niv, bool u4) { return hi_region(niv) + 3 * lo_region(niv, u4); }
-// LDS ring slots per value wave: 4 (tiles staged three ahead of use), 3 where
-// four slots would not fit in LDS (uniform 4-bit, R_v = 1024)
-constexpr int value_slots(int niv, bool u4) { return u4 && niv == 8 ? 3 : 4; }
+// LDS ring slots per value wave: 4 (tiles staged three ahead of use); 3
+// where four slots would not fit in LDS (uniform 4-bit, R_v = 1024), and for
+// R_v <= 256, where a tile is small enough that two tiles in flight keep the
+// stream busy and a shorter opening burst lets short splits start sooner
+constexpr int value_slots(int niv, bool u4) { return (u4 && niv == 8) || niv <= 2 ? 3 : 4; }
 // fp32 row stride of the epilogue's per-wave staging of partial rows (kept
 // in the value ring): 32 rows of 32 NIV columns, padded so the two row halves
 // a store instruction writes fall in different LDS banks
