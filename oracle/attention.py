@@ -138,7 +138,7 @@ def project_latents(x, a_key, a_value, n_kv_heads, key_rank):
 
 
 def prefill(cache, ctx_len, x, a_key, a_value, q, bk, bv, sm_scale,
-            n_q_heads, rotate, rows=None, heads=None):
+            n_q_heads, rotate, rows=None, heads=None, rope_theta=0.0):
     """Chunked causal prefill of a one-sequence cache.
 
     Projects the chunk X [C, D] into latents, appends them at [ctx_len,
@@ -151,14 +151,17 @@ def prefill(cache, ctx_len, x, a_key, a_value, q, bk, bv, sm_scale,
     zk, zv = project_latents(x, a_key, a_value, cache.H, cache.rk)
     cache.append(zk[None], zv[None], ctx_len, c)
     return causal_attention(cache, ctx_len, q, bk, bv, sm_scale, n_q_heads,
-                            rotate, rows, heads)
+                            rotate, rows, heads, rope_theta=rope_theta)
 
 
 def causal_attention(cache, ctx_len, q, bk, bv, sm_scale, n_q_heads, rotate,
-                     rows=None, heads=None, batch=0):
+                     rows=None, heads=None, batch=0, rope_theta=0.0):
     """Causal attention of a chunk's queries q [C, Hq, d_h] (query i at
     absolute position ctx_len + i) over positions 0 .. ctx_len + i of the
-    stored cache of one batch element.  out [len(rows), len(heads), d_h]."""
+    stored cache of one batch element.  out [len(rows), len(heads), d_h].
+
+    rope_theta > 0: as in `decode`, every reconstructed key is rotated by
+    `rope` at its own position and query i at position ctx_len + i."""
     c = q.shape[0]
     total = ctx_len + c
     q = np.asarray(q, np.float64)
@@ -175,7 +178,11 @@ def causal_attention(cache, ctx_len, q, bk, bv, sm_scale, n_q_heads, rotate,
         g = h // group
         k = zkl[:, g, :] @ bk_e[g].T
         v = zvl @ bv_e[g * d_h:(g + 1) * d_h].T
-        a = sm_scale * (q[rows, h] @ k.T)                   # [rows, total]
+        qh = q[rows, h]
+        if rope_theta:
+            k = rope(k, pos, rope_theta)
+            qh = rope(qh, ctx_len + rows, rope_theta)
+        a = sm_scale * (qh @ k.T)                           # [rows, total]
         a = np.where(pos[None, :] <= (ctx_len + rows)[:, None], a, -np.inf)
         out[:, hi] = softmax(a) @ v
     return out

@@ -74,7 +74,7 @@ def decode_paged(pool, table, seq_lens, q, bk, bv, sm_scale, n_q_heads, rotate,
 
 
 def prefill_paged(pool, table, ctx_len, z_key, z_value, q, bk, bv, sm_scale,
-                  n_q_heads, rotate, rows=None, heads=None):
+                  n_q_heads, rotate, rows=None, heads=None, rope_theta=0.0):
     """Chunked causal prefill of every sequence b of a paged pool: the
     chunk's latents z_key [B, C, Hkv, r_k], z_value [B, C, R_v] are appended
     at [ctx_len, ctx_len + C) of sequence b's pages (technical review of
@@ -90,6 +90,7 @@ def prefill_paged(pool, table, ctx_len, z_key, z_value, q, bk, bv, sm_scale,
         c = gather(pool, table, b, n_tiles)
         c.append(z_key[b:b + 1], z_value[b:b + 1], ctx_len, n)
         outs.append(attention.causal_attention(c, ctx_len, q[b], bk, bv, sm_scale,
-                                               n_q_heads, rotate, rows, heads))
+                                               n_q_heads, rotate, rows, heads,
+                                               rope_theta=rope_theta))
         scatter(pool, table, b, c)
     return np.stack(outs)

@@ -13,7 +13,11 @@ pos * theta^(-2i/d_h)).  Pinned by:
 * scores depend on positions only through j - t (shift invariance);
 * decode with RoPE equals a scalar-loop implementation (math.cos/sin per
   pair) on tiny shapes, with GQA;
-* rope_theta = 0 is the unrotated oracle.
+* rope_theta = 0 is the unrotated oracle;
+* chunked causal prefill with RoPE: a scalar-loop implementation on a tiny
+  shape (query i at position ctx + i sees positions 0 .. ctx + i), and each
+  prefill row equals the RoPE decode of the same query over the prefix it
+  sees.
 """
 
 import math
@@ -112,3 +116,54 @@ def test_rope_theta_zero_is_the_unrotated_oracle():
     assert np.array_equal(a, b)
     r = oa.decode(c, 30, q, bk, bv, 0.5, 2, rotate=False, rope_theta=10000.0)
     assert np.abs(r - a).max() > 1e-3      # and RoPE does change the result
+
+
+@pytest.mark.parametrize("hq,hkv,ctx,c", [(2, 2, 5, 4), (4, 2, 0, 6), (2, 1, 9, 3)])
+def test_causal_prefill_with_rope_brute_force(hq, hkv, ctx, c):
+    rng = np.random.default_rng(ctx * 7 + c)
+    d, rk, rv, theta, scale = 6, 3, 5, 50.0, 0.6
+    t = ctx + c
+    cache = oc.Cache(1, hkv, rk, rv, 64, "f32")
+    zk = rng.standard_normal((1, t, hkv, rk)).astype(np.float32)
+    zv = rng.standard_normal((1, t, rv)).astype(np.float32)
+    cache.append(zk, zv, 0, t)
+    bk = rng.standard_normal((hkv, d, rk))
+    bv = rng.standard_normal((hkv * d, rv))
+    q = rng.standard_normal((c, hq, d))
+    out = oa.causal_attention(cache, ctx, q, bk, bv, scale, hq, False, rope_theta=theta)
+    g = hq // hkv
+    for i in range(c):
+        for h in range(hq):
+            kv = h // g
+            qr = _rot_scalar(list(q[i, h]), ctx + i, theta)
+            sc = []
+            for j in range(ctx + i + 1):
+                k = [sum(float(zk[0, j, kv, r]) * bk[kv, e, r] for r in range(rk))
+                     for e in range(d)]
+                kr = _rot_scalar(k, j, theta)
+                sc.append(scale * sum(a * b for a, b in zip(qr, kr)))
+            m = max(sc)
+            ex = [math.exp(x - m) for x in sc]
+            for e in range(d):
+                v = sum(ex[j] * sum(float(zv[0, j, r]) * bv[kv * d + e, r] for r in range(rv))
+                        for j in range(ctx + i + 1)) / sum(ex)
+                assert abs(v - out[i, h, e]) <= 1e-12 * max(1.0, abs(v))
+
+
+def test_prefill_rows_with_rope_equal_rope_decode():
+    rng = np.random.default_rng(11)
+    hq, hkv, d, rk, rv, ctx, c, theta = 4, 2, 8, 4, 6, 37, 29, 10000.0
+    cache = oc.Cache(1, hkv, rk, rv, 128, "f32")
+    cache.append(rng.standard_normal((1, ctx + c, hkv, rk)).astype(np.float32),
+                 rng.standard_normal((1, ctx + c, rv)).astype(np.float32), 0, ctx + c)
+    bk, bv = rng.standard_normal((hkv, d, rk)), rng.standard_normal((hkv * d, rv))
+    q = rng.standard_normal((c, hq, d))
+    rows = [0, 1, 13, 28]
+    out = oa.causal_attention(cache, ctx, q, bk, bv, 0.4, hq, False, rows=rows,
+                              rope_theta=theta)
+    for ri, i in enumerate(rows):
+        dec = oa.decode(cache, ctx + i + 1, q[i][None], bk, bv, 0.4, hq, False,
+                        rope_theta=theta)
+        assert np.allclose(out[ri], dec[0], atol=1e-12)
+    plain = oa.causal_attention(cache, ctx, q, bk, bv, 0.4, hq, False, rows=rows)
+    assert np.abs(plain - out).max() > 1e-3
