@@ -22,7 +22,9 @@ number of steps in which the library records events between its kernels.
 
 --workload longchat_prefill times the chunked causal prefill instead (one
 starkv_prefill of an 8192-token chunk on 24576 cached tokens per step) and
-reports the attention kernel against the MFMA peak.
+reports the attention kernel against the MFMA peak; with --rope-theta the
+keys are reconstructed and rotated at their positions, and the scores run
+over d_h channels instead of r_k.
 
 --t-sweep runs the default decode workload at T = 8K, 16K, 32K, 64K and 128K
 (one child process each) and prints one JSON line per T plus a line with the
@@ -108,8 +110,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
     p.add_argument("--rope-theta", type=float, default=0.0,
-                   help="rotary position embedding of the keys (base theta), "
-                        "fused into the latent-key scoring")
+                   help="rotary position embedding of the keys (base theta): "
+                        "fused into the latent-key scoring (decode) or applied "
+                        "to the reconstructed keys (prefill)")
     p.add_argument("--hidden", type=int, default=0,
                    help="decode through the fused value/output factor into a "
                         "hidden size of this width (starkv_decode_hidden)")
@@ -254,7 +257,7 @@ def prefill_pairs(ctx, chunk, n_q_heads):
     return n_q_heads * (chunk * ctx + chunk * (chunk + 1) // 2)
 
 
-def cpu_baseline_prefill(w, n_rows=64, min_s=10.0, max_reps=30):
+def cpu_baseline_prefill(w, n_rows=64, min_s=10.0, max_reps=30, rope_theta=0.0):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
     causal attention of n_rows evenly spaced queries of the chunk (all heads)
     over the cache, repeated until at least min_s seconds of CPU work;
@@ -282,7 +285,7 @@ def cpu_baseline_prefill(w, n_rows=64, min_s=10.0, max_reps=30):
     while dt < min_s and reps < max_reps:
         t0 = time.perf_counter()
         out = oa.causal_attention(c, ctx, q, bk, bv, 1 / math.sqrt(w.head_dim),
-                                  w.n_q_heads, w.rotate, rows=rows)
+                                  w.n_q_heads, w.rotate, rows=rows, rope_theta=rope_theta)
         dt += time.perf_counter() - t0
         reps += 1
         assert np.isfinite(out).all()
@@ -291,18 +294,22 @@ def cpu_baseline_prefill(w, n_rows=64, min_s=10.0, max_reps=30):
             "kind": "oracle",
             "sample": f"{reps} x causal attention of {n_rows} evenly spaced queries "
                       f"x {w.n_q_heads} heads of the {chunk}-token chunk over "
-                      f"{ctx}+ cached tokens (fp64 numpy, {dt:.1f} s total)"}
+                      f"{ctx}+ cached tokens"
+                      + (f", rotary keys theta {rope_theta:g}" if rope_theta else "")
+                      + f" (fp64 numpy, {dt:.1f} s total)"}
 
 
 def run_prefill(args, w, torch, sk, synth):
     ctx, chunk = (args.seq_len or w.seq_len), w.chunk
     T = ((ctx + chunk + 63) // 64) * 64
+    rope = args.rope_theta
     cfg = sk.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
-                         w.key_rank, w.value_rank, T, w.cache, w.rotate, **qbits(w))
+                         w.key_rank, w.value_rank, T, w.cache, w.rotate, rope_theta=rope,
+                         **qbits(w))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"# workload {w.name} B={w.batch} ctx={ctx} chunk={chunk}", file=sys.stderr,
-          flush=True)
+    print(f"# workload {w.name} B={w.batch} ctx={ctx} chunk={chunk} rope_theta={rope}",
+          file=sys.stderr, flush=True)
     cache = sk.LatentCache(cfg)
     if ctx:
         fill_cache(w, cfg, cache, ctx, sk, torch)
@@ -348,7 +355,9 @@ def run_prefill(args, w, torch, sk, synth):
     ms = mean(step_ms)
     attn_ms = mean(kern[3])
     pairs = prefill_pairs(ctx, chunk, w.n_q_heads) * w.batch
-    attn_flops = pairs * 2 * (w.key_rank + w.value_rank)
+    # scores over the r_k latent channels, or over the d_h channels of the
+    # reconstructed rotary keys; then the value contraction over R_v
+    attn_flops = pairs * 2 * ((w.head_dim if rope else w.key_rank) + w.value_rank)
     gemm_flops = 2 * w.batch * chunk * w.hidden * (w.n_kv_heads * w.key_rank + w.value_rank)
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     res = {
@@ -358,7 +367,8 @@ def run_prefill(args, w, torch, sk, synth):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": f"{w.name} prefill", "batch": w.batch,
+        "config": {"workload": f"{w.name} prefill" + (" rope" if rope else ""),
+                   "batch": w.batch, "rope_theta": rope,
                    "ctx_len": ctx, "chunk": chunk, "hidden": w.hidden,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "key_rank": w.key_rank,
@@ -367,7 +377,7 @@ def run_prefill(args, w, torch, sk, synth):
         "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel",
                      "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS,
-                     "traffic": prefill_traffic_from_counters(w, ctx, chunk)},
+                     "traffic": None if rope else prefill_traffic_from_counters(w, ctx, chunk)},
         "kernels_ms": {"gemm": mean(kern[0]), "append": mean(kern[1]),
                        "qproj": mean(kern[2]), "attention": attn_ms,
                        "merge_vproj": mean(kern[4])},
@@ -380,7 +390,7 @@ def run_prefill(args, w, torch, sk, synth):
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline_prefill(w)
+        res["cpu_baseline"] = cpu_baseline_prefill(w, rope_theta=rope)
     print(json.dumps(res))
 
 

@@ -42,7 +42,8 @@ int check_config(const starkv_config* c) {
     // quantized caches pad every head to the 32-channel key tile (eq. 15's
     // padding term): ranks are checked against key_rank = 32 above
   }
-  // rotary keys: the 4/3-bit cache's decode only (rope.hip), head_dim 64 or 128
+  // rotary keys: quantized caches (decode: rope.hip, prefill: prefill.hip),
+  // head_dim 64 or 128
   if (c->rope_theta > 0.0f &&
       (!quant || (c->head_dim != 64 && c->head_dim != 128)))
     return STARKV_EUNSUPPORTED;
@@ -155,7 +156,7 @@ size_t starkv_workspace_bytes(const starkv_config* cfg, int32_t op,
     return decode_ws_layout(d, choose_splits(*cfg, n_tokens), n_tokens).total;
   }
   if (op == STARKV_OP_PREFILL) {
-    if (!prefill_supported(d) || cfg->rope_theta > 0.0f) return 0;
+    if (!prefill_supported(d)) return 0;
     return prefill_ws_layout(d, n_tokens).total;
   }
   return 0;
@@ -439,8 +440,7 @@ static int prefill_impl(const starkv_config* cfg, const starkv_cache* cache,
       !aligned16(out) || (z_debug && !aligned16(z_debug)))
     return STARKV_EINVAL;
   Dims d = make_dims(*cfg);
-  if (hidden % 64 != 0 || !prefill_supported(d) || cfg->rope_theta > 0.0f)
-    return STARKV_EUNSUPPORTED;
+  if (hidden % 64 != 0 || !prefill_supported(d)) return STARKV_EUNSUPPORTED;
   if (page_table) {
     // every sequence's positions [0, ctx_len + chunk) must have pages
     if (pages_per_seq < 1 || (int64_t)pages_per_seq * kTile < (int64_t)ctx_len + chunk ||

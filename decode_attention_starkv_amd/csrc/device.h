@@ -176,4 +176,25 @@ __device__ inline float key_score(const KeyLane& k, const uint32_t* rec) {
               fmaf((float)ml[0], al, fmaf((float)mh[1], qs_hi, (float)ml[1] * qs_lo)));
 }
 
+// Rotary frequency of pair p, theta^(-2 p / dh), in fp64.
+__device__ inline double rope_freq(int p, int dh, double log2_theta) {
+  return exp2(-2.0 * p / dh * log2_theta);
+}
+
+// sin / cos of the rotary angle pos * w, reduced modulo 2 pi in fp64.
+__device__ inline void rope_sincos(int pos, double w, float* c, float* s) {
+  const double a = (double)pos * w;
+  const double turns = a * 0.15915494309189535;     // 1 / (2 pi)
+  const float phi = (float)((turns - floor(turns)) * 6.283185307179586);
+  *c = cosf(phi);
+  *s = sinf(phi);
+}
+
+// sin / cos of the rotary angle of pair p at position pos,
+// pos * theta^(-2 p / dh)
+__device__ inline void rope_angle(int pos, int p, int dh, double log2_theta, float* c,
+                                  float* s) {
+  rope_sincos(pos, rope_freq(p, dh, log2_theta), c, s);
+}
+
 }  // namespace starkv

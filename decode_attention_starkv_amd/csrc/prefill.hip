@@ -137,20 +137,12 @@ __device__ inline void wait_vmcnt() {
 
 // ------------------------------------------------------------- key dequant --
 
-// fp16 key latents z + s * code of positions [0, n) of every sequence and KV
-// head, channels in their natural order: [B][T_max][Hkv][32] (64 bytes per
-// token and head), from a 4/3-bit or a uniform 4-bit key tile.  One thread
-// per (sequence, position, KV head).  The attention kernel reads them as
-// MFMA operands.
-__global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restrict__ key,
-                                                          const u32x2* __restrict__ kmeta,
-                                                          Dims d, int n,
-                                                          _Float16* __restrict__ kd) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)d.B * n * d.Hkv) return;
-  const int h = idx % d.Hkv;
-  const int t = (idx / d.Hkv) % n;
-  const int b = idx / ((size_t)d.Hkv * n);
+// The stored key latent z + s * code (fp32, channels in their natural
+// order, still in the rotated basis when the cache rotates) of position t of
+// KV head h of sequence b, from a 4/3-bit or a uniform 4-bit key tile.
+__device__ inline void key_latent(const uint8_t* __restrict__ key,
+                                  const u32x2* __restrict__ kmeta, const Dims& d, int b,
+                                  int t, int h, float (&v)[32]) {
   const int tile = t / kTile, u = t % kTile;
   // the tile's slot: b * NT + tile, or its page in a paged pool
   const size_t blk = tile_index(d, b, tile) * d.Hkv + h;
@@ -168,17 +160,15 @@ __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restr
   const _Float16 z_hi = __builtin_bit_cast(_Float16, (uint16_t)(m0 >> 16));
   const _Float16 s_lo = __builtin_bit_cast(_Float16, (uint16_t)(m1 & 0xFFFFu));
   const _Float16 z_lo = __builtin_bit_cast(_Float16, (uint16_t)(m1 >> 16));
-  _Float16 v[32];
 #pragma unroll
   for (int c = 0; c < 8; ++c)
-    v[c] = (_Float16)fmaf((float)s_hi, (float)((whi >> (4 * c)) & 15u), (float)z_hi);
+    v[c] = fmaf((float)s_hi, (float)((whi >> (4 * c)) & 15u), (float)z_hi);
   if (d.lob == 4) {
     // uniform 4-bit: channel 8p + c at bits 4c of plane p
     const uint32_t pl[3] = {w0, w1, w2};
 #pragma unroll
     for (int i = 0; i < 24; ++i)
-      v[8 + i] = (_Float16)fmaf((float)s_lo, (float)((pl[i / 8] >> (4 * (i % 8))) & 15u),
-                                (float)z_lo);
+      v[8 + i] = fmaf((float)s_lo, (float)((pl[i / 8] >> (4 * (i % 8))) & 15u), (float)z_lo);
   } else {
     // 3-bit channel i (= key channel 8 + i): i < 5 lo0 bits 3i, i < 10 lo1
     // bits 3(i-5), i < 15 lo0 bits 16+3(i-10), i < 20 lo1 bits 16+3(i-15),
@@ -191,14 +181,129 @@ __global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restr
       else if (i < 15) code = (w0 >> (16 + 3 * (i - 10))) & 7u;
       else if (i < 20) code = (w1 >> (16 + 3 * (i - 15))) & 7u;
       else code = (R >> (3 * (i - 20))) & 7u;
-      v[8 + i] = (_Float16)fmaf((float)s_lo, (float)code, (float)z_lo);
+      v[8 + i] = fmaf((float)s_lo, (float)code, (float)z_lo);
     }
   }
+}
+
+// fp16 key latents of positions [0, n) of every sequence and KV head,
+// channels in their natural order: [B][T_max][Hkv][32] (64 bytes per token
+// and head).  One thread per (sequence, position, KV head).  The attention
+// kernel reads them as MFMA operands.
+__global__ __launch_bounds__(256) void key_dequant_kernel(const uint8_t* __restrict__ key,
+                                                          const u32x2* __restrict__ kmeta,
+                                                          Dims d, int n,
+                                                          _Float16* __restrict__ kd) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)d.B * n * d.Hkv) return;
+  const int h = idx % d.Hkv;
+  const int t = (idx / d.Hkv) % n;
+  const int b = idx / ((size_t)d.Hkv * n);
+  float v[32];
+  key_latent(key, kmeta, d, b, t, h, v);
   h8* dst = reinterpret_cast<h8*>(kd + (((size_t)b * d.Tmax + t) * d.Hkv + h) * 32);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    dst[k] = h8{v[8 * k], v[8 * k + 1], v[8 * k + 2], v[8 * k + 3],
-                v[8 * k + 4], v[8 * k + 5], v[8 * k + 6], v[8 * k + 7]};
+    dst[k] = h8{(_Float16)v[8 * k], (_Float16)v[8 * k + 1], (_Float16)v[8 * k + 2],
+                (_Float16)v[8 * k + 3], (_Float16)v[8 * k + 4], (_Float16)v[8 * k + 5],
+                (_Float16)v[8 * k + 6], (_Float16)v[8 * k + 7]};
+}
+
+// ------------------------------------------------------------ rotary keys --
+
+// Rotary keys of positions [0, n) of every sequence and KV head (section 5.3
+// of the review, Algorithm 2 steps 4b-4c: the stored keys stay pre-RoPE
+// latents, reconstructed and rotated at run time): the stored latent, its
+// block rotation undone (eq. 13; the 8-channel Hadamard blocks are
+// symmetric), times the key factor (eq. 2: k = B_key[g] z, columns past the
+// head's key rank taken as zero), then each pair (i, i + d_h/2) turned by
+// the angle of its position.  fp16 [B][T_max][Hkv][d_h], d_h = 64 or 128.
+// One block per (64 positions, KV head, sequence): the 64 latents go to LDS
+// first; thread (pair i, token group) then keeps rows i and i + d_h/2 of
+// B_key[g] in registers and walks its tokens, reading each latent as an LDS
+// broadcast.
+__global__ __launch_bounds__(256) void rope_key_kernel(const uint8_t* __restrict__ key,
+                                                       const u32x2* __restrict__ kmeta,
+                                                       const uint16_t* __restrict__ bk,
+                                                       Dims d, int n, double log2_theta,
+                                                       _Float16* __restrict__ kd) {
+  __shared__ float zl[kTile][33];
+  const int g = blockIdx.y, b = blockIdx.z, t0 = blockIdx.x * kTile;
+  const int tid = threadIdx.x;
+  if (tid < kTile) {
+    float z[32];
+    const int t = t0 + tid;
+    if (t < n) {
+      key_latent(key, kmeta, d, b, t, g, z);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) z[c] = 0.0f;
+    }
+    if (d.rotate) {
+      // z <- H8 z per block of 8 channels (butterflies, then 1/sqrt(8))
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (!(e & st)) {
+              const float x = z[8 * blk + e], y = z[8 * blk + e + st];
+              z[8 * blk + e] = x + y;
+              z[8 * blk + e + st] = x - y;
+            }
+#pragma unroll
+      for (int c = 0; c < 32; ++c) z[c] *= inv_sqrt_pow2(8);
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) zl[tid][c] = z[c];
+  }
+  __syncthreads();
+  const int half = d.dh / 2;                   // pairs: 32 or 64
+  const int i = tid % half, grp = tid / half, ngrp = 256 / half;
+  const int rank = d.krank[g];
+  const double w = rope_freq(i, d.dh, log2_theta);
+  float b1[32], b2[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    b1[c] = c < rank ? bf16v(bk[((size_t)g * d.dh + i) * 32 + c]) : 0.0f;
+    b2[c] = c < rank ? bf16v(bk[((size_t)g * d.dh + i + half) * 32 + c]) : 0.0f;
+  }
+  for (int u = grp; u < kTile; u += ngrp) {
+    const int t = t0 + u;
+    if (t >= n) break;
+    float k1 = 0.0f, k2 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      k1 = fmaf(b1[c], zl[u][c], k1);
+      k2 = fmaf(b2[c], zl[u][c], k2);
+    }
+    float cs, sn;
+    rope_sincos(t, w, &cs, &sn);
+    _Float16* dst = kd + (((size_t)b * d.Tmax + t) * d.Hkv + g) * d.dh;
+    dst[i] = (_Float16)(k1 * cs - k2 * sn);
+    dst[i + half] = (_Float16)(k1 * sn + k2 * cs);
+  }
+}
+
+// Rotary queries of the chunk: query i of sequence b (position ctx + i)
+// turned pair by pair like the keys and scaled by sm_scale log2(e), fp16
+// [rows][Hq][d_h].  One thread per (row, head, pair).
+__global__ __launch_bounds__(256) void rope_query_kernel(const uint16_t* __restrict__ q,
+                                                         Dims d, int rows, int chunk, int ctx,
+                                                         double log2_theta, float qscale,
+                                                         _Float16* __restrict__ qn) {
+  const int half = d.dh / 2;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)rows * d.Hq * half) return;
+  const int i = idx % half;
+  const size_t rh = idx / half;                  // row * Hq + head
+  const int pos = ctx + (int)((rh / d.Hq) % chunk);
+  const float x1 = bf16v(q[rh * d.dh + i]), x2 = bf16v(q[rh * d.dh + i + half]);
+  float cs, sn;
+  rope_angle(pos, i, d.dh, log2_theta, &cs, &sn);
+  qn[rh * d.dh + i] = (_Float16)((x1 * cs - x2 * sn) * qscale);
+  qn[rh * d.dh + i + half] = (_Float16)((x1 * sn + x2 * cs) * qscale);
 }
 
 // ------------------------------------------------------------------ qproj --
@@ -395,9 +500,13 @@ hipError_t launch_prefill_vproj(const Dims& d, int rows, const float* po, const 
 
 // ------------------------------------------------------------------- attn --
 
-constexpr int kPQ = 16;       // queries per workgroup
-constexpr int kPH = 8;        // query heads per workgroup
-constexpr int kRows = kPQ * kPH;   // rows of the stacked P tile
+// A workgroup's stacked P tile has 128 rows: kPQ queries x kPH query heads.
+// Both depend on the width DK of the keys it scores against (32 latent
+// channels, or d_h channels of rotary keys), so that one tile's keys of the
+// workgroup's KV heads stay within kKeySlot.
+constexpr int kRows = 128;
+constexpr int kPHof(int dk) { return dk == 32 ? 8 : 256 / dk; }   // query heads
+constexpr int kPQof(int dk) { return kRows / kPHof(dk); }          // queries
 constexpr int kPS = 72;       // P row stride (halves)
 constexpr int kMaxRv = 1024;
 constexpr int kMaxCols = 512;      // value columns per workgroup (at most)
@@ -407,8 +516,9 @@ constexpr int kMetaHalf = (kMaxCols / 32) * kTile * 2;
 // groups of 1024 B (a uniform 4-bit cache; a 4/3-bit block of 512 columns
 // holds at most eight 4-bit and eight 3-bit groups, 14 KB)
 constexpr int kCodeSlot = 16 * 1024;
-// bytes of one tile's fp16 key latents of the workgroup's KV heads
-constexpr int kKeySlot = kPH * kTile * 64;
+// bytes of one tile's fp16 keys of the workgroup's KV heads (8 KV heads of
+// 32 latent channels, or 256 / d_h heads of d_h rotary-key channels)
+constexpr int kKeySlot = 32 * 1024;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -418,8 +528,8 @@ struct AttnArgs {
   int ctx, chunk, n_qb, n_qb_pad, n_hg, n_cb;
   const uint8_t* value;
   const uint16_t* vmeta;
-  const _Float16* qn;     // [B*C][Hq][32] query latents, natural channel order
-  const _Float16* kd;     // [B][T_max][Hkv][32] fp16 key latents
+  const _Float16* qn;     // [B*C][Hq][DK] query latents, natural channel order
+  const _Float16* kd;     // [B][T_max][Hkv][DK] fp16 keys
   float* part_o;          // B*C x Hq rows of R_v, element order of po_index
   float* part_ml;         // [B*C][Hq][2]
 };
@@ -469,13 +579,14 @@ __device__ inline h8 value_frag(const u32x4& w, int r, const u32x4& S, const u32
   return __builtin_bit_cast(h8, u32x4{o[0], o[1], o[2], o[3]});
 }
 
-// Workgroup = (16 consecutive queries, 8 query heads, R_v / n_cb value
-// columns, sequence b), 8 waves.  Rows of the stacked P tile: row = query * 8
-// + head (128 rows = four MFMA row tiles).  Wave w
-//   - scores query head w for the 16 queries on MFMA 16x16x32 with the keys
-//     as the A operand (a lane then holds four consecutive tokens of one
-//     query) and a lazy online softmax, writing fp16 probabilities to a P
-//     slot;
+// Workgroup = (PQ consecutive queries, PH query heads, R_v / n_cb value
+// columns, sequence b), 8 waves; PQ x PH = 128 (16 x 8 for DK = 32 latent
+// keys, 64 x 2 for rotary keys of d_h = 128).  Rows of the stacked P tile:
+// row = query * PH + head (128 rows = four MFMA row tiles).  Wave w
+//   - scores query head w % PH for queries 16 (w / PH) .. + 15 on MFMA
+//     16x16x32 (DK / 32 steps) with the keys as the A operand (a lane then
+//     holds four consecutive tokens of one query) and a lazy online softmax,
+//     writing fp16 probabilities to a P slot;
 //   - owns value groups 2w and 2w + 1 of the workgroup's columns for all
 //     128 rows: it dequantizes their codes with their scales and zeros
 //     straight into MFMA B operands and contracts them with P on MFMA
@@ -488,18 +599,23 @@ __device__ inline h8 value_frag(const u32x4& w, int r, const u32x4& S, const u32
 // Causal mask: query i (absolute position ctx + i) sees cached positions
 // 0 .. ctx + i.  Value tokens past the workgroup's last position are zeroed
 // so that unwritten cache bytes never reach the MFMA operands.
-template <int G>
+template <int G, int DK>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
+  constexpr int PH = kPHof(DK), PQ = kPQof(DK);
+  constexpr int CPT = DK / 8;             // 16-byte chunks per key row
+  constexpr int TPP = 1024 / (DK * 2);    // key rows per 1 KB staging piece
+  constexpr int KS = DK / 32;             // K steps of a score MFMA
+  // swizzle of a key row's chunks: the 16 rows a score operand read takes
+  // fall in 16 different groups of 4 banks
+  auto swz = [](int u) { return (u / (16 / CPT)) & (CPT - 1); };
   const Dims& d = a.d;
   __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kRows * kPS];
   __shared__ __attribute__((aligned(16))) uint8_t meta_l[2][2 * kMetaHalf];
   __shared__ __attribute__((aligned(16))) uint8_t code_l[2][kCodeSlot];
-  // key latents [KV head][token][4 chunks of 16 B], chunk c of token u at
-  // position c ^ ((u >> 2) & 3) so that a score operand read (16 tokens,
-  // one chunk) touches every bank once
+  // keys [KV head][token][CPT chunks of 16 B], chunk c of token u at
+  // position c ^ swz(u) so that a score operand read (16 tokens, one chunk)
+  // touches every bank once
   __shared__ __attribute__((aligned(16))) uint8_t key_l[2][kKeySlot];
-  // the queries' latent vectors in natural channel order (fp16)
-  __shared__ __attribute__((aligned(16))) _Float16 qnat[kRows * 32];
   __shared__ __attribute__((aligned(16))) float alpha_l[2][kRows];
   __shared__ int flag_l[2];
 
@@ -514,8 +630,8 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int qb = a.n_qb_pad - 1 - ((k / per_qb) * 8 + xcd);
   if (qb >= a.n_qb) return;   // padding workgroup; uniform, before any barrier
   const int b = blockIdx.y;
-  const int q0 = qb * kPQ;
-  const int nq = min(kPQ, a.chunk - q0);
+  const int q0 = qb * PQ;
+  const int nq = min(PQ, a.chunk - q0);
   const int pfirst = a.ctx + q0;            // first query's position
   const int pmax = pfirst + nq - 1;         // last position any row may see
   const int tile_last = pmax / kTile;
@@ -526,25 +642,24 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const int m = lane & 31, j = lane >> 5;   // 32x32 operand coordinates
   const int c16 = lane & 15, g16 = lane >> 4;  // 16x16 operand coordinates
 
-  // the 16 queries' latent vectors of the 8 heads: one 16-byte piece each
-  {
-    const int qh = tid >> 2, piece = tid & 3;    // (query, head), 8 channels
-    const int qi = qh / kPH;
-    h8 v = h8{};
-    if (qi < nq)
-      v = *reinterpret_cast<const h8*>(
-          a.qn + (((size_t)b * a.chunk + q0 + qi) * d.Hq + hg * kPH + qh % kPH) * 32 + piece * 8);
-    *reinterpret_cast<h8*>(&qnat[qh * 32 + piece * 8]) = v;
-  }
   if (tid < 2) flag_l[tid] = -1;
   __syncthreads();
 
   // ------------------------------------------------------------ score setup
-  const int hl = wave;                          // query head within the group
-  const int h = hg * kPH + hl;
+  const int hl = wave % PH;                     // query head within the group
+  const int qs = wave / PH;                     // the wave's 16 queries
+  const int h = hg * PH + hl;
   const int g = h / G;
-  // B operand of the score MFMA: query c16, channels 8 g16 .. 8 g16 + 7
-  const h8 bq = *reinterpret_cast<const h8*>(&qnat[(c16 * kPH + hl) * 32 + g16 * 8]);
+  const int qi = 16 * qs + c16;                 // the lane's query
+  const int R = qi * PH + hl;                   // its row of the P tile
+  // B operands of the score MFMA: query qi, channels 32 ks + 8 g16 .. + 7
+  h8 bq[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    bq[ks] = qi < nq ? *reinterpret_cast<const h8*>(
+                           a.qn + (((size_t)b * a.chunk + q0 + qi) * d.Hq + h) * DK + 32 * ks +
+                           8 * g16)
+                     : h8{};
   // lazy softmax state of query c16 (the same in its four lanes).  The
   // running max starts finite so that exp2(x - m) needs no guard: a row's
   // first real score always moves it (alpha = exp2(-1e30 - m) = 0), and rows
@@ -556,27 +671,47 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
     return &p_l[slot][R * kPS + (((u >> 3) ^ (R >> 5)) << 3) + (u & 7)];
   };
   // A operands of the score MFMA: tokens bl * 16 + c16 of a tile, channels
-  // 8 g16 .. 8 g16 + 7 of KV head g (local head g - g0)
-  const int g0 = hg * kPH / G;
-  const int key_lane = (g - g0) * (kTile * 64) + c16 * 64 + ((g16 ^ (c16 >> 2)) << 4);
-  auto load_keys = [&](int slot, h8 (&kk)[4]) {
+  // 32 ks + 8 g16 .. + 7 of KV head g (local head g - g0); swz(bl * 16 + c16)
+  // = swz(c16)
+  const int g0 = hg * PH / G;
+  const int key_lane = (g - g0) * (kTile * DK * 2) + c16 * (DK * 2);
+  auto key_at = [&](int slot, int bl, int ks) {
+    return *reinterpret_cast<const h8*>(
+        &key_l[slot][key_lane + bl * 16 * (DK * 2) + (((4 * ks + g16) ^ swz(c16)) << 4)]);
+  };
+  // (latent keys: the next tile's operands are read ahead of its scores;
+  // rotary keys: each 16-token block's operands right before its MFMAs)
+  constexpr int KK = DK == 32 ? 4 : 1;
+  auto load_keys = [&](int slot, h8 (&kk)[KK]) {
+    if constexpr (DK == 32) {
 #pragma unroll
-    for (int bl = 0; bl < 4; ++bl)
-      kk[bl] = *reinterpret_cast<const h8*>(&key_l[slot][key_lane + bl * 16 * 64]);
+      for (int bl = 0; bl < 4; ++bl) kk[bl] = key_at(slot, bl, 0);
+    }
   };
 
   // scores of tile `tile` (index it in the loop) into P slot `slot`
-  auto score = [&](int tile, int it, int slot, const h8 (&kk)[4]) {
-    float x[4][4];   // [16-token block][token 4 g16 + v], query c16
+  auto score = [&](int tile, int it, int slot, const h8 (&kk)[KK]) {
+    float x[4][4];   // [16-token block][token 4 g16 + v], query qi
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl) {
-      const f32x4v sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kk[bl], bq, f32x4v{}, 0, 0, 0);
+      f32x4v sc;
+      if constexpr (DK == 32) {
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kk[bl], bq[0], f32x4v{}, 0, 0, 0);
+      } else {
+        h8 kb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[ks] = key_at(slot, bl, ks);
+        sc = f32x4v{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[ks], bq[ks], sc, 0, 0, 0);
+      }
 #pragma unroll
       for (int v = 0; v < 4; ++v) x[bl][v] = sc[v];
     }
     if (tile * kTile + kTile - 1 > pfirst) {   // uniform: some token is hidden
-      // last token of the tile query c16 sees (none for padding queries)
-      const int lim = c16 < nq ? pfirst + c16 - tile * kTile : -1;
+      // last token of the tile query qi sees (none for padding queries)
+      const int lim = qi < nq ? pfirst + qi - tile * kTile : -1;
 #pragma unroll
       for (int bl = 0; bl < 4; ++bl)
 #pragma unroll
@@ -599,7 +734,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
         flag_l[slot] = it;
       }
     }
-    if (lane < kPQ) alpha_l[slot][c16 * kPH + hl] = alpha;
+    if (lane < 16) alpha_l[slot][R] = alpha;
     float ls = 0.0f;
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl) {
@@ -609,7 +744,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
         p[v] = __builtin_amdgcn_exp2f(x[bl][v] - m_ref);
         ls += p[v];
       }
-      *reinterpret_cast<h4*>(p_at(slot, c16 * kPH + hl, bl * 16 + 4 * g16)) =
+      *reinterpret_cast<h4*>(p_at(slot, R, bl * 16 + 4 * g16)) =
           h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     }
     l_lane += ls;
@@ -623,16 +758,18 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   const size_t mtile = (size_t)2 * NG * kTile;     // fp16 elements
   const int meta_bytes = ngrp * kTile * 2;
   // Direct-to-LDS staging, in 1 KB pieces spread over the waves: the fp16
-  // keys of tile `kt` into key slot kt & 1 (4 pieces per KV head) and the
+  // keys of tile `kt` into key slot kt & 1 (CPT pieces per KV head) and the
   // value codes, scales and zeros of tile `ct` into slot ct & 1.  A key
-  // piece is 16 tokens of one head; lane l moves chunk
-  // (l & 3) ^ ((l >> 4) & 3) of token l >> 2 (the swizzle of key_l).
+  // piece is TPP tokens of one head; lane l moves chunk
+  // (l % CPT) ^ swz(u) of token u = TPP * piece + l / CPT (the swizzle of
+  // key_l).
   auto goff = [&](int gi) { return gi < NH ? gi * 1024 : NH * 1024 + (gi - NH) * 768; };
   const int code_lo = goff(g_first), code_bytes = goff(g_first + ngrp) - code_lo;
-  const int nkp = 4 * (kPH / G);               // key pieces
+  constexpr int KVW = PH / G > 0 ? PH / G : 1;   // KV heads of the workgroup
+  const int nkp = CPT * KVW;                   // key pieces
   const int ncp = (code_bytes + 1023) / 1024;  // code pieces
   const int nmp = (meta_bytes + 1023) / 1024;  // pieces per scale / zero plane
-  const int key_src_lane = (lane >> 2) * d.Hkv * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  const int key_tl = lane / CPT, key_pos = lane % CPT;
   auto dma = [&](const uint8_t* src, uint8_t* dst) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   };
@@ -643,13 +780,16 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   auto first_piece = [&](int p0) { return p0 + ((wave - p0) & 7); };
   auto stage = [&](int kt, int ct) {
     if (kt <= tile_last) {
-      // piece p: KV head g0 + p / 4, tokens 16 (p % 4) .. + 15 of tile kt
+      // piece p: KV head g0 + p / CPT, tokens TPP (p % CPT) .. + TPP - 1 of
+      // tile kt
       const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kd) +
-          (((size_t)b * d.Tmax + (size_t)kt * kTile) * d.Hkv + g0) * 64 + key_src_lane;
+          (((size_t)b * d.Tmax + (size_t)kt * kTile) * d.Hkv + g0) * (DK * 2);
       uint8_t* kdst = &key_l[kt & 1][0];
       for (int p = wave; p < nkp; p += 8) {
-        const int kh = p >> 2, blk = p & 3;
-        dma(kbase + ((size_t)blk * 16 * d.Hkv + kh) * 64, kdst + kh * (kTile * 64) + blk * 1024);
+        const int kh = p / CPT, blk = p % CPT;
+        const int u = blk * TPP + key_tl;
+        dma(kbase + ((size_t)u * d.Hkv + kh) * (DK * 2) + ((key_pos ^ swz(u)) << 4),
+            kdst + kh * (kTile * DK * 2) + blk * 1024);
       }
     }
     if (ct <= tile_last) {
@@ -748,7 +888,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
     wait_vmcnt<0>();
     __syncthreads();        // keys of tiles 0, 1 and values of tile 0 in LDS
     {
-      h8 kk[4];
+      h8 kk[KK];
       load_keys(0, kk);
       score(0, 0, 0, kk);
     }
@@ -763,7 +903,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
       if (active) contract(cur, it, tile, lastc);
       if constexpr (!kLast) {
         __builtin_amdgcn_sched_barrier(0);
-        h8 kk[4];
+        h8 kk[KK];
         load_keys(nxt, kk);
         score(tile + 1, it + 1, nxt, kk);
         wait_vmcnt<0>();    // this wave's staging landed
@@ -784,33 +924,47 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int rr = rt * 32 + acc_row(v, lane);
-          const int qi = rr >> 3, hh = rr & 7;
-          if (qi < nq)
-            a.part_o[po_index(d, (size_t)d.B * a.chunk, hg * kPH + hh,
-                              (size_t)b * a.chunk + q0 + qi,
+          const int rq = rr / PH, hh = rr % PH;
+          if (rq < nq)
+            a.part_o[po_index(d, (size_t)d.B * a.chunk, hg * PH + hh,
+                              (size_t)b * a.chunk + q0 + rq,
                               col0 + (2 * wave + gp) * 32 + m)] = acc[rt][gp][v];
         }
   }
   if (cb == 0) {
     float l = l_lane + __shfl_xor(l_lane, 16);
     l += __shfl_xor(l, 32);
-    if (lane < kPQ && c16 < nq) {
-      const size_t o = (((size_t)b * a.chunk + q0 + c16) * d.Hq + h) * 2;
+    if (lane < 16 && qi < nq) {
+      const size_t o = (((size_t)b * a.chunk + q0 + qi) * d.Hq + h) * 2;
       a.part_ml[o] = m_ref;
       a.part_ml[o + 1] = l;
     }
   }
 }
 
-hipError_t launch_attn(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t s) {
+// Width of the keys the attention kernel scores against: the 32 latent
+// channels, or the d_h channels of reconstructed rotary keys.
+int attn_key_width(const Dims& d) { return d.rope_theta > 0.0f ? d.dh : 32; }
+
+template <int DK>
+hipError_t launch_attn_dk(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t s) {
   switch (d.G) {
-    case 1: prefill_attn_kernel<1><<<grid, 512, 0, s>>>(aa); break;
-    case 2: prefill_attn_kernel<2><<<grid, 512, 0, s>>>(aa); break;
-    case 4: prefill_attn_kernel<4><<<grid, 512, 0, s>>>(aa); break;
-    case 8: prefill_attn_kernel<8><<<grid, 512, 0, s>>>(aa); break;
+    case 1: prefill_attn_kernel<1, DK><<<grid, 512, 0, s>>>(aa); break;
+    case 2: prefill_attn_kernel<2, DK><<<grid, 512, 0, s>>>(aa); break;
+    case 4: prefill_attn_kernel<4, DK><<<grid, 512, 0, s>>>(aa); break;
+    case 8: prefill_attn_kernel<8, DK><<<grid, 512, 0, s>>>(aa); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t s) {
+  switch (attn_key_width(d)) {
+    case 32: return launch_attn_dk<32>(d, grid, aa, s);
+    case 64: return launch_attn_dk<64>(d, grid, aa, s);
+    case 128: return launch_attn_dk<128>(d, grid, aa, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 }  // namespace
@@ -825,10 +979,11 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
   off += align256p(M * d.Hkv * d.rk * 4);
   w.zv = off;
   off += align256p(M * d.rv * 4);
-  w.qt = off;   // fp16 query latents [rows][Hq][32]
-  off += align256p(M * d.Hq * 32 * 2);
-  w.kd = off;   // fp16 key latents of every cached position, [B][T_max][Hkv][32]
-  off += align256p((size_t)d.B * d.Tmax * d.Hkv * 32 * 2);
+  const int dk = attn_key_width(d);
+  w.qt = off;   // fp16 query latents (or rotary queries) [rows][Hq][dk]
+  off += align256p(M * d.Hq * dk * 2);
+  w.kd = off;   // fp16 key latents (or rotary keys) of every cached position, [B][T_max][Hkv][dk]
+  off += align256p((size_t)d.B * d.Tmax * d.Hkv * dk * 2);
   w.part_o = off;
   off += align256p(M * d.Hq * d.rv * 4);
   w.part_ml = off;
@@ -840,7 +995,9 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
 }
 
 bool prefill_supported(const Dims& d) {
-  return d.dtype == STARKV_CACHE_Q43 && d.rk == 32 && d.Hq % kPH == 0 &&
+  // rotary keys: reconstructed at d_h = 64 or 128 channels
+  if (d.rope_theta > 0.0f && d.dh != 64 && d.dh != 128) return false;
+  return d.dtype == STARKV_CACHE_Q43 && d.rk == 32 && d.Hq % kPHof(attn_key_width(d)) == 0 &&
          (d.G == 1 || d.G == 2 || d.G == 4 || d.G == 8) && d.rv % 256 == 0 &&
          d.rv <= kMaxRv && d.dh % 64 == 0 && d.dh <= 256;
 }
@@ -884,24 +1041,38 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   if (e != hipSuccess) return e;
   mark(2);
 
-  // fp16 key latents of every position the chunk's queries can see
   _Float16* kd = reinterpret_cast<_Float16*>(ws + lay.kd);
-  {
-    const int n = ctx_len + chunk;
+  _Float16* qn = reinterpret_cast<_Float16*>(ws + lay.qt);
+  const int n = ctx_len + chunk;
+  if (d.rope_theta > 0.0f) {
+    // rotary keys of every position the chunk's queries can see, and the
+    // chunk's rotary queries
+    const double log2_theta = log2((double)d.rope_theta);
+    rope_key_kernel<<<dim3((n + kTile - 1) / kTile, d.Hkv, d.B), 256, 0, s>>>(
+        static_cast<const uint8_t*>(cache.key), static_cast<const u32x2*>(cache.key_meta),
+        static_cast<const uint16_t*>(bk), d, n, log2_theta, kd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t items = (size_t)M * d.Hq * (d.dh / 2);
+    rope_query_kernel<<<(unsigned)((items + 255) / 256), 256, 0, s>>>(
+        static_cast<const uint16_t*>(q), d, M, chunk, ctx_len, log2_theta, sm_scale * kLog2e,
+        qn);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    // fp16 key latents of every position the chunk's queries can see
     const size_t items = (size_t)d.B * n * d.Hkv;
     key_dequant_kernel<<<(unsigned)((items + 255) / 256), 256, 0, s>>>(
         static_cast<const uint8_t*>(cache.key), static_cast<const u32x2*>(cache.key_meta), d, n, kd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // query latents of every (query, head) of the chunk
+    prefill_qproj_kernel<<<dim3((M + 127) / 128, d.Hq), 256, 0, s>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(bk), d, M,
+        sm_scale * kLog2e, qn);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-
-  // query latents of every (query, head) of the chunk
-  _Float16* qn = reinterpret_cast<_Float16*>(ws + lay.qt);
-  prefill_qproj_kernel<<<dim3((M + 127) / 128, d.Hq), 256, 0, s>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(bk), d, M,
-      sm_scale * kLog2e, qn);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   mark(3);
 
   // causal latent attention
@@ -909,9 +1080,10 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   aa.d = d;
   aa.ctx = ctx_len;
   aa.chunk = chunk;
-  aa.n_qb = (chunk + kPQ - 1) / kPQ;
+  const int pq = kPQof(attn_key_width(d)), ph = kPHof(attn_key_width(d));
+  aa.n_qb = (chunk + pq - 1) / pq;
   aa.n_qb_pad = (aa.n_qb + 7) / 8 * 8;
-  aa.n_hg = d.Hq / kPH;
+  aa.n_hg = d.Hq / ph;
   aa.n_cb = d.rv > kMaxCols ? 2 : 1;
   aa.value = static_cast<const uint8_t*>(cache.value);
   aa.vmeta = static_cast<const uint16_t*>(cache.value_meta);

@@ -35,17 +35,6 @@ namespace {
 constexpr int kRopeHeads = 8;     // query heads per score workgroup (4 waves x 2)
 constexpr int kQtStride = 36;     // floats per token row of the transpose buffer
 
-// sin / cos of pos * theta^(-2 p / dh), the angle reduced modulo 2 pi in fp64
-__device__ inline void rope_angle(int pos, int p, int dh, double log2_theta, float* c,
-                                  float* s) {
-  const double w = exp2(-2.0 * p / dh * log2_theta);
-  const double a = (double)pos * w;
-  const double turns = a * 0.15915494309189535;     // 1 / (2 pi)
-  const float phi = (float)((turns - floor(turns)) * 6.283185307179586);
-  *c = cosf(phi);
-  *s = sinf(phi);
-}
-
 // Trig[tile][s][j][lane][e] = T[i = 16 s + 8 (lane / 32) + e][token 64 tile +
 // 32 j + lane % 32], T[i][pos] = cos(pos w_i) (i < dh/2), sin(pos w_{i-dh/2}).
 __global__ __launch_bounds__(256) void rope_trig_kernel(int dh, int n_tiles,

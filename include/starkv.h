@@ -127,7 +127,8 @@ typedef struct starkv_config {
   float rope_theta;    /* 0: no rotary position embedding.  > 0: RoPE base
                           (section 5.3 and Algorithm 2 step 4c: keys stay
                           pre-RoPE latents, reconstructed and rotated inside
-                          the scoring); see starkv_decode */
+                          the scoring); see starkv_decode and
+                          starkv_prefill */
   const int32_t* key_ranks; /* (host) NULL: every KV head has key_rank
                           channels.  Otherwise n_kv_heads per-head ranks
                           (section 4 / Fig. 2: learned per-head ranks; eq. 15
@@ -428,12 +429,20 @@ STARKV_API size_t starkv_noalloc_scratch_bytes(void);
  *   z_debug fp32 [B][C][Hkv*r_k + R_v] or NULL: the projected latents
  * Projects Z = x A, appends it at [ctx_len, ctx_len + C) exactly as
  * starkv_append would, then query i (absolute position ctx_len + i) attends
- * to cached positions 0 .. ctx_len + i.  Workspace:
- * starkv_workspace_bytes(cfg, PREFILL, C).
+ * to cached positions 0 .. ctx_len + i.  With rope_theta > 0 (review
+ * section 5.3, Algorithm 2 steps 4b-4c) the keys of every visible position
+ * are reconstructed from the stored latents (k = B_key[g] z) and rotated at
+ * their positions, query i is rotated at ctx_len + i, and the scores run
+ * over d_h channels; the values are not rotated.  Workspace:
+ * starkv_workspace_bytes(cfg, PREFILL, C) (with rotary keys it holds fp16
+ * keys of d_h channels for every position, B * max_tokens * Hkv * d_h * 2
+ * bytes, instead of the 32-channel latents).
  * Errors: EINVAL, ECAPACITY (ctx_len + C > max_tokens), EWORKSPACE,
- * ELAUNCH; EUNSUPPORTED unless the cache is Q43 with r_k = 32, Hq a multiple
- * of 8, Hq / Hkv in {1, 2, 4, 8}, R_v a multiple of 256 up to 1024, d_h a
- * multiple of 64 up to 256 and D a multiple of 64. */
+ * ELAUNCH; EUNSUPPORTED unless the cache is Q43 with r_k = 32, Hq / Hkv in
+ * {1, 2, 4, 8}, R_v a multiple of 256 up to 1024, D a multiple of 64, and
+ * either (no rotary keys) Hq a multiple of 8 and d_h a multiple of 64 up to
+ * 256, or (rotary keys) d_h = 128 with Hq even or d_h = 64 with Hq a
+ * multiple of 4. */
 STARKV_API int starkv_prefill(const starkv_config* cfg, const starkv_cache* cache,
                    int32_t ctx_len, int32_t chunk, const void* x,
                    int32_t hidden, const void* A_key, const void* A_value,

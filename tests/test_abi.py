@@ -165,14 +165,16 @@ def test_uniform_4bit_support():
     for hq, hkv, rv in ((32, 8, 256), (16, 2, 512), (16, 4, 768), (8, 8, 1024)):
         c = _cfg(w, n_q_heads=hq, n_kv_heads=hkv, value_rank=rv)
         assert sk.starkv_decode_splits(c, 1000) > 0, (hq, hkv, rv)
-    # the prefill reads both layouts; with rotary keys it is refused (decode
-    # only) before any HIP call
+    # the prefill reads both layouts, with or without rotary keys; rotary
+    # keys of d_h 256 are refused before any HIP call
     small = _cfg(w, max_tokens=256)
     assert sk.starkv_workspace_bytes(small, sk.OP_PREFILL, 64) > 0
     assert sk.starkv_workspace_bytes(_cfg(w, max_tokens=256, rope_theta=1e4),
-                                     sk.OP_PREFILL, 64) == 0
+                                     sk.OP_PREFILL, 64) > 0
+    wide = _cfg(w, max_tokens=256, head_dim=256, rope_theta=1e4)
+    assert sk.starkv_workspace_bytes(wide, sk.OP_PREFILL, 64) == 0
     cache = _fake_cache()
-    st = lib.starkv_prefill(ctypes.byref(_cfg(w, max_tokens=256, rope_theta=1e4)),
+    st = lib.starkv_prefill(ctypes.byref(wide),
                             ctypes.byref(cache), 0, 64, 0x1000, 4096, 0x2000, 0x3000,
                             0x4000, 0x5000, 0x6000, ctypes.c_float(0.1), 0x7000, None,
                             0x8000, 1 << 30, None)
@@ -278,11 +280,19 @@ def test_rope_support_and_workspace():
                 _cfg(w, head_dim=256, rope_theta=10000.0)):             # head dim 256
         assert lib.starkv_decode(ctypes.byref(cfg), ctypes.byref(cache), 100,
                                  *args) == sk.STARKV_EUNSUPPORTED
-    # prefill with rotary keys is not built
-    pre = _cfg(synth.WORKLOADS["longchat_prefill"], rope_theta=10000.0)
+    # prefill with rotary keys: the keys are reconstructed at d_h channels
+    # (workspace grows by the wider keys and queries); d_h 64 and 128 only
+    lc = synth.WORKLOADS["longchat_prefill"]
+    pre = _cfg(lc, rope_theta=10000.0)
+    assert sk.starkv_workspace_bytes(pre, sk.OP_PREFILL, 4096) > \
+        sk.starkv_workspace_bytes(_cfg(lc), sk.OP_PREFILL, 4096)
+    assert sk.starkv_workspace_bytes(_cfg(lc, head_dim=64, rope_theta=10000.0),
+                                     sk.OP_PREFILL, 4096) > 0
+    wide = _cfg(lc, head_dim=256, rope_theta=10000.0)
+    assert sk.starkv_workspace_bytes(wide, sk.OP_PREFILL, 4096) == 0
     pargs = (0x1000, 4096, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000,
              ctypes.c_float(0.1), 0x7000, None)
-    assert lib.starkv_prefill(ctypes.byref(pre), ctypes.byref(cache), 0, 64, *pargs,
+    assert lib.starkv_prefill(ctypes.byref(wide), ctypes.byref(cache), 0, 64, *pargs,
                               0x8000, 1 << 34, None) == sk.STARKV_EUNSUPPORTED
 
 
@@ -308,13 +318,13 @@ def test_paged_validation():
     short = tail[:6] + (16, None)
     assert lib.starkv_decode_paged(cp, cc, 0x100, 4, 0x200, 100, *short) == sk.STARKV_EWORKSPACE
     # prefill: a table is required, its pages must cover ctx_len + chunk,
-    # rotary keys are decode-only; all before any HIP call
+    # rotary keys of d_h 256 are refused; all before any HIP call
     pre = (0x1000, 4096, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, ctypes.c_float(0.1),
            0x7000, None, 0x8000, 1 << 40, None)
     assert lib.starkv_prefill_paged(cp, cc, None, 8, 0, 64, *pre) == sk.STARKV_EINVAL
     assert lib.starkv_prefill_paged(cp, cc, 0x100, 2, 100, 64, *pre) == sk.STARKV_EINVAL
     assert lib.starkv_prefill_paged(cp, cc, 0x102, 8, 100, 64, *pre) == sk.STARKV_EINVAL
-    rope = _cfg(w, rope_theta=1e4)
+    rope = _cfg(w, head_dim=256, rope_theta=1e4)
     assert lib.starkv_prefill_paged(ctypes.byref(rope), cc, 0x100, 8, 100, 64,
                                     *pre) == sk.STARKV_EUNSUPPORTED
     assert lib.starkv_prefill_paged(cp, cc, 0x100, 8, 100, 64,

@@ -128,17 +128,25 @@ def test_paged_prefill_uniform_4bit():
     run_paged_prefill("longchat_prefill", 90, 60, lo_bits=4)
 
 
-def run_paged_prefill(name, ctx, chunk, lo_bits):
+def test_paged_prefill_rotary_keys():
+    """Rotary keys over the paged pool: the key reconstruction reads each
+    position's latent through the page table."""
+    run_paged_prefill("longchat_prefill", 70, 100, lo_bits=3, rope_theta=10000.0,
+                      head_dim=128)
+
+
+def run_paged_prefill(name, ctx, chunk, lo_bits, rope_theta=0.0, head_dim=64):
     import torch
     B = 2
-    w = synth.WORKLOADS[name].replace(batch=B, n_q_heads=8, n_kv_heads=8, head_dim=64,
+    w = synth.WORKLOADS[name].replace(batch=B, n_q_heads=8, n_kv_heads=8, head_dim=head_dim,
                                       value_rank=256, hidden=128, lo_bits=lo_bits)
     T = ((ctx + chunk + 63) // 64 + 1) * 64
-    cfg = config_for(w, max_tokens=T)
+    cfg = config_for(w, max_tokens=T, rope_theta=rope_theta)
     g = sk().LatentCache(cfg)
     o = oc.Cache.for_workload(w, max_tokens=T)
     fill_random(g, o, seed=ctx + chunk)
-    print(f"paged prefill B={B} ctx={ctx} C={chunk} lo_bits={lo_bits}", flush=True)
+    print(f"paged prefill B={B} ctx={ctx} C={chunk} lo_bits={lo_bits} theta={rope_theta} "
+          f"dh={head_dim}", flush=True)
     append_both(w, cfg, g, o, 0, ctx, B)
     rng = np.random.default_rng(ctx)
     table = rng.permutation(B * o.nt).reshape(B, o.nt).astype(np.int32)
@@ -166,7 +174,8 @@ def run_paged_prefill(name, ctx, chunk, lo_bits):
     z = zdbg.cpu().numpy()
     ref = paged.prefill_paged(o, table, ctx, z[:, :, :nk].reshape(B, chunk, w.n_kv_heads,
                                                                    w.key_rank),
-                              z[:, :, nk:], q, bk, bv, s, w.n_q_heads, w.rotate)
+                              z[:, :, nk:], q, bk, bv, s, w.n_q_heads, w.rotate,
+                              rope_theta=rope_theta)
     for i, k in enumerate(KEYS):
         assert np.array_equal(g.buffers[i][:o.buf[k].size].cpu().numpy(), o.buf[k]), k
     got = out.cpu().numpy().astype(np.float64)

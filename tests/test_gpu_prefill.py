@@ -12,7 +12,10 @@ Per case:
   max|ref| <= 5e-3.
 Shapes span several tiles, ragged chunks and contexts, GQA group sizes
 1/2/4/8, every supported value rank, rotation on and off, a batch of two,
-a peaked softmax and NaN bytes in unused cache slots.
+a peaked softmax and NaN bytes in unused cache slots.  Rotary keys (review
+section 5.3, Algorithm 2 steps 4b-4c): the same checks against the oracle
+with RoPE on keys (at their positions) and queries (at ctx + i), d_h 64
+and 128, GQA 1/2/4/8, both cache precisions, rotation on and off.
 """
 
 import math
@@ -46,11 +49,11 @@ def chunk_inputs(w, chunk, batch, q_scale):
 
 def run_prefill(ctx, chunk, batch=1, q_scale=1.0, rows=None, heads=None,
                 fill="random", oracle_context=True, name="longchat_prefill",
-                key_ranks=None, **kw):
+                key_ranks=None, rope_theta=0.0, **kw):
     import torch
     w = synth.WORKLOADS[name].replace(batch=batch, **kw)
     T = ((ctx + chunk + 63) // 64 + 1) * 64
-    cfg = config_for(w, max_tokens=T, key_ranks=key_ranks)
+    cfg = config_for(w, max_tokens=T, key_ranks=key_ranks, rope_theta=rope_theta)
     g = sk().LatentCache(cfg)
     o = oc.Cache.for_workload(w, max_tokens=T, key_ranks=key_ranks)
     if fill == "random":
@@ -59,7 +62,7 @@ def run_prefill(ctx, chunk, batch=1, q_scale=1.0, rows=None, heads=None,
         fill_byte(g, o, fill)
     print(f"prefill B={batch} ctx={ctx} C={chunk} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
           f"dh={w.head_dim} rv={w.value_rank} D={w.hidden} rot={w.rotate} "
-          f"qx{q_scale} fill={fill}", flush=True)
+          f"qx{q_scale} fill={fill} theta={rope_theta}", flush=True)
     if ctx:
         append_both(w, cfg, g, o if oracle_context else None, 0, ctx, batch)
     if not oracle_context:
@@ -99,7 +102,8 @@ def run_prefill(ctx, chunk, batch=1, q_scale=1.0, rows=None, heads=None,
     errs = []
     for b in range(batch):
         ref = oa.causal_attention(o, ctx, q[b], bk, bv, scale, w.n_q_heads,
-                                  w.rotate, rows=rows, heads=heads, batch=b)
+                                  w.rotate, rows=rows, heads=heads, batch=b,
+                                  rope_theta=rope_theta)
         gb = got[b]
         if rows is not None:
             gb = gb[np.asarray(rows)]
@@ -181,5 +185,49 @@ def test_prefill_full_size_sampled():
     heads = [0, 13, 31]
     zerr, err, _ = run_prefill(w.seq_len, w.chunk, rows=rows, heads=heads,
                                oracle_context=False)
+    assert zerr <= 1e-4
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("ctx,chunk,hq,hkv,dh,rv,rotate", [
+    (100, 70, 8, 8, 128, 256, True),       # 2 heads x 64 queries per workgroup
+    (37, 130, 16, 8, 64, 512, True),       # 4 heads x 32 queries, G = 2
+    (0, 90, 32, 8, 128, 1024, False),      # G = 4, two value column blocks
+    (200, 67, 16, 2, 128, 256, True),      # G = 8
+    (64, 1, 8, 8, 64, 256, True),          # a single query
+])
+def test_prefill_rotary_keys(ctx, chunk, hq, hkv, dh, rv, rotate):
+    kw = dict(SMALL, n_q_heads=hq, n_kv_heads=hkv, head_dim=dh, value_rank=rv,
+              rotate=rotate)
+    zerr, err, _ = run_prefill(ctx, chunk, rope_theta=10000.0, **kw)
+    assert zerr <= 1e-4
+    assert err <= TOL
+
+
+def test_prefill_rotary_keys_peaked_batch_uniform_4bit():
+    """A batch of two with sharpened queries, far positions (theta 500 turns
+    the pairs quickly) and the uniform 4-bit cache."""
+    kw = dict(SMALL, head_dim=128, lo_bits=4)
+    zerr, err, _ = run_prefill(300, 77, batch=2, q_scale=4.0, rope_theta=500.0, **kw)
+    assert zerr <= 1e-4
+    assert err <= TOL
+
+
+def test_prefill_rotary_keys_per_head_ranks():
+    kw = dict(SMALL, head_dim=128, n_q_heads=8, n_kv_heads=4)
+    zerr, err, _ = run_prefill(90, 60, key_ranks=[8, 32, 16, 24], rope_theta=10000.0, **kw)
+    assert zerr <= 1e-4
+    assert err <= TOL
+
+
+def test_prefill_rotary_keys_full_size_sampled():
+    """The full chunked-prefill workload with rotary keys (theta 10000, the
+    LLaMA base): 8192 queries at positions 24576 .. 32767, sampled rows and
+    heads; bytes and projection checked in full."""
+    w = synth.WORKLOADS["longchat_prefill"]
+    rows = [0, 63, 64, 4095, 8191]
+    heads = [0, 17, 31]
+    zerr, err, _ = run_prefill(w.seq_len, w.chunk, rows=rows, heads=heads,
+                               oracle_context=False, rope_theta=10000.0)
     assert zerr <= 1e-4
     assert err <= TOL
