@@ -411,36 +411,53 @@ __device__ inline float4 load4(const _Float16* p) {
   return float4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
 }
 
-// One workgroup per (b, h): weights of the splits from their (m, l) (wave
-// reductions), the weighted sum of their partial outputs (4 consecutive
-// channels per thread), then the inverse rotation in registers: a rotation
-// block has at most 256 channels = one wave's 64 lanes, so its butterflies
-// are in-register (strides 1, 2) or lane shuffles (strides 4 .. 128).  fp32
-// partials are unnormalised sums (weight 2^(m_s - m)); fp16 partials are
-// already divided by their own l_s (weight 2^(m_s - m) * l_s).
+// Rows of partials a merge lane keeps in flight: 16 fp16 rows, 8 fp32 rows.
+template <typename PT>
+constexpr int merge_batch() { return std::is_same<PT, _Float16>::value ? 16 : 8; }
+// Waves of a merge workgroup that share one block of 256 channels: 1 while
+// one batch holds every split, then 2, then 4 (the splits dealt out among
+// them, so that a lane's chain of row loads stays short).
+__host__ __device__ inline int merge_wsplit(int splits, int batch) {
+  return splits <= batch ? 1 : splits <= 2 * batch ? 2 : 4;
+}
+
+// One workgroup per (b, h, 4 / W blocks of 256 channels), W = merge_wsplit:
+// the weights of the splits from their (m, l) (wave reductions), then each
+// of the W waves of a channel block sums the splits s = k, k + W, k + 2W, ...
+// (k its index among them) with kBatch rows in flight per lane (4
+// consecutive channels per lane); their sums meet in LDS, and the first
+// wave of the block scales by 1 / L, undoes the block rotation and stores.
+// A rotation block has at most 256 channels, i.e. one wave's 64 lanes: its
+// butterflies are in registers (strides 1, 2) or lane shuffles (strides
+// 4 .. 128).  fp32 partials are unnormalised sums (weight 2^(m_s - m)); fp16
+// partials are already divided by their own l_s (weight 2^(m_s - m) * l_s).
 template <typename PT>
 __global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     Dims d, int splits,
                                                     float* __restrict__ obar) {
   constexpr bool kNormalised = std::is_same<PT, _Float16>::value;
+  constexpr int kBatch = merge_batch<PT>();
   __shared__ float ms[kMaxSplits];
+  __shared__ float4 red[4][64];
   const int bh = blockIdx.x;
   const int b = bh / d.Hq, h = bh % d.Hq;
   const int t = threadIdx.x, lane = t & 63;
-  const int c = 4 * t;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int W = merge_wsplit(splits, kBatch);
+  const int sw = wave % W;                      // the wave's index in its block
+  const int c = (blockIdx.y * (4 / W) + wave / W) * 256 + 4 * lane;
   const size_t stride = (size_t)d.Hq * d.rv;
   const PT* src = part_o + ((size_t)b * splits * d.Hq + h) * d.rv + min(c, d.rv - 4);
-  // (m, l) of split `lane` first, then the rows of the first kPre splits
+  // (m, l) of split `lane` first, then this wave's first batch of rows
   // (clamped addresses: every load is issued, so the wait for (m, l) does
   // not cover the rows)
   const float2 ml0 = *reinterpret_cast<const float2*>(
       part_ml + (((size_t)b * splits + min(lane, splits - 1)) * d.Hq + h) * 2);
-  // (fp32 partials come with one split per row in the prefill: one row)
-  constexpr int kPre = kNormalised ? 16 : 1;
-  float4 xp[kPre];
+  float4 xp[kBatch];
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) xp[u] = load4(src + (size_t)min(u, splits - 1) * stride);
+  for (int u = 0; u < kBatch; ++u)
+    xp[u] = load4(src + (size_t)min(sw + W * u, splits - 1) * stride);
   // every wave reduces the same (m, l) values; wave 0 publishes the weights
   float mx = lane < splits ? ml0.x : -INFINITY;
   for (int s = lane + 64; s < splits; s += 64)
@@ -464,39 +481,34 @@ __global__ __launch_bounds__(256) void merge_kernel(const PT* __restrict__ part_
   const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
   __syncthreads();
   float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (c < d.rv) {
+  auto accumulate = [&](int s0, const float4 (&x)[kBatch]) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const float wgt = u < splits ? ms[u] : 0.0f;
-      o.x = fmaf(wgt, xp[u].x, o.x);
-      o.y = fmaf(wgt, xp[u].y, o.y);
-      o.z = fmaf(wgt, xp[u].z, o.z);
-      o.w = fmaf(wgt, xp[u].w, o.w);
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = s0 + sw + W * u;
+      const float wgt = sp < splits ? ms[sp] : 0.0f;
+      o.x = fmaf(wgt, x[u].x, o.x);
+      o.y = fmaf(wgt, x[u].y, o.y);
+      o.z = fmaf(wgt, x[u].z, o.z);
+      o.w = fmaf(wgt, x[u].w, o.w);
     }
-    int s = kPre;
-    for (; s + 8 <= splits; s += 8) {
-      float4 x[8];
+  };
+  accumulate(0, xp);
+  for (int s0 = W * kBatch; s0 < splits; s0 += W * kBatch) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = load4(src + (size_t)(s + u) * stride);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wgt = ms[s + u];
-        o.x = fmaf(wgt, x[u].x, o.x);
-        o.y = fmaf(wgt, x[u].y, o.y);
-        o.z = fmaf(wgt, x[u].z, o.z);
-        o.w = fmaf(wgt, x[u].w, o.w);
-      }
-    }
-    for (; s < splits; ++s) {
-      const float4 x = load4(src + (size_t)s * stride);
-      const float wgt = ms[s];
-      o.x = fmaf(wgt, x.x, o.x);
-      o.y = fmaf(wgt, x.y, o.y);
-      o.z = fmaf(wgt, x.z, o.z);
-      o.w = fmaf(wgt, x.w, o.w);
-    }
-    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+    for (int u = 0; u < kBatch; ++u)
+      xp[u] = load4(src + (size_t)min(s0 + sw + W * u, splits - 1) * stride);
+    accumulate(s0, xp);
   }
+  if (W > 1) {
+    red[wave][lane] = o;
+    __syncthreads();
+    if (sw != 0) return;
+    for (int k = 1; k < W; ++k) {
+      const float4 r = red[wave + k][lane];
+      o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+    }
+  }
+  o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
   if (d.dtype == STARKV_CACHE_Q43 && d.rotate) {
     // undo the block rotation of the stored value latents: (Z H) H = Z (eq. 13)
     const int mb = pow2_divisor(d.rv / 4);
@@ -823,10 +835,14 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
     mark(4);
     return e;
   }
+  // channels per merge workgroup: 4 / W blocks of 256
+  const int mw = merge_wsplit(lay.splits, FMT == STARKV_CACHE_F32 ? merge_batch<float>()
+                                                                  : merge_batch<_Float16>());
+  const dim3 mgrid(d.B * d.Hq, (d.rv + 256 * (4 / mw) - 1) / (256 * (4 / mw)));
   if constexpr (FMT == STARKV_CACHE_F32)
-    merge_kernel<float><<<d.B * d.Hq, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
+    merge_kernel<float><<<mgrid, 256, 0, s>>>(part_o, part_ml, d, lay.splits, obar);
   else   // fp16 partial rows, each divided by its own l
-    merge_kernel<_Float16><<<d.B * d.Hq, 256, 0, s>>>(
+    merge_kernel<_Float16><<<mgrid, 256, 0, s>>>(
         reinterpret_cast<const _Float16*>(part_o), part_ml, d, lay.splits, obar);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
