@@ -5,11 +5,17 @@
 //
 //   gemm      Z = X [A_key | A_value] (bf16 in, fp32 out) on MFMA 32x32x16
 //   append    the decode-path append kernels (rotation + 4/3-bit packing)
-//   qproj     q~ for every query of the chunk on MFMA (natural channel order)
-//   attn      per (16 queries, 8 query heads, up to 512 value columns):
-//             latent scores on MFMA with a lazy online softmax, then P Z_v
-//             on MFMA with each wave dequantizing its own value groups
-//             straight into MFMA operands (section 5.3, eq. 12)
+//   keys      the key latents of every visible position as fp16; with
+//             rotary keys, the keys themselves: reconstructed through the
+//             key factor and rotated at their positions (section 5.3,
+//             Algorithm 2 steps 4b-4c)
+//   qproj     q~ for every query of the chunk on MFMA (natural channel
+//             order); with rotary keys, the queries rotated at their positions
+//   attn      per (128 stacked rows of queries x query heads, up to 512
+//             value columns): scores on MFMA (over the 32 latent channels,
+//             or the d_h channels of rotary keys) with a lazy online softmax,
+//             then P Z_v on MFMA with each wave dequantizing its own value
+//             groups straight into MFMA operands (section 5.3, eq. 12)
 //   vproj     the attention rows times the value factor rotated like the
 //             stored latents, on MFMA, divided by the softmax denominator
 #include <type_traits>
