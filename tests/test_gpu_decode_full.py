@@ -92,3 +92,11 @@ def test_full_gqa_q43_b32_t16384():
 
 def test_full_tiny():
     assert run_full("tiny", 1, 256, [0]) <= TOL
+
+
+def test_full_q43_b1_t131072():
+    """One sequence of 128K tokens (the longest context of the pages' speed
+    figures), 4/3-bit rotated: 256 automatic splits, so the merge deals the
+    splits out among four waves per channel block over four batches of
+    row loads, and the kernels index tiles up to 2047."""
+    assert run_full("l2_q43", 1, 131072, [0]) <= TOL
