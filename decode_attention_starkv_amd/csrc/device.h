@@ -181,13 +181,14 @@ __device__ inline double rope_freq(int p, int dh, double log2_theta) {
   return exp2(-2.0 * p / dh * log2_theta);
 }
 
-// sin / cos of the rotary angle pos * w, reduced modulo 2 pi in fp64.
+// sin / cos of the rotary angle pos * w, reduced modulo 2 pi in fp64; the
+// hardware sine and cosine take the angle in turns, here in [0, 1).
 __device__ inline void rope_sincos(int pos, double w, float* c, float* s) {
   const double a = (double)pos * w;
   const double turns = a * 0.15915494309189535;     // 1 / (2 pi)
-  const float phi = (float)((turns - floor(turns)) * 6.283185307179586);
-  *c = cosf(phi);
-  *s = sinf(phi);
+  const float frac = (float)(turns - floor(turns));
+  *c = __builtin_amdgcn_cosf(frac);
+  *s = __builtin_amdgcn_sinf(frac);
 }
 
 // sin / cos of the rotary angle of pair p at position pos,

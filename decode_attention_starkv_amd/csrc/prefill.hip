@@ -233,7 +233,8 @@ __global__ __launch_bounds__(256) void rope_key_kernel(const uint8_t* __restrict
                                                        const uint16_t* __restrict__ bk,
                                                        Dims d, int n, double log2_theta,
                                                        _Float16* __restrict__ kd) {
-  __shared__ float zl[kTile][33];
+  // rows padded to 36 floats: 16-byte aligned for the 16-byte broadcasts
+  __shared__ __attribute__((aligned(16))) float zl[kTile][36];
   const int g = blockIdx.y, b = blockIdx.z, t0 = blockIdx.x * kTile;
   const int tid = threadIdx.x;
   if (tid < kTile) {
@@ -280,9 +281,16 @@ __global__ __launch_bounds__(256) void rope_key_kernel(const uint8_t* __restrict
     if (t >= n) break;
     float k1 = 0.0f, k2 = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      k1 = fmaf(b1[c], zl[u][c], k1);
-      k2 = fmaf(b2[c], zl[u][c], k2);
+    for (int c4 = 0; c4 < 8; ++c4) {
+      const float4 z4 = *reinterpret_cast<const float4*>(&zl[u][4 * c4]);
+      k1 = fmaf(b1[4 * c4], z4.x, k1);
+      k1 = fmaf(b1[4 * c4 + 1], z4.y, k1);
+      k1 = fmaf(b1[4 * c4 + 2], z4.z, k1);
+      k1 = fmaf(b1[4 * c4 + 3], z4.w, k1);
+      k2 = fmaf(b2[4 * c4], z4.x, k2);
+      k2 = fmaf(b2[4 * c4 + 1], z4.y, k2);
+      k2 = fmaf(b2[4 * c4 + 2], z4.z, k2);
+      k2 = fmaf(b2[4 * c4 + 3], z4.w, k2);
     }
     float cs, sn;
     rope_sincos(t, w, &cs, &sn);
