@@ -169,8 +169,11 @@ hipError_t launch_append_qproj(const Dims& d, const starkv_cache& cache,
 
 // Workspace carve-up of one prefill call (byte offsets, 256-aligned).
 struct PrefillWs {
-  size_t zk, zv, qt, kd, part_o, part_ml, bvr, total;
+  size_t zk, zv, qt, kd, part_o, part_ml, bvr, zvd, bvh, vt, total;
 };
+// Whether a prefill chunk reconstructs the values once per call (eq. 12 in
+// its left-hand order) instead of contracting with the joint latent.
+bool prefill_reconstructs(const Dims& d, int chunk);
 PrefillWs prefill_ws_layout(const Dims& d, int chunk);
 hipError_t launch_prefill(const Dims& d, const starkv_cache& cache,
                           int ctx_len, int chunk, const void* x, int hidden,

@@ -401,7 +401,8 @@ __host__ __device__ inline size_t bvr_index(const Dims& d, int g, int n, int c, 
 
 __global__ __launch_bounds__(256) void prefill_rotate_bv_kernel(const uint16_t* __restrict__ bv,
                                                                 Dims d,
-                                                                uint16_t* __restrict__ bvr) {
+                                                                uint16_t* __restrict__ bvr,
+                                                                _Float16* __restrict__ bvh) {
   const size_t row = blockIdx.x;
   const int t = threadIdx.x, c = 4 * t;
   const int cc = min(c, d.rv - 4);
@@ -423,7 +424,11 @@ __global__ __launch_bounds__(256) void prefill_rotate_bv_kernel(const uint16_t* 
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] *= cst;
   }
-  if (c < d.rv) {
+  if (c < d.rv && bvh) {
+    // (B_v H) as fp16 rows [Hkv d_h][R_v], for the value reconstruction
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bvh[row * d.rv + c + e] = (_Float16)o[e];
+  } else if (c < d.rv) {
     const int g = (int)(row / d.dh), n = (int)(row % d.dh);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -956,6 +961,395 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------ reconstructed values (prefill) --
+//
+// eq. 12 read in its left-hand order for the prefill: p_h (Z_v B_v[h]^T).
+// Decode contracts P with the joint latent (2 R_v flop per query, head and
+// token) because each token meets one query; a chunk's queries share every
+// cached token, so reconstructing the values once per call (2 Hkv d_h R_v
+// flop per token) and contracting over d_h (2 d_h per pair) is cheaper as
+// soon as C Hq (R_v - d_h) > Hkv d_h R_v.  The stored latents are rotated
+// (eq. 13), so the factor is rotated the same way: Z H (B_v H)^T = Z B_v^T.
+
+// Element (sequence b, KV head g, position t, channel c) of the
+// reconstructed values: per (b, g, 64-position tile) d_h rows of 64
+// positions (fp16), the 16-byte chunk q (positions 8q .. 8q + 7) of channel c
+// at chunk q ^ ((c >> 1) & 7) of its row, so that an operand read of 16
+// channels at one chunk touches every LDS bank once.
+__host__ __device__ inline size_t vrec_index(const Dims& d, int b, int g, int t, int c) {
+  return ((((size_t)b * d.Hkv + g) * d.NT + t / kTile) * d.dh + c) * kTile +
+         ((((t % kTile) >> 3) ^ ((c >> 1) & 7)) << 3) + (t & 7);
+}
+
+// Value latents of positions [0, n) of every sequence, dequantized from the
+// stored tiles (z + s * code per 32-channel group), fp16 [B][T_max][R_v]
+// (position-major, still rotated).  One thread per (sequence, tile, group,
+// channel m, half j): the 32 positions of one value run.
+__global__ __launch_bounds__(256) void value_dequant_kernel(const uint8_t* __restrict__ value,
+                                                            const uint16_t* __restrict__ vmeta,
+                                                            Dims d, int n,
+                                                            _Float16* __restrict__ zv) {
+  const int NG = d.rv / 32, NH = d.lob == 4 ? NG : d.rv / 128;
+  const int ntn = (n + kTile - 1) / kTile;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)d.B * ntn * NG * 64) return;
+  const int run = (int)(idx % 64), m = run & 31, j = run >> 5;
+  size_t rest = idx / 64;
+  const int grp = (int)(rest % NG);
+  rest /= NG;
+  const int tile = (int)(rest % ntn), b = (int)(rest / ntn);
+  const size_t tix = tile_index(d, b, tile);   // the tile's slot or page
+  const uint8_t* tb = value + tix * value_tile_bytes(d.rv, d.lob);
+  const bool four = grp < NH;
+  uint32_t w[4];
+  if (four) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tb + grp * 1024 + run * 16);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(tb + NH * 1024 + (grp - NH) * 768 + run * 12);
+    w[0] = p[0]; w[1] = p[1]; w[2] = p[2]; w[3] = 0u;
+  }
+  const _Float16* meta = reinterpret_cast<const _Float16*>(vmeta) + tix * (size_t)(2 * NG * kTile);
+  const _Float16* sc = meta + grp * kTile + 32 * j;
+  const _Float16* ze = meta + (NG + grp) * kTile + 32 * j;
+  const int t0 = tile * kTile + 32 * j;
+  _Float16* dst = zv + ((size_t)b * d.Tmax + t0) * d.rv + grp * 32 + m;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    // codes of positions 2p and 2p + 1 of the run (the run layout of the
+    // append: see run_pair_inplace)
+    uint32_t c0, c1;
+    if (four) {
+      c0 = (w[p >> 2] >> (4 * (p & 3))) & 15u;
+      c1 = (w[p >> 2] >> (16 + 4 * (p & 3))) & 15u;
+    } else if (p < 15) {
+      c0 = (w[p / 5] >> (3 * (p % 5))) & 7u;
+      c1 = (w[p / 5] >> (16 + 3 * (p % 5))) & 7u;
+    } else {
+      c0 = ((w[0] >> 15) & 1u) | ((w[1] >> 14) & 2u) | ((w[2] >> 13) & 4u);
+      c1 = ((w[0] >> 31) & 1u) | ((w[1] >> 30) & 2u) | ((w[2] >> 29) & 4u);
+    }
+    // s * code is exact in fp32 and so is the sum with z: one rounding to fp16
+    if (t0 + 2 * p < n)
+      dst[(size_t)(2 * p) * d.rv] =
+          (_Float16)fmaf((float)sc[2 * p], (float)c0, (float)ze[2 * p]);
+    if (t0 + 2 * p + 1 < n)
+      dst[(size_t)(2 * p + 1) * d.rv] =
+          (_Float16)fmaf((float)sc[2 * p + 1], (float)c1, (float)ze[2 * p + 1]);
+  }
+}
+
+// V^ = Zv (B_v H)^T of one sequence (blockIdx.z), fp16 x fp16 -> fp32 on
+// MFMA 32x32x16, written as fp16 in the order of vrec_index for positions
+// [0, 64 ceil(n / 64)) (zeros past n: those rows of Zv read as zero).  Both
+// operands are read with the reduction index contiguous: Zv [T][R_v] and
+// (B_v H) [Hkv d_h][R_v].  Workgroup tile 128 positions x 128 channels, four
+// waves in 2 x 2, K steps of 32 through LDS.
+constexpr int kRS = 32 + 8;   // LDS row stride (fp16): 16-row reads hit 16 bank groups
+__global__ __launch_bounds__(256) void value_recon_kernel(const _Float16* __restrict__ zv,
+                                                          const _Float16* __restrict__ bvh,
+                                                          Dims d, int n,
+                                                          _Float16* __restrict__ vt) {
+  __shared__ __attribute__((aligned(16))) _Float16 as[kGT * kRS];
+  __shared__ __attribute__((aligned(16))) _Float16 bs[kGT * kRS];
+  const int b = blockIdx.z, t0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
+  const int N = d.Hkv * d.dh, K = d.rv;
+  const int tend = ((n + kTile - 1) / kTile) * kTile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m = lane & 31, j = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  // one K step: 128 rows x 32 channels of each operand = 512 runs of 16 B
+  u32x4 ar[2], br[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      const int r = c >> 2, kc = (c & 3) * 8;
+      const int t = t0 + r, col = n0 + r;
+      ar[i] = t < n ? *reinterpret_cast<const u32x4*>(zv + ((size_t)b * d.Tmax + t) * K + k0 + kc)
+                    : u32x4{0u, 0u, 0u, 0u};
+      br[i] = col < N ? *reinterpret_cast<const u32x4*>(bvh + (size_t)col * K + k0 + kc)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      const int r = c >> 2, kc = (c & 3) * 8;
+      *reinterpret_cast<u32x4*>(&as[r * kRS + kc]) = ar[i];
+      *reinterpret_cast<u32x4*>(&bs[r * kRS + kc]) = br[i];
+    }
+    __syncthreads();
+    if (k0 + 32 < K) load(k0 + 32);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      h8 af[2], bf[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        af[x] = *reinterpret_cast<const h8*>(&as[(wm * 64 + x * 32 + m) * kRS + s * 16 + j * 8]);
+        bf[x] = *reinterpret_cast<const h8*>(&bs[(wn * 64 + x * 32 + m) * kRS + s * 16 + j * 8]);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[x], bf[y], acc[x][y], 0, 0, 0);
+    }
+  }
+  // lane (m, j): channel column m of its tiles; registers 4q .. 4q + 3 are
+  // positions 8q + 4j .. + 3 of the tile: one 8-byte store each
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int col = n0 + wn * 64 + y * 32 + m;
+    if (col >= N) continue;
+    const int g = col / d.dh, c = col % d.dh;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + wm * 64 + x * 32 + 8 * q + 4 * j;
+        if (t >= tend) continue;
+        const h4 v = h4{(_Float16)acc[x][y][4 * q], (_Float16)acc[x][y][4 * q + 1],
+                        (_Float16)acc[x][y][4 * q + 2], (_Float16)acc[x][y][4 * q + 3]};
+        *reinterpret_cast<h4*>(vt + vrec_index(d, b, g, t, c)) = v;
+      }
+  }
+}
+
+struct RecArgs {
+  Dims d;
+  int ctx, chunk, n_qb, n_qb_pad;
+  const _Float16* qn;     // [B*C][Hq][DK] query latents (or rotary queries)
+  const _Float16* kd;     // [B][T_max][Hkv][DK] fp16 key latents (or rotary keys)
+  const _Float16* vt;     // reconstructed values, vrec_index order
+  float* out;             // [B*C][Hq][d_h]
+};
+
+// Workgroup = (128 / G consecutive queries, the G query heads of one KV head
+// g, sequence b), 8 waves; rows of the stacked P tile: row = query * G +
+// head (128).  Wave w scores query head w % G for queries 16 (w / G) .. + 15
+// exactly as prefill_attn_kernel does (keys of DK channels, lazy online
+// softmax, fp16 P slot), then contracts P with the KV head's reconstructed
+// values on MFMA 32x32x16: row tile w % 4, channel tiles (w / 4) TPW ..
+// + TPW - 1 of 32 (d_h = 64 TPW); a step takes positions 16 s + 8 j .. + 7 in
+// k-slot j.  Keys (two tiles ahead) and value tiles (one ahead) reach LDS
+// by direct-to-LDS loads; one barrier per tile.  The rows are divided by
+// their softmax denominators and written to out: no partial rows, no
+// up-projection.
+template <int G, int DK, int TPW>
+__global__ __launch_bounds__(512) void prefill_attn_rec_kernel(RecArgs a) {
+  constexpr int PH = G, PQ = kRows / G;
+  constexpr int CPT = DK / 8;             // 16-byte chunks per key row
+  constexpr int TPP = 1024 / (DK * 2);    // key rows per 1 KB staging piece
+  constexpr int KS = DK / 32;             // K steps of a score MFMA
+  constexpr int DH = 64 * TPW;            // d_h
+  auto swz = [](int u) { return (u / (16 / CPT)) & (CPT - 1); };
+  const Dims& d = a.d;
+  __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kRows * kPS];
+  __shared__ __attribute__((aligned(16))) uint8_t key_l[2][kTile * DK * 2];
+  __shared__ __attribute__((aligned(16))) _Float16 v_l[2][DH * kTile];
+  __shared__ __attribute__((aligned(16))) float alpha_l[2][kRows];
+  __shared__ float l_l[kRows];
+  __shared__ int flag_l[2];
+
+  // XCD-aware order: the KV heads of one query block run on one XCD; the
+  // query blocks with the longest causal span start first
+  const int L = blockIdx.x;
+  const int xcd = L & 7, k = L >> 3;
+  const int g = k % d.Hkv;
+  const int qb = a.n_qb_pad - 1 - ((k / d.Hkv) * 8 + xcd);
+  if (qb >= a.n_qb) return;   // padding workgroup; uniform, before any barrier
+  const int b = blockIdx.y;
+  const int q0 = qb * PQ;
+  const int nq = min(PQ, a.chunk - q0);
+  const int pfirst = a.ctx + q0;
+  const int pmax = pfirst + nq - 1;
+  const int tile_last = pmax / kTile;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31, j = lane >> 5;
+  const int c16 = lane & 15, g16 = lane >> 4;
+  if (tid < 2) flag_l[tid] = -1;
+  __syncthreads();
+
+  // ------------------------------------------------------------ score setup
+  const int hl = wave % PH, qs = wave / PH;
+  const int h = g * G + hl;
+  const int qi = 16 * qs + c16;
+  const int R = qi * PH + hl;
+  h8 bq[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    bq[ks] = qi < nq ? *reinterpret_cast<const h8*>(
+                           a.qn + (((size_t)b * a.chunk + q0 + qi) * d.Hq + h) * DK + 32 * ks +
+                           8 * g16)
+                     : h8{};
+  float m_ref = -1e30f, l_lane = 0.0f;
+  auto p_at = [&](int slot, int R, int u) -> _Float16* {
+    return &p_l[slot][R * kPS + (((u >> 3) ^ (R >> 5)) << 3) + (u & 7)];
+  };
+  const int key_lane = c16 * (DK * 2);
+  auto key_at = [&](int slot, int bl, int ks) {
+    return *reinterpret_cast<const h8*>(
+        &key_l[slot][key_lane + bl * 16 * (DK * 2) + (((4 * ks + g16) ^ swz(c16)) << 4)]);
+  };
+  auto score = [&](int tile, int it, int slot) {
+    float x[4][4];
+#pragma unroll
+    for (int bl = 0; bl < 4; ++bl) {
+      h8 kb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kb[ks] = key_at(slot, bl, ks);
+      f32x4v sc = f32x4v{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[ks], bq[ks], sc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) x[bl][v] = sc[v];
+    }
+    if (tile * kTile + kTile - 1 > pfirst) {   // uniform: some token is hidden
+      const int lim = qi < nq ? pfirst + qi - tile * kTile : -1;
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          x[bl][v] = bl * 16 + 4 * g16 + v > lim ? -INFINITY : x[bl][v];
+    }
+    float tmax = x[0][0];
+#pragma unroll
+    for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, x[bl][v]);
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kLazy) != 0) {
+      float gm = fmaxf(tmax, __shfl_xor(tmax, 16));
+      gm = fmaxf(gm, __shfl_xor(gm, 32));
+      if (gm > m_ref + kLazy) {
+        alpha = __builtin_amdgcn_exp2f(m_ref - gm);
+        m_ref = gm;
+        l_lane *= alpha;
+        flag_l[slot] = it;
+      }
+    }
+    if (lane < 16) alpha_l[slot][R] = alpha;
+    float ls = 0.0f;
+#pragma unroll
+    for (int bl = 0; bl < 4; ++bl) {
+      float p[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        p[v] = __builtin_amdgcn_exp2f(x[bl][v] - m_ref);
+        ls += p[v];
+      }
+      *reinterpret_cast<h4*>(p_at(slot, R, bl * 16 + 4 * g16)) =
+          h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    }
+    l_lane += ls;
+  };
+
+  // ---------------------------------------------------------------- staging
+  // keys of tile kt (CPT pieces of TPP positions) into key slot kt & 1, the
+  // value tile ct (DH / 8 pieces) into value slot ct & 1; wave w issues the
+  // pieces p with p % 8 == w, keys first
+  const int key_tl = lane / CPT, key_pos = lane % CPT;
+  auto dma = [&](const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  constexpr int nkp = CPT, nvp = DH / 8;
+  auto stage = [&](int kt, int ct) {
+    if (kt <= tile_last) {
+      const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kd) +
+          (((size_t)b * d.Tmax + (size_t)kt * kTile) * d.Hkv + g) * (DK * 2);
+      for (int p = wave; p < nkp; p += 8) {
+        const int u = p * TPP + key_tl;
+        dma(kbase + (size_t)u * d.Hkv * (DK * 2) + ((key_pos ^ swz(u)) << 4),
+            &key_l[kt & 1][p * 1024]);
+      }
+    }
+    if (ct <= tile_last) {
+      const uint8_t* vbase =
+          reinterpret_cast<const uint8_t*>(a.vt + vrec_index(d, b, g, ct * kTile, 0)) + lane * 16;
+      uint8_t* vdst = reinterpret_cast<uint8_t*>(&v_l[ct & 1][0]);
+      for (int p = nkp + ((wave - nkp) & 7); p < nkp + nvp; p += 8)
+        dma(vbase + (p - nkp) * 1024, vdst + (p - nkp) * 1024);
+    }
+  };
+
+  // -------------------------------------------------------- value contraction
+  const int rt = wave & 3, ct0 = (wave >> 2) * TPW;
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x16{};
+  auto contract = [&](int slot, int it) {
+    if (__builtin_amdgcn_readfirstlane(flag_l[slot]) == it) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float al = alpha_l[slot][rt * 32 + acc_row(v, lane)];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t][v] *= al;
+      }
+    }
+    const _Float16* pa = &p_l[slot][(rt * 32 + m) * kPS];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // P row rt * 32 + m, positions 16 s + 8 j: chunk (2 s + j) ^ rt
+      const h8 A = *reinterpret_cast<const h8*>(pa + (((2 * s + j) ^ rt) << 3));
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int c = (ct0 + t) * 32 + m;
+        const h8 B = *reinterpret_cast<const h8*>(
+            &v_l[slot][c * kTile + (((2 * s + j) ^ ((c >> 1) & 7)) << 3)]);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, acc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  stage(0, 0);
+  stage(1, tile_last + 1);
+  wait_vmcnt<0>();
+  __syncthreads();        // keys of tiles 0, 1 and values of tile 0 in LDS
+  score(0, 0, 0);
+  for (int tile = 0; tile <= tile_last; ++tile) {
+    const int cur = tile & 1, nxt = cur ^ 1;
+    lds_barrier();        // P of `tile`, staging of the previous step visible
+    if (tile < tile_last) stage(tile + 2, tile + 1);
+    contract(cur, tile);
+    if (tile < tile_last) {
+      __builtin_amdgcn_sched_barrier(0);
+      score(tile + 1, tile + 1, nxt);
+      wait_vmcnt<0>();    // this wave's staging landed
+    }
+  }
+
+  // ---------------------------------------------------------------- output
+  {
+    float l = l_lane + __shfl_xor(l_lane, 16);
+    l += __shfl_xor(l, 32);
+    if (lane < 16) l_l[R] = l;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int rr = rt * 32 + acc_row(v, lane);
+    const int rq = rr / PH, hh = rr % PH;
+    if (rq < nq) {
+      const float inv = 1.0f / l_l[rr];
+      float* o = a.out + (((size_t)b * a.chunk + q0 + rq) * d.Hq + g * G + hh) * DH;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) o[(ct0 + t) * 32 + m] = acc[t][v] * inv;
+    }
+  }
+}
+
 // Width of the keys the attention kernel scores against: the 32 latent
 // channels, or the d_h channels of reconstructed rotary keys.
 int attn_key_width(const Dims& d) { return d.rope_theta > 0.0f ? d.dh : 32; }
@@ -981,13 +1375,42 @@ hipError_t launch_attn(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t
   }
 }
 
+template <int DK, int TPW>
+hipError_t launch_rec_dk(const Dims& d, dim3 grid, const RecArgs& ra, hipStream_t s) {
+  switch (d.G) {
+    case 1: prefill_attn_rec_kernel<1, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
+    case 2: prefill_attn_rec_kernel<2, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
+    case 4: prefill_attn_rec_kernel<4, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
+    case 8: prefill_attn_rec_kernel<8, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rec(const Dims& d, dim3 grid, const RecArgs& ra, hipStream_t s) {
+  const int dk = attn_key_width(d);
+  if (dk == 32 && d.dh == 64) return launch_rec_dk<32, 1>(d, grid, ra, s);
+  if (dk == 32 && d.dh == 128) return launch_rec_dk<32, 2>(d, grid, ra, s);
+  if (dk == 64 && d.dh == 64) return launch_rec_dk<64, 1>(d, grid, ra, s);
+  if (dk == 128 && d.dh == 128) return launch_rec_dk<128, 2>(d, grid, ra, s);
+  return hipErrorNotSupported;
+}
+
 }  // namespace
 
 static size_t align256p(size_t x) { return (x + 255) & ~(size_t)255; }
 
+bool prefill_reconstructs(const Dims& d, int chunk) {
+  // the chunk's queries outweigh one reconstruction of every position's
+  // values: C Hq (R_v - d_h) > Hkv d_h R_v (flop per cached position)
+  return (d.dh == 64 || d.dh == 128) && d.rv > d.dh &&
+         (int64_t)chunk * d.Hq * (d.rv - d.dh) > (int64_t)d.Hkv * d.dh * d.rv;
+}
+
 PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
   PrefillWs w;
   const size_t M = (size_t)d.B * chunk;
+  const bool rec = prefill_reconstructs(d, chunk);
   size_t off = 0;
   w.zk = off;
   off += align256p(M * d.Hkv * d.rk * 4);
@@ -998,12 +1421,22 @@ PrefillWs prefill_ws_layout(const Dims& d, int chunk) {
   off += align256p(M * d.Hq * dk * 2);
   w.kd = off;   // fp16 key latents (or rotary keys) of every cached position, [B][T_max][Hkv][dk]
   off += align256p((size_t)d.B * d.Tmax * d.Hkv * dk * 2);
-  w.part_o = off;
-  off += align256p(M * d.Hq * d.rv * 4);
-  w.part_ml = off;
-  off += align256p(M * d.Hq * 2 * 4);
-  w.bvr = off;  // rotated value factor, bf16 high then low parts
-  off += align256p((size_t)2 * d.Hkv * d.dh * d.rv * 2);
+  w.part_o = w.part_ml = w.bvr = w.zvd = w.bvh = w.vt = 0;
+  if (rec) {
+    w.zvd = off;  // fp16 value latents of every position, [B][T_max][R_v]
+    off += align256p((size_t)d.B * d.Tmax * d.rv * 2);
+    w.bvh = off;  // rotated value factor as fp16 rows
+    off += align256p((size_t)d.Hkv * d.dh * d.rv * 2);
+    w.vt = off;   // reconstructed values, vrec_index order
+    off += align256p((size_t)d.B * d.NT * kTile * d.Hkv * d.dh * 2);
+  } else {
+    w.part_o = off;
+    off += align256p(M * d.Hq * d.rv * 4);
+    w.part_ml = off;
+    off += align256p(M * d.Hq * 2 * 4);
+    w.bvr = off;  // rotated value factor, bf16 high then low parts
+    off += align256p((size_t)2 * d.Hkv * d.dh * d.rv * 2);
+  }
   w.total = off;
   return w;
 }
@@ -1087,6 +1520,44 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (prefill_reconstructs(d, chunk)) {
+    // values of every visible position reconstructed once (eq. 12, left-hand
+    // order), then attention straight into out
+    _Float16* zvd = reinterpret_cast<_Float16*>(ws + lay.zvd);
+    _Float16* bvh = reinterpret_cast<_Float16*>(ws + lay.bvh);
+    _Float16* vt = reinterpret_cast<_Float16*>(ws + lay.vt);
+    const int ntn = (n + kTile - 1) / kTile;
+    const size_t vitems = (size_t)d.B * ntn * (d.rv / 32) * 64;
+    value_dequant_kernel<<<(unsigned)((vitems + 255) / 256), 256, 0, s>>>(
+        static_cast<const uint8_t*>(cache.value), static_cast<const uint16_t*>(cache.value_meta),
+        d, n, zvd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prefill_rotate_bv_kernel<<<d.Hkv * d.dh, 256, 0, s>>>(static_cast<const uint16_t*>(bv), d,
+                                                           nullptr, bvh);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    value_recon_kernel<<<dim3((d.Hkv * d.dh + kGT - 1) / kGT, (ntn * kTile + kGT - 1) / kGT, d.B),
+                         256, 0, s>>>(zvd, bvh, d, n, vt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    mark(3);
+    RecArgs ra;
+    ra.d = d;
+    ra.ctx = ctx_len;
+    ra.chunk = chunk;
+    ra.n_qb = (chunk + kRows / d.G - 1) / (kRows / d.G);
+    ra.n_qb_pad = (ra.n_qb + 7) / 8 * 8;
+    ra.qn = qn;
+    ra.kd = kd;
+    ra.vt = vt;
+    ra.out = out;
+    e = launch_rec(d, dim3(ra.n_qb_pad * d.Hkv, d.B), ra, s);
+    if (e != hipSuccess) return e;
+    mark(4);
+    mark(5);
+    return hipSuccess;
+  }
   mark(3);
 
   // causal latent attention
@@ -1111,7 +1582,8 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
 
   // up-project per head through the rotated factor and normalise
   uint16_t* bvr = reinterpret_cast<uint16_t*>(ws + lay.bvr);
-  prefill_rotate_bv_kernel<<<d.Hkv * d.dh, 256, 0, s>>>(static_cast<const uint16_t*>(bv), d, bvr);
+  prefill_rotate_bv_kernel<<<d.Hkv * d.dh, 256, 0, s>>>(static_cast<const uint16_t*>(bv), d, bvr,
+                                                         nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_prefill_vproj(d, M, aa.part_o, aa.part_ml, bvr, out, s);

@@ -231,3 +231,30 @@ def test_prefill_rotary_keys_full_size_sampled():
                                oracle_context=False, rope_theta=10000.0)
     assert zerr <= 1e-4
     assert err <= TOL
+
+
+@pytest.mark.parametrize("case", [
+    dict(ctx=30, chunk=150, fill=0xFF),                          # NaN unused slots
+    dict(ctx=100, chunk=160, lo_bits=4),                         # uniform 4-bit
+    dict(ctx=70, chunk=140, batch=2, q_scale=8.0, rotate=False),
+    dict(ctx=100, chunk=150, key_ranks=[8, 32, 16, 24, 8, 16, 32, 24]),
+    dict(ctx=40, chunk=150, n_q_heads=16, n_kv_heads=2, head_dim=128),   # G = 8
+    dict(ctx=90, chunk=100, n_q_heads=16, n_kv_heads=4, head_dim=128, value_rank=512),
+])
+def test_prefill_reconstructed_values(case):
+    """Chunks long enough that the values of every visible position are
+    reconstructed once per call (C Hq (R_v - d_h) > Hkv d_h R_v: eq. 12 in
+    its left-hand order) and the attention contracts over d_h: the same
+    bar against the oracle, with unused slots NaN-filled, the uniform 4-bit
+    cache, a peaked batch of two without rotation, per-head key ranks, G 8
+    and d_h 128."""
+    kw = dict(SMALL)
+    kw.update(case)
+    ctx, chunk = kw.pop("ctx"), kw.pop("chunk")
+    hq, hkv, dh, rv = kw["n_q_heads"], kw["n_kv_heads"], kw["head_dim"], kw["value_rank"]
+    assert chunk * hq * (rv - dh) > hkv * dh * rv          # the reconstructing path
+    assert rv <= hkv * dh                                  # orthonormal synthetic factors
+    zerr, err, got = run_prefill(ctx, chunk, **kw)
+    assert np.isfinite(got).all()
+    assert zerr <= 1e-4
+    assert err <= TOL
