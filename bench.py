@@ -87,6 +87,16 @@ def prefill_traffic_from_counters(w, ctx, chunk):
 
 
 
+def prefill_reconstructs(w, chunk):
+    """The library's choice for a prefill chunk: reconstruct the values of
+    every visible position once (eq. 12 in its left-hand order) when the
+    chunk's queries outweigh it, C Hq (R_v - d_h) > Hkv d_h R_v, for d_h 64
+    or 128; else contract with the joint latent."""
+    return (w.cache == "q43" and w.head_dim in (64, 128) and w.value_rank > w.head_dim
+            and chunk * w.n_q_heads * (w.value_rank - w.head_dim)
+            > w.n_kv_heads * w.head_dim * w.value_rank)
+
+
 def cache_label(w):
     kind = "u4" if w.cache == "q43" and w.lo_bits == 4 else w.cache
     return kind + (" rotated" if w.rotate else "")
@@ -355,9 +365,15 @@ def run_prefill(args, w, torch, sk, synth):
     ms = mean(step_ms)
     attn_ms = mean(kern[3])
     pairs = prefill_pairs(ctx, chunk, w.n_q_heads) * w.batch
+    rec = prefill_reconstructs(w, chunk)
     # scores over the r_k latent channels, or over the d_h channels of the
-    # reconstructed rotary keys; then the value contraction over R_v
-    attn_flops = pairs * 2 * ((w.head_dim if rope else w.key_rank) + w.value_rank)
+    # reconstructed rotary keys; then the value contraction over d_h
+    # (reconstructed values) or over R_v (the joint latent)
+    attn_flops = pairs * 2 * ((w.head_dim if rope else w.key_rank)
+                              + (w.head_dim if rec else w.value_rank))
+    # the reconstruction itself (a pre-pass): 2 Hkv d_h R_v per position
+    recon_flops = (2 * w.batch * (ctx + chunk) * w.n_kv_heads * w.head_dim * w.value_rank
+                   if rec else 0)
     gemm_flops = 2 * w.batch * chunk * w.hidden * (w.n_kv_heads * w.key_rank + w.value_rank)
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     res = {
@@ -374,19 +390,25 @@ def run_prefill(args, w, torch, sk, synth):
                    "head_dim": w.head_dim, "key_rank": w.key_rank,
                    "value_rank": w.value_rank,
                    "cache": cache_label(w)},
-        "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel",
+        "roofline": {"bound": "mfma",
+                     "kernel": "prefill_attn_rec_kernel" if rec else "prefill_attn_kernel",
                      "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS,
                      "traffic": None if rope else prefill_traffic_from_counters(w, ctx, chunk)},
+        # prepasses: the keys and queries of the scores (and, when the values
+        # are reconstructed, their dequantization and reconstruction GEMM);
+        # up_projection: empty when the attention writes d_h-wide rows
+        "values": "reconstructed" if rec else "joint latent",
         "kernels_ms": {"gemm": mean(kern[0]), "append": mean(kern[1]),
-                       "qproj": mean(kern[2]), "attention": attn_ms,
-                       "merge_vproj": mean(kern[4])},
+                       "prepasses": mean(kern[2]), "attention": attn_ms,
+                       "up_projection": mean(kern[4])},
         # the latent projection Z = X A (Algorithm 2, step 1) on MFMA
         "projection_gemm_mfma": {
             "flop": gemm_flops,
             "tflops": gemm_flops / (mean(kern[0]) * 1e-3) / 1e12,
             "frac": gemm_flops / (mean(kern[0]) * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS},
-        "algorithmic_flops": {"attention": attn_flops, "projection": gemm_flops},
+        "algorithmic_flops": {"attention": attn_flops, "projection": gemm_flops,
+                              "value_reconstruction": recon_flops},
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)

@@ -433,10 +433,19 @@ STARKV_API size_t starkv_noalloc_scratch_bytes(void);
  * section 5.3, Algorithm 2 steps 4b-4c) the keys of every visible position
  * are reconstructed from the stored latents (k = B_key[g] z) and rotated at
  * their positions, query i is rotated at ctx_len + i, and the scores run
- * over d_h channels; the values are not rotated.  Workspace:
+ * over d_h channels; the values are not rotated.  The values enter in one
+ * of eq. 12's two orders, chosen from the shape alone: when
+ * C * Hq * (R_v - d_h) > Hkv * d_h * R_v and d_h is 64 or 128, the values of
+ * every visible position are reconstructed once per call (Z_v B_value^T per
+ * KV head, fp16) and the attention contracts over d_h, writing out
+ * directly; otherwise it contracts the probabilities with the joint value
+ * latent and up-projects (the decode order).  Workspace:
  * starkv_workspace_bytes(cfg, PREFILL, C) (with rotary keys it holds fp16
  * keys of d_h channels for every position, B * max_tokens * Hkv * d_h * 2
- * bytes, instead of the 32-channel latents).
+ * bytes, instead of the 32-channel latents; with reconstructed values, the
+ * fp16 values B * max_tokens * Hkv * d_h * 2 bytes and the fp16 value
+ * latents B * max_tokens * R_v * 2 bytes instead of the fp32 partial rows
+ * B * C * Hq * R_v * 4 bytes).
  * Errors: EINVAL, ECAPACITY (ctx_len + C > max_tokens), EWORKSPACE,
  * ELAUNCH; EUNSUPPORTED unless the cache is Q43 with r_k = 32, Hq / Hkv in
  * {1, 2, 4, 8}, R_v a multiple of 256 up to 1024, D a multiple of 64, and
