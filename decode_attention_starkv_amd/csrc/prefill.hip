@@ -1133,31 +1133,32 @@ struct RecArgs {
   float* out;             // [B*C][Hq][d_h]
 };
 
-// Workgroup = (128 / G consecutive queries, the G query heads of one KV head
-// g, sequence b), 8 waves; rows of the stacked P tile: row = query * G +
-// head (128).  Wave w scores query head w % G for queries 16 (w / G) .. + 15
-// exactly as prefill_attn_kernel does (keys of DK channels, lazy online
-// softmax, fp16 P slot), then contracts P with the KV head's reconstructed
-// values on MFMA 32x32x16: row tile w % 4, channel tiles (w / 4) TPW ..
-// + TPW - 1 of 32 (d_h = 64 TPW); a step takes positions 16 s + 8 j .. + 7 in
-// k-slot j.  Keys (two tiles ahead) and value tiles (one ahead) reach LDS
+// Workgroup = (16 NW / G consecutive queries, the G query heads of one KV
+// head g, sequence b), NW waves; rows of the stacked P tile: row = query * G
+// + head (16 NW).  Wave w scores query head w % G for queries 16 (w / G) ..
+// + 15 exactly as prefill_attn_kernel does (keys of DK channels, lazy
+// online softmax, fp16 P slot), then contracts P with the KV head's
+// reconstructed values on MFMA 32x32x16: row tile w % (NW / 2), channel
+// tiles TPW (w / (NW / 2)) .. + TPW - 1 of 32 (d_h = 64 TPW); a step takes
+// positions 16 s + 8 j .. + 7 in k-slot j.  Keys (two tiles ahead) and value tiles (one ahead) reach LDS
 // by direct-to-LDS loads; one barrier per tile.  The rows are divided by
 // their softmax denominators and written to out: no partial rows, no
 // up-projection.
-template <int G, int DK, int TPW>
-__global__ __launch_bounds__(512) void prefill_attn_rec_kernel(RecArgs a) {
-  constexpr int PH = G, PQ = kRows / G;
+template <int G, int DK, int TPW, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
+  constexpr int ROWS = 16 * NW;           // stacked rows: 16 per wave
+  constexpr int PH = G, PQ = ROWS / G;
   constexpr int CPT = DK / 8;             // 16-byte chunks per key row
   constexpr int TPP = 1024 / (DK * 2);    // key rows per 1 KB staging piece
   constexpr int KS = DK / 32;             // K steps of a score MFMA
   constexpr int DH = 64 * TPW;            // d_h
   auto swz = [](int u) { return (u / (16 / CPT)) & (CPT - 1); };
   const Dims& d = a.d;
-  __shared__ __attribute__((aligned(16))) _Float16 p_l[2][kRows * kPS];
+  __shared__ __attribute__((aligned(16))) _Float16 p_l[2][ROWS * kPS];
   __shared__ __attribute__((aligned(16))) uint8_t key_l[2][kTile * DK * 2];
   __shared__ __attribute__((aligned(16))) _Float16 v_l[2][DH * kTile];
-  __shared__ __attribute__((aligned(16))) float alpha_l[2][kRows];
-  __shared__ float l_l[kRows];
+  __shared__ __attribute__((aligned(16))) float alpha_l[2][ROWS];
+  __shared__ float l_l[ROWS];
   __shared__ int flag_l[2];
 
   // XCD-aware order: the KV heads of one query block run on one XCD; the
@@ -1269,7 +1270,7 @@ __global__ __launch_bounds__(512) void prefill_attn_rec_kernel(RecArgs a) {
     if (kt <= tile_last) {
       const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kd) +
           (((size_t)b * d.Tmax + (size_t)kt * kTile) * d.Hkv + g) * (DK * 2);
-      for (int p = wave; p < nkp; p += 8) {
+      for (int p = wave; p < nkp; p += NW) {
         const int u = p * TPP + key_tl;
         dma(kbase + (size_t)u * d.Hkv * (DK * 2) + ((key_pos ^ swz(u)) << 4),
             &key_l[kt & 1][p * 1024]);
@@ -1279,13 +1280,14 @@ __global__ __launch_bounds__(512) void prefill_attn_rec_kernel(RecArgs a) {
       const uint8_t* vbase =
           reinterpret_cast<const uint8_t*>(a.vt + vrec_index(d, b, g, ct * kTile, 0)) + lane * 16;
       uint8_t* vdst = reinterpret_cast<uint8_t*>(&v_l[ct & 1][0]);
-      for (int p = nkp + ((wave - nkp) & 7); p < nkp + nvp; p += 8)
+      for (int p = nkp + ((wave - nkp) & (NW - 1)); p < nkp + nvp; p += NW)
         dma(vbase + (p - nkp) * 1024, vdst + (p - nkp) * 1024);
     }
   };
 
   // -------------------------------------------------------- value contraction
-  const int rt = wave & 3, ct0 = (wave >> 2) * TPW;
+  // row tile wave % (NW / 2), channel tiles of the wave's half of d_h
+  const int rt = wave % (NW / 2), ct0 = (wave / (NW / 2)) * TPW;
   f32x16 acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = f32x16{};
@@ -1375,24 +1377,28 @@ hipError_t launch_attn(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t
   }
 }
 
-template <int DK, int TPW>
+template <int DK, int TPW, int NW>
 hipError_t launch_rec_dk(const Dims& d, dim3 grid, const RecArgs& ra, hipStream_t s) {
   switch (d.G) {
-    case 1: prefill_attn_rec_kernel<1, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
-    case 2: prefill_attn_rec_kernel<2, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
-    case 4: prefill_attn_rec_kernel<4, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
-    case 8: prefill_attn_rec_kernel<8, DK, TPW><<<grid, 512, 0, s>>>(ra); break;
+    case 1: prefill_attn_rec_kernel<1, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
+    case 2: prefill_attn_rec_kernel<2, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
+    case 4: prefill_attn_rec_kernel<4, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
+    case 8: prefill_attn_rec_kernel<8, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
 
+// Waves of a reconstructed-value attention workgroup: 16 (256 rows) where a
+// wave fits in 128 VGPRs (four waves per SIMD), else 8
+int rec_waves(const Dims& d) { return attn_key_width(d) == 128 ? 8 : 16; }
+
 hipError_t launch_rec(const Dims& d, dim3 grid, const RecArgs& ra, hipStream_t s) {
   const int dk = attn_key_width(d);
-  if (dk == 32 && d.dh == 64) return launch_rec_dk<32, 1>(d, grid, ra, s);
-  if (dk == 32 && d.dh == 128) return launch_rec_dk<32, 2>(d, grid, ra, s);
-  if (dk == 64 && d.dh == 64) return launch_rec_dk<64, 1>(d, grid, ra, s);
-  if (dk == 128 && d.dh == 128) return launch_rec_dk<128, 2>(d, grid, ra, s);
+  if (dk == 32 && d.dh == 64) return launch_rec_dk<32, 1, 16>(d, grid, ra, s);
+  if (dk == 32 && d.dh == 128) return launch_rec_dk<32, 2, 16>(d, grid, ra, s);
+  if (dk == 64 && d.dh == 64) return launch_rec_dk<64, 1, 16>(d, grid, ra, s);
+  if (dk == 128 && d.dh == 128) return launch_rec_dk<128, 2, 8>(d, grid, ra, s);
   return hipErrorNotSupported;
 }
 
@@ -1546,7 +1552,8 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
     ra.d = d;
     ra.ctx = ctx_len;
     ra.chunk = chunk;
-    ra.n_qb = (chunk + kRows / d.G - 1) / (kRows / d.G);
+    const int pq = 16 * rec_waves(d) / d.G;   // queries per workgroup
+    ra.n_qb = (chunk + pq - 1) / pq;
     ra.n_qb_pad = (ra.n_qb + 7) / 8 * 8;
     ra.qn = qn;
     ra.kd = kd;
