@@ -973,12 +973,17 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(AttnArgs a) {
 
 // Element (sequence b, KV head g, position t, channel c) of the
 // reconstructed values: per (b, g, 64-position tile) d_h rows of 64
-// positions (fp16), the 16-byte chunk q (positions 8q .. 8q + 7) of channel c
-// at chunk q ^ ((c >> 1) & 7) of its row, so that an operand read of 16
-// channels at one chunk touches every LDS bank once.
+// positions (fp16).  Within a row, position 32 k + 16 h + 4 q + e (h < 2,
+// q < 4, e < 4) sits in 16-byte chunk 4 k + q at half h: a chunk holds the
+// eight positions one lane of the attention's value operand takes (the
+// k-slots of a score MFMA's output).  Chunk p of channel c is stored at
+// chunk p ^ ((c >> 1) & 7), so that an operand read of 16 channels touches
+// every LDS bank once.
 __host__ __device__ inline size_t vrec_index(const Dims& d, int b, int g, int t, int c) {
+  const int u = t % kTile, r = u & 31;
+  const int chunk = 4 * (u >> 5) + ((r >> 2) & 3);
   return ((((size_t)b * d.Hkv + g) * d.NT + t / kTile) * d.dh + c) * kTile +
-         ((((t % kTile) >> 3) ^ ((c >> 1) & 7)) << 3) + (t & 7);
+         ((chunk ^ ((c >> 1) & 7)) << 3) + 4 * (r >> 4) + (r & 3);
 }
 
 // Value latents of positions [0, n) of every sequence, dequantized from the
@@ -1044,8 +1049,9 @@ __global__ __launch_bounds__(256) void value_dequant_kernel(const uint8_t* __res
 // [0, 64 ceil(n / 64)) (zeros past n: those rows of Zv read as zero).  Both
 // operands are read with the reduction index contiguous: Zv [T][R_v] and
 // (B_v H) [Hkv d_h][R_v].  Workgroup tile 128 positions x 128 channels, four
-// waves in 2 x 2, K steps of 32 through LDS.
-constexpr int kRS = 32 + 8;   // LDS row stride (fp16): 16-row reads hit 16 bank groups
+// waves in 2 x 2, K steps of 64 through LDS.
+constexpr int kRK = 64;       // K step
+constexpr int kRS = kRK + 8;  // LDS row stride (fp16): 16-row reads hit 16 bank groups
 __global__ __launch_bounds__(256) void value_recon_kernel(const _Float16* __restrict__ zv,
                                                           const _Float16* __restrict__ bvh,
                                                           Dims d, int n,
@@ -1063,13 +1069,13 @@ __global__ __launch_bounds__(256) void value_recon_kernel(const _Float16* __rest
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
-  // one K step: 128 rows x 32 channels of each operand = 512 runs of 16 B
-  u32x4 ar[2], br[2];
+  // one K step: 128 rows x 64 channels of each operand = 1024 runs of 16 B
+  u32x4 ar[4], br[4];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int c = tid + i * 256;
-      const int r = c >> 2, kc = (c & 3) * 8;
+      const int r = c >> 3, kc = (c & 7) * 8;
       const int t = t0 + r, col = n0 + r;
       ar[i] = t < n ? *reinterpret_cast<const u32x4*>(zv + ((size_t)b * d.Tmax + t) * K + k0 + kc)
                     : u32x4{0u, 0u, 0u, 0u};
@@ -1078,19 +1084,19 @@ __global__ __launch_bounds__(256) void value_recon_kernel(const _Float16* __rest
     }
   };
   load(0);
-  for (int k0 = 0; k0 < K; k0 += 32) {
+  for (int k0 = 0; k0 < K; k0 += kRK) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int c = tid + i * 256;
-      const int r = c >> 2, kc = (c & 3) * 8;
+      const int r = c >> 3, kc = (c & 7) * 8;
       *reinterpret_cast<u32x4*>(&as[r * kRS + kc]) = ar[i];
       *reinterpret_cast<u32x4*>(&bs[r * kRS + kc]) = br[i];
     }
     __syncthreads();
-    if (k0 + 32 < K) load(k0 + 32);
+    if (k0 + kRK < K) load(k0 + kRK);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kRK / 16; ++s) {
       h8 af[2], bf[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
@@ -1105,7 +1111,8 @@ __global__ __launch_bounds__(256) void value_recon_kernel(const _Float16* __rest
     }
   }
   // lane (m, j): channel column m of its tiles; registers 4q .. 4q + 3 are
-  // positions 8q + 4j .. + 3 of the tile: one 8-byte store each
+  // positions 8q + 4j .. + 3 of the tile, adjacent in vrec_index order: one
+  // 8-byte store each
 #pragma unroll
   for (int y = 0; y < 2; ++y) {
     const int col = n0 + wn * 64 + y * 32 + m;
@@ -1134,32 +1141,30 @@ struct RecArgs {
 };
 
 // Workgroup = (16 NW / G consecutive queries, the G query heads of one KV
-// head g, sequence b), NW waves; rows of the stacked P tile: row = query * G
-// + head (16 NW).  Wave w scores query head w % G for queries 16 (w / G) ..
-// + 15 exactly as prefill_attn_kernel does (keys of DK channels, lazy
-// online softmax, fp16 P slot), then contracts P with the KV head's
-// reconstructed values on MFMA 32x32x16: row tile w % (NW / 2), channel
-// tiles TPW (w / (NW / 2)) .. + TPW - 1 of 32 (d_h = 64 TPW); a step takes
-// positions 16 s + 8 j .. + 7 in k-slot j.  Keys (two tiles ahead) and value tiles (one ahead) reach LDS
-// by direct-to-LDS loads; one barrier per tile.  The rows are divided by
-// their softmax denominators and written to out: no partial rows, no
-// up-projection.
-template <int G, int DK, int TPW, int NW>
+// head g, sequence b), NW waves.  Wave w owns query head w % G for queries
+// 16 (w / G) .. + 15 from end to end: it scores them as prefill_attn_kernel
+// does (MFMA 16x16x32 over DK key channels, keys as the A operand, lazy
+// online softmax), keeps the probabilities in registers and contracts them
+// with the KV head's reconstructed values on MFMA 16x16x32 (DH / 16 channel
+// tiles, two K steps of 32 positions per tile).  A score MFMA leaves a lane
+// four consecutive positions 16 bl + 4 g16 .. + 3 of query c16: those of
+// blocks 2k and 2k + 1 are the lane's eight k-values of K step k (A
+// operand), and the value operand takes the same positions in the same
+// k-slots (two 8-byte reads).  Waves share only the staging: keys and value
+// tiles reach LDS by direct-to-LDS loads one tile ahead, one barrier per
+// tile.  The rows are divided by their softmax denominators and written to
+// out: no partial rows, no up-projection.
+template <int G, int DK, int DH, int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
-  constexpr int ROWS = 16 * NW;           // stacked rows: 16 per wave
-  constexpr int PH = G, PQ = ROWS / G;
+  constexpr int PH = G, PQ = 16 * NW / G;
   constexpr int CPT = DK / 8;             // 16-byte chunks per key row
   constexpr int TPP = 1024 / (DK * 2);    // key rows per 1 KB staging piece
   constexpr int KS = DK / 32;             // K steps of a score MFMA
-  constexpr int DH = 64 * TPW;            // d_h
+  constexpr int NCT = DH / 16;            // channel tiles of the contraction
   auto swz = [](int u) { return (u / (16 / CPT)) & (CPT - 1); };
   const Dims& d = a.d;
-  __shared__ __attribute__((aligned(16))) _Float16 p_l[2][ROWS * kPS];
   __shared__ __attribute__((aligned(16))) uint8_t key_l[2][kTile * DK * 2];
   __shared__ __attribute__((aligned(16))) _Float16 v_l[2][DH * kTile];
-  __shared__ __attribute__((aligned(16))) float alpha_l[2][ROWS];
-  __shared__ float l_l[ROWS];
-  __shared__ int flag_l[2];
 
   // XCD-aware order: the KV heads of one query block run on one XCD; the
   // query blocks with the longest causal span start first
@@ -1177,16 +1182,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m = lane & 31, j = lane >> 5;
   const int c16 = lane & 15, g16 = lane >> 4;
-  if (tid < 2) flag_l[tid] = -1;
-  __syncthreads();
 
   // ------------------------------------------------------------ score setup
   const int hl = wave % PH, qs = wave / PH;
   const int h = g * G + hl;
-  const int qi = 16 * qs + c16;
-  const int R = qi * PH + hl;
+  const int qw = 16 * qs;                       // the wave's first query
+  const int qi = qw + c16;                      // the lane's query (scores)
   h8 bq[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -1194,16 +1196,54 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
                            a.qn + (((size_t)b * a.chunk + q0 + qi) * d.Hq + h) * DK + 32 * ks +
                            8 * g16)
                      : h8{};
+  // lazy softmax state of query qi (the same in its four lanes); the running
+  // max starts finite so that exp2(x - m) needs no guard
   float m_ref = -1e30f, l_lane = 0.0f;
-  auto p_at = [&](int slot, int R, int u) -> _Float16* {
-    return &p_l[slot][R * kPS + (((u >> 3) ^ (R >> 5)) << 3) + (u & 7)];
-  };
   const int key_lane = c16 * (DK * 2);
   auto key_at = [&](int slot, int bl, int ks) {
     return *reinterpret_cast<const h8*>(
         &key_l[slot][key_lane + bl * 16 * (DK * 2) + (((4 * ks + g16) ^ swz(c16)) << 4)]);
   };
-  auto score = [&](int tile, int it, int slot) {
+  // value operand of K step kk for channel c: positions 32 kk + 4 g16 .. + 3
+  // and 32 kk + 16 + 4 g16 .. + 3, one chunk (4 kk + g16) of the row
+  auto v_at = [&](int slot, int c, int kk) {
+    return *reinterpret_cast<const h8*>(
+        &v_l[slot][c * kTile + (((4 * kk + g16) ^ ((c >> 1) & 7)) << 3)]);
+  };
+
+  // ---------------------------------------------------------------- staging
+  const int key_tl = lane / CPT, key_pos = lane % CPT;
+  auto dma = [&](const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  constexpr int nkp = CPT, nvp = DH / 8;
+  auto stage = [&](int t) {   // keys and values of tile t into slot t & 1
+    if (t > tile_last) return;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kd) +
+        (((size_t)b * d.Tmax + (size_t)t * kTile) * d.Hkv + g) * (DK * 2);
+    for (int p = wave; p < nkp; p += NW) {
+      const int u = p * TPP + key_tl;
+      dma(kbase + (size_t)u * d.Hkv * (DK * 2) + ((key_pos ^ swz(u)) << 4),
+          &key_l[t & 1][p * 1024]);
+    }
+    const uint8_t* vbase =
+        reinterpret_cast<const uint8_t*>(a.vt + vrec_index(d, b, g, t * kTile, 0)) + lane * 16;
+    uint8_t* vdst = reinterpret_cast<uint8_t*>(&v_l[t & 1][0]);
+    for (int p = nkp + ((wave - nkp) & (NW - 1)); p < nkp + nvp; p += NW)
+      dma(vbase + (p - nkp) * 1024, vdst + (p - nkp) * 1024);
+  };
+
+  f32x4v acc[NCT];
+#pragma unroll
+  for (int t = 0; t < NCT; ++t) acc[t] = f32x4v{};
+
+  stage(0);
+  wait_vmcnt<0>();
+  for (int tile = 0; tile <= tile_last; ++tile) {
+    const int slot = tile & 1;
+    lds_barrier();        // this tile's staging visible; the other slot free
+    stage(tile + 1);
+    // scores of the tile: x[bl][v] = position 16 bl + 4 g16 + v, query qi
     float x[4][4];
 #pragma unroll
     for (int bl = 0; bl < 4; ++bl) {
@@ -1230,124 +1270,61 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
     for (int bl = 0; bl < 4; ++bl)
 #pragma unroll
       for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, x[bl][v]);
-    float alpha = 1.0f;
     if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kLazy) != 0) {
       float gm = fmaxf(tmax, __shfl_xor(tmax, 16));
       gm = fmaxf(gm, __shfl_xor(gm, 32));
-      if (gm > m_ref + kLazy) {
+      float alpha = 1.0f;
+      if (gm > m_ref + kLazy) {        // the same in the query's four lanes
         alpha = __builtin_amdgcn_exp2f(m_ref - gm);
         m_ref = gm;
         l_lane *= alpha;
-        flag_l[slot] = it;
       }
-    }
-    if (lane < 16) alpha_l[slot][R] = alpha;
-    float ls = 0.0f;
-#pragma unroll
-    for (int bl = 0; bl < 4; ++bl) {
-      float p[4];
+      // accumulator rows are queries qw + 4 g16 + v: their alphas sit in
+      // lanes 4 g16 + v
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        p[v] = __builtin_amdgcn_exp2f(x[bl][v] - m_ref);
-        ls += p[v];
+        const float av = __shfl(alpha, 4 * g16 + v);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) acc[t][v] *= av;
       }
-      *reinterpret_cast<h4*>(p_at(slot, R, bl * 16 + 4 * g16)) =
-          h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    }
+    h8 A[2];
+    float ls = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(x[2 * kk + (e >> 2)][e & 3] - m_ref);
+        ls += p[e];
+      }
+      A[kk] = h8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                 (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
     }
     l_lane += ls;
-  };
-
-  // ---------------------------------------------------------------- staging
-  // keys of tile kt (CPT pieces of TPP positions) into key slot kt & 1, the
-  // value tile ct (DH / 8 pieces) into value slot ct & 1; wave w issues the
-  // pieces p with p % 8 == w, keys first
-  const int key_tl = lane / CPT, key_pos = lane % CPT;
-  auto dma = [&](const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-  };
-  constexpr int nkp = CPT, nvp = DH / 8;
-  auto stage = [&](int kt, int ct) {
-    if (kt <= tile_last) {
-      const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kd) +
-          (((size_t)b * d.Tmax + (size_t)kt * kTile) * d.Hkv + g) * (DK * 2);
-      for (int p = wave; p < nkp; p += NW) {
-        const int u = p * TPP + key_tl;
-        dma(kbase + (size_t)u * d.Hkv * (DK * 2) + ((key_pos ^ swz(u)) << 4),
-            &key_l[kt & 1][p * 1024]);
-      }
-    }
-    if (ct <= tile_last) {
-      const uint8_t* vbase =
-          reinterpret_cast<const uint8_t*>(a.vt + vrec_index(d, b, g, ct * kTile, 0)) + lane * 16;
-      uint8_t* vdst = reinterpret_cast<uint8_t*>(&v_l[ct & 1][0]);
-      for (int p = nkp + ((wave - nkp) & (NW - 1)); p < nkp + nvp; p += NW)
-        dma(vbase + (p - nkp) * 1024, vdst + (p - nkp) * 1024);
-    }
-  };
-
-  // -------------------------------------------------------- value contraction
-  // row tile wave % (NW / 2), channel tiles of the wave's half of d_h
-  const int rt = wave % (NW / 2), ct0 = (wave / (NW / 2)) * TPW;
-  f32x16 acc[TPW];
+    // P (16 queries x 64 positions) times the tile's values
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x16{};
-  auto contract = [&](int slot, int it) {
-    if (__builtin_amdgcn_readfirstlane(flag_l[slot]) == it) {
+    for (int t = 0; t < NCT; ++t) {
+      const int c = 16 * t + c16;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float al = alpha_l[slot][rt * 32 + acc_row(v, lane)];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t][v] *= al;
-      }
+      for (int kk = 0; kk < 2; ++kk)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[kk], v_at(slot, c, kk), acc[t], 0, 0, 0);
     }
-    const _Float16* pa = &p_l[slot][(rt * 32 + m) * kPS];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // P row rt * 32 + m, positions 16 s + 8 j: chunk (2 s + j) ^ rt
-      const h8 A = *reinterpret_cast<const h8*>(pa + (((2 * s + j) ^ rt) << 3));
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int c = (ct0 + t) * 32 + m;
-        const h8 B = *reinterpret_cast<const h8*>(
-            &v_l[slot][c * kTile + (((2 * s + j) ^ ((c >> 1) & 7)) << 3)]);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, acc[t], 0, 0, 0);
-      }
-    }
-  };
-
-  stage(0, 0);
-  stage(1, tile_last + 1);
-  wait_vmcnt<0>();
-  __syncthreads();        // keys of tiles 0, 1 and values of tile 0 in LDS
-  score(0, 0, 0);
-  for (int tile = 0; tile <= tile_last; ++tile) {
-    const int cur = tile & 1, nxt = cur ^ 1;
-    lds_barrier();        // P of `tile`, staging of the previous step visible
-    if (tile < tile_last) stage(tile + 2, tile + 1);
-    contract(cur, tile);
-    if (tile < tile_last) {
-      __builtin_amdgcn_sched_barrier(0);
-      score(tile + 1, tile + 1, nxt);
-      wait_vmcnt<0>();    // this wave's staging landed
-    }
+    wait_vmcnt<0>();      // this wave's staging of the next tile landed
   }
 
   // ---------------------------------------------------------------- output
-  {
-    float l = l_lane + __shfl_xor(l_lane, 16);
-    l += __shfl_xor(l, 32);
-    if (lane < 16) l_l[R] = l;
-  }
-  __syncthreads();
+  float l = l_lane + __shfl_xor(l_lane, 16);
+  l += __shfl_xor(l, 32);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int rr = rt * 32 + acc_row(v, lane);
-    const int rq = rr / PH, hh = rr % PH;
+  for (int v = 0; v < 4; ++v) {
+    const int rq = qw + 4 * g16 + v;            // this register's query
+    const float lv = __shfl(l, 4 * g16 + v);
     if (rq < nq) {
-      const float inv = 1.0f / l_l[rr];
-      float* o = a.out + (((size_t)b * a.chunk + q0 + rq) * d.Hq + g * G + hh) * DH;
+      const float inv = 1.0f / lv;
+      float* o = a.out + (((size_t)b * a.chunk + q0 + rq) * d.Hq + h) * DH;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) o[(ct0 + t) * 32 + m] = acc[t][v] * inv;
+      for (int t = 0; t < NCT; ++t) o[16 * t + c16] = acc[t][v] * inv;
     }
   }
 }
@@ -1377,28 +1354,28 @@ hipError_t launch_attn(const Dims& d, dim3 grid, const AttnArgs& aa, hipStream_t
   }
 }
 
-template <int DK, int TPW, int NW>
+template <int DK, int DH, int NW>
 hipError_t launch_rec_dk(const Dims& d, dim3 grid, const RecArgs& ra, hipStream_t s) {
   switch (d.G) {
-    case 1: prefill_attn_rec_kernel<1, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
-    case 2: prefill_attn_rec_kernel<2, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
-    case 4: prefill_attn_rec_kernel<4, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
-    case 8: prefill_attn_rec_kernel<8, DK, TPW, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
+    case 1: prefill_attn_rec_kernel<1, DK, DH, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
+    case 2: prefill_attn_rec_kernel<2, DK, DH, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
+    case 4: prefill_attn_rec_kernel<4, DK, DH, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
+    case 8: prefill_attn_rec_kernel<8, DK, DH, NW><<<grid, 64 * NW, 0, s>>>(ra); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
 
-// Waves of a reconstructed-value attention workgroup: 16 (256 rows) where a
-// wave fits in 128 VGPRs (four waves per SIMD), else 8
-int rec_waves(const Dims& d) { return attn_key_width(d) == 128 ? 8 : 16; }
+// Waves of a reconstructed-value attention workgroup (16 rows each): 16,
+// four per SIMD (every variant fits 128 VGPRs)
+int rec_waves(const Dims&) { return 16; }
 
 hipError_t launch_rec(const Dims& d, dim3 grid, const RecArgs& ra, hipStream_t s) {
   const int dk = attn_key_width(d);
-  if (dk == 32 && d.dh == 64) return launch_rec_dk<32, 1, 16>(d, grid, ra, s);
-  if (dk == 32 && d.dh == 128) return launch_rec_dk<32, 2, 16>(d, grid, ra, s);
-  if (dk == 64 && d.dh == 64) return launch_rec_dk<64, 1, 16>(d, grid, ra, s);
-  if (dk == 128 && d.dh == 128) return launch_rec_dk<128, 2, 8>(d, grid, ra, s);
+  if (dk == 32 && d.dh == 64) return launch_rec_dk<32, 64, 16>(d, grid, ra, s);
+  if (dk == 32 && d.dh == 128) return launch_rec_dk<32, 128, 16>(d, grid, ra, s);
+  if (dk == 64 && d.dh == 64) return launch_rec_dk<64, 64, 16>(d, grid, ra, s);
+  if (dk == 128 && d.dh == 128) return launch_rec_dk<128, 128, 16>(d, grid, ra, s);
   return hipErrorNotSupported;
 }
 
