@@ -445,7 +445,9 @@ STARKV_API size_t starkv_noalloc_scratch_bytes(void);
  * bytes, instead of the 32-channel latents; with reconstructed values, the
  * fp16 values B * max_tokens * Hkv * d_h * 2 bytes and the fp16 value
  * latents B * max_tokens * R_v * 2 bytes instead of the fp32 partial rows
- * B * C * Hq * R_v * 4 bytes).
+ * B * C * Hq * R_v * 4 bytes).  Because the two orders need different
+ * buffers, the size is not monotone in C: query it for every chunk length
+ * a caller uses (or take the largest over them).
  * Errors: EINVAL, ECAPACITY (ctx_len + C > max_tokens), EWORKSPACE,
  * ELAUNCH; EUNSUPPORTED unless the cache is Q43 with r_k = 32, Hq / Hkv in
  * {1, 2, 4, 8}, R_v a multiple of 256 up to 1024, D a multiple of 64, and

@@ -400,3 +400,22 @@ def test_call_validation_before_any_hip_call():
         assert sk.starkv_cache_bytes(c, 0) > 0
         assert lib.starkv_prefill(ctypes.byref(c), cc, 0, 64, *pargs, 0x8000, 1 << 34,
                                   None) == sk.STARKV_EUNSUPPORTED, dh
+
+
+def test_prefill_workspace_follows_the_value_order():
+    """The prefill's workspace per chunk length follows the value order it
+    takes: fp32 partial rows (C Hq R_v 4 bytes) below the reconstruction
+    threshold, position-sized value buffers above it (host only)."""
+    w = synth.WORKLOADS["longchat_prefill"]
+    cfg = _cfg(w)
+    thr = w.n_kv_heads * w.head_dim * w.value_rank // (w.n_q_heads * (w.value_rank - w.head_dim))
+    below = sk.starkv_workspace_bytes(cfg, sk.OP_PREFILL, thr)        # joint latent
+    above = sk.starkv_workspace_bytes(cfg, sk.OP_PREFILL, thr + 1)    # reconstructed
+    assert below > 0 and above > 0
+    part_rows = w.batch * thr * w.n_q_heads * w.value_rank * 4
+    values = w.batch * w.max_tokens * w.n_kv_heads * w.head_dim * 2
+    assert below >= part_rows
+    assert above >= values
+    # the full chunk reconstructs: no C-sized fp32 partial rows
+    full = sk.starkv_workspace_bytes(cfg, sk.OP_PREFILL, w.chunk)
+    assert full < w.batch * w.chunk * w.n_q_heads * w.value_rank * 4
