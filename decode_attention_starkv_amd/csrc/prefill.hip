@@ -270,11 +270,23 @@ __global__ __launch_bounds__(256) void rope_key_kernel(const uint8_t* __restrict
   const int i = tid % half, grp = tid / half, ngrp = 256 / half;
   const int rank = d.krank[g];
   const double w = rope_freq(i, d.dh, log2_theta);
+  // rows i and i + d_h/2 of B_key[g] (32 bf16 each): four 16-byte loads per row
   float b1[32], b2[32];
+  {
+    const u32x4* r1 = reinterpret_cast<const u32x4*>(bk + ((size_t)g * d.dh + i) * 32);
+    const u32x4* r2 = reinterpret_cast<const u32x4*>(bk + ((size_t)g * d.dh + i + half) * 32);
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    b1[c] = c < rank ? bf16v(bk[((size_t)g * d.dh + i) * 32 + c]) : 0.0f;
-    b2[c] = c < rank ? bf16v(bk[((size_t)g * d.dh + i + half) * 32 + c]) : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 w1 = r1[q], w2 = r2[q];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * q + e;
+        const uint32_t h1 = (w1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t h2 = (w2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        b1[c] = c < rank ? bf16v(h1) : 0.0f;
+        b2[c] = c < rank ? bf16v(h2) : 0.0f;
+      }
+    }
   }
   for (int u = grp; u < kTile; u += ngrp) {
     const int t = t0 + u;
