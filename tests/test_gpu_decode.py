@@ -154,3 +154,27 @@ def test_q43_shapes(kw):
     counts of the split kernel, with a ragged tail and a peaked softmax."""
     err, _ = run_case("l3_gqa_q43", 333, q_scale=4.0, **kw)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("name,batch,splits,kw", [
+    # one sequence; weights of splits past the first 64 lanes
+    ("l2_q43", 1, 70, dict()),
+    # three sequences, value rank 512
+    ("l2_q43", 3, 20, dict(value_rank=512)),
+    # nine sequences, value rank 768
+    ("l2_q43", 9, 5, dict(n_q_heads=8, n_kv_heads=8, value_rank=768)),
+    # d_h 64
+    ("l2_q43", 5, 12, dict(n_q_heads=8, n_kv_heads=8, head_dim=64, value_rank=512)),
+    # 256 and 257 splits (splits dealt out among 4 waves per channel block)
+    ("l2_q43", 2, 256, dict(n_q_heads=8, n_kv_heads=8, value_rank=512)),
+    ("l2_q43", 2, 257, dict(n_q_heads=8, n_kv_heads=8, value_rank=512)),
+    # bf16 cache (no rotation), value rank 1024, three sequences
+    ("l2_bf16", 3, 33, dict()),
+])
+def test_wide_value_merge(name, batch, splits, kw):
+    """Merge and up-projection for value ranks 512, 768 and 1024: batches
+    that fill no multiple of 4 or 8 sequences, both head sizes, and split
+    counts from 5 to 257 (one tile per split)."""
+    # one tile per split (the last one ragged), so the split count is exact
+    err, _ = run_case(name, 64 * splits - 7, batch=batch, num_splits=splits, q_scale=4.0, **kw)
+    assert err <= TOL
