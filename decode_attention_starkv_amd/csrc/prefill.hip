@@ -1178,12 +1178,22 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t key_l[2][kTile * DK * 2];
   __shared__ __attribute__((aligned(16))) _Float16 v_l[2][DH * kTile];
 
-  // XCD-aware order: the KV heads of one query block run on one XCD; the
-  // query blocks with the longest causal span start first
+  // XCD-aware order (workgroup L runs on XCD L mod 8), the query blocks
+  // with the longest causal span first.  With a multiple of 8 KV heads, XCD
+  // x takes heads x, x + 8, .., one after the other, each with all of its
+  // query blocks: the workgroups that run on an XCD at the same time stream
+  // the same key and value tiles through its L2.  Otherwise the KV heads of
+  // one query block share an XCD.
   const int L = blockIdx.x;
   const int xcd = L & 7, k = L >> 3;
-  const int g = k % d.Hkv;
-  const int qb = a.n_qb_pad - 1 - ((k / d.Hkv) * 8 + xcd);
+  int g, qb;
+  if (d.Hkv % 8 == 0) {
+    g = (k / a.n_qb_pad) * 8 + xcd;
+    qb = a.n_qb_pad - 1 - k % a.n_qb_pad;
+  } else {
+    g = k % d.Hkv;
+    qb = a.n_qb_pad - 1 - ((k / d.Hkv) * 8 + xcd);
+  }
   if (qb >= a.n_qb) return;   // padding workgroup; uniform, before any barrier
   const int b = blockIdx.y;
   const int q0 = qb * PQ;
