@@ -27,8 +27,8 @@ namespace {
 
 // ------------------------------------------------------------------- gemm --
 
-// Z[mat] [M][N] = X [M][D] * A[mat] [D][N], bf16 x bf16 -> fp32.  blockIdx.z
-// selects the key or the value projection.  Workgroup tile 128 x 128, four
+// Z[mat] [M][N] = X [M][D] * A[mat] [D][N], bf16 x bf16 -> fp32, mat = the
+// key or the value projection.  Workgroup tile 128 x 128, four
 // waves in 2 x 2, each 2 x 2 MFMA 32x32x16 tiles; K steps of 32 staged
 // through LDS.  X tiles are read as 16-byte k-runs; A is kept k-major in LDS
 // and a lane gathers its 8 k-values of one column with 2-byte reads.
@@ -38,6 +38,7 @@ struct GemmArgs {
   float* z[2];
   float* zdbg;       // optional [M][ldd] copy of both outputs side by side
   int M, D, N[2], off[2], ldd;
+  int nx, ny;        // column tiles (of the wider projection) and row tiles
 };
 constexpr int kGT = 128;          // workgroup tile (rows and columns)
 constexpr int kGK = 32;           // K step
@@ -47,10 +48,17 @@ constexpr int kGAS = kGT + 8;     // A tile row stride (bf16)
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kGT * kGXS];
   __shared__ __attribute__((aligned(16))) uint16_t as[kGK * kGAS];
-  const int mat = blockIdx.z;
+  // XCD-aware order (workgroup L runs on XCD L mod 8): every column tile of
+  // both projections for one block of 128 rows runs on one XCD, so that
+  // XCD fetches those rows of X once (row blocks padded to a multiple of 8)
+  const int L = blockIdx.x, xcd = L & 7, k = L >> 3;
+  const int per_row = 2 * g.nx;
+  const int yb = 8 * (k / per_row) + xcd;
+  const int mat = (k % per_row) / g.nx;
   const int N = g.N[mat];
-  const int m0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
-  if (n0 >= N) return;   // the other projection is wider; uniform exit
+  const int m0 = yb * kGT, n0 = (k % g.nx) * kGT;
+  // past the last row block, or the other projection is wider: uniform exit
+  if (yb >= g.ny || n0 >= N) return;
   const uint16_t* A = g.a[mat];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -1483,7 +1491,9 @@ hipError_t launch_prefill(const Dims& d, const starkv_cache& cache, int ctx_len,
   ga.off[1] = d.Hkv * d.rk;
   ga.ldd = d.Hkv * d.rk + d.rv;
   const int nmax = ga.N[0] > ga.N[1] ? ga.N[0] : ga.N[1];
-  gemm_bf16_kernel<<<dim3((nmax + kGT - 1) / kGT, (M + kGT - 1) / kGT, 2), 256, 0, s>>>(ga);
+  ga.nx = (nmax + kGT - 1) / kGT;
+  ga.ny = (M + kGT - 1) / kGT;
+  gemm_bf16_kernel<<<(unsigned)(2 * ga.nx * ((ga.ny + 7) / 8 * 8)), 256, 0, s>>>(ga);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(1);
