@@ -5,7 +5,7 @@ One step = one decode step of the whole hot path for a batch of sequences:
 one starkv_decode_step call -- the append of the step's new token (quantize +
 pack, n = 1 per sequence) and the decode over seq_len cached tokens (query
 projection, split scores + online softmax + MFMA P.Z_v, split merge, value
-up-projection); the append and the query projection share one launch.
+up-projection); the append and the query projection share one launch (every cache kind but rotary keys).
 
 Default workload: B = 16 sequences, T = 32768 cached tokens, LLaMA-2-7B-shaped
 (32 heads, d_h 128, key rank 32 per head, joint value rank 1024), 4/3-bit

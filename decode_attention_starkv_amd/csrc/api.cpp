@@ -247,6 +247,10 @@ static int decode_step_impl(const starkv_config* cfg, const starkv_cache* cache,
       e = launch_append_qproj(d, *cache, z_key, z_value, pos, n, q, B_key,
                               sm_scale * 1.4426950408889634f, ws + lay.qt, stream);
       fused = true;
+    } else if (d.dtype != STARKV_CACHE_Q43) {
+      e = launch_append_qproj_plain(d, *cache, z_key, z_value, pos, n, q, B_key,
+                                    sm_scale * 1.4426950408889634f, ws + lay.qt, stream);
+      fused = true;
     } else {
       e = launch_append(d, *cache, z_key, z_value, pos, n, stream);
     }

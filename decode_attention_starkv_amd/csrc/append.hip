@@ -85,11 +85,12 @@ __device__ inline uint16_t bf16_bits_rn(float x) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// One element of the appended keys / values per thread (idx over the
+// z_key / z_value rows of the new tokens).
 template <bool kBf16>
-__global__ void append_plain_keys(const float* __restrict__ zk, void* key,
-                                  Dims d, int pos, int n) {
+__device__ inline void plain_key_elem(const float* __restrict__ zk, void* key,
+                                      const Dims& d, int pos, int n, size_t idx) {
   size_t total = (size_t)d.B * n * d.Hkv * d.rk;
-  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   int c = idx % d.rk;
   size_t r = idx / d.rk;
@@ -109,10 +110,9 @@ __global__ void append_plain_keys(const float* __restrict__ zk, void* key,
 }
 
 template <bool kBf16>
-__global__ void append_plain_values(const float* __restrict__ zv, void* value,
-                                    Dims d, int pos, int n) {
+__device__ inline void plain_value_elem(const float* __restrict__ zv, void* value,
+                                        const Dims& d, int pos, int n, size_t idx) {
   size_t total = (size_t)d.B * n * d.rv;
-  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   int c = idx % d.rv;
   size_t r = idx / d.rv;
@@ -127,6 +127,18 @@ __global__ void append_plain_values(const float* __restrict__ zv, void* value,
     static_cast<uint16_t*>(value)[dst] = bf16_bits_rn(zv[idx]);
   else
     static_cast<float*>(value)[dst] = zv[idx];
+}
+
+template <bool kBf16>
+__global__ void append_plain_keys(const float* __restrict__ zk, void* key,
+                                  Dims d, int pos, int n) {
+  plain_key_elem<kBf16>(zk, key, d, pos, n, (size_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+template <bool kBf16>
+__global__ void append_plain_values(const float* __restrict__ zv, void* value,
+                                    Dims d, int pos, int n) {
+  plain_value_elem<kBf16>(zv, value, d, pos, n, (size_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // ------------------------------------------------------------------- Q43 --
@@ -407,6 +419,28 @@ __global__ __launch_bounds__(256) void step_q43_kernel(
   append_q43_values(zv, value, vmeta, d, pos, n, cb, rest % tiles, rest / tiles, codes);
 }
 
+// The decode step's first launch for an unquantized cache: blocks
+// [0, key_blocks) append key elements, the next value_blocks blocks value
+// elements, and the last B Hq blocks project the queries.
+template <int FMT>
+__global__ __launch_bounds__(256) void step_plain_kernel(
+    const float* __restrict__ zk, const float* __restrict__ zv, void* key, void* value,
+    Dims d, int pos, int n, int key_blocks, int value_blocks,
+    const void* __restrict__ q, const void* __restrict__ bk, float qscale,
+    void* __restrict__ qt) {
+  constexpr bool kBf = FMT == STARKV_CACHE_BF16;
+  const int blk = blockIdx.x;
+  if (blk < key_blocks) {
+    plain_key_elem<kBf>(zk, key, d, pos, n, (size_t)blk * 256 + threadIdx.x);
+    return;
+  }
+  if (blk < key_blocks + value_blocks) {
+    plain_value_elem<kBf>(zv, value, d, pos, n, (size_t)(blk - key_blocks) * 256 + threadIdx.x);
+    return;
+  }
+  qproj_block<FMT>(q, bk, d, qscale, qt, blk - key_blocks - value_blocks);
+}
+
 }  // namespace
 
 hipError_t launch_append_qproj(const Dims& d, const starkv_cache& cache,
@@ -423,6 +457,23 @@ hipError_t launch_append_qproj(const Dims& d, const starkv_cache& cache,
       zk, zv, static_cast<uint8_t*>(cache.key), static_cast<uint16_t*>(cache.key_meta),
       static_cast<uint8_t*>(cache.value), static_cast<uint16_t*>(cache.value_meta), d,
       pos, n, (int)key_blocks, tiles, (int)append_blocks, q, bk, qscale, qt);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_qproj_plain(const Dims& d, const starkv_cache& cache,
+                                     const float* zk, const float* zv, int pos, int n,
+                                     const void* q, const void* bk, float qscale,
+                                     void* qt, hipStream_t s) {
+  const int T = 256;
+  const size_t kb = ((size_t)d.B * n * d.Hkv * d.rk + T - 1) / T;
+  const size_t vb = ((size_t)d.B * n * d.rv + T - 1) / T;
+  const size_t blocks = kb + vb + (size_t)d.B * d.Hq;
+  if (d.dtype == STARKV_CACHE_BF16)
+    step_plain_kernel<STARKV_CACHE_BF16><<<(unsigned)blocks, T, 0, s>>>(
+        zk, zv, cache.key, cache.value, d, pos, n, (int)kb, (int)vb, q, bk, qscale, qt);
+  else
+    step_plain_kernel<STARKV_CACHE_F32><<<(unsigned)blocks, T, 0, s>>>(
+        zk, zv, cache.key, cache.value, d, pos, n, (int)kb, (int)vb, q, bk, qscale, qt);
   return hipGetLastError();
 }
 

@@ -166,6 +166,11 @@ hipError_t launch_append_qproj(const Dims& d, const starkv_cache& cache,
                                const float* zk, const float* zv, int pos, int n,
                                const void* q, const void* bk, float qscale,
                                void* qt, hipStream_t s);
+// The same for an unquantized (fp32 / bf16) cache.
+hipError_t launch_append_qproj_plain(const Dims& d, const starkv_cache& cache,
+                                     const float* zk, const float* zv, int pos, int n,
+                                     const void* q, const void* bk, float qscale,
+                                     void* qt, hipStream_t s);
 
 // Workspace carve-up of one prefill call (byte offsets, 256-aligned).
 struct PrefillWs {
