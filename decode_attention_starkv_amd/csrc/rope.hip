@@ -10,9 +10,10 @@
 //   A_i = q'_i B_i + q'_{i'} B_{i'},   C_i = q'_{i'} B_i - q'_i B_{i'}   (i' = i + d_h/2),
 // i.e. per token q~_j = Trig_j M (M = [A; C], d_h x r_k per query head) and
 // score_j = q~_j . z_j.  Per call:
-//   rope_trig_kernel   Trig for positions 0 .. seq_len-1, fp16, already in the
-//                      MFMA B-operand order (angles reduced in fp64);
-//   rope_qproj_kernel  M per (sequence, query head): q rotated to its own
+//   rope_prep_kernel   one launch for two independent parts:
+//                      Trig for positions 0 .. seq_len-1, fp16, already in
+//                      the MFMA B-operand order (angles reduced in fp64);
+//                      M per (sequence, query head): q rotated to its own
 //                      position, A and C, the key latent's block rotation and
 //                      sm_scale * log2(e) folded in, fp16 in A-operand order;
 //   rope_score_kernel  per (split, group of 8 query heads, sequence): q~ for a
@@ -37,36 +38,42 @@ constexpr int kQtStride = 36;     // floats per token row of the transpose buffe
 
 // Trig[tile][s][j][lane][e] = T[i = 16 s + 8 (lane / 32) + e][token 64 tile +
 // 32 j + lane % 32], T[i][pos] = cos(pos w_i) (i < dh/2), sin(pos w_{i-dh/2}).
-__global__ __launch_bounds__(256) void rope_trig_kernel(int dh, int n_tiles,
-                                                        double log2_theta,
-                                                        _Float16* __restrict__ trig) {
-  const int per_tile = dh * 64;               // halves per tile
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)n_tiles * per_tile) return;
-  const int tile = (int)(idx / per_tile);
-  int r = (int)(idx % per_tile);
+// Item x (one thread) is a (pair p, position) and writes its cosine and its
+// sine: x's bits are e (3), lane % 32 (5), lane / 32 (1), j (1), then s for
+// p = 16 s + 8 (lane / 32) + e, so consecutive items write consecutive
+// halves.
+__device__ inline void rope_trig_pair(int dh, int n_tiles, double log2_theta,
+                                      _Float16* __restrict__ trig, size_t x) {
+  const int half = dh / 2;
+  const int per_tile = half * kTile;          // items per tile
+  if (x >= (size_t)n_tiles * per_tile) return;
+  const int tile = (int)(x / per_tile);
+  int r = (int)(x % per_tile);
   const int e = r & 7;
   r >>= 3;
-  const int lane = r & 63;
-  r >>= 6;
-  const int j = r & 1, s = r >> 1;
-  const int i = 16 * s + 8 * (lane >> 5) + e;
-  const int pos = tile * kTile + 32 * j + (lane & 31);
+  const int u = r & 31;
+  r >>= 5;
+  const int lh = r & 1;
+  r >>= 1;
+  const int j = r & 1, sp = r >> 1;
+  const int p = 16 * sp + 8 * lh + e;
+  const int pos = tile * kTile + 32 * j + u;
   float c, sn;
-  rope_angle(pos, i % (dh / 2), dh, log2_theta, &c, &sn);
-  trig[idx] = (_Float16)(i < dh / 2 ? c : sn);
+  rope_angle(pos, p, dh, log2_theta, &c, &sn);
+  _Float16* t = trig + (size_t)tile * dh * kTile + (32 * lh + u) * 8 + e;
+  t[(size_t)(2 * sp + j) * 512] = (_Float16)c;                     // row i = p
+  t[(size_t)(2 * (sp + half / 16) + j) * 512] = (_Float16)sn;      // row i = p + dh/2
 }
 
-// M for one (sequence, query head) = blockIdx.x, in A-operand order
+// M for one (sequence, query head) = bh, in A-operand order
 // frag[s][lane][e] = M[i = 16 s + 8 (lane / 32) + e][r = lane % 32].
-__global__ __launch_bounds__(256) void rope_qproj_kernel(const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ bk,
-                                                         Dims d, int q_pos,
-                                                         double log2_theta, float qscale,
-                                                         _Float16* __restrict__ mrec) {
+__device__ inline void rope_qproj_block(const uint16_t* __restrict__ q,
+                                        const uint16_t* __restrict__ bk, const Dims& d,
+                                        int q_pos, double log2_theta, float qscale,
+                                        _Float16* __restrict__ mrec, int bh) {
   __shared__ float qr[256];
   __shared__ float Mf[256][33];
-  const int bh = blockIdx.x, h = bh % d.Hq, g = h / d.G;
+  const int h = bh % d.Hq, g = h / d.G;
   const int t = threadIdx.x;
   const int half = d.dh / 2;
   // the query sits at its sequence's last position (ragged batches: its own)
@@ -119,6 +126,23 @@ __global__ __launch_bounds__(256) void rope_qproj_kernel(const uint16_t* __restr
     const int i = 16 * s + 8 * (lane >> 5) + e;
     mrec[(size_t)bh * ks * 512 + x] = (_Float16)(Mf[i][lane & 31] * qscale);
   }
+}
+
+// The rotary decode's first launch: blocks [0, trig_blocks) fill the trig
+// table, the next B Hq blocks compute the rotated query coefficients.
+__global__ __launch_bounds__(256) void rope_prep_kernel(int n_tiles, int trig_blocks,
+                                                        const uint16_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ bk, Dims d,
+                                                        int q_pos, double log2_theta,
+                                                        float qscale,
+                                                        _Float16* __restrict__ trig,
+                                                        _Float16* __restrict__ mrec) {
+  const int blk = blockIdx.x;
+  if (blk < trig_blocks) {
+    rope_trig_pair(d.dh, n_tiles, log2_theta, trig, (size_t)blk * 256 + threadIdx.x);
+    return;
+  }
+  rope_qproj_block(q, bk, d, q_pos, log2_theta, qscale, mrec, blk - trig_blocks);
 }
 
 template <int N>
@@ -351,18 +375,14 @@ hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_
                               hipEvent_t before_scores) {
   const double log2_theta = log2((double)d.rope_theta);
   const int n_tiles = (seq_len + kTile - 1) / kTile;
-  const size_t n_trig = (size_t)n_tiles * d.dh * kTile;
+  const size_t n_items = (size_t)n_tiles * (d.dh / 2) * kTile;   // (pair, position)
+  const int trig_blocks = (int)((n_items + 255) / 256);
   _Float16* trig = reinterpret_cast<_Float16*>(ws + rw.trig);
   _Float16* mrec = reinterpret_cast<_Float16*>(ws + rw.mrec);
-  rope_trig_kernel<<<(unsigned)((n_trig + 255) / 256), 256, 0, s>>>(d.dh, n_tiles,
-                                                                     log2_theta, trig);
+  rope_prep_kernel<<<(unsigned)(trig_blocks + d.B * d.Hq), 256, 0, s>>>(
+      n_tiles, trig_blocks, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(bk), d,
+      seq_len - 1, log2_theta, sm_scale * kLog2e, trig, mrec);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  rope_qproj_kernel<<<d.B * d.Hq, 256, 0, s>>>(static_cast<const uint16_t*>(q),
-                                                static_cast<const uint16_t*>(bk), d,
-                                                seq_len - 1, log2_theta,
-                                                sm_scale * kLog2e, mrec);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   RopeArgs a;
   a.d = d;
