@@ -240,14 +240,17 @@ def test_prefill_rotary_keys_full_size_sampled():
     dict(ctx=100, chunk=150, key_ranks=[8, 32, 16, 24, 8, 16, 32, 24]),
     dict(ctx=40, chunk=150, n_q_heads=16, n_kv_heads=2, head_dim=128),   # G = 8
     dict(ctx=90, chunk=100, n_q_heads=16, n_kv_heads=4, head_dim=128, value_rank=512),
+    # 16 KV heads (two per XCD in the workgroup order) and 3 query blocks
+    # of a ragged chunk, padded to 8
+    dict(ctx=77, chunk=600, n_q_heads=16, n_kv_heads=16, value_rank=512),
 ])
 def test_prefill_reconstructed_values(case):
     """Chunks long enough that the values of every visible position are
     reconstructed once per call (C Hq (R_v - d_h) > Hkv d_h R_v: eq. 12 in
     its left-hand order) and the attention contracts over d_h: the same
     bar against the oracle, with unused slots NaN-filled, the uniform 4-bit
-    cache, a peaked batch of two without rotation, per-head key ranks, G 8
-    and d_h 128."""
+    cache, a peaked batch of two without rotation, per-head key ranks, G 8,
+    d_h 128, and 16 KV heads over several query blocks."""
     kw = dict(SMALL)
     kw.update(case)
     ctx, chunk = kw.pop("ctx"), kw.pop("chunk")
