@@ -1332,13 +1332,23 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
                  (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
     }
     l_lane += ls;
-    // P (16 queries x 64 positions) times the tile's values
+    // P (16 queries x 64 positions) times the tile's values, four channel
+    // tiles at a time: their eight operand reads are issued before their
+    // eight MFMAs, which go K-step-major so that consecutive MFMAs are
+    // independent
 #pragma unroll
-    for (int t = 0; t < NCT; ++t) {
-      const int c = 16 * t + c16;
+    for (int t0 = 0; t0 < NCT; t0 += 4) {
+      h8 vo[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) vo[t][kk] = v_at(slot, 16 * (t0 + t) + c16, kk);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[kk], v_at(slot, c, kk), acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[kk], vo[t][kk], acc[t0 + t], 0, 0, 0);
     }
     wait_vmcnt<0>();      // this wave's staging of the next tile landed
   }
