@@ -1274,19 +1274,23 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
     lds_barrier();        // this tile's staging visible; the other slot free
     stage(tile + 1);
     // scores of the tile: x[bl][v] = position 16 bl + 4 g16 + v, query qi
+    // (K-step-major: each step's four key operands are read before its four
+    // MFMAs, which go to four different accumulators)
     float x[4][4];
+    f32x4v sc[4] = {f32x4v{}, f32x4v{}, f32x4v{}, f32x4v{}};
 #pragma unroll
-    for (int bl = 0; bl < 4; ++bl) {
-      h8 kb[KS];
+    for (int ks = 0; ks < KS; ++ks) {
+      h8 kb[4];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kb[ks] = key_at(slot, bl, ks);
-      f32x4v sc = f32x4v{};
+      for (int bl = 0; bl < 4; ++bl) kb[bl] = key_at(slot, bl, ks);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[ks], bq[ks], sc, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) x[bl][v] = sc[v];
+      for (int bl = 0; bl < 4; ++bl)
+        sc[bl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[bl], bq[ks], sc[bl], 0, 0, 0);
     }
+#pragma unroll
+    for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) x[bl][v] = sc[bl][v];
     if (tile * kTile + kTile - 1 > pfirst) {   // uniform: some token is hidden
       const int lim = qi < nq ? pfirst + qi - tile * kTile : -1;
 #pragma unroll
