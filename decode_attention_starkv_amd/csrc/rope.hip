@@ -245,6 +245,19 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
 
     const h8* tr = &trig_l[slot][0];
     const bool valid = tile * kTile + l < seq_len;
+    // q~ tiles of both heads: each trig operand is read once and feeds both
+    // heads' MFMAs (four independent accumulators)
+    f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const h8 t0 = tr[(2 * s2) * 64 + l], t1 = tr[(2 * s2 + 1) * 64 + l];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[0][s2], t0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[0][s2], t1, acc[0][1], 0, 0, 0);
+      if (on1) {
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[1][s2], t0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[1][s2], t1, acc[1][1], 0, 0, 0);
+      }
+    }
     float zf[32];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -280,13 +293,8 @@ __global__ __launch_bounds__(256) void rope_score_kernel(RopeArgs a) {
           }
         }
       }
-      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) {
-        const h8 t0 = tr[(2 * s2) * 64 + l], t1 = tr[(2 * s2 + 1) * 64 + l];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s2], t0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf[hh][s2], t1, acc1, 0, 0, 0);
-      }
+      const f32x16& acc0 = acc[hh][0];
+      const f32x16& acc1 = acc[hh][1];
       // D[r][token]: lane l holds token l % 32 (acc0) and 32 + l % 32 (acc1),
       // rows acc_row(v, l); through LDS so that lane = token
 #pragma unroll
