@@ -128,21 +128,22 @@ __device__ inline void rope_qproj_block(const uint16_t* __restrict__ q,
   }
 }
 
-// The rotary decode's first launch: blocks [0, trig_blocks) fill the trig
-// table, the next B Hq blocks compute the rotated query coefficients.
-__global__ __launch_bounds__(256) void rope_prep_kernel(int n_tiles, int trig_blocks,
+// The rotary decode's first launch: blocks [0, B Hq) compute the rotated
+// query coefficients (a chain of dependent steps each, so they go first and
+// overlap the table), the blocks after them fill the trig table.
+__global__ __launch_bounds__(256) void rope_prep_kernel(int n_tiles,
                                                         const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ bk, Dims d,
                                                         int q_pos, double log2_theta,
                                                         float qscale,
                                                         _Float16* __restrict__ trig,
                                                         _Float16* __restrict__ mrec) {
-  const int blk = blockIdx.x;
-  if (blk < trig_blocks) {
-    rope_trig_pair(d.dh, n_tiles, log2_theta, trig, (size_t)blk * 256 + threadIdx.x);
+  const int blk = blockIdx.x, nq = d.B * d.Hq;
+  if (blk < nq) {
+    rope_qproj_block(q, bk, d, q_pos, log2_theta, qscale, mrec, blk);
     return;
   }
-  rope_qproj_block(q, bk, d, q_pos, log2_theta, qscale, mrec, blk - trig_blocks);
+  rope_trig_pair(d.dh, n_tiles, log2_theta, trig, (size_t)(blk - nq) * 256 + threadIdx.x);
 }
 
 template <int N>
@@ -388,7 +389,7 @@ hipError_t launch_rope_scores(const Dims& d, const starkv_cache& cache, int seq_
   _Float16* trig = reinterpret_cast<_Float16*>(ws + rw.trig);
   _Float16* mrec = reinterpret_cast<_Float16*>(ws + rw.mrec);
   rope_prep_kernel<<<(unsigned)(trig_blocks + d.B * d.Hq), 256, 0, s>>>(
-      n_tiles, trig_blocks, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(bk), d,
+      n_tiles, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(bk), d,
       seq_len - 1, log2_theta, sm_scale * kLog2e, trig, mrec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
