@@ -72,6 +72,13 @@ def test_rope_mha(seq_len, splits):
                     n_q_heads=8, n_kv_heads=8, value_rank=256) <= TOL
 
 
+def test_rope_odd_head_count():
+    """Three query heads: the second score wave owns a single head, and the
+    MFMAs of its second head slot are skipped."""
+    assert run_rope("l2_q43", 500, 10000.0, n_q_heads=3, n_kv_heads=3,
+                    value_rank=256, q_scale=4.0) <= TOL
+
+
 def test_rope_gqa_base_5e5():
     assert run_rope("l3_gqa_q43", 1000, 500000.0, n_q_heads=8, n_kv_heads=2) <= TOL
 
