@@ -234,7 +234,8 @@ STARKV_API int starkv_decode(const starkv_config* cfg, const starkv_cache* cache
  * exactly starkv_append followed by starkv_decode (same bytes, same output),
  * but the append and the query projection share one launch (they are
  * independent; every cache kind except rotary keys), which saves launches
- * and overlaps their memory latencies.  Arguments as in those two calls; n == 0 decodes only.
+ * and overlaps their memory latencies.  Arguments as in those two calls;
+ * n == 0 decodes only.
  * Workspace: starkv_workspace_bytes(cfg, DECODE, pos + n).
  * Errors: EINVAL (pos < 0, n < 0, null or misaligned pointer), ECAPACITY
  * (pos + n > max_tokens), EWORKSPACE, EUNSUPPORTED, ELAUNCH. */
