@@ -1283,6 +1283,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_rec_kernel(RecArgs a) {
       h8 kb[4];
 #pragma unroll
       for (int bl = 0; bl < 4; ++bl) kb[bl] = key_at(slot, bl, ks);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int bl = 0; bl < 4; ++bl)
         sc[bl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[bl], bq[ks], sc[bl], 0, 0, 0);
