@@ -120,12 +120,10 @@ size_t cache_bytes(const starkv_config& c, int which) {
   }
 }
 
-// MI355X has 256 compute units; the split count fills every unit with as
-// many decode workgroups as stay resident on it.
-constexpr int kComputeUnits = 256;
-
 }  // namespace
 
+// The split count fills every compute unit with as many decode workgroups
+// as stay resident on it.
 int choose_splits(const starkv_config& c, int seq_len) {
   const int n_tiles = (seq_len + kTile - 1) / kTile;
   const int groups = kComputeUnits * decode_groups_per_cu(make_dims(c));

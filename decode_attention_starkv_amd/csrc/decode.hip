@@ -205,6 +205,10 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   const int tile0 = sp * a.tiles_per_split;
   const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
   const int GV = d.rv / 32;
+  // value slice blockIdx.z of gridDim.z: this workgroup contracts value
+  // groups [g_lo, g_hi) only (every slice scores all heads)
+  const int GVs = GV / (int)gridDim.z;
+  const int g_lo = (int)blockIdx.z * GVs, g_hi = g_lo + GVs;
 
   for (int i = tid; i < 2 * 32 * PS; i += 512) p_raw[i] = 0.0f;
   for (int i = tid; i < d.Hq * kPlainRec; i += 512)
@@ -232,13 +236,13 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
       const uint16_t* vbase = static_cast<const uint16_t*>(a.value);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int n = wave + ni * NW;
+        const int n = g_lo + wave + ni * NW;
         // K-step r, lane half j: tokens 16r + 8j .. +7 = token block 2r + j
         const uint16_t* zp =
-            vbase + (((size_t)b * d.NT + tile) * GV + min(n, GV - 1)) * (8 * 256) + (j * 32 + m) * 8;
+            vbase + (((size_t)b * d.NT + tile) * GV + min(n, g_hi - 1)) * (8 * 256) + (j * 32 + m) * 8;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          Zv[ni][r] = n < GV ? __builtin_nontemporal_load(reinterpret_cast<const bf8*>(zp + r * 512))
+          Zv[ni][r] = n < g_hi ? __builtin_nontemporal_load(reinterpret_cast<const bf8*>(zp + r * 512))
                              : bf8{};
       }
     };
@@ -290,8 +294,8 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
         }
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const int n = wave + ni * NW;
-          if (n < GV) {
+          const int n = g_lo + wave + ni * NW;
+          if (n < g_hi) {
             bf8 Z = Zv[ni][r];
             if (partial) {
               // unused cache slots never reach the operands
@@ -310,8 +314,8 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
       const float* vbase = static_cast<const float*>(a.value);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int n = wave + ni * NW;
-        if (n < GV) {
+        const int n = g_lo + wave + ni * NW;
+        if (n < g_hi) {
           const float* zp = vbase + (((size_t)b * d.NT + tile) * GV + n) * (8 * 256) + m * 8;
           for (int r = 0; r < 32; ++r) {
             const int u = 32 * j + r;
@@ -334,8 +338,10 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
         if (lane == 0) {
           const int h = kh * G + jj;
           l_row[h] = l;
-          a.part_ml[(obase + h) * 2] = m_ref[ki * G + jj];
-          a.part_ml[(obase + h) * 2 + 1] = l;
+          if (blockIdx.z == 0) {   // the same (m, l) in every value slice
+            a.part_ml[(obase + h) * 2] = m_ref[ki * G + jj];
+            a.part_ml[(obase + h) * 2 + 1] = l;
+          }
         }
       }
     }
@@ -363,8 +369,8 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
       const int c = lane + 64 * k;
       const int row = c / (NI * 4), q = c % (NI * 4);
       const int ni = q >> 2, part = q & 3;
-      const int n = wave + ni * NW;
-      if (row < d.Hq && n < GV) {
+      const int n = g_lo + wave + ni * NW;
+      if (row < d.Hq && n < g_hi) {
         const h8 o = *reinterpret_cast<const h8*>(&stg[wave][row][ni * 32 + part * 8]);
         __builtin_nontemporal_store(o, reinterpret_cast<h8*>(po + (obase + row) * d.rv + n * 32 + part * 8));
       }
@@ -372,8 +378,8 @@ __global__ __launch_bounds__(512) void split_kernel(SplitArgs a) {
   } else {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int n = wave + ni * NW;
-      if (n < GV) {
+      const int n = g_lo + wave + ni * NW;
+      if (n < g_hi) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = acc_row(v, lane);
@@ -822,7 +828,20 @@ hipError_t decode_fmt(const Dims& d, const starkv_cache& cache, int seq_len,
   sa.qt = qt;
   sa.part_o = part_o;
   sa.part_ml = part_ml;
-  e = launch_split<FMT>(d, dim3(lay.splits, d.B), sa, s);
+  // unquantized caches: when the splits leave compute units idle (short
+  // contexts, small batches), each tile's value groups are dealt out among
+  // up to 4 workgroups, which all score it: one unit fetches only about
+  // 1/256 of the chip's bandwidth, so fewer bytes per workgroup on more
+  // units finish sooner
+  int vslices = 1;
+  if constexpr (FMT != STARKV_CACHE_Q43) {
+    const int gv = d.rv / 32;
+    // (at least 8 groups per slice: one per wave)
+    while (vslices < 4 && lay.splits * d.B * vslices * 2 <= kComputeUnits &&
+           gv % (vslices * 2) == 0 && gv / (vslices * 2) >= 8)
+      vslices *= 2;
+  }
+  e = launch_split<FMT>(d, dim3(lay.splits, d.B, vslices), sa, s);
   if (e != hipSuccess) return e;
   mark(2);
   if (FMT != STARKV_CACHE_F32 && !latent_only && merge_vproj_fits(d, lay.splits)) {

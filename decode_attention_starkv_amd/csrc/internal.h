@@ -21,6 +21,7 @@ __host__ __device__ constexpr int value_tile_bytes(int rv, int lo_bits) {
 constexpr int kMaxQHeads = 32;     // rows of the stacked-head P operand
 constexpr int kDecodeWaves = 8;    // waves per decode workgroup
 constexpr int kMaxSplits = 1024;   // decode token splits per sequence
+constexpr int kComputeUnits = 256;  // MI355X compute units (split-count sizing)
 
 // Shape of one call, copied by value into every kernel.
 struct Dims {
